@@ -1,0 +1,330 @@
+"""CPU oracle for direct bitplane-prefix expert execution.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this module.  The product library never calls
+it, shares no code with it, and must fail loudly when its HIP build is absent.
+
+It is a plain, slow, obviously correct NumPy implementation: fp32 where the
+stored format is fp32 (the tree codebook), fp64 for every sum.
+
+Sources (titles of the pages the method is described on):
+  [T]   "PagedMoE: Cross-Precision Expert Caching for SSD-Resident MoE
+        Inference", podcast episode transcript; "T cN" = subtitle cue N.
+  [Abs] "PagedMoE: Cross-Precision Expert Caching for Token-Level Dynamic
+        Precision in SSD-Resident MoE Inference", arxivlens page, Abstract.
+  [Met] the same arxivlens page, Analysis, "Methodology".
+The numeric format (group size, fp32 nodes, MSB-first uint32 planes along the
+input dimension, SwiGLU experts, unweighted parent mean) is the workload's
+stated form; the pages leave it open.
+
+Pins: every function here is pinned in tests/test_oracle_pins.py against
+closed forms, library routines, hand-worked fixtures (tests/golden/) or brute
+force; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NBITS = 8                  # stored code width: 8 planes, 256 leaves per block
+NLEAF = 1 << NBITS
+
+
+# ---------------------------------------------------------------------------
+# Tree codebook  ([T] c19, c21; [Abs] "prefix-compatible tree codebook")
+# ---------------------------------------------------------------------------
+def tree_levels(leaves, counts=None, depth=NBITS):
+    """Levels of the binary-tree codebook over sorted leaves.
+
+    leaves: float32 [..., 2**depth], ascending along the last axis.  They are
+    the deepest level (depth `depth`).  Each parent is the mean of its two
+    children ([T] c19: parent = average of its two children), so node p at
+    depth d is the reconstruction of every code whose top d bits equal p
+    ([T] c21: truncating an index lands on a valid reconstruction).
+
+    counts=None: the unweighted mean, (left + right) * 0.5 in fp32.
+    counts: integer [..., 2**depth], how many weights landed on each leaf;
+    a parent is then the frequency-weighted mean of its children ([T] c19,
+    c21), evaluated in fp64 from the fp32 children and rounded to fp32; its
+    count is the sum of the children's.  A parent whose children hold no
+    weights falls back to the unweighted mean.
+
+    Returns {d: float32 [..., 2**d]} for d = 1..depth (depth 0, the root, is
+    not a usable prefix: k >= 1).
+    """
+    leaves = np.asarray(leaves, dtype=np.float32)
+    if leaves.shape[-1] != (1 << depth):
+        raise ValueError("last axis must hold 2**depth leaves")
+    if np.any(np.diff(leaves, axis=-1) < 0):
+        raise ValueError("leaves must be ascending")
+    levels = {depth: leaves.copy()}
+    node = leaves
+    cnt = None if counts is None else np.asarray(counts, dtype=np.float64)
+    for d in range(depth - 1, 0, -1):
+        left = node[..., 0::2]
+        right = node[..., 1::2]
+        if cnt is None:
+            parent = (left + right) * np.float32(0.5)
+        else:
+            nl = cnt[..., 0::2]
+            nr = cnt[..., 1::2]
+            tot = nl + nr
+            mean = (left + right) * np.float32(0.5)
+            with np.errstate(invalid="ignore", divide="ignore"):
+                wmean = (nl * left.astype(np.float64) + nr * right.astype(np.float64)) / tot
+            parent = np.where(tot > 0, wmean.astype(np.float32), mean)
+            cnt = tot
+        levels[d] = parent.astype(np.float32)
+        node = levels[d]
+    return levels
+
+
+def leaf_counts(codes, group):
+    """How many weights of each block landed on each leaf: int64
+    [rows][cols/group][256], the frequencies of the weighted tree ([T] c19)."""
+    codes = np.asarray(codes)
+    rows, cols = codes.shape
+    blocks = codes.reshape(rows, cols // group, group).astype(np.int64)
+    out = np.zeros((rows, cols // group, NLEAF), dtype=np.int64)
+    for g in range(cols // group):
+        for o in range(rows):
+            out[o, g] = np.bincount(blocks[o, g], minlength=NLEAF)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Bitplanes  ([T] c25: plane one holds the first index bit of every weight)
+# ---------------------------------------------------------------------------
+def pack_planes(codes):
+    """codes uint8 [rows][cols] -> uint32 [8][rows][cols/32].
+
+    Plane p holds bit (7 - p) of every code (MSB first: plane 0 is the first
+    index bit).  Along the input dimension the bits are packed 32 to a word:
+    bit j of word w is column 32*w + j.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, cols = codes.shape
+    if cols % 32:
+        raise ValueError("cols must be a multiple of 32")
+    c = codes.reshape(rows, cols // 32, 32).astype(np.uint32)
+    planes = np.zeros((NBITS, rows, cols // 32), dtype=np.uint32)
+    for p in range(NBITS):
+        bit = (c >> np.uint32(NBITS - 1 - p)) & np.uint32(1)
+        for j in range(32):
+            planes[p] |= bit[:, :, j] << np.uint32(j)
+    return planes
+
+
+def plane_bits(planes, p):
+    """Bit of plane p for every weight: uint8 [rows][cols]."""
+    w = np.asarray(planes[p], dtype=np.uint32)
+    rows, nw = w.shape
+    j = np.arange(32, dtype=np.uint32)
+    bits = (w[:, :, None] >> j[None, None, :]) & np.uint32(1)
+    return bits.reshape(rows, nw * 32).astype(np.uint8)
+
+
+def prefix_codes(planes, k):
+    """k-bit prefix of every weight, read from planes 0..k-1 only:
+    prefix = sum_{p<k} bit_p << (k-1-p).  Planes k..7 are never touched
+    ([T] c25: going from k-1 to k bits reads exactly one more plane)."""
+    if not 1 <= k <= NBITS:
+        raise ValueError("k must be in 1..8")
+    pre = None
+    for p in range(k):
+        b = plane_bits(planes, p).astype(np.int64)
+        pre = b if pre is None else (pre << 1) | b
+    return pre
+
+
+# ---------------------------------------------------------------------------
+# Decode and GEMV  ([Abs] "directly executes cached 1-8-bit prefixes";
+# [T] c37: indices assembled from the requested planes, codebook lookup,
+# dot product; no full-precision matrix is needed)
+# ---------------------------------------------------------------------------
+def dequant(planes, levels, k, group):
+    """W_k[o][i] = node at depth k of block (o, i // group) selected by the
+    k-bit prefix of (o, i).  float32 [rows][cols], exact table values."""
+    pre = prefix_codes(planes, k)
+    rows, cols = pre.shape
+    lv = levels[k]                                   # [rows][cols/group][2**k]
+    gidx = np.arange(cols) // group
+    return lv[np.arange(rows)[:, None], gidx[None, :], pre]
+
+
+def gemv(planes, levels, k, group, x):
+    """y[o] = sum_i W_k[o][i] * x[i] in fp64, with the error scale
+    S[o] = sum_i |W_k[o][i] * x[i]|.  Returns (y float64, S float64)."""
+    w = dequant(planes, levels, k, group).astype(np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    return w @ x, np.abs(w) @ np.abs(x)
+
+
+def gemv_materialized_fp16(planes, levels, k, group, x):
+    """The materialize-then-multiply comparator ([T] c37): the decoded matrix
+    is first written at fp16 (round to nearest even), then multiplied."""
+    w = dequant(planes, levels, k, group).astype(np.float16).astype(np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    return w @ x, np.abs(w) @ np.abs(x)
+
+
+def silu(z):
+    """z * sigmoid(z) = z / (1 + exp(-z)), fp64."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(expert, kg, ku, kd, x):
+    """One SwiGLU expert read at prefixes (kg, ku, kd) of gate, up, down.
+
+    expert: dict with 'planes' [3] (uint32 [8][rows][cols/32]), 'levels' [3]
+    ({d: fp32}), 'group'.  g = W_gate x, u = W_up x, h = silu(g) * u,
+    y = W_down h (fp64 throughout).  Returns dict with g, u, h, y and the
+    error scales Sg, Su, Sy (Sy computed with this h)."""
+    G = expert["group"]
+    g, sg = gemv(expert["planes"][0], expert["levels"][0], kg, G, x)
+    u, su = gemv(expert["planes"][1], expert["levels"][1], ku, G, x)
+    h = silu(g) * u
+    y, sy = gemv(expert["planes"][2], expert["levels"][2], kd, G, h)
+    return {"g": g, "u": u, "h": h, "y": y, "Sg": sg, "Su": su, "Sy": sy}
+
+
+def encode_expert(leaves_codes, group, weighted=False):
+    """Encode one expert from its [gate, up, down] (leaves, codes): the tree
+    levels of every block and the 8 bitplanes of every matrix."""
+    planes, levels = [], []
+    for lv, cd in leaves_codes:
+        counts = leaf_counts(cd, group) if weighted else None
+        levels.append(tree_levels(lv, counts))
+        planes.append(pack_planes(cd))
+    return {"planes": planes, "levels": levels, "group": group}
+
+
+# ---------------------------------------------------------------------------
+# Routing  ([T] c4: a router picks a few experts per token, weights sum to 1)
+# ---------------------------------------------------------------------------
+def route(logits, top_k):
+    """Top-k experts by descending logit (ties: lower index first) and their
+    softmax weights renormalised over the selected k, computed in fp64 and
+    rounded to fp32.  Returns (ids int32 [k], w float32 [k])."""
+    logits = np.asarray(logits, dtype=np.float32)
+    n = logits.shape[0]
+    order = sorted(range(n), key=lambda e: (-float(logits[e]), e))
+    ids = np.array(order[:top_k], dtype=np.int32)
+    sel = logits[ids].astype(np.float64)
+    ex = np.exp(sel - sel.max())
+    w = (ex / ex.sum()).astype(np.float32)
+    return ids, w
+
+
+# ---------------------------------------------------------------------------
+# Pre-I/O bit allocation  ([T] c29, c31; [Abs] "selects the required prefix
+# length before I/O using current routing weights and offline
+# expert-specific error profiles")
+# ---------------------------------------------------------------------------
+def isotonic_nonincreasing(d):
+    """Least-squares fit of a non-increasing sequence to d (pool adjacent
+    violators, equal weights)."""
+    blocks = []                        # [sum, count]
+    for v in d:
+        blocks.append([float(v), 1])
+        while len(blocks) > 1 and blocks[-2][0] / blocks[-2][1] < blocks[-1][0] / blocks[-1][1]:
+            s, c = blocks.pop()
+            blocks[-1][0] += s
+            blocks[-1][1] += c
+    out = []
+    for s, c in blocks:
+        out.extend([s / c] * c)
+    return np.array(out, dtype=np.float64)
+
+
+def repair_profile(err):
+    """Make a profile convex: the marginal gains err(b) - err(b+1) are
+    replaced by their non-increasing isotonic fit ([T] c31: each extra bit
+    must help less than the one before; profiles that do not are repaired by
+    isotonic regression).  err: float64 [nbits] for b = 1..nbits."""
+    err = np.asarray(err, dtype=np.float64)
+    gains = err[:-1] - err[1:]
+    fit = isotonic_nonincreasing(gains)
+    out = np.empty_like(err)
+    out[0] = err[0]
+    for b in range(1, err.shape[0]):
+        out[b] = out[b - 1] - fit[b - 1]
+    return out
+
+
+def allocate_bits(w, err, budget, kmin=1, kmax=NBITS):
+    """Greedy prefix-length allocation for one token ([T] c29).
+
+    Minimises sum_e w_e^2 * err_e(b_e) subject to sum_e b_e = budget: every
+    expert starts at kmin bits, then the single bit with the largest gain
+    w_e^2 * (err_e(b_e) - err_e(b_e + 1)) is granted, repeatedly, until the
+    budget is spent.  Profiles are repaired to convexity first ([T] c31), so
+    the granted bits of an expert always form a prefix.  Gains are compared in
+    fp64 as (w*w) * (err(b) - err(b+1)) with w widened from fp32; ties go to
+    the larger routing weight, then the lower slot.
+
+    w: float32 [n]; err: float64 [n][kmax] (err[e][b-1] for b = 1..kmax).
+    Returns int32 [n]."""
+    w = np.asarray(w, dtype=np.float32)
+    n = w.shape[0]
+    if not n * kmin <= budget <= n * kmax:
+        raise ValueError("budget outside [n*kmin, n*kmax]")
+    prof = [repair_profile(err[e]) for e in range(n)]
+    b = [kmin] * n
+    for _ in range(budget - n * kmin):
+        best = None
+        for e in range(n):
+            if b[e] >= kmax:
+                continue
+            wd = float(w[e])
+            gain = (wd * wd) * (prof[e][b[e] - 1] - prof[e][b[e]])
+            key = (gain, wd, -e)
+            if best is None or key > best[0]:
+                best = (key, e)
+        b[best[1]] += 1
+    return np.array(b, dtype=np.int32)
+
+
+# ---------------------------------------------------------------------------
+# Residency rule  ([T] c13, c35: a plane is usable only when every earlier
+# plane is resident; a request reads only the missing planes)
+# ---------------------------------------------------------------------------
+def missing_planes(resident, k):
+    """Planes (0-based) to fetch when `resident` leading planes are held and a
+    k-bit prefix is requested."""
+    return list(range(resident, k)) if resident < k else []
+
+
+# ---------------------------------------------------------------------------
+# One MoE layer for a batch of tokens
+# ---------------------------------------------------------------------------
+def moe_forward(experts, ids, w, k, x):
+    """y[t] = sum_j w[t][j] * FFN_{ids[t][j]}(x[t]) at prefixes k[t][j][0..2].
+
+    experts: {expert id: encoded expert}; ids int [B][topk]; w float32
+    [B][topk]; k int [B][topk][3]; x float32 [B][hidden].  Returns (y fp64
+    [B][hidden], S fp64 [B][hidden]) with S[t][o] = sum_j |w_tj| * Sy_tj[o]."""
+    B, topk = np.asarray(ids).shape
+    out = None
+    scale = None
+    for t in range(B):
+        yt = None
+        st = None
+        for j in range(topk):
+            e = int(ids[t][j])
+            r = expert_ffn(experts[e], int(k[t][j][0]), int(k[t][j][1]), int(k[t][j][2]), x[t])
+            wt = float(w[t][j])
+            yt = wt * r["y"] if yt is None else yt + wt * r["y"]
+            st = abs(wt) * r["Sy"] if st is None else st + abs(wt) * r["Sy"]
+        if out is None:
+            out = np.zeros((B, yt.shape[0]))
+            scale = np.zeros((B, yt.shape[0]))
+        out[t] = yt
+        scale[t] = st
+    return out, scale
+
+
+def within_tolerance(got, want, scale, rel=1e-4, abs_=1e-6):
+    """The acceptance bound |got - want| <= rel * scale + abs_ per output."""
+    got = np.asarray(got, dtype=np.float64)
+    return np.abs(got - want) <= rel * np.asarray(scale) + abs_

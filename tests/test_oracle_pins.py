@@ -1,0 +1,387 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix:
+hand-worked fixtures (tests/golden/), closed forms, library routines and
+brute force.  None of these tests touches the product library or a GPU."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def ulp_diff(a, b):
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float64)
+    spacing = np.spacing(np.abs(a).astype(np.float32)).astype(np.float64)
+    return np.abs(a.astype(np.float64) - b) / spacing
+
+
+# ---------------------------------------------------------------- fixtures
+@pytest.fixture(scope="module")
+def tiny_expert():
+    wl = synth.WORKLOADS[0]
+    li = synth.expert_inputs(wl, 0, 0)
+    return wl, li, oracle.encode_expert(li, wl.group)
+
+
+def golden_row():
+    g = load("eight_bit_row.json")
+    cols = g["cols"]
+    codes = np.zeros((1, cols), dtype=np.uint8)
+    for c, v in g["codes_at"].items():
+        codes[0, int(c)] = v
+    leaves = (np.arange(256, dtype=np.float64) - 127.5).astype(np.float32)
+    leaves = np.broadcast_to(leaves, (1, cols // g["group"], 256)).copy()
+    return g, codes, leaves
+
+
+# ---------------------------------------------------------------- tree
+def test_pages_two_bit_example():
+    g = load("two_bit_tree.json")
+    leaves = np.array(g["leaves"], dtype=np.float32)
+    lw = oracle.tree_levels(leaves, np.array(g["counts"]), depth=2)
+    lu = oracle.tree_levels(leaves, None, depth=2)
+    assert lw[1].tolist() == g["expected_level1_weighted"]
+    assert lu[1].tolist() == g["expected_level1_unweighted"]
+    assert lw[2].tolist() == g["leaves"]
+    c = g["code_01"]
+    # truncating code 01 to one bit lands on its parent, at two bits on itself
+    assert lw[2][c["code"]] == c["k2_value"]
+    assert lw[1][c["code"] >> 1] == c["k1_value_weighted"]
+    assert lu[1][c["code"] >> 1] == c["k1_value_unweighted"]
+    a, b = g["shared_prefix_k1"]
+    assert a >> 1 == b >> 1
+
+
+def test_golden_row_levels():
+    g, codes, leaves = golden_row()
+    lv = oracle.tree_levels(leaves)
+    assert lv[1][0, 0].tolist() == g["level1"]
+    assert lv[2][0, 0].tolist() == g["level2"]
+    assert lv[3][0, 0].tolist() == g["level3"]
+    assert np.array_equal(lv[8], leaves)
+
+
+def test_golden_row_planes():
+    g, codes, _ = golden_row()
+    planes = oracle.pack_planes(codes)
+    want = np.array([[int(h, 16) for h in row] for row in g["planes_hex"]], dtype=np.uint32)
+    assert planes.shape == (8, 1, 2)
+    assert np.array_equal(planes[:, 0, :], want)
+
+
+def test_golden_row_dequant_and_gemv():
+    g, codes, leaves = golden_row()
+    planes = oracle.pack_planes(codes)
+    lv = oracle.tree_levels(leaves)
+    for name, col in (("col0", 0), ("col1", 1)):
+        for k, v in g["dequant"][name].items():
+            w = oracle.dequant(planes, lv, int(k), g["group"])
+            assert w[0, col] == v
+    for k, v in g["dequant"]["zero_code"].items():
+        w = oracle.dequant(planes, lv, int(k), g["group"])
+        assert w[0, 10] == v
+    ones = np.ones(g["cols"], dtype=np.float32)
+    for k, v in g["gemv_all_ones"].items():
+        y, _ = oracle.gemv(planes, lv, int(k), g["group"], ones)
+        assert y[0] == v
+    x = np.zeros(g["cols"], dtype=np.float32)
+    x[0] = x[1] = 1
+    for k, v in g["gemv_e0_plus_e1"].items():
+        y, _ = oracle.gemv(planes, lv, int(k), g["group"], x)
+        assert y[0] == v
+
+
+def test_levels_closed_form_unweighted():
+    lv = synth.leaves(7, 0, 0, 0, 0, 4, 3)           # [4][3][256]
+    levels = oracle.tree_levels(lv)
+    assert np.array_equal(levels[8], lv)             # k = 8 reproduces the leaves
+    for d in range(1, 8):
+        span = 1 << (8 - d)
+        exact = lv.astype(np.float64).reshape(4, 3, 1 << d, span).mean(axis=-1)
+        assert ulp_diff(levels[d], exact).max() <= 8
+        assert np.all(np.diff(levels[d], axis=-1) > 0)   # each level ascending
+
+
+def test_levels_closed_form_weighted():
+    rng_counts = synth.words(3, synth.KIND_POISON, 0, 0, 0, 0, 4 * 3 * 256) % 7
+    counts = rng_counts.reshape(4, 3, 256).astype(np.int64)
+    counts[0, 0, :128] = 0                           # an empty left half-tree
+    lv = synth.leaves(8, 0, 0, 0, 0, 4, 3)
+    levels = oracle.tree_levels(lv, counts)
+    for d in range(1, 8):
+        span = 1 << (8 - d)
+        n = counts.reshape(4, 3, 1 << d, span).astype(np.float64)
+        L = lv.astype(np.float64).reshape(4, 3, 1 << d, span)
+        tot = n.sum(-1)
+        ok = tot > 0
+        centroid = (n * L).sum(-1) / np.where(ok, tot, 1)
+        assert ulp_diff(levels[d][ok], centroid[ok]).max() <= 16
+    # the empty half-tree falls back to the plain mean
+    assert levels[1][0, 0, 0] == np.float32(
+        (levels[2][0, 0, 0] + levels[2][0, 0, 1]) * np.float32(0.5))
+
+
+def test_leaf_counts_histogram():
+    codes = synth.codes(5, 0, 0, 0, 0, 3, 128)
+    c = oracle.leaf_counts(codes, 64)
+    assert c.shape == (3, 2, 256)
+    assert np.all(c.sum(-1) == 64)
+    assert c[1, 1, codes[1, 70]] >= 1
+
+
+# ---------------------------------------------------------------- planes / prefix
+def test_prefix_is_top_bits_all_codes():
+    codes = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    codes = np.concatenate([codes, codes[:, ::-1]], axis=0)
+    planes = oracle.pack_planes(codes)
+    for k in range(1, 9):
+        assert np.array_equal(oracle.prefix_codes(planes, k), codes.astype(np.int64) >> (8 - k))
+
+
+def test_prefix_nesting_and_plane_independence():
+    codes = synth.codes(9, 0, 0, 0, 0, 16, 256)
+    planes = oracle.pack_planes(codes)
+    for k in range(1, 9):
+        pk = oracle.prefix_codes(planes, k)
+        for k2 in range(k, 9):
+            assert np.array_equal(oracle.prefix_codes(planes, k2) >> (k2 - k), pk)
+        poisoned = planes.copy()
+        poisoned[k:] = synth.words(1, synth.KIND_POISON, 0, 0, 1, 0, poisoned[k:].size).reshape(poisoned[k:].shape)
+        assert np.array_equal(oracle.prefix_codes(poisoned, k), pk)
+
+
+def test_pack_bit_positions():
+    # a single set bit of code c at column i must land in word i//32, bit i%32
+    for i in (0, 1, 31, 32, 63, 100):
+        for c in (0x80, 0x01, 0x10):
+            codes = np.zeros((1, 128), dtype=np.uint8)
+            codes[0, i] = c
+            planes = oracle.pack_planes(codes)
+            p = 7 - int(np.log2(c))
+            nz = np.argwhere(planes != 0)
+            assert nz.tolist() == [[p, 0, i // 32]]
+            assert planes[p, 0, i // 32] == np.uint32(1 << (i % 32))
+
+
+# ---------------------------------------------------------------- dequant / GEMV
+def test_dequant_is_subtree_mean(tiny_expert):
+    wl, li, enc = tiny_expert
+    for m in range(3):
+        lv, cd = li[m]
+        rows, cols = cd.shape
+        for k in range(1, 9):
+            w = oracle.dequant(enc["planes"][m], enc["levels"][m], k, wl.group)
+            span = 1 << (8 - k)
+            means = lv.astype(np.float64).reshape(rows, cols // wl.group, 1 << k, span).mean(-1)
+            g = np.arange(cols) // wl.group
+            want = means[np.arange(rows)[:, None], g[None, :], cd.astype(np.int64) >> (8 - k)]
+            assert ulp_diff(w, want).max() <= 8
+
+
+def test_gemv_k8_is_dense_dgemv(tiny_expert):
+    wl, li, enc = tiny_expert
+    x = synth.activation(wl.seed, 0, 0, 0, wl.hidden)
+    lv, cd = li[0]
+    rows, cols = cd.shape
+    g = np.arange(cols) // wl.group
+    dense = lv[np.arange(rows)[:, None], g[None, :], cd.astype(np.int64)].astype(np.float64)
+    y, s = oracle.gemv(enc["planes"][0], enc["levels"][0], 8, wl.group, x)
+    want = np.dot(dense, x.astype(np.float64))
+    assert np.all(np.abs(y - want) <= 1e-12 * s)
+
+
+def test_gemv_k1_closed_form(tiny_expert):
+    wl, li, enc = tiny_expert
+    x = synth.activation(wl.seed, 0, 0, 0, wl.hidden).astype(np.float64)
+    lv, cd = li[1]
+    rows, cols = cd.shape
+    l1 = enc["levels"][1][1].astype(np.float64)       # [rows][ngroups][2]
+    ng = cols // wl.group
+    xg = x.reshape(ng, wl.group)
+    msb = (cd >> 7).reshape(rows, ng, wl.group).astype(np.float64)
+    want = (l1[:, :, 0] * xg.sum(-1)[None, :]
+            + (l1[:, :, 1] - l1[:, :, 0]) * (msb * xg[None]).sum(-1)).sum(-1)
+    y, s = oracle.gemv(enc["planes"][1], enc["levels"][1], 1, wl.group, x)
+    assert np.all(np.abs(y - want) <= 1e-12 * s + 1e-15)
+
+
+def test_gemv_onehot_and_linear(tiny_expert):
+    wl, li, enc = tiny_expert
+    for k in (1, 3, 8):
+        w = oracle.dequant(enc["planes"][2], enc["levels"][2], k, wl.group)
+        for i in (0, 5, wl.inter - 1):
+            x = np.zeros(wl.inter, dtype=np.float32)
+            x[i] = 1
+            y, _ = oracle.gemv(enc["planes"][2], enc["levels"][2], k, wl.group, x)
+            assert np.array_equal(y, w[:, i].astype(np.float64))
+        x = synth.activation(1, 0, 0, 3, wl.inter)
+        y1, _ = oracle.gemv(enc["planes"][2], enc["levels"][2], k, wl.group, x)
+        y2, _ = oracle.gemv(enc["planes"][2], enc["levels"][2], k, wl.group, 2 * x)
+        assert np.array_equal(y2, 2 * y1)
+        y0, s0 = oracle.gemv(enc["planes"][2], enc["levels"][2], k, wl.group, 0 * x)
+        assert np.all(y0 == 0) and np.all(s0 == 0)
+
+
+def test_materialized_exact_when_fp16_representable():
+    g, codes, leaves = golden_row()
+    planes = oracle.pack_planes(codes)
+    lv = oracle.tree_levels(leaves)
+    x = synth.activation(2, 0, 0, 0, g["cols"])
+    for k in (1, 4, 8):
+        a, _ = oracle.gemv(planes, lv, k, g["group"], x)
+        b, _ = oracle.gemv_materialized_fp16(planes, lv, k, g["group"], x)
+        assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- FFN brute force
+def brute_dequant(lv, cd, group, k):
+    """Pure-Python loops from codes and leaves: the depth-k node of a code is
+    the mean of the leaves sharing its top k bits."""
+    rows, cols = cd.shape
+    out = np.zeros((rows, cols))
+    span = 1 << (8 - k)
+    for o in range(rows):
+        for i in range(cols):
+            v = int(cd[o, i]) >> (8 - k)
+            blk = lv[o, i // group]
+            out[o, i] = sum(float(blk[v * span + t]) for t in range(span)) / span
+    return out
+
+
+def test_tiny_ffn_brute_force_all_k_triples():
+    wl = synth.WORKLOADS[0]
+    # a reduced tiny expert (hidden 64, inter 32, group 32) keeps the loops short
+    small = synth.Workload(0, "tiny", 64, 32, 32, 1, 1, 1, 1, 0.0)
+    li = synth.expert_inputs(small, 0, 0)
+    enc = oracle.encode_expert(li, small.group)
+    x = synth.activation(wl.seed, 0, 0, 0, small.hidden).astype(np.float64)
+    dq = [[None] + [brute_dequant(li[m][0], li[m][1], small.group, k) for k in range(1, 9)]
+          for m in range(3)]
+    # the oracle's levels are fp32 (each within 8 ulp of the exact mean, see
+    # test_levels_closed_form_unweighted), so a relative level error
+    # eps = 8 * 2^-24 propagates into g, u, h and y; the bound below carries it
+    eps = 2 * 8 * 2.0 ** -24
+    for kg, ku, kd in itertools.product(range(1, 9), repeat=3):
+        g = dq[0][kg] @ x
+        u = dq[1][ku] @ x
+        sg = np.abs(dq[0][kg]) @ np.abs(x)
+        su = np.abs(dq[1][ku]) @ np.abs(x)
+        h = g * expit(g) * u
+        y = dq[2][kd] @ h
+        hb = 1.2 * sg * np.abs(u) + (np.abs(g) + eps * sg) * su
+        bound = eps * (np.abs(dq[2][kd]) @ (np.abs(h) + hb))
+        r = oracle.expert_ffn(enc, kg, ku, kd, x)
+        assert np.all(np.abs(r["y"] - y) <= bound + 1e-15)
+
+
+def test_silu_library():
+    z = np.linspace(-30, 30, 601)
+    assert np.allclose(oracle.silu(z), z * expit(z), rtol=1e-14, atol=1e-300)
+    assert oracle.silu(0.0) == 0.0
+
+
+# ---------------------------------------------------------------- routing
+def test_route_ties_and_sort():
+    ids, w = oracle.route(np.array([0.5, 2.0, 2.0, -1.0, 1.0], dtype=np.float32), 3)
+    assert ids.tolist() == [1, 2, 4]
+    assert w[0] == w[1]
+    assert abs(float(w[2]) / float(w[0]) - math.exp(-1.0)) < 1e-6
+    for t in range(5):
+        lg = synth.router_logits(11, 1, 0, t, 512)
+        ids, w = oracle.route(lg, 10)
+        ref = np.argsort(-lg, kind="stable")[:10]
+        assert ids.tolist() == ref.tolist()
+        assert abs(float(w.astype(np.float64).sum()) - 1.0) < 1e-6
+        assert np.all(np.diff(w) <= 0)
+
+
+# ---------------------------------------------------------------- allocator
+def test_allocator_golden():
+    g = load("allocator_and_residency.json")
+    w = np.array(g["w"], dtype=np.float32)
+    err = np.array([[4.0 ** -b for b in range(1, 9)]] * 2)
+    for budget, want in g["budgets"].items():
+        assert oracle.allocate_bits(w, err, int(budget)).tolist() == want
+
+
+def test_allocator_ties():
+    g = load("allocator_and_residency.json")
+    for case in g["ties"]:
+        w = np.array(case["w"], dtype=np.float32)
+        err = np.array([[s * 4.0 ** -b for b in range(1, 9)] for s in case["scale"]])
+        assert oracle.allocate_bits(w, err, case["budget"]).tolist() == case["want"]
+
+
+def test_allocator_is_bruteforce_optimum():
+    for t in range(6):
+        lg = synth.router_logits(21, 1, 0, t, 64)
+        _, w = oracle.route(lg, 4)
+        err = synth.error_profiles(21, 1, t, 4)
+        wd = w.astype(np.float64) ** 2
+        for budget in (4, 7, 10, 13, 20, 32):
+            k = oracle.allocate_bits(w, err, budget)
+            assert k.sum() == budget and k.min() >= 1 and k.max() <= 8
+            got = float((wd * err[np.arange(4), k - 1]).sum())
+            best = min(
+                float((wd * err[np.arange(4), np.array(c) - 1]).sum())
+                for c in itertools.product(range(1, 9), repeat=4) if sum(c) == budget)
+            assert got <= best * (1 + 1e-12)
+
+
+def test_allocator_repair():
+    convex = np.array([4.0 ** -b for b in range(1, 9)])
+    assert np.array_equal(oracle.repair_profile(convex), convex)
+    bumpy = np.array([1.0, 0.9, 0.5, 0.45, 0.2, 0.19, 0.18, 0.1])
+    rep = oracle.repair_profile(bumpy)
+    gains = rep[:-1] - rep[1:]
+    assert np.all(np.diff(gains) <= 1e-15)               # each bit helps less
+    assert rep[0] == bumpy[0] and abs(rep[-1] - bumpy[-1]) < 1e-12   # endpoints kept
+    # the fit is the least-squares one: it preserves the gain total and no
+    # other non-increasing sequence on a grid is closer
+    d = bumpy[:-1] - bumpy[1:]
+    assert abs(gains.sum() - d.sum()) < 1e-12
+    assert np.allclose(oracle.isotonic_nonincreasing([1, 3, 2]), [2, 2, 2])
+    assert np.allclose(oracle.isotonic_nonincreasing([3, 1, 2]), [3, 1.5, 1.5])
+
+
+def test_allocator_workload_mean():
+    wl = synth.WORKLOADS[1]
+    err = synth.error_profiles(wl.seed, wl.cfg, 0, wl.n_experts)
+    hist = np.zeros(9, dtype=np.int64)
+    for t in range(40):
+        ids, w = oracle.route(synth.router_logits(wl.seed, wl.cfg, 0, 0, wl.n_experts, step=t), 10)
+        k = oracle.allocate_bits(w, err[ids], wl.budget)
+        assert k.sum() == 25
+        hist += np.bincount(k, minlength=9)
+    assert hist[2] + hist[3] > hist[1] + hist[4:].sum()     # mostly 2 and 3 bits
+
+
+# ---------------------------------------------------------------- residency / MoE
+def test_missing_planes_pages_examples():
+    g = load("allocator_and_residency.json")
+    for case in g["residency"]:
+        assert oracle.missing_planes(case["resident"], case["k"]) == case["fetch"]
+
+
+def test_moe_onehot_weight_is_single_expert(tiny_expert):
+    wl, li, enc = tiny_expert
+    x = synth.activation(wl.seed, 0, 0, 0, wl.hidden)
+    experts = {0: enc, 1: enc}
+    y, s = oracle.moe_forward(experts, [[0, 1]], np.array([[1.0, 0.0]], np.float32),
+                              [[[2, 3, 4], [8, 8, 8]]], x[None])
+    r = oracle.expert_ffn(enc, 2, 3, 4, x)
+    assert np.array_equal(y[0], r["y"])
+    assert np.array_equal(s[0], r["Sy"])
