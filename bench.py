@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of direct bitplane-prefix expert execution on one MI355X.
+
+A step is one pm_moe_token_forward: one decode token through one MoE layer
+of 512 SwiGLU experts (hidden 4096, intermediate 1024, group 128), top-10
+routing, per-expert prefixes from the greedy allocator at a mean of 2.5 bits.
+Every step draws a fresh token (router logits, activation), so consecutive
+steps read different experts of the 512-expert pool (109 GB in HBM) and the
+256 MB Infinity Cache cannot serve repeated reads.
+
+The JSON line reports achieved GB/s on the algorithmic bytes (planes 0..k-1
+plus depth-k codebook nodes of every selected matrix, plus x and y), the rate
+of expert GEMVs, the roofline of the dominant kernel (HIP events on the
+library's stream) and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) + expert-GEMVs/s at avg 2.5-bit prefixes"
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def matrix_bytes(rows, cols, group, k):
+    """Bytes one matrix read at prefix k moves: planes 0..k-1 and the depth-k
+    nodes of every block."""
+    return rows * cols * k // 8 + rows * (cols // group) * (1 << k) * 4
+
+
+def step_bytes(wl, kk):
+    """Algorithmic bytes of one token-layer step: payload of the 30 matrices
+    at their prefixes, x read, y written (h is internal and not counted)."""
+    b = 0
+    for k3 in kk:
+        for m in range(3):
+            r, c = (wl.inter, wl.hidden) if m < 2 else (wl.hidden, wl.inter)
+            b += matrix_bytes(r, c, wl.group, int(k3[m]))
+    return b + 2 * wl.hidden * 4
+
+
+def gateup_bytes(wl, kk):
+    b = 0
+    for k3 in kk:
+        for m in range(2):
+            b += matrix_bytes(wl.inter, wl.hidden, wl.group, int(k3[m]))
+    return b + wl.hidden * 4
+
+
+def cpu_baseline(wl, plans, budget_s):
+    """The oracle, untouched, on a bounded sample: the first token's 10
+    experts, every matrix restricted to its first 256 rows, repeated until
+    about budget_s seconds of oracle time.  BLAS is held to one thread."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:
+        limiter = None
+    ids, w, kk = plans[0]
+    rows = 256
+    mats = []
+    nbytes = 0
+    for j in range(len(ids)):
+        for m in range(3):
+            R, C = synth.matrix_shape(wl, m)
+            lv = synth.leaves(wl.seed, wl.cfg, 0, int(ids[j]), m, R, C // wl.group, 0, rows)
+            cd = synth.codes(wl.seed, wl.cfg, 0, int(ids[j]), m, R, C, 0, rows)
+            x = synth.activation(wl.seed, wl.cfg, 0, 0, C)
+            mats.append((oracle.pack_planes(cd), oracle.tree_levels(lv), int(kk[j][m]), x))
+            nbytes += matrix_bytes(rows, C, wl.group, int(kk[j][m]))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for pl, lvl, k, x in mats:
+            oracle.gemv(pl, lvl, k, wl.group, x)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    gbs = nbytes * reps / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{len(mats)} matrices (10 experts x gate/up/down of step 0) x first "
+                       f"{rows} rows, {reps} passes, {el:.1f} s; numpy fp64, 1 BLAS thread"),
+            "expert_gemvs_per_s": round(len(mats) * reps / el * (rows / 1024) / 1.0, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--experts", type=int, default=512)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the path is built and timed on a single MI355X)", file=sys.stderr)
+        return 2
+
+    import torch
+    import bitplane_quantized_expert_amd as pm
+    import synth
+    from synth.pool import PoolFiller
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    wl = synth.WORKLOADS[1]
+    n_exp = args.experts
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    st = pm.pm_store_create(e, 1, wl.n_experts)
+    filler = PoolFiller(wl)
+    t0 = time.time()
+    for i in range(n_exp):
+        filler.fill(st, 0, i)
+        if i % 64 == 63:
+            torch.cuda.synchronize()
+            log(f"filled {i + 1}/{n_exp} experts ({time.time() - t0:.1f} s)")
+    torch.cuda.synchronize()
+    log(f"pool ready: {n_exp} experts, {time.time() - t0:.1f} s")
+
+    # per-step inputs: fresh token, product routing and allocation
+    total = args.warmup + args.steps
+    err = synth.error_profiles(wl.seed, wl.cfg, 0, wl.n_experts)
+    logits = np.stack([synth.router_logits(wl.seed, wl.cfg, 0, 0, wl.n_experts, step=s)
+                       for s in range(total)])
+    if n_exp < wl.n_experts:
+        logits[:, n_exp:] = -np.inf
+    ids, w = pm.pm_route_topk(logits, wl.top_k)
+    kk = pm.pm_allocate_bits(ids, w, err, wl.budget)
+    k3 = np.repeat(kk[:, :, None], 3, axis=2)
+    x = torch.from_numpy(np.stack([synth.activation(wl.seed, wl.cfg, 0, 0, wl.hidden, step=s)
+                                   for s in range(total)])).cuda()
+    y = torch.empty_like(x)
+    plans = [(ids[s], w[s], k3[s]) for s in range(total)]
+    stream = torch.cuda.current_stream()
+    log(f"inputs ready: {total} tokens, mean k {kk.mean():.3f}")
+
+    def run(s):
+        pm.pm_moe_token_forward(st, 0, ids[s:s + 1], w[s:s + 1], k3[s:s + 1], x[s:s + 1],
+                                y[s:s + 1], stream)
+
+    for s in range(args.warmup):
+        run(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, total):
+        run(s)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    steps = range(args.warmup, total)
+    nbytes = sum(step_bytes(wl, k3[s]) for s in steps)
+    gbs = nbytes / el / 1e9
+    ms = el / args.steps * 1e3
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step, {gbs:.1f} GB/s")
+
+    # roofline pass: HIP events around each stage on the library's stream
+    evs = []
+    for s in steps:
+        four = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for ev in four:
+            ev.record(stream)
+        evs.append(four)
+    torch.cuda.synchronize()
+    for s, four in zip(steps, evs):
+        pm.pm_store_set_profile_events(st, four)
+        run(s)
+    pm.pm_store_set_profile_events(st, [])
+    torch.cuda.synchronize()
+    gu_ms = np.array([a.elapsed_time(b) for a, b, _, _ in evs])
+    dn_ms = np.array([b.elapsed_time(c) for _, b, c, _ in evs])
+    cb_ms = np.array([c.elapsed_time(d) for _, _, c, d in evs])
+    gu_b = np.array([gateup_bytes(wl, k3[s]) for s in steps])
+    achieved = float(gu_b.mean() / (gu_ms.mean() * 1e-3) / 1e9)
+    log(f"gate/up {gu_ms.mean() * 1e3:.1f} us, down {dn_ms.mean() * 1e3:.1f} us, "
+        f"combine {cb_ms.mean() * 1e3:.1f} us; gate/up {achieved:.1f} GB/s")
+
+    out = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "experts": wl.n_experts, "hidden": wl.hidden,
+                   "inter": wl.inter, "group": wl.group, "top_k": wl.top_k, "batch": 1,
+                   "mean_k": round(float(kk[args.warmup:].mean()), 4), "pool_experts": n_exp},
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "expert_gemvs_per_s": round(3 * wl.top_k * args.steps / el, 1),
+        "stage_us": {"gateup": round(gu_ms.mean() * 1e3, 2), "down": round(dn_ms.mean() * 1e3, 2),
+                     "combine": round(cb_ms.mean() * 1e3, 2)},
+        "roofline": {"bound": "hbm", "kernel": "gateup", "achieved": round(achieved, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(wl, plans, args.cpu_seconds)
+    st.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

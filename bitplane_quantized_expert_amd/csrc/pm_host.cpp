@@ -1,0 +1,885 @@
+// Host side of libpm: argument validation, the offline encoder, routing, the
+// pre-I/O bit allocator, the plane store and the orchestration of one MoE
+// layer.  Every device computation is a HIP kernel in pm_kernels.hip.
+#include <algorithm>
+#include <array>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "pm_internal.h"
+
+using namespace pm;
+
+// ---------------------------------------------------------------- errors
+static thread_local std::string g_last_error;
+
+static pm_status fail(pm_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+static pm_status hip_fail(hipError_t e, const char* what) {
+    return fail(PM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr)                                           \
+    do {                                                        \
+        hipError_t _e = (expr);                                 \
+        if (_e != hipSuccess) return hip_fail(_e, #expr);       \
+    } while (0)
+
+extern "C" const char* pm_last_error(void) { return g_last_error.c_str(); }
+extern "C" const char* pm_version(void) { return "libpm 0.1 (gfx950)"; }
+
+// ---------------------------------------------------------------- shapes
+static bool shape_ok(pm_matrix_shape s) {
+    return s.rows >= 0 && s.cols >= 0 && s.group >= 32 && s.group % 32 == 0 &&
+           s.cols % s.group == 0;
+}
+
+static pm_status check_shape(pm_matrix_shape s) {
+    if (!shape_ok(s))
+        return fail(PM_ERR_SHAPE,
+                    "shape rows=%d cols=%d group=%d: need rows>=0, group a positive "
+                    "multiple of 32, cols a multiple of group",
+                    s.rows, s.cols, s.group);
+    return PM_OK;
+}
+
+static pm_status check_k(int k) {
+    if (k < 1 || k > kBits) return fail(PM_ERR_PREFIX, "prefix k=%d outside 1..8", k);
+    return PM_OK;
+}
+
+static size_t nblocks(pm_matrix_shape s) { return size_t(s.rows) * size_t(s.cols / s.group); }
+
+extern "C" size_t pm_plane_words(pm_matrix_shape s) {
+    return shape_ok(s) ? size_t(s.rows) * size_t(s.cols) / 32 : 0;
+}
+extern "C" size_t pm_levels_floats(pm_matrix_shape s) {
+    return shape_ok(s) ? nblocks(s) * kLevelFloatsPerBlock : 0;
+}
+extern "C" size_t pm_level_offset(pm_matrix_shape s, int d) {
+    if (!shape_ok(s) || d < 1 || d > kBits) return size_t(-1);
+    return level_offset(nblocks(s), d);
+}
+
+static bool expert_ok(pm_expert_shape e) {
+    return e.hidden > 0 && e.inter > 0 && e.group >= 32 && e.group % 32 == 0 &&
+           e.hidden % e.group == 0 && e.inter % e.group == 0;
+}
+
+static pm_matrix_shape matrix_of(pm_expert_shape e, int m) {
+    if (m == 2) return pm_matrix_shape{e.hidden, e.inter, e.group};
+    return pm_matrix_shape{e.inter, e.hidden, e.group};
+}
+
+extern "C" size_t pm_expert_plane_words(pm_expert_shape e) {
+    if (!expert_ok(e)) return 0;
+    return 2 * pm_plane_words(matrix_of(e, 0)) + pm_plane_words(matrix_of(e, 2));
+}
+extern "C" size_t pm_expert_levels_floats(pm_expert_shape e) {
+    if (!expert_ok(e)) return 0;
+    return 2 * pm_levels_floats(matrix_of(e, 0)) + pm_levels_floats(matrix_of(e, 2));
+}
+extern "C" pm_status pm_expert_matrix_offsets(pm_expert_shape e, int m, size_t* pw, size_t* lf,
+                                              pm_matrix_shape* shape_out) {
+    if (!expert_ok(e)) return fail(PM_ERR_SHAPE, "invalid expert shape");
+    if (m < 0 || m > 2) return fail(PM_ERR_ARG, "matrix index %d outside 0..2", m);
+    size_t p = 0, l = 0;
+    for (int i = 0; i < m; ++i) {
+        p += pm_plane_words(matrix_of(e, i));
+        l += pm_levels_floats(matrix_of(e, i));
+    }
+    if (pw) *pw = p;
+    if (lf) *lf = l;
+    if (shape_out) *shape_out = matrix_of(e, m);
+    return PM_OK;
+}
+
+static Geom make_geom(pm_expert_shape e) {
+    Geom g{};
+    g.hidden = e.hidden;
+    g.inter = e.inter;
+    g.group = e.group;
+    g.plane_words = pm_expert_plane_words(e);
+    for (int m = 0; m < 3; ++m) {
+        pm_matrix_shape s;
+        pm_expert_matrix_offsets(e, m, &g.plane_off[m], &g.level_off[m], &s);
+        g.rows[m] = s.rows;
+        g.cols[m] = s.cols;
+    }
+    return g;
+}
+
+// ---------------------------------------------------------------- host encoder
+// The tree rule of the stored format: parent = (left + right) * 0.5f, or the
+// count-weighted mean in fp64 when counts are given.  Compiled without FP
+// contraction so both rules round exactly as written.
+static pm_status encode_host(pm_matrix_shape s, const uint8_t* codes, const float* leaves,
+                             const uint32_t* counts, uint32_t* planes, size_t pstride,
+                             float* levels) {
+    const int W = s.cols / 32;
+    const int nb_row = s.cols / s.group;
+    const size_t nb = nblocks(s);
+    for (size_t b = 0; b < nb; ++b) {
+        const float* lf = leaves + b * kLeaves;
+        for (int v = 1; v < kLeaves; ++v)
+            if (!(lf[v - 1] <= lf[v]))
+                return fail(PM_ERR_ARG, "leaves of block %zu are not ascending at %d", b, v);
+    }
+    for (int p = 0; p < kBits; ++p) {
+        for (int o = 0; o < s.rows; ++o) {
+            for (int w = 0; w < W; ++w) {
+                const uint8_t* c = codes + size_t(o) * s.cols + size_t(32) * w;
+                uint32_t word = 0;
+                for (int j = 0; j < 32; ++j) word |= uint32_t((c[j] >> (7 - p)) & 1u) << j;
+                planes[size_t(p) * pstride + size_t(o) * W + w] = word;
+            }
+        }
+    }
+    std::vector<float> node(kLeaves), parent(kLeaves);
+    std::vector<uint64_t> cnt(kLeaves), pcnt(kLeaves);
+    for (size_t b = 0; b < nb; ++b) {
+        (void)nb_row;
+        const float* lf = leaves + b * kLeaves;
+        for (int v = 0; v < kLeaves; ++v) {
+            node[v] = lf[v];
+            cnt[v] = counts ? counts[b * kLeaves + v] : 0;
+        }
+        float* out8 = levels + level_offset(nb, kBits) + (b << kBits);
+        for (int v = 0; v < kLeaves; ++v) out8[v] = node[v];
+        for (int d = kBits - 1; d >= 1; --d) {
+            const int n = 1 << d;
+            for (int p = 0; p < n; ++p) {
+                const float L = node[2 * p], R = node[2 * p + 1];
+                const float mean = (L + R) * 0.5f;
+                if (counts) {
+                    const uint64_t nl = cnt[2 * p], nr = cnt[2 * p + 1];
+                    const uint64_t tot = nl + nr;
+                    if (tot > 0) {
+                        const double num = double(nl) * double(L) + double(nr) * double(R);
+                        parent[p] = float(num / double(tot));
+                    } else {
+                        parent[p] = mean;
+                    }
+                    pcnt[p] = tot;
+                } else {
+                    parent[p] = mean;
+                }
+            }
+            float* out = levels + level_offset(nb, d) + (b << d);
+            for (int p = 0; p < n; ++p) {
+                out[p] = parent[p];
+                node[p] = parent[p];
+                cnt[p] = pcnt[p];
+            }
+        }
+    }
+    return PM_OK;
+}
+
+extern "C" pm_status pm_encode_matrix(pm_matrix_shape s, const uint8_t* codes,
+                                      const float* leaves, const uint32_t* counts,
+                                      uint32_t* planes_out, size_t pstride, float* levels_out) {
+    pm_status st = check_shape(s);
+    if (st) return st;
+    if (s.rows == 0 || s.cols == 0) return PM_OK;
+    if (!codes || !leaves || !planes_out || !levels_out)
+        return fail(PM_ERR_ARG, "pm_encode_matrix: null pointer");
+    if (pstride < pm_plane_words(s))
+        return fail(PM_ERR_ARG, "plane stride %zu below plane size %zu", pstride,
+                    pm_plane_words(s));
+    return encode_host(s, codes, leaves, counts, planes_out, pstride, levels_out);
+}
+
+extern "C" pm_status pm_encode_expert(pm_expert_shape e, const uint8_t* const codes[3],
+                                      const float* const leaves[3],
+                                      const uint32_t* const counts[3], uint32_t* planes_out,
+                                      float* levels_out) {
+    if (!expert_ok(e)) return fail(PM_ERR_SHAPE, "invalid expert shape");
+    if (!codes || !leaves || !planes_out || !levels_out)
+        return fail(PM_ERR_ARG, "pm_encode_expert: null pointer");
+    const size_t pw = pm_expert_plane_words(e);
+    for (int m = 0; m < 3; ++m) {
+        size_t po, lo;
+        pm_matrix_shape s;
+        pm_expert_matrix_offsets(e, m, &po, &lo, &s);
+        pm_status st = pm_encode_matrix(s, codes[m], leaves[m], counts ? counts[m] : nullptr,
+                                        planes_out + po, pw, levels_out + lo);
+        if (st) return st;
+    }
+    return PM_OK;
+}
+
+extern "C" pm_status pm_encode_matrix_device(pm_matrix_shape s, const uint8_t* d_codes,
+                                             const float* d_leaves, const uint32_t* d_counts,
+                                             uint32_t* d_planes, size_t pstride, float* d_levels,
+                                             void* stream) {
+    pm_status st = check_shape(s);
+    if (st) return st;
+    if (s.rows == 0 || s.cols == 0) return PM_OK;
+    if (!d_codes || !d_leaves || !d_planes || !d_levels)
+        return fail(PM_ERR_ARG, "pm_encode_matrix_device: null pointer");
+    if (pstride < pm_plane_words(s))
+        return fail(PM_ERR_ARG, "plane stride %zu below plane size %zu", pstride,
+                    pm_plane_words(s));
+    HIP_TRY(launch_encode_device(s.rows, s.cols, s.group, d_codes, d_leaves, d_counts,
+                                 d_planes, pstride, d_levels, (hipStream_t)stream));
+    return PM_OK;
+}
+
+// ---------------------------------------------------------------- device calls
+static pm_status check_matrix_call(pm_matrix_shape s, int k, const void* planes,
+                                   size_t pstride, const void* a, const void* b) {
+    pm_status st = check_shape(s);
+    if (st) return st;
+    st = check_k(k);
+    if (st) return st;
+    if (s.rows == 0) return PM_OK;
+    if (!planes || !a || !b) return fail(PM_ERR_ARG, "null device pointer");
+    if (pstride < pm_plane_words(s))
+        return fail(PM_ERR_ARG, "plane stride %zu below plane size %zu", pstride,
+                    pm_plane_words(s));
+    return PM_OK;
+}
+
+extern "C" pm_status pm_expert_gemv(pm_matrix_shape s, int k, const uint32_t* d_planes,
+                                    size_t pstride, const float* d_levels, const float* d_x,
+                                    float* d_y, void* stream) {
+    pm_status st = check_matrix_call(s, k, d_planes, pstride, d_levels, d_y);
+    if (st) return st;
+    if (s.rows == 0) return PM_OK;
+    if (s.cols > 0 && !d_x) return fail(PM_ERR_ARG, "null x");
+    HIP_TRY(launch_gemv(s.rows, s.cols, s.group, k, d_planes, pstride, d_levels, d_x, d_y,
+                        (hipStream_t)stream));
+    return PM_OK;
+}
+
+extern "C" pm_status pm_debug_unpack_prefix(pm_matrix_shape s, int k, const uint32_t* d_planes,
+                                            size_t pstride, uint8_t* d_out, void* stream) {
+    pm_status st = check_matrix_call(s, k, d_planes, pstride, d_out, d_out);
+    if (st) return st;
+    if (s.rows == 0 || s.cols == 0) return PM_OK;
+    HIP_TRY(launch_unpack_prefix(s.rows, s.cols, k, d_planes, pstride, d_out,
+                                 (hipStream_t)stream));
+    return PM_OK;
+}
+
+extern "C" pm_status pm_debug_dequant(pm_matrix_shape s, int k, const uint32_t* d_planes,
+                                      size_t pstride, const float* d_levels, float* d_w,
+                                      void* stream) {
+    pm_status st = check_matrix_call(s, k, d_planes, pstride, d_levels, d_w);
+    if (st) return st;
+    if (s.rows == 0 || s.cols == 0) return PM_OK;
+    HIP_TRY(launch_dequant(s.rows, s.cols, s.group, k, d_planes, pstride, d_levels, d_w,
+                           nullptr, (hipStream_t)stream));
+    return PM_OK;
+}
+
+extern "C" pm_status pm_materialize_fp16(pm_matrix_shape s, int k, const uint32_t* d_planes,
+                                         size_t pstride, const float* d_levels, uint16_t* d_w,
+                                         void* stream) {
+    pm_status st = check_matrix_call(s, k, d_planes, pstride, d_levels, d_w);
+    if (st) return st;
+    if (s.rows == 0 || s.cols == 0) return PM_OK;
+    HIP_TRY(launch_dequant(s.rows, s.cols, s.group, k, d_planes, pstride, d_levels, nullptr,
+                           d_w, (hipStream_t)stream));
+    return PM_OK;
+}
+
+extern "C" pm_status pm_gemv_fp16(pm_matrix_shape s, const uint16_t* d_w, const float* d_x,
+                                  float* d_y, void* stream) {
+    pm_status st = check_shape(s);
+    if (st) return st;
+    if (s.rows == 0) return PM_OK;
+    if (!d_y || (s.cols > 0 && (!d_w || !d_x))) return fail(PM_ERR_ARG, "null device pointer");
+    HIP_TRY(launch_gemv_fp16(s.rows, s.cols, d_w, d_x, d_y, (hipStream_t)stream));
+    return PM_OK;
+}
+
+// ---------------------------------------------------------------- routing
+extern "C" pm_status pm_route_topk(int n_tokens, int n_experts, int top_k, const float* logits,
+                                   int32_t* ids_out, float* w_out) {
+    if (n_tokens < 0 || n_experts < 1 || top_k < 1 || top_k > n_experts)
+        return fail(PM_ERR_ARG, "route: n_tokens=%d n_experts=%d top_k=%d", n_tokens,
+                    n_experts, top_k);
+    if (n_tokens == 0) return PM_OK;
+    if (!logits || !ids_out || !w_out) return fail(PM_ERR_ARG, "route: null pointer");
+    std::vector<int32_t> order(n_experts);
+    std::vector<double> ex(top_k);
+    for (int t = 0; t < n_tokens; ++t) {
+        const float* l = logits + size_t(t) * n_experts;
+        for (int e = 0; e < n_experts; ++e) {
+            if (std::isnan(l[e])) return fail(PM_ERR_ARG, "route: NaN logit");
+            order[e] = e;
+        }
+        std::partial_sort(order.begin(), order.begin() + top_k, order.end(),
+                          [l](int32_t a, int32_t b) {
+                              return l[a] > l[b] || (l[a] == l[b] && a < b);
+                          });
+        const double lmax = double(l[order[0]]);
+        double sum = 0.0;
+        for (int j = 0; j < top_k; ++j) {
+            ex[j] = std::exp(double(l[order[j]]) - lmax);
+            sum += ex[j];
+        }
+        for (int j = 0; j < top_k; ++j) {
+            ids_out[size_t(t) * top_k + j] = order[j];
+            w_out[size_t(t) * top_k + j] = float(ex[j] / sum);
+        }
+    }
+    return PM_OK;
+}
+
+// ---------------------------------------------------------------- allocator
+// Least-squares non-increasing fit by pooling adjacent violators.
+static void fit_nonincreasing(const double* d, int n, double* out) {
+    std::vector<double> bsum;
+    std::vector<int> bcnt;
+    for (int i = 0; i < n; ++i) {
+        bsum.push_back(d[i]);
+        bcnt.push_back(1);
+        while (bsum.size() > 1) {
+            const size_t z = bsum.size();
+            if (!(bsum[z - 2] / bcnt[z - 2] < bsum[z - 1] / bcnt[z - 1])) break;
+            bsum[z - 2] += bsum[z - 1];
+            bcnt[z - 2] += bcnt[z - 1];
+            bsum.pop_back();
+            bcnt.pop_back();
+        }
+    }
+    int i = 0;
+    for (size_t b = 0; b < bsum.size(); ++b)
+        for (int c = 0; c < bcnt[b]; ++c) out[i++] = bsum[b] / bcnt[b];
+}
+
+static void convex_profile(const double* err, double* out) {
+    double gains[kBits - 1], fit[kBits - 1];
+    for (int b = 0; b < kBits - 1; ++b) gains[b] = err[b] - err[b + 1];
+    fit_nonincreasing(gains, kBits - 1, fit);
+    out[0] = err[0];
+    for (int b = 1; b < kBits; ++b) out[b] = out[b - 1] - fit[b - 1];
+}
+
+extern "C" pm_status pm_allocate_bits(int n_tokens, int top_k, const int32_t* ids,
+                                      const float* w, int n_experts, const double* err,
+                                      int budget, uint8_t* k_out) {
+    if (n_tokens < 0 || top_k < 1 || n_experts < 1)
+        return fail(PM_ERR_ARG, "allocate: n_tokens=%d top_k=%d n_experts=%d", n_tokens, top_k,
+                    n_experts);
+    if (budget < top_k || budget > kBits * top_k)
+        return fail(PM_ERR_ARG, "allocate: budget %d outside [%d, %d]", budget, top_k,
+                    kBits * top_k);
+    if (n_tokens == 0) return PM_OK;
+    if (!ids || !w || !err || !k_out) return fail(PM_ERR_ARG, "allocate: null pointer");
+    std::vector<double> prof(size_t(top_k) * kBits);
+    std::vector<int> b(top_k);
+    for (int t = 0; t < n_tokens; ++t) {
+        for (int j = 0; j < top_k; ++j) {
+            const int32_t e = ids[size_t(t) * top_k + j];
+            if (e < 0 || e >= n_experts)
+                return fail(PM_ERR_ARG, "allocate: expert id %d outside 0..%d", e,
+                            n_experts - 1);
+            convex_profile(err + size_t(e) * kBits, &prof[size_t(j) * kBits]);
+            b[j] = 1;
+        }
+        for (int step = 0; step < budget - top_k; ++step) {
+            int best = -1;
+            double bg = 0.0, bw = 0.0;
+            for (int j = 0; j < top_k; ++j) {
+                if (b[j] >= kBits) continue;
+                const double wd = double(w[size_t(t) * top_k + j]);
+                const double* p = &prof[size_t(j) * kBits];
+                const double gain = (wd * wd) * (p[b[j] - 1] - p[b[j]]);
+                if (best < 0 || gain > bg || (gain == bg && wd > bw)) {
+                    best = j;
+                    bg = gain;
+                    bw = wd;
+                }
+            }
+            b[best] += 1;
+        }
+        for (int j = 0; j < top_k; ++j) k_out[size_t(t) * top_k + j] = uint8_t(b[j]);
+    }
+    return PM_OK;
+}
+
+// ---------------------------------------------------------------- store
+namespace {
+
+struct Slot {
+    uint32_t* planes = nullptr;    // 8 chunks of plane_words
+    float* levels = nullptr;
+    int resident = 0;              // leading planes that are valid
+    bool levels_ready = false;
+    const uint32_t* h_planes = nullptr;
+    const float* h_levels = nullptr;
+    hipEvent_t ready = nullptr;    // recorded after the slot's last top-up copy
+    bool pending = false;          // a top-up is in flight on the side stream
+};
+
+struct Workspace {
+    float* d_buf = nullptr;        // G, U, Y partial results
+    size_t d_floats = 0;
+    char* h_ring = nullptr;        // pinned staging of work lists
+    char* d_ring = nullptr;
+    size_t slot_bytes = 0;
+    static constexpr int kSlots = 16;
+    hipEvent_t ring_ev[kSlots] = {};
+    int next = 0;
+};
+
+}  // namespace
+
+struct pm_store {
+    pm_expert_shape shape;
+    Geom geom;
+    int n_layers, n_experts;
+    size_t capacity, used = 0;
+    bool host_fake;
+    size_t plane_bytes, level_bytes;   // per plane chunk, per slot levels
+    std::vector<Slot> slots;
+    hipStream_t side = nullptr;        // the store's own top-up stream
+    hipEvent_t last_done = nullptr;    // end of the last forward
+    bool have_last = false;
+    Workspace ws;
+    int last_first = -1, last_count = 0;
+    uint64_t total_planes = 0, total_bytes = 0;
+    hipEvent_t prof[4] = {};
+    bool profiling = false;
+};
+
+static pm_status slot_of(const pm_store* s, int layer, int expert, size_t* idx) {
+    if (!s) return fail(PM_ERR_ARG, "null store");
+    if (layer < 0 || layer >= s->n_layers || expert < 0 || expert >= s->n_experts)
+        return fail(PM_ERR_ARG, "slot (%d, %d) outside %d layers x %d experts", layer, expert,
+                    s->n_layers, s->n_experts);
+    *idx = size_t(layer) * s->n_experts + expert;
+    return PM_OK;
+}
+
+static pm_status ensure_slot(pm_store* s, Slot& sl) {
+    if (sl.planes) return PM_OK;
+    const size_t pbytes = kBits * s->plane_bytes;
+    const size_t pad = (pbytes + 255) & ~size_t(255);
+    const size_t total = pad + s->level_bytes;
+    if (s->capacity && s->used + total > s->capacity)
+        return fail(PM_ERR_OOM, "store capacity %zu bytes exceeded (%zu used, %zu more)",
+                    s->capacity, s->used, total);
+    char* mem = nullptr;
+    if (s->host_fake) {
+        mem = static_cast<char*>(std::calloc(total, 1));
+        if (!mem) return fail(PM_ERR_OOM, "host allocation of %zu bytes failed", total);
+    } else {
+        hipError_t e = hipMalloc(&mem, total);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(PM_ERR_OOM, "hipMalloc of %zu bytes failed: %s", total,
+                        hipGetErrorString(e));
+        }
+        HIP_TRY(hipEventCreateWithFlags(&sl.ready, hipEventDisableTiming));
+    }
+    sl.planes = reinterpret_cast<uint32_t*>(mem);
+    sl.levels = reinterpret_cast<float*>(mem + pad);
+    sl.resident = 0;
+    sl.levels_ready = false;
+    s->used += total;
+    return PM_OK;
+}
+
+extern "C" pm_status pm_store_create(pm_expert_shape e, int n_layers, int n_experts,
+                                     size_t capacity, uint32_t flags, pm_store** out) {
+    if (!out) return fail(PM_ERR_ARG, "null output pointer");
+    *out = nullptr;
+    if (!expert_ok(e)) return fail(PM_ERR_SHAPE, "invalid expert shape");
+    if (n_layers < 1 || n_experts < 1) return fail(PM_ERR_ARG, "empty store");
+    if (flags & ~uint32_t(PM_STORE_HOST_FAKE)) return fail(PM_ERR_ARG, "unknown store flags");
+    pm_store* s = new pm_store();
+    s->shape = e;
+    s->geom = make_geom(e);
+    s->n_layers = n_layers;
+    s->n_experts = n_experts;
+    s->capacity = capacity;
+    s->host_fake = flags & PM_STORE_HOST_FAKE;
+    s->plane_bytes = pm_expert_plane_words(e) * sizeof(uint32_t);
+    s->level_bytes = pm_expert_levels_floats(e) * sizeof(float);
+    s->slots.resize(size_t(n_layers) * n_experts);
+    if (!s->host_fake) {
+        hipError_t er = hipStreamCreateWithFlags(&s->side, hipStreamNonBlocking);
+        if (er == hipSuccess) er = hipEventCreateWithFlags(&s->last_done, hipEventDisableTiming);
+        if (er != hipSuccess) {
+            pm_store_destroy(s);
+            return hip_fail(er, "store stream/event creation");
+        }
+    }
+    *out = s;
+    return PM_OK;
+}
+
+extern "C" pm_status pm_store_destroy(pm_store* s) {
+    if (!s) return PM_OK;
+    if (!s->host_fake) (void)hipDeviceSynchronize();
+    for (Slot& sl : s->slots) {
+        if (!sl.planes) continue;
+        if (s->host_fake) {
+            std::free(sl.planes);
+        } else {
+            (void)hipFree(sl.planes);
+            if (sl.ready) (void)hipEventDestroy(sl.ready);
+        }
+    }
+    if (!s->host_fake) {
+        Workspace& w = s->ws;
+        if (w.d_buf) (void)hipFree(w.d_buf);
+        if (w.d_ring) (void)hipFree(w.d_ring);
+        if (w.h_ring) (void)hipHostFree(w.h_ring);
+        for (hipEvent_t ev : w.ring_ev)
+            if (ev) (void)hipEventDestroy(ev);
+        if (s->last_done) (void)hipEventDestroy(s->last_done);
+        if (s->side) (void)hipStreamDestroy(s->side);
+    }
+    delete s;
+    return PM_OK;
+}
+
+extern "C" pm_status pm_store_slot(pm_store* s, int layer, int expert, uint32_t** planes,
+                                   float** levels) {
+    size_t i;
+    pm_status st = slot_of(s, layer, expert, &i);
+    if (st) return st;
+    st = ensure_slot(s, s->slots[i]);
+    if (st) return st;
+    if (planes) *planes = s->slots[i].planes;
+    if (levels) *levels = s->slots[i].levels;
+    return PM_OK;
+}
+
+extern "C" pm_status pm_store_set_resident(pm_store* s, int layer, int expert, int r) {
+    size_t i;
+    pm_status st = slot_of(s, layer, expert, &i);
+    if (st) return st;
+    if (r < 0 || r > kBits) return fail(PM_ERR_PREFIX, "resident prefix %d outside 0..8", r);
+    if (!s->slots[i].planes) return fail(PM_ERR_STATE, "slot (%d, %d) has no memory", layer, expert);
+    s->slots[i].resident = r;
+    s->slots[i].levels_ready = true;
+    s->slots[i].pending = false;
+    return PM_OK;
+}
+
+extern "C" pm_status pm_store_attach_host(pm_store* s, int layer, int expert,
+                                          const uint32_t* h_planes, const float* h_levels) {
+    size_t i;
+    pm_status st = slot_of(s, layer, expert, &i);
+    if (st) return st;
+    if (!h_planes || !h_levels) return fail(PM_ERR_ARG, "null host source");
+    s->slots[i].h_planes = h_planes;
+    s->slots[i].h_levels = h_levels;
+    return PM_OK;
+}
+
+static pm_status topup_slot(pm_store* s, Slot& sl, int k, hipStream_t side) {
+    if (k <= sl.resident) {            // a resident deeper prefix serves it: no copy
+        s->last_first = sl.resident;
+        s->last_count = 0;
+        return PM_OK;
+    }
+    if (!sl.h_planes || !sl.h_levels) return fail(PM_ERR_STATE, "slot has no host source");
+    pm_status st = ensure_slot(s, sl);
+    if (st) return st;
+    const int first = sl.resident;
+    const size_t pw = s->plane_bytes / sizeof(uint32_t);
+    if (s->host_fake) {
+        if (!sl.levels_ready) std::memcpy(sl.levels, sl.h_levels, s->level_bytes);
+        std::memcpy(sl.planes + size_t(first) * pw, sl.h_planes + size_t(first) * pw,
+                    size_t(k - first) * s->plane_bytes);
+    } else {
+        // the copy must not overwrite planes a previous forward may still read
+        if (s->have_last) HIP_TRY(hipStreamWaitEvent(side, s->last_done, 0));
+        if (!sl.levels_ready)
+            HIP_TRY(hipMemcpyAsync(sl.levels, sl.h_levels, s->level_bytes,
+                                   hipMemcpyHostToDevice, side));
+        HIP_TRY(hipMemcpyAsync(sl.planes + size_t(first) * pw, sl.h_planes + size_t(first) * pw,
+                               size_t(k - first) * s->plane_bytes, hipMemcpyHostToDevice, side));
+        HIP_TRY(hipEventRecord(sl.ready, side));
+        sl.pending = true;
+    }
+    if (!sl.levels_ready) s->total_bytes += s->level_bytes;
+    sl.levels_ready = true;
+    sl.resident = k;
+    s->last_first = first;
+    s->last_count = k - first;
+    s->total_planes += uint64_t(k - first);
+    s->total_bytes += uint64_t(k - first) * s->plane_bytes;
+    return PM_OK;
+}
+
+extern "C" pm_status pm_store_topup(pm_store* s, int layer, int expert, int k, void* side) {
+    size_t i;
+    pm_status st = slot_of(s, layer, expert, &i);
+    if (st) return st;
+    st = check_k(k);
+    if (st) return st;
+    return topup_slot(s, s->slots[i], k, side ? (hipStream_t)side : s->side);
+}
+
+extern "C" pm_status pm_store_truncate(pm_store* s, int layer, int expert, int keep) {
+    size_t i;
+    pm_status st = slot_of(s, layer, expert, &i);
+    if (st) return st;
+    if (keep < 0 || keep > kBits) return fail(PM_ERR_PREFIX, "keep %d outside 0..8", keep);
+    s->slots[i].resident = std::min(s->slots[i].resident, keep);
+    return PM_OK;
+}
+
+extern "C" pm_status pm_store_resident(const pm_store* s, int layer, int expert, int* r_out) {
+    size_t i;
+    pm_status st = slot_of(s, layer, expert, &i);
+    if (st) return st;
+    if (!r_out) return fail(PM_ERR_ARG, "null output pointer");
+    *r_out = s->slots[i].resident;
+    return PM_OK;
+}
+
+extern "C" pm_status pm_store_copy_stats(const pm_store* s, int* last_first, int* last_count,
+                                         uint64_t* total_planes, uint64_t* total_bytes) {
+    if (!s) return fail(PM_ERR_ARG, "null store");
+    if (last_first) *last_first = s->last_first;
+    if (last_count) *last_count = s->last_count;
+    if (total_planes) *total_planes = s->total_planes;
+    if (total_bytes) *total_bytes = s->total_bytes;
+    return PM_OK;
+}
+
+extern "C" pm_status pm_store_set_profile_events(pm_store* s, void* const* events, int n) {
+    if (!s) return fail(PM_ERR_ARG, "null store");
+    if (n == 0) {
+        s->profiling = false;
+        return PM_OK;
+    }
+    if (n < 4 || !events) return fail(PM_ERR_ARG, "need 4 events");
+    for (int i = 0; i < 4; ++i) s->prof[i] = (hipEvent_t)events[i];
+    s->profiling = true;
+    return PM_OK;
+}
+
+// ---------------------------------------------------------------- MoE forward
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+static pm_status ensure_workspace(pm_store* s, size_t floats, size_t list_bytes) {
+    Workspace& w = s->ws;
+    if (floats > w.d_floats) {
+        if (w.d_buf) {
+            HIP_TRY(hipDeviceSynchronize());
+            HIP_TRY(hipFree(w.d_buf));
+            w.d_buf = nullptr;
+        }
+        size_t n = std::max(floats, size_t(1) << 20);
+        hipError_t e = hipMalloc(&w.d_buf, n * sizeof(float));
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(PM_ERR_OOM, "workspace allocation failed: %s", hipGetErrorString(e));
+        }
+        w.d_floats = n;
+    }
+    if (list_bytes > w.slot_bytes) {
+        if (w.h_ring) {
+            HIP_TRY(hipDeviceSynchronize());
+            HIP_TRY(hipHostFree(w.h_ring));
+            HIP_TRY(hipFree(w.d_ring));
+            w.h_ring = nullptr;
+            w.d_ring = nullptr;
+        }
+        size_t sb = std::max(align256(list_bytes), size_t(64) << 10);
+        HIP_TRY(hipHostMalloc(&w.h_ring, sb * Workspace::kSlots, 0));
+        HIP_TRY(hipMalloc(&w.d_ring, sb * Workspace::kSlots));
+        for (hipEvent_t& ev : w.ring_ev)
+            if (!ev) HIP_TRY(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+        w.slot_bytes = sb;
+    }
+    return PM_OK;
+}
+
+extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, int top_k,
+                                          const int32_t* h_ids, const float* h_w,
+                                          const uint8_t* h_k, const float* d_x, float* d_y,
+                                          void* compute_v, uint32_t flags) {
+    if (!s) return fail(PM_ERR_ARG, "null store");
+    if (s->host_fake) return fail(PM_ERR_STATE, "a host-backed store cannot compute");
+    if (flags & ~uint32_t(PM_AUTO_TOPUP)) return fail(PM_ERR_ARG, "unknown forward flags");
+    if (layer < 0 || layer >= s->n_layers) return fail(PM_ERR_ARG, "layer %d outside store", layer);
+    if (n_tokens < 0 || top_k < 1) return fail(PM_ERR_ARG, "n_tokens=%d top_k=%d", n_tokens, top_k);
+    if (n_tokens == 0) return PM_OK;
+    if (!h_ids || !h_w || !h_k || !d_x || !d_y) return fail(PM_ERR_ARG, "null pointer");
+    hipStream_t compute = (hipStream_t)compute_v;
+    const Geom& g = s->geom;
+
+    // ---- validate and group uses by expert (order of first appearance)
+    const int n_uses = n_tokens * top_k;
+    std::vector<Use> uses(n_uses);
+    std::map<int, int> item_of;
+    std::vector<int> item_expert;
+    std::vector<std::vector<int>> item_uses;
+    for (int t = 0; t < n_tokens; ++t) {
+        for (int j = 0; j < top_k; ++j) {
+            const int u = t * top_k + j;
+            const int e = h_ids[u];
+            if (e < 0 || e >= s->n_experts)
+                return fail(PM_ERR_ARG, "ids[%d][%d]=%d outside 0..%d", t, j, e, s->n_experts - 1);
+            if (!std::isfinite(h_w[u])) return fail(PM_ERR_ARG, "w[%d][%d] not finite", t, j);
+            for (int m = 0; m < 3; ++m) {
+                const int k = h_k[size_t(u) * 3 + m];
+                if (k < 1 || k > kBits)
+                    return fail(PM_ERR_PREFIX, "k[%d][%d][%d]=%d outside 1..8", t, j, m, k);
+                uses[u].k[m] = k;
+            }
+            uses[u].w = h_w[u];
+            uses[u].tok = t;
+            uses[u].slot = j;
+            auto it = item_of.find(e);
+            int d;
+            if (it == item_of.end()) {
+                d = int(item_expert.size());
+                item_of[e] = d;
+                item_expert.push_back(e);
+                item_uses.emplace_back();
+            } else {
+                d = it->second;
+            }
+            item_uses[d].push_back(u);
+        }
+    }
+    const int n_items = int(item_expert.size());
+    std::vector<int> kneed(n_items, 0);
+    std::vector<std::array<int, 3>> kmax(n_items, {0, 0, 0});
+    for (int d = 0; d < n_items; ++d) {
+        if (int(item_uses[d].size()) > max_uses_per_item())
+            return fail(PM_ERR_ARG, "expert %d is used %zu times; at most %d per call",
+                        item_expert[d], item_uses[d].size(), max_uses_per_item());
+        for (int u : item_uses[d])
+            for (int m = 0; m < 3; ++m) kmax[d][m] = std::max(kmax[d][m], uses[u].k[m]);
+        kneed[d] = std::max(kmax[d][0], std::max(kmax[d][1], kmax[d][2]));
+    }
+    // ---- residency: every short slot must be topped up (or the call fails)
+    std::vector<char> late(n_items, 0);
+    for (int d = 0; d < n_items; ++d) {
+        const Slot& sl = s->slots[size_t(layer) * s->n_experts + item_expert[d]];
+        const bool ok = sl.planes && sl.levels_ready && sl.resident >= kneed[d];
+        if (!ok) {
+            if (!(flags & PM_AUTO_TOPUP))
+                return fail(PM_ERR_NOT_RESIDENT,
+                            "expert (%d, %d) holds %d planes, %d requested", layer,
+                            item_expert[d], sl.planes ? sl.resident : 0, kneed[d]);
+            if (!sl.h_planes || !sl.h_levels)
+                return fail(PM_ERR_STATE, "expert (%d, %d) is short and has no host source",
+                            layer, item_expert[d]);
+            late[d] = 1;
+        }
+    }
+    // resident items first so their kernels can run while top-ups copy
+    std::vector<int> order(n_items);
+    for (int d = 0; d < n_items; ++d) order[d] = d;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return late[a] < late[b]; });
+    int n_res = 0;
+    while (n_res < n_items && !late[order[n_res]]) ++n_res;
+
+    // ---- workspace
+    const size_t fG = align256(size_t(n_uses) * g.inter);
+    const size_t fY = align256(size_t(n_uses) * g.hidden);
+    const size_t list_bytes = align256(sizeof(Item) * n_items) + align256(sizeof(Use) * n_uses) +
+                              align256(sizeof(int32_t) * n_uses);
+    pm_status st = ensure_workspace(s, 2 * fG + fY, list_bytes);
+    if (st) return st;
+    if (s->have_last) HIP_TRY(hipStreamWaitEvent(compute, s->last_done, 0));
+
+    // ---- top-ups (side stream) for late items
+    for (int i = n_res; i < n_items; ++i) {
+        const int d = order[i];
+        Slot& sl = s->slots[size_t(layer) * s->n_experts + item_expert[d]];
+        st = topup_slot(s, sl, kneed[d], s->side);
+        if (st) return st;
+    }
+
+    // ---- work list into the pinned ring, then to the device
+    Workspace& w = s->ws;
+    const int rs = w.next;
+    w.next = (w.next + 1) % Workspace::kSlots;
+    HIP_TRY(hipEventSynchronize(w.ring_ev[rs]));
+    char* hb = w.h_ring + size_t(rs) * w.slot_bytes;
+    char* db = w.d_ring + size_t(rs) * w.slot_bytes;
+    Item* hitems = reinterpret_cast<Item*>(hb);
+    Use* huses = reinterpret_cast<Use*>(hb + align256(sizeof(Item) * n_items));
+    int32_t* hlist = reinterpret_cast<int32_t*>(hb + align256(sizeof(Item) * n_items) +
+                                                align256(sizeof(Use) * n_uses));
+    const int rpb_gu = gateup_rows_per_block(), rpb_dn = down_rows_per_block();
+    const int gu_blocks_per_item = (g.inter + rpb_gu - 1) / rpb_gu;
+    const int dn_blocks_per_item = (g.hidden + rpb_dn - 1) / rpb_dn;
+    int lpos = 0;
+    for (int i = 0; i < n_items; ++i) {
+        const int d = order[i];
+        const Slot& sl = s->slots[size_t(layer) * s->n_experts + item_expert[d]];
+        Item& it = hitems[i];
+        it.planes = sl.planes;
+        it.levels = sl.levels;
+        it.use0 = lpos;
+        it.nuse = int(item_uses[d].size());
+        for (int m = 0; m < 3; ++m) it.kmax[m] = kmax[d][m];
+        it.blk_gu = (i < n_res ? i : i - n_res) * gu_blocks_per_item;
+        it.blk_dn = i * dn_blocks_per_item;
+        for (int u : item_uses[d]) hlist[lpos++] = u;
+    }
+    std::memcpy(huses, uses.data(), sizeof(Use) * n_uses);
+    HIP_TRY(hipMemcpyAsync(db, hb, list_bytes, hipMemcpyHostToDevice, compute));
+    HIP_TRY(hipEventRecord(w.ring_ev[rs], compute));
+    const Item* ditems = reinterpret_cast<const Item*>(db);
+    const Use* duses = reinterpret_cast<const Use*>(db + align256(sizeof(Item) * n_items));
+    const int32_t* dlist = reinterpret_cast<const int32_t*>(
+        db + align256(sizeof(Item) * n_items) + align256(sizeof(Use) * n_uses));
+    float* G = w.d_buf;
+    float* U = w.d_buf + fG;
+    float* Y = w.d_buf + 2 * fG;
+
+    // ---- kernels
+    // resident slots topped up by an earlier explicit call may still be copying
+    for (int i = 0; i < n_res; ++i) {
+        Slot& sl = s->slots[size_t(layer) * s->n_experts + item_expert[order[i]]];
+        if (sl.pending) {
+            HIP_TRY(hipStreamWaitEvent(compute, sl.ready, 0));
+            sl.pending = false;
+        }
+    }
+    if (s->profiling) HIP_TRY(hipEventRecord(s->prof[0], compute));
+    if (n_res > 0)
+        HIP_TRY(launch_gateup(g, ditems, 0, n_res, n_res * gu_blocks_per_item, duses, dlist,
+                              top_k, d_x, G, U, compute));
+    if (n_res < n_items) {
+        for (int i = n_res; i < n_items; ++i) {
+            Slot& sl = s->slots[size_t(layer) * s->n_experts + item_expert[order[i]]];
+            HIP_TRY(hipStreamWaitEvent(compute, sl.ready, 0));
+            sl.pending = false;
+        }
+        HIP_TRY(launch_gateup(g, ditems, n_res, n_items - n_res,
+                              (n_items - n_res) * gu_blocks_per_item, duses, dlist, top_k, d_x,
+                              G, U, compute));
+    }
+    if (s->profiling) HIP_TRY(hipEventRecord(s->prof[1], compute));
+    HIP_TRY(launch_down(g, ditems, n_items, n_items * dn_blocks_per_item, duses, dlist, n_uses,
+                        G, U, Y, compute));
+    if (s->profiling) HIP_TRY(hipEventRecord(s->prof[2], compute));
+    HIP_TRY(launch_combine(n_tokens, top_k, g.hidden, duses, Y, d_y, compute));
+    if (s->profiling) HIP_TRY(hipEventRecord(s->prof[3], compute));
+    HIP_TRY(hipEventRecord(s->last_done, compute));
+    s->have_last = true;
+    return PM_OK;
+}

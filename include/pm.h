@@ -1,0 +1,243 @@
+/*
+ * pm.h -- C ABI of libpm: direct execution of mixture-of-experts experts from
+ * a cached k-bit prefix (k = 1..8) of a prefix-compatible binary-tree
+ * codebook stored as bitplanes, on one AMD MI355X (gfx950).
+ *
+ * Sources (page titles):
+ *   [T]   "PagedMoE: Cross-Precision Expert Caching for SSD-Resident MoE
+ *         Inference", podcast episode transcript; "T cN" = subtitle cue N.
+ *   [Abs] "PagedMoE: Cross-Precision Expert Caching for Token-Level Dynamic
+ *         Precision in SSD-Resident MoE Inference", arxivlens page, Abstract.
+ *   [Met] the same page, Analysis, "Methodology".
+ *
+ * Stored format (the pages fix the idea, the workload fixes the numbers):
+ *   - A matrix has `rows` outputs and `cols` inputs.  Each weight is an 8-bit
+ *     index into the codebook of its block; a block is `group` consecutive
+ *     inputs of one row (group % 32 == 0, cols % group == 0).
+ *   - Planes [T c25]: uint32 [8][rows][cols/32].  Plane p holds bit (7 - p)
+ *     of every index (MSB first), and bit j of word w of a row is input
+ *     column 32*w + j.  Planes are `plane_stride_words` apart (>= rows*cols/32)
+ *     so that the three matrices of an expert can share one contiguous chunk
+ *     per plane.
+ *   - Levels [T c19, c21]: the tree over a block's 256 sorted leaves; each
+ *     parent is the mean of its two children.  Depths 1..8 are stored
+ *     (510 fp32 per block), level-major: the node of depth d, row o, block g,
+ *     value v (v < 2^d) sits at
+ *         pm_level_offset(s, d) + ((o * (cols/group) + g) << d) + v,
+ *     pm_level_offset(s, d) = rows * (cols/group) * (2^d - 2).
+ *   - The k-bit prefix of a weight is sum_{p<k} bit_p << (k-1-p), i.e. the top
+ *     k bits of its index [T c21]; its value at precision k is the depth-k
+ *     node of its block selected by that prefix.  Reading precision k touches
+ *     planes 0..k-1 and depth k only [T c25; Abs].
+ *
+ * Conventions:
+ *   - Every call validates all arguments before any launch or copy; on error
+ *     nothing is launched and pm_last_error() describes the failure.
+ *   - d_ pointers are device memory, h_ pointers host memory; the caller owns
+ *     both unless a call says otherwise.  Streams are hipStream_t handles
+ *     passed as void* (NULL = the null stream).  Device calls are
+ *     asynchronous on their stream and never synchronise the device.
+ *   - Every HIP error is returned as PM_ERR_HIP with HIP's text in
+ *     pm_last_error().  Reductions run in a fixed order: the same call on the
+ *     same inputs gives bit-identical outputs.
+ *   - A pm_store is not thread-safe.
+ */
+#ifndef PM_H
+#define PM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pm_status;
+enum {
+    PM_OK = 0,
+    PM_ERR_ARG = -1,          /* null pointer, bad count, bad flag            */
+    PM_ERR_SHAPE = -2,        /* group/cols/rows not of the stored format      */
+    PM_ERR_PREFIX = -3,       /* k outside 1..8                                */
+    PM_ERR_NOT_RESIDENT = -4, /* a prefix longer than the resident planes      */
+    PM_ERR_OOM = -5,          /* store capacity or device memory exhausted     */
+    PM_ERR_HIP = -6,          /* a HIP runtime call failed                     */
+    PM_ERR_STATE = -7         /* call out of order (e.g. no host source)       */
+};
+
+/* Thread-local text of the last failure on this thread ("" if none). */
+const char* pm_last_error(void);
+/* Library version string. */
+const char* pm_version(void);
+
+typedef struct { int32_t rows, cols, group; } pm_matrix_shape;
+/* An expert: gate [inter x hidden], up [inter x hidden], down [hidden x inter]. */
+typedef struct { int32_t hidden, inter, group; } pm_expert_shape;
+
+/* Sizes of the stored format; 0 for a shape that is not valid.
+ * pm_level_offset returns (size_t)-1 for d outside 1..8. */
+size_t pm_plane_words(pm_matrix_shape s);            /* rows*cols/32           */
+size_t pm_levels_floats(pm_matrix_shape s);          /* rows*(cols/group)*510  */
+size_t pm_level_offset(pm_matrix_shape s, int d);
+/* Expert layout: plane p of an expert is one chunk of
+ * pm_expert_plane_words(e) words holding gate, up, down planes back to back
+ * (the unit of a top-up [T c25, c35]); levels are gate, up, down back to back.
+ * pm_expert_matrix_offsets gives, for matrix m (0 gate, 1 up, 2 down), its word
+ * offset inside a plane chunk and its float offset inside the levels. */
+size_t pm_expert_plane_words(pm_expert_shape e);
+size_t pm_expert_levels_floats(pm_expert_shape e);
+pm_status pm_expert_matrix_offsets(pm_expert_shape e, int m, size_t* plane_word_off,
+                                   size_t* level_float_off, pm_matrix_shape* shape_out);
+
+/* ---------------------------------------------------------------- encoding
+ * Offline encoder [T c19, c21, c25; Abs "stores each expert once using a
+ * prefix-compatible tree codebook and bitplane layout"].
+ *   codes:  uint8 [rows][cols], the 8-bit leaf index of every weight.
+ *   leaves: fp32 [rows][cols/group][256], ascending per block (else
+ *           PM_ERR_ARG).
+ *   counts: uint32 [rows][cols/group][256] or NULL.  NULL: parent =
+ *           (left + right) * 0.5f in fp32.  Otherwise parent = the
+ *           count-weighted mean of its children [T c19, c21], evaluated in
+ *           fp64 from the fp32 children and rounded to fp32, the parent's
+ *           count being the sum of its children's; a parent whose children
+ *           hold no weight takes the unweighted mean.
+ *   planes_out: uint32, planes p at planes_out + p*plane_stride_words.
+ *   levels_out: fp32 [pm_levels_floats(s)].
+ * The host versions compute on the calling thread; the device versions take
+ * device pointers and run on `stream`. */
+pm_status pm_encode_matrix(pm_matrix_shape s, const uint8_t* codes, const float* leaves,
+                           const uint32_t* counts, uint32_t* planes_out,
+                           size_t plane_stride_words, float* levels_out);
+pm_status pm_encode_expert(pm_expert_shape e, const uint8_t* const codes[3],
+                           const float* const leaves[3], const uint32_t* const counts[3],
+                           uint32_t* planes_out, float* levels_out);
+pm_status pm_encode_matrix_device(pm_matrix_shape s, const uint8_t* d_codes,
+                                  const float* d_leaves, const uint32_t* d_counts,
+                                  uint32_t* d_planes_out, size_t plane_stride_words,
+                                  float* d_levels_out, void* stream);
+
+/* ---------------------------------------------------------------- prefix GEMV
+ * y[o] = sum_i node(k, o, i/group, prefix_k(o, i)) * x[i]: one matrix read
+ * directly at a k-bit prefix, no decoded matrix is formed [Abs "directly
+ * executes cached 1-8-bit prefixes without materializing full-precision
+ * experts"; T c37].  Reads planes 0..k-1 and depth k only.
+ *   d_x fp32 [cols], d_y fp32 [rows] (overwritten; cols == 0 gives zeros).
+ *   Errors: PM_ERR_PREFIX (k), PM_ERR_SHAPE, PM_ERR_ARG (null pointer or
+ *   plane_stride_words < rows*cols/32). */
+pm_status pm_expert_gemv(pm_matrix_shape s, int k, const uint32_t* d_planes,
+                         size_t plane_stride_words, const float* d_levels,
+                         const float* d_x, float* d_y, void* stream);
+
+/* ---------------------------------------------------------------- routing
+ * [T c4]: a router picks a few experts per token with weights summing to 1.
+ * logits fp32 [n_tokens][n_experts] -> ids int32 [n_tokens][top_k] (largest
+ * logit first, ties to the lower expert id) and w fp32 [n_tokens][top_k], the
+ * softmax over the selected logits computed in fp64 and rounded to fp32.
+ * Host memory. */
+pm_status pm_route_topk(int n_tokens, int n_experts, int top_k, const float* logits,
+                        int32_t* ids_out, float* w_out);
+
+/* Pre-I/O prefix-length allocation [T c29, c31; Abs "selects the required
+ * prefix length before I/O using current routing weights and offline
+ * expert-specific error profiles"].  Per token: minimise
+ * sum_j w_j^2 * err_{ids_j}(b_j) subject to sum_j b_j = budget: start every
+ * selected expert at 1 bit and grant, one at a time, the bit with the largest
+ * gain (w*w) * (err(b) - err(b+1)) (fp64, w widened from fp32; ties to the
+ * larger w, then the lower slot).  Profiles are first made convex: their
+ * marginal gains are replaced by the least-squares non-increasing fit (pool
+ * adjacent violators) [T c31].
+ *   err_profiles float64 [n_experts][8] (err(b) at b = 1..8), host.
+ *   k_out uint8 [n_tokens][top_k]; budget in [top_k, 8*top_k]. */
+pm_status pm_allocate_bits(int n_tokens, int top_k, const int32_t* ids, const float* w,
+                           int n_experts, const double* err_profiles, int budget,
+                           uint8_t* k_out);
+
+/* ---------------------------------------------------------------- plane store
+ * HBM store of encoded experts with plane-granular residency [T c13, c35;
+ * Abs "cached data ... reused or extended by fetching only missing
+ * bitplanes"].  A slot (layer, expert) holds the 8 plane chunks and the levels
+ * of one expert; its resident prefix r counts the leading planes that are
+ * valid.  A plane is usable only when every earlier plane is resident, so r
+ * is always a prefix count.  The store owns all slot memory.
+ * flags: PM_STORE_HOST_FAKE backs slots with host memory and copies with
+ * memcpy (bookkeeping tests without a GPU; compute calls reject such a
+ * store).  capacity_bytes > 0 caps the slot memory (PM_ERR_OOM beyond). */
+typedef struct pm_store pm_store;
+enum { PM_STORE_HOST_FAKE = 1u };
+pm_status pm_store_create(pm_expert_shape e, int n_layers, int n_experts,
+                          size_t capacity_bytes, uint32_t flags, pm_store** out);
+pm_status pm_store_destroy(pm_store* s);
+/* Slot memory (allocated on first use, r = 0): plane chunk p at
+ * *planes + p * pm_expert_plane_words(e); levels at *levels. */
+pm_status pm_store_slot(pm_store* s, int layer, int expert, uint32_t** planes,
+                        float** levels);
+/* Declare that the caller has written planes 0..r-1 and all levels of a slot
+ * (e.g. with pm_encode_matrix_device); r in 0..8. */
+pm_status pm_store_set_resident(pm_store* s, int layer, int expert, int r);
+/* Register the host source of a slot: h_planes uint32 [8][plane words],
+ * h_levels fp32 [levels floats].  Caller-owned, pinned (hipHostMalloc) for an
+ * asynchronous copy, alive as long as the store uses it. */
+pm_status pm_store_attach_host(pm_store* s, int layer, int expert,
+                               const uint32_t* h_planes, const float* h_levels);
+/* Make planes r..k-1 resident by copying exactly those plane chunks from the
+ * host source (plus the levels on a slot's first fill) on `side`, then
+ * record the slot's ready event there; r becomes k.  No copy if r >= k
+ * [T c13, c35: a resident deeper prefix serves a shallower request].
+ * PM_ERR_STATE without a host source. */
+pm_status pm_store_topup(pm_store* s, int layer, int expert, int k, void* side);
+/* r = min(r, keep): the deepest planes age out first [T c35]. */
+pm_status pm_store_truncate(pm_store* s, int layer, int expert, int keep);
+pm_status pm_store_resident(const pm_store* s, int layer, int expert, int* r_out);
+/* Planes copied by the last top-up of any slot (first plane, count) and the
+ * running totals of plane chunks and bytes copied by top-ups. */
+pm_status pm_store_copy_stats(const pm_store* s, int* last_first, int* last_count,
+                              uint64_t* total_planes, uint64_t* total_bytes);
+/* Optional timing hook: when n >= 4, each pm_moe_token_forward on this store
+ * records events[0] before its first kernel, events[1] after the gate/up
+ * kernel, events[2] after the down kernel and events[3] after the combine
+ * (hipEvent_t handles on the compute stream).  n = 0 switches it off. */
+pm_status pm_store_set_profile_events(pm_store* s, void* const* events, int n);
+
+/* ---------------------------------------------------------------- MoE layer
+ * One MoE layer for n_tokens tokens:
+ *   y[t] = sum_j w[t][j] * W_down(k2) (silu(W_gate(k0) x[t]) * W_up(k1) x[t])
+ * with expert ids[t][j] read at prefixes h_k[t][j][0..2] (gate, up, down)
+ * [T c4, c37; Abs].  Tokens that share an expert are grouped: its planes are
+ * read once up to the largest prefix any of them needs, and each token stops
+ * at its own prefix [Abs; T c25].
+ *   h_ids int32 [n_tokens][top_k], h_w fp32 [n_tokens][top_k],
+ *   h_k uint8 [n_tokens][top_k][3] -- host memory, read before return.
+ *   d_x fp32 [n_tokens][hidden], d_y fp32 [n_tokens][hidden] (overwritten).
+ * flags: PM_AUTO_TOPUP tops up every short slot from its host source on the
+ * store's side stream and makes `compute` wait for it (kernels of resident
+ * experts are issued first); without it a short slot is PM_ERR_NOT_RESIDENT.
+ * The store keeps per-call workspace; calls on one store are serialised on
+ * `compute`. */
+enum { PM_AUTO_TOPUP = 1u };
+pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, int top_k,
+                               const int32_t* h_ids, const float* h_w, const uint8_t* h_k,
+                               const float* d_x, float* d_y, void* compute, uint32_t flags);
+
+/* ---------------------------------------------------------------- checks and baselines
+ * Bit-exact views of what the kernels decode (not on the hot path):
+ *   pm_debug_unpack_prefix: d_prefix_out uint8 [rows][cols], the k-bit prefix.
+ *   pm_debug_dequant:       d_w_out fp32 [rows][cols], the depth-k node.
+ * The materialize-then-multiply comparator [T c37; Met]:
+ *   pm_materialize_fp16: d_w_fp16 uint16 [rows][cols], the depth-k node
+ *                        rounded to fp16 (nearest even).
+ *   pm_gemv_fp16:        y[o] = sum_i fp16 W[o][i] * x[i] (fp32 sums). */
+pm_status pm_debug_unpack_prefix(pm_matrix_shape s, int k, const uint32_t* d_planes,
+                                 size_t plane_stride_words, uint8_t* d_prefix_out,
+                                 void* stream);
+pm_status pm_debug_dequant(pm_matrix_shape s, int k, const uint32_t* d_planes,
+                           size_t plane_stride_words, const float* d_levels, float* d_w_out,
+                           void* stream);
+pm_status pm_materialize_fp16(pm_matrix_shape s, int k, const uint32_t* d_planes,
+                              size_t plane_stride_words, const float* d_levels,
+                              uint16_t* d_w_fp16, void* stream);
+pm_status pm_gemv_fp16(pm_matrix_shape s, const uint16_t* d_w, const float* d_x, float* d_y,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PM_H */

@@ -1,0 +1,418 @@
+"""GPU parity of libpm against the CPU oracle, through the C ABI.
+
+Bit-exact: device-drawn inputs, device-encoded planes and levels, unpacked
+prefixes, dequantised values, one-hot GEMV columns, poisoned planes/levels,
+repeated runs.  Within |gpu - oracle| <= 1e-4 * sum|w*x| + 1e-6 per output:
+every fp32 GEMV and MoE output, on every workload configuration (the large
+ones on sampled output rows)."""
+import numpy as np
+import pytest
+import torch
+
+import bitplane_quantized_expert_amd as pm
+import oracle
+import oracle_cases as oc
+import synth
+from synth.device import DeviceSynth
+from synth.pool import PoolFiller
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+ABS = 1e-6
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_close(got, want, scale, what=""):
+    ok = oracle.within_tolerance(got, want, scale, TOL, ABS)
+    if not ok.all():
+        i = int(np.argmin(ok))
+        raise AssertionError(f"{what}: {int((~ok).sum())} outputs out of tolerance; first at {i}: "
+                             f"got {got[i]!r} want {want[i]!r} scale {scale[i]!r}")
+
+
+def report(name):
+    print(f"[gpu case] {name}", flush=True)
+
+
+# ---------------------------------------------------------------- tiny expert on device
+class DevExpert:
+    """An expert encoded on the device by the library's device encoder."""
+
+    def __init__(self, wl, layer=0, expert=0, weighted=False):
+        self.wl = wl
+        self.e = pm.eshape(wl.hidden, wl.inter, wl.group)
+        self.pw = pm.pm_expert_plane_words(self.e)
+        self.planes = torch.zeros(8 * self.pw, dtype=torch.int32, device="cuda")
+        self.levels = torch.zeros(pm.pm_expert_levels_floats(self.e), dtype=torch.float32,
+                                  device="cuda")
+        self.li = synth.expert_inputs(wl, layer, expert)
+        self.shapes = []
+        for m in range(3):
+            po, lo, sh = pm.pm_expert_matrix_offsets(self.e, m)
+            lv, cd = self.li[m]
+            cnt = dev(oracle.leaf_counts(cd, wl.group).astype(np.uint32)) if weighted else None
+            pm.pm_encode_matrix_device(sh, dev(cd), dev(lv), cnt,
+                                       self.planes.data_ptr() + 4 * po, self.pw,
+                                       self.levels.data_ptr() + 4 * lo)
+            self.shapes.append((po, lo, sh))
+        torch.cuda.synchronize()
+        self.enc = oracle.encode_expert(self.li, wl.group, weighted=weighted)
+
+    def mat(self, m):
+        po, lo, sh = self.shapes[m]
+        return sh, self.planes.data_ptr() + 4 * po, self.levels.data_ptr() + 4 * lo
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    report("tiny expert (hidden 256, inter 128, group 64)")
+    return DevExpert(synth.WORKLOADS[0])
+
+
+def test_device_synth_is_host_synth():
+    report("device synth vs host synth")
+    syn = DeviceSynth()
+    for (cfg, layer, e, m, rows, cols, g, r0, n) in [(1, 0, 5, 0, 1024, 4096, 128, 0, 3),
+                                                     (1, 0, 511, 2, 4096, 1024, 128, 4090, 6),
+                                                     (0, 0, 0, 1, 128, 256, 64, 7, 9)]:
+        wl = synth.WORKLOADS[cfg]
+        buf = torch.empty(n * (cols // g) * 256, dtype=torch.float32, device="cuda")
+        syn.leaves_into(buf, wl.seed, cfg, layer, e, m, cols // g, r0, n)
+        want = synth.leaves(wl.seed, cfg, layer, e, m, rows, cols // g, r0, r0 + n)
+        assert np.array_equal(host(buf).view(np.uint32), want.reshape(-1).view(np.uint32))
+        cb = torch.empty(n * cols, dtype=torch.uint8, device="cuda")
+        syn.codes_into(cb, wl.seed, cfg, layer, e, m, cols, r0, n)
+        assert np.array_equal(host(cb), synth.codes(wl.seed, cfg, layer, e, m, rows, cols, r0,
+                                                    r0 + n).reshape(-1))
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_device_encoder_bit_exact(weighted):
+    report(f"device encoder weighted={weighted}")
+    x = DevExpert(synth.WORKLOADS[0], weighted=weighted)
+    planes = host(x.planes).view(np.uint32).reshape(8, x.pw)
+    levels = host(x.levels)
+    for m in range(3):
+        po, lo, sh = x.shapes[m]
+        n = pm.pm_plane_words(sh)
+        assert np.array_equal(planes[:, po:po + n].reshape(8, sh.rows, sh.cols // 32),
+                              x.enc["planes"][m])
+        want = np.concatenate([x.enc["levels"][m][d].reshape(-1) for d in range(1, 9)])
+        got = levels[lo:lo + pm.pm_levels_floats(sh)]
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_unpack_and_dequant_bit_exact(tiny):
+    report("unpack prefix + dequant, all k")
+    for m in range(3):
+        sh, pp, lp = tiny.mat(m)
+        for k in range(1, 9):
+            pre = torch.empty(sh.rows * sh.cols, dtype=torch.uint8, device="cuda")
+            pm.pm_debug_unpack_prefix(sh, k, pp, tiny.pw, pre)
+            want = oracle.prefix_codes(tiny.enc["planes"][m], k)
+            assert np.array_equal(host(pre).reshape(sh.rows, sh.cols), want)
+            wv = torch.empty(sh.rows * sh.cols, dtype=torch.float32, device="cuda")
+            pm.pm_debug_dequant(sh, k, pp, tiny.pw, lp, wv)
+            wq = oracle.dequant(tiny.enc["planes"][m], tiny.enc["levels"][m], k, tiny.wl.group)
+            assert np.array_equal(host(wv).reshape(sh.rows, sh.cols).view(np.uint32),
+                                  wq.view(np.uint32))
+            w16 = torch.empty(sh.rows * sh.cols, dtype=torch.int16, device="cuda")
+            pm.pm_materialize_fp16(sh, k, pp, tiny.pw, lp, w16)
+            assert np.array_equal(host(w16).view(np.float16).reshape(sh.rows, sh.cols),
+                                  wq.astype(np.float16))
+
+
+def test_gemv_all_k_and_determinism(tiny):
+    report("prefix GEMV, 3 matrices x 8 prefixes")
+    for m in range(3):
+        sh, pp, lp = tiny.mat(m)
+        x = synth.activation(tiny.wl.seed, 0, 0, m, sh.cols)
+        xd = dev(x)
+        for k in range(1, 9):
+            y = torch.empty(sh.rows, dtype=torch.float32, device="cuda")
+            pm.pm_expert_gemv(sh, k, pp, tiny.pw, lp, xd, y)
+            want, S = oracle.gemv(tiny.enc["planes"][m], tiny.enc["levels"][m], k, tiny.wl.group, x)
+            got = host(y)
+            assert_close(got, want, S, f"m={m} k={k}")
+            y2 = torch.empty_like(y)
+            pm.pm_expert_gemv(sh, k, pp, tiny.pw, lp, xd, y2)
+            assert np.array_equal(host(y2).view(np.uint32), got.view(np.uint32))
+
+
+def test_gemv_onehot_columns_bit_exact(tiny):
+    report("one-hot columns")
+    for m in (0, 2):
+        sh, pp, lp = tiny.mat(m)
+        for k in (1, 2, 3, 5, 8):
+            wq = oracle.dequant(tiny.enc["planes"][m], tiny.enc["levels"][m], k, tiny.wl.group)
+            for i in (0, 1, 31, 32, sh.cols - 1):
+                x = np.zeros(sh.cols, np.float32)
+                x[i] = 1.0
+                y = torch.empty(sh.rows, dtype=torch.float32, device="cuda")
+                pm.pm_expert_gemv(sh, k, pp, tiny.pw, lp, dev(x), y)
+                assert np.array_equal(host(y).view(np.uint32), wq[:, i].view(np.uint32))
+
+
+def test_gemv_poisoned_planes_and_levels(tiny):
+    report("poison planes >= k and levels != k")
+    syn = DeviceSynth()
+    sh, pp, lp = tiny.mat(1)
+    x = dev(synth.activation(3, 0, 0, 0, sh.cols))
+    for k in range(1, 9):
+        y = torch.empty(sh.rows, dtype=torch.float32, device="cuda")
+        pm.pm_expert_gemv(sh, k, pp, tiny.pw, lp, x, y)
+        base = host(y).copy()
+        planes = tiny.planes.clone()
+        levels = tiny.levels.clone()
+        pv = planes.view(8, tiny.pw)
+        if k < 8:
+            syn.poison_into(pv[k:].reshape(-1), 99, k)
+        po, lo, _ = tiny.shapes[1]
+        lvv = levels[lo:lo + pm.pm_levels_floats(sh)]
+        for d in range(1, 9):
+            if d == k:
+                continue
+            a = pm.pm_level_offset(sh, d)
+            n = pm.pm_levels_floats(sh) // 510 * (1 << d)
+            syn.poison_into(lvv[a:a + n].view(torch.int32), 7, d)
+        y2 = torch.empty_like(y)
+        pm.pm_expert_gemv(sh, k, planes.data_ptr() + 4 * po, tiny.pw, levels.data_ptr() + 4 * lo,
+                          x, y2)
+        assert np.array_equal(host(y2).view(np.uint32), base.view(np.uint32)), f"k={k}"
+
+
+@pytest.mark.parametrize("rows,cols,group", [(37, 96, 32), (1, 32, 32), (5, 4096, 128),
+                                             (4096, 1024, 128), (3, 0, 64)])
+def test_gemv_edge_shapes(rows, cols, group):
+    report(f"edge shape {rows}x{cols} g{group}")
+    sh = pm.mshape(rows, cols, group)
+    lv = synth.leaves(5, 0, 0, 1, 0, rows, cols // group) if cols else np.zeros((rows, 0, 256), np.float32)
+    cd = synth.codes(5, 0, 0, 1, 0, rows, cols) if cols else np.zeros((rows, 0), np.uint8)
+    pw = max(1, rows * cols // 32)
+    planes = np.zeros((8, pw), np.uint32)
+    levels = np.zeros(max(1, pm.pm_levels_floats(sh)), np.float32)
+    pm.pm_encode_matrix(sh, cd, lv, None, planes, pw, levels)
+    x = synth.activation(5, 0, 0, 0, max(cols, 1))[:cols]
+    dp, dl, dx = dev(planes), dev(levels), dev(np.concatenate([x, [0.0]]).astype(np.float32))
+    for k in (1, 2, 3, 4, 6, 8):
+        y = torch.full((rows,), 7.0, dtype=torch.float32, device="cuda")
+        pm.pm_expert_gemv(sh, k, dp, pw, dl, dx, y)
+        got = host(y)
+        if cols == 0:
+            assert np.all(got == 0)
+            continue
+        pl = planes[:, :rows * cols // 32].reshape(8, rows, cols // 32)
+        lvd = oracle.tree_levels(lv)
+        want, S = oracle.gemv(pl, lvd, k, group, x)
+        assert_close(got, want, S, f"{rows}x{cols} k={k}")
+
+
+# ---------------------------------------------------------------- MoE forward
+def single_expert_store(wl, li=None):
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    st = pm.pm_store_create(e, 1, 1)
+    PoolFiller(wl).fill(st, 0, 0)
+    return st
+
+
+def test_forward_tiny_all_k_triples():
+    report("forward, tiny expert, all 512 k triples")
+    wl = synth.WORKLOADS[0]
+    st = single_expert_store(wl)
+    enc = oracle.encode_expert(synth.expert_inputs(wl, 0, 0), wl.group)
+    x = synth.activation(wl.seed, 0, 0, 0, wl.hidden)
+    xd = dev(x[None])
+    ys = []
+    triples = [(a, b, c) for a in range(1, 9) for b in range(1, 9) for c in range(1, 9)]
+    for (a, b, c) in triples:
+        y = torch.empty((1, wl.hidden), dtype=torch.float32, device="cuda")
+        pm.pm_moe_token_forward(st, 0, np.array([[0]]), np.array([[1.0]], np.float32),
+                                np.array([[[a, b, c]]]), xd, y)
+        ys.append(y)
+    torch.cuda.synchronize()
+    for (a, b, c), y in zip(triples, ys):
+        r = oracle.expert_ffn(enc, a, b, c, x)
+        assert_close(host(y)[0], r["y"], r["Sy"], f"k=({a},{b},{c})")
+    st.close()
+
+
+@pytest.fixture(scope="module")
+def layer_store():
+    """configs[1]: a 512-expert layer; slots are filled on demand."""
+    wl = synth.WORKLOADS[1]
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    st = pm.pm_store_create(e, 1, wl.n_experts)
+    filler = PoolFiller(wl)
+    filled = set()
+
+    def ensure(ids):
+        for i in ids:
+            if int(i) not in filled:
+                filler.fill(st, 0, int(i))
+                filled.add(int(i))
+        torch.cuda.synchronize()
+
+    yield wl, st, ensure
+    st.close()
+
+
+def test_forward_layer_full_size(layer_store):
+    report("configs[1]: 512-expert layer, one token, mean k 2.5, sampled rows")
+    wl, st, ensure = layer_store
+    ids, w, k = oc.route_and_bits(1, 0, step=0)
+    # the product's routing and allocation agree with the oracle's
+    pids, pw_ = pm.pm_route_topk(synth.router_logits(wl.seed, 1, 0, 0, wl.n_experts, step=0)[None], 10)
+    assert pids[0].tolist() == ids.tolist()
+    err = synth.error_profiles(wl.seed, 1, 0, wl.n_experts)
+    assert pm.pm_allocate_bits(ids[None], w[None], err, wl.budget)[0].tolist() == k[:, 0].tolist()
+    assert int(k[:, 0].sum()) == 25
+    ensure(ids)
+    x = synth.activation(wl.seed, 1, 0, 0, wl.hidden, step=0)
+    y = torch.empty((1, wl.hidden), dtype=torch.float32, device="cuda")
+    pm.pm_moe_token_forward(st, 0, ids[None], w[None], k[None], dev(x[None]), y)
+    got = host(y)[0]
+    rows = oc.sample_rows(wl.hidden, 48, 1)
+    want, S = oc.token_layer(1, 0, ids, w, k, x, rows)
+    assert_close(got[rows], want, S, "configs[1]")
+    # determinism
+    y2 = torch.empty_like(y)
+    pm.pm_moe_token_forward(st, 0, ids[None], w[None], k[None], dev(x[None]), y2)
+    assert np.array_equal(host(y2).view(np.uint32), host(y).view(np.uint32))
+
+
+@pytest.mark.parametrize("kfix", [4, 8, None])
+def test_forward_uniform_precisions_and_materialize(layer_store, kfix):
+    report(f"configs[3]: k={kfix or 'mixed'} direct and materialize-fp16")
+    wl, st, ensure = layer_store
+    ids, w, k = oc.route_and_bits(1, 0, step=0, kfix=kfix)
+    ensure(ids)
+    x = synth.activation(wl.seed, 1, 0, 0, wl.hidden, step=0)
+    y = torch.empty((1, wl.hidden), dtype=torch.float32, device="cuda")
+    pm.pm_moe_token_forward(st, 0, ids[None], w[None], k[None], dev(x[None]), y)
+    rows = oc.sample_rows(wl.hidden, 24, 2)
+    want, S = oc.token_layer(1, 0, ids, w, k, x, rows)
+    assert_close(host(y)[0][rows], want, S, f"direct k={kfix}")
+    # the materialize-then-GEMV comparator on the first selected expert's gate
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    pp, lp = pm.pm_store_slot(st, 0, int(ids[0]))
+    po, lo, sh = pm.pm_expert_matrix_offsets(e, 0)
+    w16 = torch.empty(sh.rows * sh.cols, dtype=torch.int16, device="cuda")
+    pm.pm_materialize_fp16(sh, int(k[0][0]), pp + 4 * po, pm.pm_expert_plane_words(e),
+                           lp + 4 * lo, w16)
+    yg = torch.empty(sh.rows, dtype=torch.float32, device="cuda")
+    pm.pm_gemv_fp16(sh, w16, dev(x), yg)
+    (pg, lg), _ = oc.gate_up(1, 0, int(ids[0]))
+    wg, sg = oracle.gemv_materialized_fp16(pg, lg, int(k[0][0]), wl.group, x)
+    assert_close(host(yg), wg, sg, "materialized gate")
+
+
+def test_forward_sixty_layers():
+    report("configs[2]: 60 layers x top-10, sampled rows on 2 layers")
+    wl = synth.WORKLOADS[2]
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    st = pm.pm_store_create(e, wl.n_layers, wl.n_experts)
+    filler = PoolFiller(wl)
+    plan = []
+    for layer in range(wl.n_layers):
+        ids, w, k = oc.route_and_bits(2, layer, step=0)
+        for i in ids:
+            filler.fill(st, layer, int(i))
+        plan.append((ids, w, k))
+    torch.cuda.synchronize()
+    xs = [synth.activation(wl.seed, 2, layer, 0, wl.hidden) for layer in range(wl.n_layers)]
+    ys = []
+    for layer, (ids, w, k) in enumerate(plan):
+        y = torch.empty((1, wl.hidden), dtype=torch.float32, device="cuda")
+        pm.pm_moe_token_forward(st, layer, ids[None], w[None], k[None], dev(xs[layer][None]), y)
+        ys.append(y)
+    torch.cuda.synchronize()
+    for layer in (0, 59):
+        ids, w, k = plan[layer]
+        rows = oc.sample_rows(wl.hidden, 16, 3 + layer)
+        want, S = oc.token_layer(2, layer, ids, w, k, xs[layer], rows)
+        assert_close(host(ys[layer])[0][rows], want, S, f"layer {layer}")
+    st.close()
+
+
+def test_forward_batch8_grouped_with_topup():
+    report("configs[4]: B=8 grouped, 20% topped up from pinned host")
+    wl = synth.WORKLOADS[4]
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    pw = pm.pm_expert_plane_words(e)
+    st = pm.pm_store_create(e, 1, wl.n_experts)
+    filler = PoolFiller(wl)
+    B = wl.n_tokens
+    routes = [oc.route_and_bits(4, 0, step=0, token=t) for t in range(B)]
+    ids = np.stack([r[0] for r in routes])
+    w = np.stack([r[1] for r in routes])
+    k = np.stack([r[2] for r in routes])
+    distinct = sorted(set(int(i) for i in ids.reshape(-1)))
+    for i in distinct:
+        filler.fill(st, 0, i)
+    torch.cuda.synchronize()
+    kmax = {i: int(k[ids == i].max()) for i in distinct}
+    cand = [i for i in distinct if kmax[i] >= 2]
+    pick = synth.words(wl.seed, synth.KIND_TRUNC, 4, 0, 0, 0, len(cand)).argsort()
+    n_short = int(np.ceil(0.2 * len(distinct)))
+    short = [cand[int(j)] for j in pick[:n_short]]
+    sources = {}
+    expected_planes = 0
+    syn = DeviceSynth()
+    for j, i in enumerate(short):
+        pp, lp = pm.pm_store_slot(st, 0, i)
+        planes_t = torch.empty(8 * pw, dtype=torch.int32, device="cuda")
+        levels_t = torch.empty(pm.pm_expert_levels_floats(e), dtype=torch.float32, device="cuda")
+        # keep a pinned host source of the full expert
+        torch.cuda.synchronize()
+        src_p = torch.empty(8 * pw, dtype=torch.int32, pin_memory=True)
+        src_l = torch.empty(pm.pm_expert_levels_floats(e), dtype=torch.float32, pin_memory=True)
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        assert hip.hipMemcpy(ctypes.c_void_p(src_p.data_ptr()), ctypes.c_void_p(pp),
+                             ctypes.c_size_t(8 * pw * 4), 2) == 0
+        assert hip.hipMemcpy(ctypes.c_void_p(src_l.data_ptr()), ctypes.c_void_p(lp),
+                             ctypes.c_size_t(src_l.numel() * 4), 2) == 0
+        sources[i] = (src_p, src_l)
+        del planes_t, levels_t
+        pm.pm_store_attach_host(st, 0, i, src_p.data_ptr(), src_l.data_ptr())
+        r = 1 + int(synth.words(wl.seed, synth.KIND_TRUNC, 4, 0, 1, j, 1)[0] % (kmax[i] - 1))
+        pm.pm_store_truncate(st, 0, i, r)
+        # poison the planes that are no longer resident
+        slot_planes = torch.empty(0)
+        n_poison = (8 - r) * pw
+        tmp = torch.empty(n_poison, dtype=torch.int32, device="cuda")
+        syn.poison_into(tmp, 5, j)
+        assert hip.hipMemcpy(ctypes.c_void_p(pp + 4 * r * pw), ctypes.c_void_p(tmp.data_ptr()),
+                             ctypes.c_size_t(n_poison * 4), 3) == 0
+        expected_planes += kmax[i] - r
+    x = np.stack([synth.activation(wl.seed, 4, 0, t, wl.hidden) for t in range(B)])
+    xd = dev(x)
+    y = torch.empty((B, wl.hidden), dtype=torch.float32, device="cuda")
+    with pytest.raises(pm.PMError) as ei:
+        pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y)
+    assert ei.value.status == pm.PM_ERR_NOT_RESIDENT
+    _, _, planes_before, _ = pm.pm_store_copy_stats(st)
+    pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y, flags=pm.PM_AUTO_TOPUP)
+    got = host(y)
+    _, _, planes_after, _ = pm.pm_store_copy_stats(st)
+    assert planes_after - planes_before == expected_planes
+    for i in short:
+        assert pm.pm_store_resident(st, 0, i) == kmax[i]
+    # each token of the batch equals that token run alone
+    for t in (0, 5):
+        y1 = torch.empty((1, wl.hidden), dtype=torch.float32, device="cuda")
+        pm.pm_moe_token_forward(st, 0, ids[t:t + 1], w[t:t + 1], k[t:t + 1], xd[t:t + 1], y1)
+        assert np.array_equal(host(y1)[0].view(np.uint32), got[t].view(np.uint32))
+    for t in (0, 3):
+        rows = oc.sample_rows(wl.hidden, 12, 10 + t)
+        want, S = oc.token_layer(4, 0, ids[t], w[t], k[t], x[t], rows)
+        assert_close(got[t][rows], want, S, f"token {t}")
+    st.close()
