@@ -14,7 +14,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpm.so")
+# PM_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("PM_LIB") or os.path.join(_HERE, "libpm.so")
 
 PM_OK = 0
 PM_ERR_ARG = -1

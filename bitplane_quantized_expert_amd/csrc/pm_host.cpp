@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -255,6 +256,9 @@ static pm_status check_matrix_call(pm_matrix_shape s, int k, const void* planes,
     return PM_OK;
 }
 
+pm_status gemv_lut(pm_matrix_shape s, int k, const uint32_t* d_planes, size_t pstride,
+                   const float* d_levels, const float* d_x, float* d_y, hipStream_t st);
+
 extern "C" pm_status pm_expert_gemv(pm_matrix_shape s, int k, const uint32_t* d_planes,
                                     size_t pstride, const float* d_levels, const float* d_x,
                                     float* d_y, void* stream) {
@@ -262,6 +266,8 @@ extern "C" pm_status pm_expert_gemv(pm_matrix_shape s, int k, const uint32_t* d_
     if (st) return st;
     if (s.rows == 0) return PM_OK;
     if (s.cols > 0 && !d_x) return fail(PM_ERR_ARG, "null x");
+    if (k <= kLutMaxK && s.cols > 0 && s.cols % kSliceCols == 0 && kSliceCols % s.group == 0)
+        return gemv_lut(s, k, d_planes, pstride, d_levels, d_x, d_y, (hipStream_t)stream);
     HIP_TRY(launch_gemv(s.rows, s.cols, s.group, k, d_planes, pstride, d_levels, d_x, d_y,
                         (hipStream_t)stream));
     return PM_OK;
@@ -674,6 +680,161 @@ extern "C" pm_status pm_store_set_profile_events(pm_store* s, void* const* event
     return PM_OK;
 }
 
+// ---- LUT path: launch descriptions travel as kernel arguments.
+// Target number of LUT workgroups per launch: one per compute unit (each
+// holds 132 KiB of LDS).
+static int lut_wg_target() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            cus > 0)
+            n = cus;
+        else
+            n = 256;
+    }
+    return n;
+}
+
+namespace {
+struct JobSpec {                       // a LUT job before it is packed into a launch
+    KJob job;
+    int64_t cost;                      // rows * lut_row_cost
+};
+}  // namespace
+
+// Workgroups per job for the per-job map: n_total split by cost (largest
+// remainder), at least one each.
+static void assign_wg0(std::vector<JobSpec>& js, size_t j0, size_t j1, int n_total, KLaunch& L) {
+    const size_t n = j1 - j0;
+    n_total = std::max<int>(n_total, int(n));
+    double C = 0;
+    for (size_t j = j0; j < j1; ++j) C += double(js[j].cost);
+    std::vector<int> a(n);
+    std::vector<double> share(n);
+    int sum = 0;
+    for (size_t j = 0; j < n; ++j) {
+        share[j] = C > 0 ? n_total * double(js[j0 + j].cost) / C : double(n_total) / n;
+        a[j] = std::max(1, int(share[j]));
+        sum += a[j];
+    }
+    while (sum > n_total) {
+        size_t b = 0;
+        for (size_t j = 1; j < n; ++j)
+            if (a[j] > a[b]) b = j;
+        if (a[b] <= 1) break;
+        --a[b];
+        --sum;
+    }
+    while (sum < n_total) {
+        size_t b = 0;
+        for (size_t j = 1; j < n; ++j)
+            if (share[j] - a[j] > share[b] - a[b]) b = j;
+        ++a[b];
+        ++sum;
+    }
+    int w = 0;
+    for (size_t j = 0; j < n; ++j) {
+        L.job[j] = js[j0 + j].job;
+        L.job[j].wg0 = w;
+        w += a[j];
+    }
+    L.n_jobs = int(n);
+    L.n_wgq = w;
+}
+
+// Pack jobs into launches of at most kMaxLaunchJobs.  contig: one source for
+// all jobs (a workgroup may span several); else one job per workgroup.
+static void pack_launches(std::vector<JobSpec>& js, const KLaunch& proto, bool contig,
+                          std::vector<KLaunch>& out) {
+    int64_t all = 0;
+    for (auto& j : js) all += j.cost;
+    const int target = std::max(1, lut_wg_target() / proto.S);
+    for (size_t j0 = 0; j0 < js.size(); j0 += kMaxLaunchJobs) {
+        const size_t j1 = std::min(js.size(), j0 + kMaxLaunchJobs);
+        int64_t part = 0;
+        for (size_t j = j0; j < j1; ++j) part += js[j].cost;
+        const int n = std::max(1, int(std::lround(double(target) * double(part) / double(all))));
+        out.push_back(proto);
+        KLaunch& L = out.back();
+        if (contig) {
+            L.map = kMapContig;
+            L.n_jobs = int(j1 - j0);
+            for (size_t j = j0; j < j1; ++j) L.job[j - j0] = js[j].job;
+            L.n_wgq = n;
+        } else {
+            L.map = kMapPerJob;
+            assign_wg0(js, j0, j1, n, L);
+        }
+    }
+}
+
+// Per-stream partial-sum buffers of pm_expert_gemv's LUT path.
+namespace {
+struct StreamBuf {
+    float* p = nullptr;
+    size_t n = 0;
+};
+std::mutex g_gemv_mu;
+std::map<hipStream_t, StreamBuf> g_gemv_bufs;
+}  // namespace
+
+static pm_status gemv_partials(hipStream_t st, size_t n, float** out) {
+    std::lock_guard<std::mutex> lk(g_gemv_mu);
+    StreamBuf& b = g_gemv_bufs[st];
+    if (b.n < n) {
+        if (b.p) {
+            HIP_TRY(hipStreamSynchronize(st));
+            HIP_TRY(hipFree(b.p));
+            b.p = nullptr;
+            b.n = 0;
+        }
+        hipError_t e = hipMalloc(&b.p, n * sizeof(float));
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(PM_ERR_OOM, "GEMV workspace allocation failed: %s", hipGetErrorString(e));
+        }
+        b.n = n;
+    }
+    *out = b.p;
+    return PM_OK;
+}
+
+pm_status gemv_lut(pm_matrix_shape s, int k, const uint32_t* d_planes, size_t pstride,
+                   const float* d_levels, const float* d_x, float* d_y, hipStream_t st) {
+    const int S = s.cols / kSliceCols;
+    const size_t nb = size_t(s.rows) * (s.cols / s.group);
+    KLaunch L{};
+    L.x = d_x;
+    L.pstride = pstride;
+    L.S = S;
+    L.rows = s.rows;
+    L.W = s.cols / 32;
+    L.wpg = s.group / 32;
+    L.out_stride = s.rows;
+    L.x_stride = 0;
+    L.map = kMapContig;
+    L.n_jobs = 1;
+    KJob& jb = L.job[0];
+    jb.planes = d_planes;
+    jb.lvk = d_levels + level_offset(nb, k);
+    jb.k = int8_t(k);
+    jb.src = 0;
+    if (S == 1) {
+        jb.out = d_y;
+    } else {
+        pm_status r = gemv_partials(st, size_t(S) * s.rows, &jb.out);
+        if (r) return r;
+    }
+    // workgroups per slice: enough to fill the device, at least 32 rows each
+    const int target = std::max(1, lut_wg_target() / S);
+    L.n_wgq = std::max(1, std::min(target, (s.rows + 31) / 32));
+    HIP_TRY(launch_lut(L, false, st));
+    if (S > 1) HIP_TRY(launch_sum_slices(jb.out, S, s.rows, d_y, st));
+    return PM_OK;
+}
+
 // ---------------------------------------------------------------- MoE forward
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -722,6 +883,8 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     if (n_tokens < 0 || top_k < 1) return fail(PM_ERR_ARG, "n_tokens=%d top_k=%d", n_tokens, top_k);
     if (n_tokens == 0) return PM_OK;
     if (!h_ids || !h_w || !h_k || !d_x || !d_y) return fail(PM_ERR_ARG, "null pointer");
+    if (top_k > kMaxLaunchUses)
+        return fail(PM_ERR_ARG, "top_k=%d above %d", top_k, kMaxLaunchUses);
     hipStream_t compute = (hipStream_t)compute_v;
     const Geom& g = s->geom;
 
@@ -738,15 +901,16 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
             if (e < 0 || e >= s->n_experts)
                 return fail(PM_ERR_ARG, "ids[%d][%d]=%d outside 0..%d", t, j, e, s->n_experts - 1);
             if (!std::isfinite(h_w[u])) return fail(PM_ERR_ARG, "w[%d][%d] not finite", t, j);
+            Use& us = uses[u];
             for (int m = 0; m < 3; ++m) {
                 const int k = h_k[size_t(u) * 3 + m];
                 if (k < 1 || k > kBits)
                     return fail(PM_ERR_PREFIX, "k[%d][%d][%d]=%d outside 1..8", t, j, m, k);
-                uses[u].k[m] = k;
+                us.k[m] = k;
             }
-            uses[u].w = h_w[u];
-            uses[u].tok = t;
-            uses[u].slot = j;
+            us.w = h_w[u];
+            us.tok = t;
+            us.slot = j;
             auto it = item_of.find(e);
             int d;
             if (it == item_of.end()) {
@@ -793,91 +957,236 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return late[a] < late[b]; });
     int n_res = 0;
     while (n_res < n_items && !late[order[n_res]]) ++n_res;
+    auto slot_of_item = [&](int d) -> Slot& {
+        return s->slots[size_t(layer) * s->n_experts + item_expert[d]];
+    };
 
-    // ---- workspace
-    const size_t fG = align256(size_t(n_uses) * g.inter);
-    const size_t fY = align256(size_t(n_uses) * g.hidden);
-    const size_t list_bytes = align256(sizeof(Item) * n_items) + align256(sizeof(Use) * n_uses) +
-                              align256(sizeof(int32_t) * n_uses);
-    pm_status st = ensure_workspace(s, 2 * fG + fY, list_bytes);
+    // ---- path of every (use, matrix): LUT for an unshared expert at k <= 5
+    // when the columns split into 1024-column slices (at most 15), else direct
+    const bool gu_lut_shape = g.hidden % kSliceCols == 0 && kSliceCols % g.group == 0 &&
+                              g.hidden / kSliceCols <= 15;
+    const bool dn_lut_shape = g.inter % kSliceCols == 0 && kSliceCols % g.group == 0;
+    const int S_gu = gu_lut_shape ? g.hidden / kSliceCols : 1;
+    const int S_dn = dn_lut_shape ? g.inter / kSliceCols : 1;
+    for (int d = 0; d < n_items; ++d) {
+        const bool alone = item_uses[d].size() == 1;
+        for (int u : item_uses[d]) {
+            for (int m = 0; m < 3; ++m) {
+                const bool shape_ok = m < 2 ? gu_lut_shape : dn_lut_shape;
+                const bool lut = alone && shape_ok && uses[u].k[m] <= kLutMaxK;
+                uses[u].direct[m] = lut ? 0 : 1;
+                uses[u].slices[m] = lut ? (m < 2 ? S_gu : S_dn) : 1;
+            }
+        }
+    }
+
+    // ---- workspace: partial sums (device)
+    const size_t fGU = align256(size_t(n_uses) * 2 * S_gu * g.inter);
+    const size_t fH = align256(size_t(n_uses) * g.inter);
+    const size_t fY = align256(size_t(n_uses) * S_dn * g.hidden);
+    // the work list is uploaded only when direct-path items exist
+    std::vector<int> dir_gu[2], dir_dn;      // positions in `order`
+    for (int grp = 0; grp < 2; ++grp) {
+        const int i0 = grp == 0 ? 0 : n_res, i1 = grp == 0 ? n_res : n_items;
+        for (int i = i0; i < i1; ++i) {
+            bool any = false;
+            for (int u : item_uses[order[i]]) any |= uses[u].direct[0] || uses[u].direct[1];
+            if (any) dir_gu[grp].push_back(i);
+        }
+    }
+    for (int i = 0; i < n_items; ++i) {
+        bool any = false;
+        for (int u : item_uses[order[i]]) any |= uses[u].direct[2] != 0;
+        if (any) dir_dn.push_back(i);
+    }
+    const size_t n_dir = dir_gu[0].size() + dir_gu[1].size() + dir_dn.size();
+    const size_t list_bytes = n_dir == 0 ? 0
+                              : align256(sizeof(Item) * n_items) + align256(sizeof(Use) * n_uses) +
+                                    align256(sizeof(int32_t) * n_uses) + align256(sizeof(Item) * n_dir);
+    pm_status st = ensure_workspace(s, fGU + fH + fY, list_bytes);
     if (st) return st;
+    Partials P;
+    P.gu = s->ws.d_buf;
+    P.h = s->ws.d_buf + fGU;
+    P.y = s->ws.d_buf + fGU + fH;
+    P.gu_smax = S_gu;
+    P.dn_smax = S_dn;
+
+    // ---- LUT launches
+    KLaunch gu_proto{};
+    gu_proto.x = d_x;
+    gu_proto.pstride = g.plane_words;
+    gu_proto.S = S_gu;
+    gu_proto.rows = g.inter;
+    gu_proto.W = g.hidden / 32;
+    gu_proto.wpg = g.group / 32;
+    gu_proto.out_stride = g.inter;
+    gu_proto.x_stride = g.hidden;
+    KLaunch dn_proto{};
+    dn_proto.gu = P.gu;
+    dn_proto.gu_smax = S_gu;
+    dn_proto.inter = g.inter;
+    dn_proto.pstride = g.plane_words;
+    dn_proto.S = S_dn;
+    dn_proto.rows = g.hidden;
+    dn_proto.W = g.inter / 32;
+    dn_proto.wpg = g.group / 32;
+    dn_proto.out_stride = g.hidden;
+    std::vector<KLaunch> L_gu[2], L_dn;
+    for (int grp = 0; grp < 2; ++grp) {
+        const int i0 = grp == 0 ? 0 : n_res, i1 = grp == 0 ? n_res : n_items;
+        std::vector<JobSpec> js;
+        for (int i = i0; i < i1; ++i) {
+            const int d = order[i];
+            const Slot& sl = slot_of_item(d);
+            for (int u : item_uses[d]) {
+                for (int m = 0; m < 2; ++m) {
+                    if (uses[u].direct[m]) continue;
+                    const int k = uses[u].k[m];
+                    JobSpec j{};
+                    j.job.planes = sl.planes + g.plane_off[m];
+                    j.job.lvk = sl.levels + g.level_off[m] +
+                                level_offset(size_t(g.inter) * (g.hidden / g.group), k);
+                    j.job.out = P.gu + (size_t(u) * 2 + m) * S_gu * g.inter;
+                    j.job.src = int16_t(uses[u].tok);
+                    j.job.k = int8_t(k);
+                    j.cost = int64_t(g.inter) * lut_row_cost(k, g.group / 32);
+                    js.push_back(j);
+                }
+            }
+        }
+        // one token: jobs may share workgroups; several tokens: one job each
+        pack_launches(js, gu_proto, n_tokens == 1, L_gu[grp]);
+    }
+    {
+        std::vector<JobSpec> js;
+        for (int i = 0; i < n_items; ++i) {
+            const int d = order[i];
+            const Slot& sl = slot_of_item(d);
+            for (int u : item_uses[d]) {
+                if (uses[u].direct[2]) continue;
+                const int k = uses[u].k[2];
+                JobSpec j{};
+                j.job.planes = sl.planes + g.plane_off[2];
+                j.job.lvk = sl.levels + g.level_off[2] +
+                            level_offset(size_t(g.hidden) * (g.inter / g.group), k);
+                j.job.out = P.y + size_t(u) * S_dn * g.hidden;
+                j.job.src = int16_t(u);
+                j.job.k = int8_t(k);
+                j.job.gsl = uint8_t(uses[u].slices[0] | (uses[u].slices[1] << 4));
+                j.cost = int64_t(g.hidden) * lut_row_cost(k, g.group / 32);
+                js.push_back(j);
+            }
+        }
+        pack_launches(js, dn_proto, false, L_dn);
+    }
+
     if (s->have_last) HIP_TRY(hipStreamWaitEvent(compute, s->last_done, 0));
 
     // ---- top-ups (side stream) for late items
     for (int i = n_res; i < n_items; ++i) {
         const int d = order[i];
-        Slot& sl = s->slots[size_t(layer) * s->n_experts + item_expert[d]];
-        st = topup_slot(s, sl, kneed[d], s->side);
+        st = topup_slot(s, slot_of_item(d), kneed[d], s->side);
         if (st) return st;
     }
 
-    // ---- work list into the pinned ring, then to the device
-    Workspace& w = s->ws;
-    const int rs = w.next;
-    w.next = (w.next + 1) % Workspace::kSlots;
-    HIP_TRY(hipEventSynchronize(w.ring_ev[rs]));
-    char* hb = w.h_ring + size_t(rs) * w.slot_bytes;
-    char* db = w.d_ring + size_t(rs) * w.slot_bytes;
-    Item* hitems = reinterpret_cast<Item*>(hb);
-    Use* huses = reinterpret_cast<Use*>(hb + align256(sizeof(Item) * n_items));
-    int32_t* hlist = reinterpret_cast<int32_t*>(hb + align256(sizeof(Item) * n_items) +
-                                                align256(sizeof(Use) * n_uses));
-    const int rpb_gu = gateup_rows_per_block(), rpb_dn = down_rows_per_block();
-    const int gu_blocks_per_item = (g.inter + rpb_gu - 1) / rpb_gu;
-    const int dn_blocks_per_item = (g.hidden + rpb_dn - 1) / rpb_dn;
-    int lpos = 0;
-    for (int i = 0; i < n_items; ++i) {
-        const int d = order[i];
-        const Slot& sl = s->slots[size_t(layer) * s->n_experts + item_expert[d]];
-        Item& it = hitems[i];
-        it.planes = sl.planes;
-        it.levels = sl.levels;
-        it.use0 = lpos;
-        it.nuse = int(item_uses[d].size());
-        for (int m = 0; m < 3; ++m) it.kmax[m] = kmax[d][m];
-        it.blk_gu = (i < n_res ? i : i - n_res) * gu_blocks_per_item;
-        it.blk_dn = i * dn_blocks_per_item;
-        for (int u : item_uses[d]) hlist[lpos++] = u;
+    // ---- direct-path work list into the pinned ring, then to the device
+    const Use* duses = nullptr;
+    const int32_t* dlist = nullptr;
+    const Item* ddir = nullptr;
+    if (n_dir > 0) {
+        Workspace& w = s->ws;
+        const int rs = w.next;
+        w.next = (w.next + 1) % Workspace::kSlots;
+        HIP_TRY(hipEventSynchronize(w.ring_ev[rs]));
+        char* hb = w.h_ring + size_t(rs) * w.slot_bytes;
+        char* db = w.d_ring + size_t(rs) * w.slot_bytes;
+        size_t off = 0;
+        auto carve = [&](size_t bytes) {
+            const size_t o = off;
+            off += align256(bytes);
+            return o;
+        };
+        const size_t o_items = carve(sizeof(Item) * n_items);
+        const size_t o_uses = carve(sizeof(Use) * n_uses);
+        const size_t o_list = carve(sizeof(int32_t) * n_uses);
+        const size_t o_dir = carve(sizeof(Item) * n_dir);
+        Item* hitems = reinterpret_cast<Item*>(hb + o_items);
+        int32_t* hlist = reinterpret_cast<int32_t*>(hb + o_list);
+        int lpos = 0;
+        for (int i = 0; i < n_items; ++i) {
+            const int d = order[i];
+            const Slot& sl = slot_of_item(d);
+            Item& it = hitems[i];
+            it.planes = sl.planes;
+            it.levels = sl.levels;
+            it.use0 = lpos;
+            it.nuse = int(item_uses[d].size());
+            for (int m = 0; m < 3; ++m) it.kmax[m] = kmax[d][m];
+            it.pad = 0;
+            for (int u : item_uses[d]) hlist[lpos++] = u;
+        }
+        std::memcpy(hb + o_uses, uses.data(), sizeof(Use) * n_uses);
+        Item* hdir = reinterpret_cast<Item*>(hb + o_dir);
+        size_t ndi = 0;
+        for (auto* v : {&dir_gu[0], &dir_gu[1], &dir_dn})
+            for (int i : *v) hdir[ndi++] = hitems[i];
+        HIP_TRY(hipMemcpyAsync(db, hb, off, hipMemcpyHostToDevice, compute));
+        HIP_TRY(hipEventRecord(w.ring_ev[rs], compute));
+        duses = reinterpret_cast<const Use*>(db + o_uses);
+        dlist = reinterpret_cast<const int32_t*>(db + o_list);
+        ddir = reinterpret_cast<const Item*>(db + o_dir);
     }
-    std::memcpy(huses, uses.data(), sizeof(Use) * n_uses);
-    HIP_TRY(hipMemcpyAsync(db, hb, list_bytes, hipMemcpyHostToDevice, compute));
-    HIP_TRY(hipEventRecord(w.ring_ev[rs], compute));
-    const Item* ditems = reinterpret_cast<const Item*>(db);
-    const Use* duses = reinterpret_cast<const Use*>(db + align256(sizeof(Item) * n_items));
-    const int32_t* dlist = reinterpret_cast<const int32_t*>(
-        db + align256(sizeof(Item) * n_items) + align256(sizeof(Use) * n_uses));
-    float* G = w.d_buf;
-    float* U = w.d_buf + fG;
-    float* Y = w.d_buf + 2 * fG;
+    const size_t d_gu0 = dir_gu[0].size(), d_gu1 = dir_gu[1].size();
 
     // ---- kernels
     // resident slots topped up by an earlier explicit call may still be copying
     for (int i = 0; i < n_res; ++i) {
-        Slot& sl = s->slots[size_t(layer) * s->n_experts + item_expert[order[i]]];
+        Slot& sl = slot_of_item(order[i]);
         if (sl.pending) {
             HIP_TRY(hipStreamWaitEvent(compute, sl.ready, 0));
             sl.pending = false;
         }
     }
     if (s->profiling) HIP_TRY(hipEventRecord(s->prof[0], compute));
-    if (n_res > 0)
-        HIP_TRY(launch_gateup(g, ditems, 0, n_res, n_res * gu_blocks_per_item, duses, dlist,
-                              top_k, d_x, G, U, compute));
+    for (const KLaunch& L : L_gu[0]) HIP_TRY(launch_lut(L, false, compute));
+    if (d_gu0) HIP_TRY(launch_direct_gateup(g, ddir, int(d_gu0), duses, dlist, d_x, P, compute));
     if (n_res < n_items) {
         for (int i = n_res; i < n_items; ++i) {
-            Slot& sl = s->slots[size_t(layer) * s->n_experts + item_expert[order[i]]];
+            Slot& sl = slot_of_item(order[i]);
             HIP_TRY(hipStreamWaitEvent(compute, sl.ready, 0));
             sl.pending = false;
         }
-        HIP_TRY(launch_gateup(g, ditems, n_res, n_items - n_res,
-                              (n_items - n_res) * gu_blocks_per_item, duses, dlist, top_k, d_x,
-                              G, U, compute));
+        for (const KLaunch& L : L_gu[1]) HIP_TRY(launch_lut(L, false, compute));
+        if (d_gu1)
+            HIP_TRY(launch_direct_gateup(g, ddir + d_gu0, int(d_gu1), duses, dlist, d_x, P,
+                                         compute));
     }
     if (s->profiling) HIP_TRY(hipEventRecord(s->prof[1], compute));
-    HIP_TRY(launch_down(g, ditems, n_items, n_items * dn_blocks_per_item, duses, dlist, n_uses,
-                        G, U, Y, compute));
+    if (!dir_dn.empty()) {
+        HIP_TRY(launch_swiglu(duses, n_uses, P, g.inter, compute));
+        HIP_TRY(launch_direct_down(g, ddir + d_gu0 + d_gu1, int(dir_dn.size()), duses, dlist, P,
+                                   compute));
+    }
+    for (const KLaunch& L : L_dn) HIP_TRY(launch_lut(L, true, compute));
     if (s->profiling) HIP_TRY(hipEventRecord(s->prof[2], compute));
-    HIP_TRY(launch_combine(n_tokens, top_k, g.hidden, duses, Y, d_y, compute));
+    const int tok_per = std::max(1, kMaxLaunchUses / top_k);
+    for (int t0 = 0; t0 < n_tokens; t0 += tok_per) {
+        KCombine C{};
+        C.Y = P.y;
+        C.y = d_y;
+        C.t0 = t0;
+        C.n_tokens = std::min(tok_per, n_tokens - t0);
+        C.top_k = top_k;
+        C.hidden = g.hidden;
+        C.dn_smax = S_dn;
+        for (int a = 0; a < C.n_tokens * top_k; ++a) {
+            const Use& us = uses[size_t(t0) * top_k + a];
+            C.w[a] = us.w;
+            C.sl[a] = uint8_t(us.slices[2]);
+        }
+        HIP_TRY(launch_combine_k(C, compute));
+    }
     if (s->profiling) HIP_TRY(hipEventRecord(s->prof[3], compute));
     HIP_TRY(hipEventRecord(s->last_done, compute));
     s->have_last = true;

@@ -34,17 +34,80 @@ struct Item {
     const float* levels;           // gate, up, down levels back to back
     int32_t use0, nuse;            // uses are list[use0 .. use0 + nuse)
     int32_t kmax[3];               // largest prefix of any use, per matrix
-    int32_t blk_gu;                // first block of this item in the gate/up grid
-    int32_t blk_dn;                // first block of this item in the down grid
+    int32_t pad;
 };
 
 // A use: token `tok` reads the expert in routing slot `slot` with weight w.
-// Its index is tok * top_k + slot.
+// Its index is tok * top_k + slot.  slices[m] is the number of partial sums
+// the stage of matrix m leaves for it (1 on the direct path, one per
+// 1024-column slice on the LUT path); direct[m] marks the direct path.
 struct Use {
     int32_t k[3];
     float w;
     int32_t tok, slot;
+    int32_t slices[3];
+    int32_t direct[3];
 };
+
+// LUT path: one matrix of one use.  Row r's partial sum over column slice s
+// goes to out[s * out_stride + r].
+struct LutJob {
+    const uint32_t* planes;        // plane 0, row 0 of the matrix
+    const float* lvk;              // depth-k nodes of the matrix
+    float* out;
+    uint64_t pstride;              // words between planes
+    int32_t k, rows, W, wpg;       // prefix, rows, words per row, words per block
+    int32_t out_stride, pad;
+};
+
+// LUT path: the rows one workgroup processes, [(job0, row0), (job1, row1)),
+// against the activation slice `slice` of source `src` (a token for gate/up,
+// a use for down).  Row boundaries are even.
+struct LutWG {
+    int32_t job0, row0, job1, row1;
+    int32_t src, slice;
+};
+
+// Partial-sum workspace of a forward call (device pointers).
+struct Partials {
+    float* gu;                     // [n_uses][2][gu_smax][inter]
+    float* h;                      // [n_uses][inter], direct down only
+    float* y;                      // [n_uses][dn_smax][hidden]
+    int gu_smax, dn_smax;
+};
+
+constexpr int kSliceCols = 1024;   // columns of x covered by one LUT
+constexpr int kLutMaxK = 5;        // largest prefix read through the LUT path
+
+// LUT-path launch description, passed as kernel arguments (no upload).
+constexpr int kMaxLaunchJobs = 96;
+struct KJob {                      // one matrix of one use
+    const uint32_t* planes;        // plane 0, row 0
+    const float* lvk;              // depth-k nodes
+    float* out;                    // row r, slice s -> out[s * out_stride + r]
+    int32_t wg0;                   // per-job map: first workgroup (per slice) of the job
+    int16_t src;                   // gate/up: token; down: use
+    int8_t k;
+    uint8_t gsl;                   // down: gate slices (bits 0-3), up slices (bits 4-7)
+};
+enum { kMapContig = 0, kMapPerJob = 1 };
+struct KLaunch {
+    KJob job[kMaxLaunchJobs];
+    const float* x;                // gate/up: activation of token t at x + t * x_stride
+    const float* gu;               // down: gate/up partials [use][2][gu_smax][inter]
+    uint64_t pstride;              // words between planes
+    int32_t n_jobs, n_wgq, S, map; // jobs, workgroups per slice, slices, row map
+    int32_t rows, W, wpg, out_stride;
+    int32_t x_stride, gu_smax, inter, pad;
+};
+// Cost of one row-slice when rows are split among workgroups: its execution
+// time, dominated by the 2^k - 1 mask lookups per word plus a fixed per-row
+// share (loads, reduction, store); k = 1 rows carry a larger fixed share.
+// Measured on gfx950 (workgroup durations per prefix), in arbitrary integer
+// units so every workgroup splits alike.
+__host__ __device__ inline int64_t lut_row_cost(int k, int /*wpg*/) {
+    return k == 1 ? 400 : 220 + 75 * ((int64_t(1) << k) - 1);
+}
 
 // Kernel launchers (pm_kernels.hip).  All return hipError_t of the launch.
 hipError_t launch_gemv(int rows, int cols, int group, int k, const uint32_t* planes,
@@ -62,22 +125,38 @@ hipError_t launch_dequant(int rows, int cols, int group, int k, const uint32_t* 
 hipError_t launch_gemv_fp16(int rows, int cols, const uint16_t* w, const float* x, float* y,
                             hipStream_t st);
 
-// MoE forward stages.  `items`, `uses`, `list` are device copies of the work
-// list; G, U: fp32 [n_uses][inter]; Y: fp32 [n_uses][hidden].
-hipError_t launch_gateup(const Geom& g, const Item* items, int item0, int n_items,
-                         int n_blocks, const Use* uses, const int32_t* list, int top_k,
-                         const float* x, float* G, float* U, hipStream_t st);
-// launch_down first turns G into h = silu(G) * U in place (n_uses rows).
-hipError_t launch_down(const Geom& g, const Item* items, int n_items, int n_blocks,
-                       const Use* uses, const int32_t* list, int n_uses, float* G,
-                       const float* U, float* Y, hipStream_t st);
-hipError_t launch_combine(int n_tokens, int top_k, int hidden, const Use* uses,
-                          const float* Y, float* y, hipStream_t st);
+// LUT path: n_wgq * S workgroups of 512 threads, about 132 KiB of LDS each.
+// Gate/up (down == false): the activation slice comes from L.x; down: h of
+// use src, formed from the gate/up partials L.gu.
+hipError_t launch_lut(const KLaunch& L, bool down, hipStream_t st);
+// Combine with the weights in the kernel arguments: tokens t0 .. t0+n-1.
+constexpr int kMaxLaunchUses = 128;
+struct KCombine {
+    const float* Y;                // [n_uses][dn_smax][hidden]
+    float* y;                      // [n_tokens][hidden]
+    int32_t t0, n_tokens, top_k, hidden, dn_smax, pad;
+    float w[kMaxLaunchUses];
+    uint8_t sl[kMaxLaunchUses];
+};
+hipError_t launch_combine_k(const KCombine& C, hipStream_t st);
+// Sum of the slice partials of one GEMV: y[r] = sum_s part[s * rows + r].
+hipError_t launch_sum_slices(const float* part, int slices, int rows, float* y, hipStream_t st);
 
-// Rows of a matrix handled by one block of the gate/up and down stages.
-int gateup_rows_per_block();
-int down_rows_per_block();
-// Largest number of uses of one expert the down stage can hold in LDS.
+// Direct path (any prefix, any shape, shared experts read once per call):
+// over `n_items` items, rows_per_block rows per block.  Writes slice 0 of the
+// partials of every (use, matrix) marked direct.
+hipError_t launch_direct_gateup(const Geom& g, const Item* items, int n_items,
+                                const Use* uses, const int32_t* list, const float* x,
+                                Partials P, hipStream_t st);
+hipError_t launch_direct_down(const Geom& g, const Item* items, int n_items, const Use* uses,
+                              const int32_t* list, Partials P, hipStream_t st);
+// h of every use marked direct for down, from the gate/up partials.
+hipError_t launch_swiglu(const Use* uses, int n_uses, Partials P, int inter, hipStream_t st);
+// y[t][o] = sum_j w[t][j] * sum_s Y[t*top_k + j][s][o], slots then slices in order.
+hipError_t launch_combine(int n_tokens, int top_k, int hidden, const Use* uses, Partials P,
+                          float* y, hipStream_t st);
+
+// Largest number of uses of one expert in one call.
 int max_uses_per_item();
 
 }  // namespace pm

@@ -1,12 +1,27 @@
 // HIP kernels of libpm for gfx950 (CDNA4, 64-wide wavefronts).
 //
-// Prefix GEMV [Abs "directly executes cached 1-8-bit prefixes without
-// materializing full-precision experts"; T c25, c37]: a wave owns one output
-// row; each lane walks the row's plane words (32 weights each), reads the k
-// leading plane words of that word, forms each weight's k-bit prefix, looks
-// its value up in the depth-k node table of its block and accumulates
-// value * x in fp32.  Rows are reduced across the wave in a fixed butterfly
-// order, so results are deterministic.
+// Two ways to execute a matrix directly from its k-bit prefix [Abs
+// "directly executes cached 1-8-bit prefixes without materializing
+// full-precision experts"; T c25, c37]:
+//
+// LUT path (k <= 5; columns in slices of 1024).  The result of one block of
+// a row is sum_v node[v] * S_v, where S_v is the sum of x over the block's
+// weights whose prefix is v.  A weight word (32 inputs) has prefix v exactly
+// where the AND of the k plane words (each taken plain or inverted by the
+// bits of v) is set, and the sum of x under a 32-bit mask is four lookups in
+// a table of all 256 subset sums of each 8-input chunk of x (an activation
+// lookup table, as in T-MAC).  The table of one 1024-column slice is 128 KiB
+// of LDS; every lookup is one v_perm (the mask byte becomes the address) and
+// one ds_read.  2^k - 1 masks per word, the last bucket by subtraction from
+// the word's total.  The codebook enters as 2^k FMAs per block and row, so no
+// weight value is ever formed.  One-hot x gives exact columns.
+//
+// Direct path (any k, any shape, an expert shared by several tokens read
+// once): per weight, the prefix is assembled from the k plane words and its
+// node read from the depth-k table.
+//
+// All sums run in a fixed order (DPP row reductions, slices and slots in
+// index order), so every output is deterministic.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -19,17 +34,512 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kRowsPerBlock = kBlock / kWave;
+#ifndef PM_LUT_THREADS
+#define PM_LUT_THREADS 512
+#endif
+constexpr int kLutThreads = PM_LUT_THREADS;
+constexpr int kLutWaves = kLutThreads / kWave;
+constexpr int kLutBytes = 128 * 1024;
+constexpr int kHbufBytes = (kSliceCols + kSliceCols / 32) * 4;
 
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
+                                           false));
+}
+
+// Sum over each 16-lane row; every lane of the row gets the row's sum.
+__device__ inline float row16_sum(float v) {
+    v += dpp<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    v += dpp<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    v += dpp<0x141, 0xF>(v);   // row_half_mirror
+    v += dpp<0x140, 0xF>(v);   // row_mirror
     return v;
 }
 
+// Sum over each 32-lane half of the wave; the total lands in lanes 16..31
+// (first half) and 48..63 (second half).
+__device__ inline float half_sum(float v) {
+    v = row16_sum(v);
+    v += dpp<0x142, 0xA>(v);   // row_bcast15 into rows 1 and 3
+    return v;
+}
+
+// Sum over the wave; the total lands in lane 63.
+__device__ inline float wave_sum(float v) {
+    v = half_sum(v);
+    v += dpp<0x143, 0xC>(v);   // row_bcast31 into rows 2 and 3
+    return v;
+}
+
+__device__ inline float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// ---------------------------------------------------------------- LUT path
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) float lds_float;
+// Global-memory views: in out-of-line functions a plain pointer would be
+// generic and its loads flat_load, which also count against the LDS wait
+// counter and would serialise the prefetch with the table lookups.
+typedef __attribute__((address_space(1))) const uint32_t g_u32;
+typedef __attribute__((address_space(1))) const float g_f32;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const f32x2 g_f32x2;
+typedef __attribute__((address_space(1))) const f32x4 g_f32x4;
+typedef __attribute__((address_space(1))) float g_f32_out;
+
+// LDS layout of the activation table of one 1024-column slice: chunk c (8
+// columns 8c..8c+7), byte value b (a subset of the chunk), t = c & 3,
+// l = c >> 2 (the word of the slice the chunk belongs to):
+//   address = (t >> 1) << 16 | b << 8 | (l + 32 * (t & 1)) << 2.
+// Lane l of a half-wave reads chunks 4l..4l+3; at every lookup the 32 lanes of
+// a half-wave touch 32 different banks.
+__device__ inline uint32_t lut_addr(int c, int b) {
+    const int t = c & 3, l = c >> 2;
+    return uint32_t(((t >> 1) << 16) | (b << 8) | ((l + 32 * (t & 1)) << 2));
+}
+
+// Sum of x over the set bits of mask m for lane word l: four lookups, each a
+// v_perm (mask byte -> address bits 8..15 over the lane's base b0 / b1) and a
+// ds_read.  The table sits at LDS address 0, so the perm result is the
+// address and the +128 of odd chunks is the instruction's offset.
+__device__ inline float lds_at(uint32_t a) {
+    return *reinterpret_cast<const lds_float*>(size_t(a));
+}
+__device__ inline void lds_put(uint32_t a, float v) {
+    *reinterpret_cast<lds_float*>(size_t(a)) = v;
+}
+__device__ inline float lut_sum(uint32_t m, uint32_t b0, uint32_t b1) {
+    const uint32_t a0 = __builtin_amdgcn_perm(b0, m, 0x0C060004u);
+    const uint32_t a1 = __builtin_amdgcn_perm(b0, m, 0x0C060104u);
+    const uint32_t a2 = __builtin_amdgcn_perm(b1, m, 0x0C060204u);
+    const uint32_t a3 = __builtin_amdgcn_perm(b1, m, 0x0C060304u);
+    float s = lds_at(a0);
+    s += lds_at(a1 + 128);
+    s += lds_at(a2);
+    s += lds_at(a3 + 128);
+    return s;
+}
+
+// Masks of the prefix tree of one word, depth first: leaf V (D == K) gets the
+// mask of the weights whose prefix is V.  Leaf 2^K - 1 is not needed (its sum
+// comes by subtraction from the word's total).
+template <int K, int D, int V>
+struct PrefixMasks {
+    static __device__ inline void go(const uint32_t (&w)[K], uint32_t m,
+                                     uint32_t (&out)[(1 << K) - 1]) {
+        PrefixMasks<K, D + 1, 2 * V>::go(w, m & ~w[D], out);
+        PrefixMasks<K, D + 1, 2 * V + 1>::go(w, m & w[D], out);
+    }
+};
+template <int K, int V>
+struct PrefixMasks<K, K, V> {
+    static __device__ inline void go(const uint32_t (&)[K], uint32_t m,
+                                     uint32_t (&out)[(1 << K) - 1]) {
+        if constexpr (V != (1 << K) - 1) out[V] = m;
+    }
+};
+
+// One row's contribution of this lane's word at prefix K:
+// sum_v node(v) * S_v, S_v = sum of x where the prefix is v.  All lookups of
+// the row are issued before any is consumed, so one LDS round trip covers the
+// row; then the bucket sums are formed in v order (each from its four chunk
+// sums in chunk order) and the last bucket by subtraction.
+template <int K>
+__device__ inline float lut_row(const uint32_t (&w)[K], const float (&tab)[1 << K], float xw,
+                                uint32_t b0, uint32_t b1) {
+    constexpr int N = (1 << K) - 1;
+    uint32_t m[N];
+    PrefixMasks<K, 0, 0>::go(w, 0xFFFFFFFFu, m);
+    float r[4 * N];
+#pragma unroll
+    for (int v = 0; v < N; ++v) {
+        r[4 * v + 0] = lds_at(__builtin_amdgcn_perm(b0, m[v], 0x0C060004u));
+        r[4 * v + 1] = lds_at(__builtin_amdgcn_perm(b0, m[v], 0x0C060104u) + 128);
+        r[4 * v + 2] = lds_at(__builtin_amdgcn_perm(b1, m[v], 0x0C060204u));
+        r[4 * v + 3] = lds_at(__builtin_amdgcn_perm(b1, m[v], 0x0C060304u) + 128);
+    }
+    float acc = 0.f, last = xw;
+#pragma unroll
+    for (int v = 0; v < N; ++v) {
+        float S = r[4 * v];
+        S += r[4 * v + 1];
+        S += r[4 * v + 2];
+        S += r[4 * v + 3];
+        last -= S;
+        acc = fmaf(tab[v], S, acc);
+    }
+    return fmaf(tab[N], last, acc);
+}
+
+// The activation slice of this workgroup into the LUT.  Thread tid owns
+// chunk c = 4l + t, l = tid % 32, t = (tid / 32) % 4, and writes its subset
+// sums b = 32q .. 32q + 31 for q = tid / 128 + j * (kLutThreads / 128),
+// j < 1024 / kLutThreads; a half-wave writes 32 different banks.  Gate/up: x
+// points at the slice.  Down: h of one use for columns tid, tid + kLutThreads,
+// .. of the slice, from the gate/up partials pg (gate, ng slices) and pu (up,
+// nu slices), `stride` floats apart.  Sums with a zero term are exact.  h is
+// staged with one pad word per 32 so that the chunk-wise reads hit 32
+// different banks.
+__device__ inline void build_lut(lds_float* hbuf, const float* x, const float* pg,
+                                 const float* pu, int ng, int nu, int stride) {
+    constexpr int kQ = kLutThreads / 128;          // q values spread over threads
+    constexpr int kPer = 8 / kQ;                   // q values per thread
+    const int tid = threadIdx.x;
+    const int l = tid & 31, t = (tid >> 5) & 3;
+    const int c8 = 8 * (4 * l + t);
+    float v[8];
+    if (pg) {
+#pragma unroll
+        for (int half = 0; half < kSliceCols / kLutThreads; ++half) {
+            g_f32* g = (g_f32*)(pg + half * kLutThreads);
+            g_f32* u = (g_f32*)(pu + half * kLutThreads);
+            float gs, us;
+            if (ng <= 4 && nu <= 4) {      // all loads in flight at once
+                float gv[4], uv[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    gv[q] = q < ng ? g[size_t(q) * stride] : 0.f;
+                    uv[q] = q < nu ? u[size_t(q) * stride] : 0.f;
+                }
+                gs = gv[0];
+                us = uv[0];
+#pragma unroll
+                for (int q = 1; q < 4; ++q) {
+                    if (q < ng) gs += gv[q];
+                    if (q < nu) us += uv[q];
+                }
+            } else {
+                gs = g[0];
+                for (int q = 1; q < ng; ++q) gs += g[size_t(q) * stride];
+                us = u[0];
+                for (int q = 1; q < nu; ++q) us += u[size_t(q) * stride];
+            }
+            const int c = tid + half * kLutThreads;
+            hbuf[c + (c >> 5)] = silu_mul(gs, us);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = hbuf[c8 + i + ((c8 + i) >> 5)];
+    } else {
+        const f32x4 a = *(g_f32x4*)(x + c8);
+        const f32x4 b = *(g_f32x4*)(x + c8 + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    const int c = 4 * l + t;
+    float sub[32];
+    sub[0] = 0.f;
+#pragma unroll
+    for (int i = 1; i < 32; ++i) sub[i] = sub[i & (i - 1)] + v[__builtin_ctz(i)];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int q = (tid >> 7) + j * kQ;
+        float base = 0.f;
+        if (q & 1) base += v[5];
+        if (q & 2) base += v[6];
+        if (q & 4) base += v[7];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) lds_put(lut_addr(c, 32 * q + i), base + sub[i]);
+    }
+}
+
+template <int K>
+struct LutRowIn {
+    uint32_t w[K];
+    float tab[1 << K];
+};
+
+template <int K>
+__device__ inline void lut_load(LutRowIn<K>& in, const uint32_t* pw, const float* t,
+                                uint64_t pstride) {
+    g_u32* gw = (g_u32*)pw;
+#pragma unroll
+    for (int p = 0; p < K; ++p) in.w[p] = __builtin_nontemporal_load(gw + p * pstride);
+    if constexpr (K == 1) {
+        const f32x2 a = *(g_f32x2*)t;
+        in.tab[0] = a.x;
+        in.tab[1] = a.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < (1 << K); i += 4) {
+            const f32x4 a = *(g_f32x4*)(t + i);
+            in.tab[i] = a.x;
+            in.tab[i + 1] = a.y;
+            in.tab[i + 2] = a.z;
+            in.tab[i + 3] = a.w;
+        }
+    }
+}
+
+template <int K>
+constexpr int lut_unroll() {
+#if PM_LUT_THREADS == 1024
+    return K == 1 ? 4 : K == 2 ? 2 : K == 3 ? 2 : 1;
+#else
+    return K == 1 ? 8 : K == 2 ? 4 : K == 3 ? 3 : K == 4 ? 2 : 1;
+#endif
+}
+
+// One job segment as plain values: the lane's word and block table in row 0.
+struct Seg {
+    const uint32_t* pw;    // plane 0, row 0, this lane's word
+    const float* tab;      // depth-k table of this lane's block, row 0
+    float* out;            // outputs of this slice
+    uint64_t pstride;      // words between planes
+    int W;                 // words per row
+    int tab_row;           // floats between tables of consecutive rows
+    int r0, r1;            // rows [r0, r1)
+};
+
+// A batch: U row pairs of this wave, pairs p, p + kLutWaves, ... (rows 2p + hw).
+template <int K, int U>
+struct Batch {
+    LutRowIn<K> in[U];
+    int row[U];
+};
+
+template <int K, int U>
+__device__ inline void batch_load(Batch<K, U>& B, const Seg& sg, int p, int p1, int hw) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int pp = p + u * kLutWaves;
+        const int row = 2 * pp + hw;
+        if (pp < p1 && row >= sg.r0 && row < sg.r1) {
+            B.row[u] = row;
+            lut_load<K>(B.in[u], sg.pw + size_t(row) * sg.W, sg.tab + size_t(row) * sg.tab_row,
+                        sg.pstride);
+        } else {
+            B.row[u] = -1;
+#pragma unroll
+            for (int q = 0; q < K; ++q) B.in[u].w[q] = 0u;
+#pragma unroll
+            for (int q = 0; q < (1 << K); ++q) B.in[u].tab[q] = 0.f;
+        }
+    }
+}
+
+template <int K, int U>
+__device__ inline void batch_compute(const Batch<K, U>& B, const Seg& sg, float xw, uint32_t b0,
+                                     uint32_t b1, int l) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float acc = lut_row<K>(B.in[u].w, B.in[u].tab, xw, b0, b1);
+        acc = half_sum(acc);
+        if (l == 31 && B.row[u] >= 0) ((g_f32_out*)sg.out)[B.row[u]] = acc;
+    }
+}
+
+// Where the LUT of a workgroup comes from (see build_lut).
+struct LutSrc {
+    const float* x;
+    const float* pg;
+    const float* pu;
+    int ng, nu, stride;
+};
+
+// Rows [r0, r1) of one job for this wave, double-buffered: the next batch is
+// in flight while this one computes.  FIRST: the workgroup's first segment --
+// its first batch is issued before the LUT is built, and the lane's total of
+// x over its word is returned.  Out of line so that every prefix gets its own
+// register allocation.
+template <int K, bool FIRST>
+__device__ __noinline__ float lut_segment(lds_float* hbuf, const uint32_t* pw, const float* tab,
+                                          float* out, uint64_t pstride, int W, int tab_row,
+                                          int r0, int r1, const float* x, const float* pg,
+                                          const float* pu, int ngnu, int hstride, float xw) {
+    constexpr int U = lut_unroll<K>();
+    const Seg sg{pw, tab, out, pstride, W, tab_row, r0, r1};
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int hw = lane >> 5, l = lane & 31;
+    const uint32_t b0 = uint32_t(l) << 2, b1 = b0 | 0x10000u;
+    const int p1 = (sg.r1 + 1) >> 1;
+    constexpr int step = kLutWaves * U;
+    int p = (sg.r0 >> 1) + wave;
+    Batch<K, U> A, B;
+    batch_load<K, U>(A, sg, p, p1, hw);
+    if constexpr (FIRST) {
+        build_lut(hbuf, x, pg, pu, ngnu & 15, ngnu >> 4, hstride);
+        __syncthreads();
+        xw = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) xw += lds_at(lut_addr(4 * l + t, 255));
+    }
+    while (p < p1) {
+        batch_load<K, U>(B, sg, p + step, p1, hw);
+        batch_compute<K, U>(A, sg, xw, b0, b1, l);
+        p += step;
+        if (p >= p1) break;
+        batch_load<K, U>(A, sg, p + step, p1, hw);
+        batch_compute<K, U>(B, sg, xw, b0, b1, l);
+        p += step;
+    }
+    return xw;
+}
+
+template <bool FIRST>
+__device__ inline float lut_segment_k(int k, lds_float* hbuf, const Seg& sg, const LutSrc& src,
+                                      float xw) {
+    const int ngnu = src.ng | (src.nu << 4);
+#define PM_SEG(KK)                                                                            \
+    lut_segment<KK, FIRST>(hbuf, sg.pw, sg.tab, sg.out, sg.pstride, sg.W, sg.tab_row, sg.r0, \
+                           sg.r1, src.x, src.pg, src.pu, ngnu, src.stride, xw)
+    switch (k) {
+        case 1: return PM_SEG(1);
+        case 2: return PM_SEG(2);
+        case 3: return PM_SEG(3);
+        case 4: return PM_SEG(4);
+        default: return PM_SEG(5);
+    }
+#undef PM_SEG
+}
+
+// The segment description of job jb, rows [r0, r1), for this lane.
+__device__ inline Seg make_seg(const KLaunch& L, const KJob& jb, int slice, int r0, int r1) {
+    const int l = threadIdx.x & 31;
+    const int wi = (kSliceCols / 32) * slice + l;
+    Seg sg;
+    sg.pw = jb.planes + wi;
+    sg.tab = jb.lvk + (size_t(wi / L.wpg) << jb.k);
+    sg.out = jb.out + size_t(slice) * L.out_stride;
+    sg.pstride = L.pstride;
+    sg.W = L.W;
+    sg.tab_row = (L.W / L.wpg) << jb.k;
+    sg.r0 = r0;
+    sg.r1 = r1;
+    return sg;
+}
+
+template <bool DOWN>
+__device__ inline LutSrc make_src(const KLaunch& L, const KJob& jb, int slice) {
+    LutSrc r{};
+    if constexpr (DOWN) {
+        const int c = kSliceCols * slice + int(threadIdx.x);     // and c + 512
+        r.pg = L.gu + (size_t(jb.src) * 2) * L.gu_smax * L.inter + c;
+        r.pu = r.pg + size_t(L.gu_smax) * L.inter;
+        r.ng = jb.gsl & 15;
+        r.nu = jb.gsl >> 4;
+        r.stride = L.inter;
+    } else {
+        r.x = L.x + size_t(jb.src) * L.x_stride + kSliceCols * slice;
+    }
+    return r;
+}
+
+// The rows of this workgroup, found by all threads at once (one job each;
+// the jobs' costs are prefix-summed in LDS) instead of a serial walk over the
+// argument block, whose every step would be a dependent memory read.
+//   per-job map: job j with wg0[j] <= q < wg0[j+1], its chunk of rows;
+//   contiguous map: cost [q C / n, (q+1) C / n) of the jobs' rows taken in
+//   order (rows * lut_row_cost each), cut at even rows; neighbouring
+//   workgroups evaluate the same integer expressions, so ranges meet exactly.
+// Result in r[0..3] = (ja, ra, jb, rb): rows from (ja, ra) to (jb, rb).
+__device__ inline void wg_range(const KLaunch& L, const KJob* jobs, int q, int64_t* s_cum,
+                                int* r) {
+    const int tid = threadIdx.x;
+    const int n = L.n_jobs;
+    const int pairs = (L.rows + 1) >> 1;
+    if (tid == 0) {             // empty unless a job claims this workgroup
+        r[0] = n;
+        r[1] = 0;
+        r[2] = -1;
+        r[3] = 0;
+    }
+    __syncthreads();
+    if (L.map == kMapPerJob) {
+        if (tid < n) {
+            const int lo = jobs[tid].wg0;
+            const int hi = tid + 1 < n ? jobs[tid + 1].wg0 : L.n_wgq;
+            if (lo <= q && q < hi) {
+                const int c = q - lo, m = hi - lo;
+                r[0] = r[2] = tid;
+                r[1] = 2 * int(int64_t(c) * pairs / m);
+                r[3] = min(L.rows, 2 * int(int64_t(c + 1) * pairs / m));
+            }
+        }
+        __syncthreads();
+        return;
+    }
+    // inclusive prefix sum of the job costs (Hillis-Steele in LDS)
+    int64_t pc = 0;
+    if (tid < n) pc = 2 * lut_row_cost(jobs[tid].k, L.wpg);
+    if (tid < kMaxLaunchJobs) s_cum[tid] = tid < n ? pc * pairs : 0;
+    __syncthreads();
+    for (int d = 1; d < kMaxLaunchJobs; d <<= 1) {
+        int64_t add = 0;
+        if (tid < kMaxLaunchJobs && tid >= d) add = s_cum[tid - d];
+        __syncthreads();
+        if (tid < kMaxLaunchJobs) s_cum[tid] += add;
+        __syncthreads();
+    }
+    const int64_t total = s_cum[kMaxLaunchJobs - 1];
+    if (tid < n) {
+        const int64_t after = s_cum[tid], before = after - pc * pairs;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int qq = q + e;
+            if (qq <= 0) {
+                if (tid == 0) { r[2 * e] = 0; r[2 * e + 1] = 0; }
+            } else if (qq >= L.n_wgq) {
+                if (tid == n - 1) { r[2 * e] = n - 1; r[2 * e + 1] = L.rows; }
+            } else {
+                const int64_t target = total * qq / L.n_wgq;
+                if (before <= target && (target < after || tid == n - 1)) {
+                    const int64_t p = (target - before + pc - 1) / pc;
+                    r[2 * e] = tid;
+                    r[2 * e + 1] = int(min(int64_t(L.rows), 2 * p));
+                }
+            }
+        }
+    }
+    __syncthreads();
+}
+
+template <bool DOWN>
+__global__ __launch_bounds__(kLutThreads) void lut_kernel(const KLaunch L) {
+    // one LDS object: the table at address 0 (lut_sum relies on it), then
+    // the padded h of the down stage
+    __shared__ __attribute__((aligned(16))) char lds_buf[kLutBytes + (DOWN ? kHbufBytes : 0)];
+    __shared__ KJob s_jobs[kMaxLaunchJobs];
+    __shared__ int64_t s_cum[kMaxLaunchJobs];
+    __shared__ int s_range[4];
+    lds_float* hb = (lds_float*)(lds_buf + kLutBytes);
+    // the job table in one parallel read of the argument block
+    if (int(threadIdx.x) < L.n_jobs) s_jobs[threadIdx.x] = L.job[threadIdx.x];
+    const int slice = blockIdx.x % L.S, q = blockIdx.x / L.S;
+    wg_range(L, s_jobs, q, s_cum, s_range);
+    int ja = s_range[0], ra = s_range[1], jb = s_range[2], rb = s_range[3];
+    if (ra >= L.rows) {         // the start lies at the end of a job
+        ++ja;
+        ra = 0;
+    }
+    if (ja >= L.n_jobs || ja > jb || (ja == jb && ra >= rb)) return;
+    float xw = 0.f;
+    for (int j = ja; j <= jb; ++j) {
+        const int r0 = j == ja ? ra : 0;
+        const int r1 = j == jb ? rb : L.rows;
+        const KJob job = s_jobs[j];
+        if (j == ja)
+            xw = lut_segment_k<true>(job.k, hb, make_seg(L, job, slice, r0, r1),
+                                     make_src<DOWN>(L, job, slice), 0.f);
+        else if (r0 < r1)
+            xw = lut_segment_k<false>(job.k, hb, make_seg(L, job, slice, r0, r1), LutSrc{}, xw);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void sum_slices_kernel(const float* __restrict__ part,
+                                                            int slices, int rows,
+                                                            float* __restrict__ y) {
+    const int r = blockIdx.x * kBlock + threadIdx.x;
+    if (r >= rows) return;
+    float s = part[r];
+    for (int q = 1; q < slices; ++q) s += part[size_t(q) * rows + r];
+    y[r] = s;
+}
+
+// ---------------------------------------------------------------- direct path
 // This lane's share of row o of one matrix at prefix k.
-//   planes: plane 0 of the matrix, planes pstride words apart
-//   lv_k:   depth-k nodes of the matrix (levels + level_offset(k))
-//   W:      words per row; wpg: words per block
 __device__ inline float row_dot_lane(const uint32_t* __restrict__ planes, size_t pstride,
                                      const float* __restrict__ lv_k, int k, int o, int W,
                                      int wpg, const float* __restrict__ x, int lane) {
@@ -54,12 +564,12 @@ __device__ inline float row_dot_lane(const uint32_t* __restrict__ planes, size_t
     return acc;
 }
 
-__global__ __launch_bounds__(kBlock) void gemv_kernel(int rows, int cols, int group, int k,
-                                                      const uint32_t* __restrict__ planes,
-                                                      size_t pstride,
-                                                      const float* __restrict__ levels,
-                                                      const float* __restrict__ x,
-                                                      float* __restrict__ y) {
+__global__ __launch_bounds__(kBlock) void gemv_direct_kernel(int rows, int cols, int group, int k,
+                                                             const uint32_t* __restrict__ planes,
+                                                             size_t pstride,
+                                                             const float* __restrict__ levels,
+                                                             const float* __restrict__ x,
+                                                             float* __restrict__ y) {
     const int lane = threadIdx.x % kWave;
     const int o = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
     if (o >= rows) return;
@@ -68,18 +578,17 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(int rows, int cols, int gr
     float acc = row_dot_lane(planes, pstride, levels + level_offset(nb, k), k, o, W, group / 32,
                              x, lane);
     acc = wave_sum(acc);
-    if (lane == 0) y[o] = acc;
+    if (lane == kWave - 1) y[o] = acc;
 }
 
-// ---- MoE stages ---------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void gateup_kernel(Geom g, const Item* __restrict__ items,
-                                                        int item0, int bpi,
-                                                        const Use* __restrict__ uses,
-                                                        const int32_t* __restrict__ list,
-                                                        const float* __restrict__ x,
-                                                        float* __restrict__ G,
-                                                        float* __restrict__ U) {
-    const Item it = items[item0 + blockIdx.x / bpi];
+__global__ __launch_bounds__(kBlock) void direct_gateup_kernel(Geom g,
+                                                               const Item* __restrict__ items,
+                                                               int bpi,
+                                                               const Use* __restrict__ uses,
+                                                               const int32_t* __restrict__ list,
+                                                               const float* __restrict__ x,
+                                                               Partials P) {
+    const Item it = items[blockIdx.x / bpi];
     const int lane = threadIdx.x % kWave;
     const int o = (blockIdx.x % bpi) * kRowsPerBlock + threadIdx.x / kWave;
     if (o >= g.inter) return;
@@ -90,30 +599,40 @@ __global__ __launch_bounds__(kBlock) void gateup_kernel(Geom g, const Item* __re
         const Use us = uses[u];
         const float* xt = x + size_t(us.tok) * g.hidden;
         for (int m = 0; m < 2; ++m) {
+            if (!us.direct[m]) continue;
             const int k = us.k[m];
             float acc = row_dot_lane(it.planes + g.plane_off[m], g.plane_words,
                                      it.levels + g.level_off[m] + level_offset(nb, k), k, o, W,
                                      g.group / 32, xt, lane);
             acc = wave_sum(acc);
-            if (lane == 0) (m == 0 ? G : U)[size_t(u) * g.inter + o] = acc;
+            if (lane == kWave - 1) P.gu[(size_t(u) * 2 + m) * P.gu_smax * g.inter + o] = acc;
         }
     }
 }
 
-// h = silu(g) * u, in place over G.
-__global__ __launch_bounds__(kBlock) void swiglu_kernel(size_t n, float* __restrict__ G,
-                                                        const float* __restrict__ U) {
-    const size_t i = size_t(blockIdx.x) * kBlock + threadIdx.x;
-    if (i >= n) return;
-    const float gv = G[i];
-    G[i] = gv / (1.0f + expf(-gv)) * U[i];
+// Gate/up partial sums of use u summed over their slices, in slice order.
+__device__ inline float gu_sum(const Partials& P, const Use& us, int u, int m, int inter, int c) {
+    const float* base = P.gu + (size_t(u) * 2 + m) * P.gu_smax * inter + c;
+    float s = base[0];
+    for (int q = 1; q < us.slices[m]; ++q) s += base[size_t(q) * inter];
+    return s;
 }
 
-__global__ __launch_bounds__(kBlock) void down_kernel(Geom g, const Item* __restrict__ items,
-                                                      int bpi, const Use* __restrict__ uses,
-                                                      const int32_t* __restrict__ list,
-                                                      const float* __restrict__ H,
-                                                      float* __restrict__ Y) {
+__global__ __launch_bounds__(kBlock) void swiglu_kernel(const Use* __restrict__ uses, int n_uses,
+                                                        Partials P, int inter) {
+    const size_t i = size_t(blockIdx.x) * kBlock + threadIdx.x;
+    if (i >= size_t(n_uses) * inter) return;
+    const int u = int(i / inter), c = int(i % inter);
+    const Use us = uses[u];
+    if (!us.direct[2]) return;
+    P.h[i] = silu_mul(gu_sum(P, us, u, 0, inter, c), gu_sum(P, us, u, 1, inter, c));
+}
+
+__global__ __launch_bounds__(kBlock) void direct_down_kernel(Geom g, const Item* __restrict__ items,
+                                                             int bpi,
+                                                             const Use* __restrict__ uses,
+                                                             const int32_t* __restrict__ list,
+                                                             Partials P) {
     const Item it = items[blockIdx.x / bpi];
     const int lane = threadIdx.x % kWave;
     const int o = (blockIdx.x % bpi) * kRowsPerBlock + threadIdx.x / kWave;
@@ -122,19 +641,48 @@ __global__ __launch_bounds__(kBlock) void down_kernel(Geom g, const Item* __rest
     const size_t nb = size_t(g.hidden) * (g.inter / g.group);
     for (int q = 0; q < it.nuse; ++q) {
         const int u = list[it.use0 + q];
-        const int k = uses[u].k[2];
+        const Use us = uses[u];
+        if (!us.direct[2]) continue;
+        const int k = us.k[2];
         float acc = row_dot_lane(it.planes + g.plane_off[2], g.plane_words,
                                  it.levels + g.level_off[2] + level_offset(nb, k), k, o, W,
-                                 g.group / 32, H + size_t(u) * g.inter, lane);
+                                 g.group / 32, P.h + size_t(u) * g.inter, lane);
         acc = wave_sum(acc);
-        if (lane == 0) Y[size_t(u) * g.hidden + o] = acc;
+        if (lane == kWave - 1) P.y[size_t(u) * P.dn_smax * g.hidden + o] = acc;
     }
 }
 
-// y[t][o] = sum_j w[t][j] * Y[t*top_k + j][o], slots in order.
+// y[t][o] = sum_j w[t][j] * sum_s Y[u][s][o], u = t*top_k + j; tokens
+// t0 .. t0 + n_tokens - 1, their weights and slice counts in the arguments.
+__global__ __launch_bounds__(kBlock) void combine_k_kernel(const KCombine C) {
+    const size_t i = size_t(blockIdx.x) * kBlock + threadIdx.x;
+    if (i >= size_t(C.n_tokens) * C.hidden) return;
+    const int t = int(i / C.hidden), o = int(i % C.hidden);
+    const int tg = C.t0 + t;
+    const float* yt = C.Y + size_t(tg) * C.top_k * C.dn_smax * C.hidden + o;
+    const size_t js = size_t(C.dn_smax) * C.hidden;   // between slots
+    float acc = 0.f;
+    for (int j0 = 0; j0 < C.top_k; j0 += 16) {
+        // every slot's first partial in flight at once, then summed in order
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = j0 + q < C.top_k ? yt[(j0 + q) * js] : 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int j = j0 + q;
+            if (j >= C.top_k) break;
+            const int a = t * C.top_k + j;
+            float s = v[q];
+            for (int r = 1; r < C.sl[a]; ++r) s += yt[j * js + size_t(r) * C.hidden];
+            acc = fmaf(C.w[a], s, acc);
+        }
+    }
+    C.y[size_t(tg) * C.hidden + o] = acc;
+}
+
+// y[t][o] = sum_j w[t][j] * sum_s Y[u][s][o], u = t*top_k + j.
 __global__ __launch_bounds__(kBlock) void combine_kernel(int n_tokens, int top_k, int hidden,
-                                                         const Use* __restrict__ uses,
-                                                         const float* __restrict__ Y,
+                                                         const Use* __restrict__ uses, Partials P,
                                                          float* __restrict__ y) {
     const size_t i = size_t(blockIdx.x) * kBlock + threadIdx.x;
     if (i >= size_t(n_tokens) * hidden) return;
@@ -142,12 +690,16 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(int n_tokens, int top_k
     float acc = 0.f;
     for (int j = 0; j < top_k; ++j) {
         const int u = t * top_k + j;
-        acc = fmaf(uses[u].w, Y[size_t(u) * hidden + o], acc);
+        const Use us = uses[u];
+        const float* yb = P.y + size_t(u) * P.dn_smax * hidden + o;
+        float s = yb[0];
+        for (int q = 1; q < us.slices[2]; ++q) s += yb[size_t(q) * hidden];
+        acc = fmaf(us.w, s, acc);
     }
     y[i] = acc;
 }
 
-// ---- encoder -------------------------------------------------------------------
+// ---------------------------------------------------------------- encoder
 // Planes: one thread per (row, word); bit j of plane p = bit (7-p) of code 32w+j.
 __global__ __launch_bounds__(kBlock) void encode_planes_kernel(int rows, int W,
                                                                const uint8_t* __restrict__ codes,
@@ -174,7 +726,7 @@ __global__ __launch_bounds__(kBlock) void encode_planes_kernel(int rows, int W,
 
 // Levels: one block of 256 threads per codebook block.  Depth 8 is the leaves;
 // each shallower node is (left + right) * 0.5f, or the count-weighted mean in
-// fp64 when counts are given (fallback to the plain mean for empty subtrees).
+// fp64 when counts are given (the plain mean for subtrees holding no weight).
 __global__ __launch_bounds__(kLeaves) void encode_levels_kernel(size_t nb,
                                                                 const float* __restrict__ leaves,
                                                                 const uint32_t* __restrict__ counts,
@@ -194,8 +746,7 @@ __global__ __launch_bounds__(kLeaves) void encode_levels_kernel(size_t nb,
         const int n = 1 << d;
         if (t < n) {
             const float L = val[cur][2 * t], R = val[cur][2 * t + 1];
-            const float mean = (L + R) * 0.5f;
-            float pv = mean;
+            float pv = (L + R) * 0.5f;
             unsigned long long tot = 0;
             if (counts) {
                 const unsigned long long nl = cnt[cur][2 * t], nr = cnt[cur][2 * t + 1];
@@ -215,7 +766,7 @@ __global__ __launch_bounds__(kLeaves) void encode_levels_kernel(size_t nb,
     }
 }
 
-// ---- checks and baselines -------------------------------------------------------
+// ---------------------------------------------------------------- checks and baselines
 __device__ inline uint32_t prefix_at(const uint32_t* __restrict__ planes, size_t pstride,
                                      size_t word, int bit, int k) {
     uint32_t v = 0;
@@ -269,22 +820,75 @@ __global__ __launch_bounds__(kBlock) void gemv_fp16_kernel(int rows, int cols,
         }
     }
     acc = wave_sum(acc);
-    if (lane == 0) y[o] = acc;
+    if (lane == kWave - 1) y[o] = acc;
 }
 
 inline unsigned grid_for(size_t n, int per) { return unsigned((n + per - 1) / per); }
 
 }  // namespace
 
-int gateup_rows_per_block() { return kRowsPerBlock; }
-int down_rows_per_block() { return kRowsPerBlock; }
 int max_uses_per_item() { return 64; }
 
 hipError_t launch_gemv(int rows, int cols, int group, int k, const uint32_t* planes,
                        size_t pstride, const float* levels, const float* x, float* y,
                        hipStream_t st) {
-    hipLaunchKernelGGL(gemv_kernel, dim3(grid_for(rows, kRowsPerBlock)), dim3(kBlock), 0, st,
-                       rows, cols, group, k, planes, pstride, levels, x, y);
+    hipLaunchKernelGGL(gemv_direct_kernel, dim3(grid_for(rows, kRowsPerBlock)), dim3(kBlock), 0,
+                       st, rows, cols, group, k, planes, pstride, levels, x, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_lut(const KLaunch& L, bool down, hipStream_t st) {
+    if (L.n_jobs == 0 || L.n_wgq == 0) return hipSuccess;
+    const dim3 grid(unsigned(L.n_wgq * L.S));
+    if (down)
+        hipLaunchKernelGGL(lut_kernel<true>, grid, dim3(kLutThreads), 0, st, L);
+    else
+        hipLaunchKernelGGL(lut_kernel<false>, grid, dim3(kLutThreads), 0, st, L);
+    return hipGetLastError();
+}
+
+hipError_t launch_sum_slices(const float* part, int slices, int rows, float* y, hipStream_t st) {
+    hipLaunchKernelGGL(sum_slices_kernel, dim3(grid_for(rows, kBlock)), dim3(kBlock), 0, st, part,
+                       slices, rows, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_direct_gateup(const Geom& g, const Item* items, int n_items, const Use* uses,
+                                const int32_t* list, const float* x, Partials P,
+                                hipStream_t st) {
+    if (n_items == 0) return hipSuccess;
+    const int bpi = (g.inter + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL(direct_gateup_kernel, dim3(n_items * bpi), dim3(kBlock), 0, st, g, items,
+                       bpi, uses, list, x, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_direct_down(const Geom& g, const Item* items, int n_items, const Use* uses,
+                              const int32_t* list, Partials P, hipStream_t st) {
+    if (n_items == 0) return hipSuccess;
+    const int bpi = (g.hidden + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL(direct_down_kernel, dim3(n_items * bpi), dim3(kBlock), 0, st, g, items,
+                       bpi, uses, list, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const Use* uses, int n_uses, Partials P, int inter, hipStream_t st) {
+    hipLaunchKernelGGL(swiglu_kernel, dim3(grid_for(size_t(n_uses) * inter, kBlock)),
+                       dim3(kBlock), 0, st, uses, n_uses, P, inter);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(int n_tokens, int top_k, int hidden, const Use* uses, Partials P,
+                          float* y, hipStream_t st) {
+    hipLaunchKernelGGL(combine_kernel, dim3(grid_for(size_t(n_tokens) * hidden, kBlock)),
+                       dim3(kBlock), 0, st, n_tokens, top_k, hidden, uses, P, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_k(const KCombine& C, hipStream_t st) {
+    if (C.n_tokens == 0) return hipSuccess;
+    hipLaunchKernelGGL(combine_k_kernel, dim3(grid_for(size_t(C.n_tokens) * C.hidden, kBlock)),
+                       dim3(kBlock), 0, st, C);
     return hipGetLastError();
 }
 
@@ -322,38 +926,6 @@ hipError_t launch_gemv_fp16(int rows, int cols, const uint16_t* w, const float* 
                             hipStream_t st) {
     hipLaunchKernelGGL(gemv_fp16_kernel, dim3(grid_for(rows, kRowsPerBlock)), dim3(kBlock), 0,
                        st, rows, cols, w, x, y);
-    return hipGetLastError();
-}
-
-hipError_t launch_gateup(const Geom& g, const Item* items, int item0, int n_items,
-                         int n_blocks, const Use* uses, const int32_t* list, int top_k,
-                         const float* x, float* G, float* U, hipStream_t st) {
-    (void)top_k;
-    if (n_items == 0) return hipSuccess;
-    const int bpi = n_blocks / n_items;
-    hipLaunchKernelGGL(gateup_kernel, dim3(n_blocks), dim3(kBlock), 0, st, g, items, item0, bpi,
-                       uses, list, x, G, U);
-    return hipGetLastError();
-}
-
-hipError_t launch_down(const Geom& g, const Item* items, int n_items, int n_blocks,
-                       const Use* uses, const int32_t* list, int n_uses, float* G,
-                       const float* U, float* Y, hipStream_t st) {
-    if (n_items == 0) return hipSuccess;
-    const size_t n = size_t(n_uses) * g.inter;
-    hipLaunchKernelGGL(swiglu_kernel, dim3(grid_for(n, kBlock)), dim3(kBlock), 0, st, n, G, U);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int bpi = n_blocks / n_items;
-    hipLaunchKernelGGL(down_kernel, dim3(n_blocks), dim3(kBlock), 0, st, g, items, bpi, uses,
-                       list, G, Y);
-    return hipGetLastError();
-}
-
-hipError_t launch_combine(int n_tokens, int top_k, int hidden, const Use* uses, const float* Y,
-                          float* y, hipStream_t st) {
-    hipLaunchKernelGGL(combine_kernel, dim3(grid_for(size_t(n_tokens) * hidden, kBlock)),
-                       dim3(kBlock), 0, st, n_tokens, top_k, hidden, uses, Y, y);
     return hipGetLastError();
 }
 

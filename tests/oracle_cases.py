@@ -10,10 +10,16 @@ import oracle
 import synth
 
 
-@lru_cache(maxsize=64)
+def _wl(w):
+    return synth.WORKLOADS[w] if isinstance(w, int) else w
+
+
+@lru_cache(maxsize=32)
 def gate_up(cfg, layer, expert):
-    """Oracle-encoded gate and up matrices of one seeded expert."""
-    wl = synth.WORKLOADS[cfg]
+    """Oracle-encoded gate and up matrices of one seeded expert (cfg is a
+    workload index or a Workload)."""
+    wl = _wl(cfg)
+    cfg = wl.cfg
     out = []
     for m in (0, 1):
         rows, cols = synth.matrix_shape(wl, m)
@@ -25,7 +31,8 @@ def gate_up(cfg, layer, expert):
 
 def down_rows(cfg, layer, expert, rows):
     """Oracle-encoded sampled rows of the down matrix."""
-    wl = synth.WORKLOADS[cfg]
+    wl = _wl(cfg)
+    cfg = wl.cfg
     R, cols = synth.matrix_shape(wl, 2)
     lv = np.concatenate([synth.leaves(wl.seed, cfg, layer, expert, 2, R, cols // wl.group, r, r + 1)
                          for r in rows])
@@ -37,7 +44,7 @@ def down_rows(cfg, layer, expert, rows):
 def token_layer(cfg, layer, ids, w, k, x, rows, materialized=False):
     """Oracle y[rows] and its error scale for one token of one layer.
     k: int [top_k][3] prefixes of gate, up, down."""
-    wl = synth.WORKLOADS[cfg]
+    wl = _wl(cfg)
     G = wl.group
     gemv = oracle.gemv_materialized_fp16 if materialized else oracle.gemv
     y = np.zeros(len(rows))
@@ -56,7 +63,8 @@ def token_layer(cfg, layer, ids, w, k, x, rows, materialized=False):
 
 def route_and_bits(cfg, layer, step, token=0, kfix=None):
     """Oracle routing and allocation of one token: ids, w, k[top_k][3]."""
-    wl = synth.WORKLOADS[cfg]
+    wl = _wl(cfg)
+    cfg = wl.cfg
     lg = synth.router_logits(wl.seed, cfg, layer, token, wl.n_experts, step=step)
     ids, w = oracle.route(lg, wl.top_k)
     if kfix is None:
