@@ -395,35 +395,49 @@ __device__ inline float lut_segment_k(int k, lds_float* hbuf, const Seg& sg, con
 #undef PM_SEG
 }
 
+// Shape of the matrices of one launch.
+struct MatArgs {
+    uint64_t pstride;      // words between planes
+    int rows, W, wpg;      // rows, words per row, words per block
+    int out_stride;        // floats between the slice outputs of a job
+};
+
+__device__ inline MatArgs mat_of(const KLaunch& L) {
+    return MatArgs{L.pstride, L.rows, L.W, L.wpg, L.out_stride};
+}
+
 // The segment description of job jb, rows [r0, r1), for this lane.
-__device__ inline Seg make_seg(const KLaunch& L, const KJob& jb, int slice, int r0, int r1) {
+__device__ inline Seg make_seg(const MatArgs& M, const KJob& jb, int slice, int r0, int r1) {
     const int l = threadIdx.x & 31;
     const int wi = (kSliceCols / 32) * slice + l;
     Seg sg;
     sg.pw = jb.planes + wi;
-    sg.tab = jb.lvk + (size_t(wi / L.wpg) << jb.k);
-    sg.out = jb.out + size_t(slice) * L.out_stride;
-    sg.pstride = L.pstride;
-    sg.W = L.W;
-    sg.tab_row = (L.W / L.wpg) << jb.k;
+    sg.tab = jb.lvk + (size_t(wi / M.wpg) << jb.k);
+    sg.out = jb.out + size_t(slice) * M.out_stride;
+    sg.pstride = M.pstride;
+    sg.W = M.W;
+    sg.tab_row = (M.W / M.wpg) << jb.k;
     sg.r0 = r0;
     sg.r1 = r1;
     return sg;
 }
 
-template <bool DOWN>
-__device__ inline LutSrc make_src(const KLaunch& L, const KJob& jb, int slice) {
+// LUT sources: the activation slice of x, or h of a use from its gate/up
+// partials (gu: [use][2][gu_smax][inter]).
+__device__ inline LutSrc src_x(const float* x, int slice) {
     LutSrc r{};
-    if constexpr (DOWN) {
-        const int c = kSliceCols * slice + int(threadIdx.x);     // and c + 512
-        r.pg = L.gu + (size_t(jb.src) * 2) * L.gu_smax * L.inter + c;
-        r.pu = r.pg + size_t(L.gu_smax) * L.inter;
-        r.ng = jb.gsl & 15;
-        r.nu = jb.gsl >> 4;
-        r.stride = L.inter;
-    } else {
-        r.x = L.x + size_t(jb.src) * L.x_stride + kSliceCols * slice;
-    }
+    r.x = x + kSliceCols * slice;
+    return r;
+}
+__device__ inline LutSrc src_h(const float* gu, int gu_smax, int inter, const KJob& jb, int use,
+                               int slice) {
+    LutSrc r{};
+    const int c = kSliceCols * slice + int(threadIdx.x);     // and c + kLutThreads ..
+    r.pg = gu + (size_t(use) * 2) * gu_smax * inter + c;
+    r.pu = r.pg + size_t(gu_smax) * inter;
+    r.ng = jb.gsl & 15;
+    r.nu = jb.gsl >> 4;
+    r.stride = inter;
     return r;
 }
 
@@ -435,11 +449,10 @@ __device__ inline LutSrc make_src(const KLaunch& L, const KJob& jb, int slice) {
 //   order (rows * lut_row_cost each), cut at even rows; neighbouring
 //   workgroups evaluate the same integer expressions, so ranges meet exactly.
 // Result in r[0..3] = (ja, ra, jb, rb): rows from (ja, ra) to (jb, rb).
-__device__ inline void wg_range(const KLaunch& L, const KJob* jobs, int q, int64_t* s_cum,
-                                int* r) {
+__device__ inline void wg_range(const KJob* jobs, int n, int rows, int n_wgq, int map, int wpg,
+                                int q, int64_t* s_cum, int* r) {
     const int tid = threadIdx.x;
-    const int n = L.n_jobs;
-    const int pairs = (L.rows + 1) >> 1;
+    const int pairs = (rows + 1) >> 1;
     if (tid == 0) {             // empty unless a job claims this workgroup
         r[0] = n;
         r[1] = 0;
@@ -447,15 +460,15 @@ __device__ inline void wg_range(const KLaunch& L, const KJob* jobs, int q, int64
         r[3] = 0;
     }
     __syncthreads();
-    if (L.map == kMapPerJob) {
+    if (map == kMapPerJob) {
         if (tid < n) {
             const int lo = jobs[tid].wg0;
-            const int hi = tid + 1 < n ? jobs[tid + 1].wg0 : L.n_wgq;
+            const int hi = tid + 1 < n ? jobs[tid + 1].wg0 : n_wgq;
             if (lo <= q && q < hi) {
                 const int c = q - lo, m = hi - lo;
                 r[0] = r[2] = tid;
                 r[1] = 2 * int(int64_t(c) * pairs / m);
-                r[3] = min(L.rows, 2 * int(int64_t(c + 1) * pairs / m));
+                r[3] = min(rows, 2 * int(int64_t(c + 1) * pairs / m));
             }
         }
         __syncthreads();
@@ -463,7 +476,7 @@ __device__ inline void wg_range(const KLaunch& L, const KJob* jobs, int q, int64
     }
     // inclusive prefix sum of the job costs (Hillis-Steele in LDS)
     int64_t pc = 0;
-    if (tid < n) pc = 2 * lut_row_cost(jobs[tid].k, L.wpg);
+    if (tid < n) pc = 2 * lut_row_cost(jobs[tid].k, wpg);
     if (tid < kMaxLaunchJobs) s_cum[tid] = tid < n ? pc * pairs : 0;
     __syncthreads();
     for (int d = 1; d < kMaxLaunchJobs; d <<= 1) {
@@ -481,19 +494,42 @@ __device__ inline void wg_range(const KLaunch& L, const KJob* jobs, int q, int64
             const int qq = q + e;
             if (qq <= 0) {
                 if (tid == 0) { r[2 * e] = 0; r[2 * e + 1] = 0; }
-            } else if (qq >= L.n_wgq) {
-                if (tid == n - 1) { r[2 * e] = n - 1; r[2 * e + 1] = L.rows; }
+            } else if (qq >= n_wgq) {
+                if (tid == n - 1) { r[2 * e] = n - 1; r[2 * e + 1] = rows; }
             } else {
-                const int64_t target = total * qq / L.n_wgq;
+                const int64_t target = total * qq / n_wgq;
                 if (before <= target && (target < after || tid == n - 1)) {
                     const int64_t p = (target - before + pc - 1) / pc;
                     r[2 * e] = tid;
-                    r[2 * e + 1] = int(min(int64_t(L.rows), 2 * p));
+                    r[2 * e + 1] = int(min(int64_t(rows), 2 * p));
                 }
             }
         }
     }
     __syncthreads();
+}
+
+// Run the rows of range (ja, ra) .. (jb, rb) of jobs[], the first segment
+// building the LUT from `first_src`.  All threads of the workgroup take part.
+__device__ inline void run_range(lds_float* hb, const KJob* jobs, int n_jobs, const MatArgs& M,
+                                 int slice, const int* rg, const LutSrc& first_src) {
+    int ja = rg[0], ra = rg[1];
+    const int jb = rg[2], rb = rg[3];
+    if (ra >= M.rows) {         // the start lies at the end of a job
+        ++ja;
+        ra = 0;
+    }
+    if (ja >= n_jobs || ja > jb || (ja == jb && ra >= rb)) return;
+    float xw = 0.f;
+    for (int j = ja; j <= jb; ++j) {
+        const int r0 = j == ja ? ra : 0;
+        const int r1 = j == jb ? rb : M.rows;
+        const KJob job = jobs[j];
+        if (j == ja)
+            xw = lut_segment_k<true>(job.k, hb, make_seg(M, job, slice, r0, r1), first_src, 0.f);
+        else if (r0 < r1)
+            xw = lut_segment_k<false>(job.k, hb, make_seg(M, job, slice, r0, r1), LutSrc{}, xw);
+    }
 }
 
 template <bool DOWN>
@@ -508,24 +544,13 @@ __global__ __launch_bounds__(kLutThreads) void lut_kernel(const KLaunch L) {
     // the job table in one parallel read of the argument block
     if (int(threadIdx.x) < L.n_jobs) s_jobs[threadIdx.x] = L.job[threadIdx.x];
     const int slice = blockIdx.x % L.S, q = blockIdx.x / L.S;
-    wg_range(L, s_jobs, q, s_cum, s_range);
-    int ja = s_range[0], ra = s_range[1], jb = s_range[2], rb = s_range[3];
-    if (ra >= L.rows) {         // the start lies at the end of a job
-        ++ja;
-        ra = 0;
-    }
-    if (ja >= L.n_jobs || ja > jb || (ja == jb && ra >= rb)) return;
-    float xw = 0.f;
-    for (int j = ja; j <= jb; ++j) {
-        const int r0 = j == ja ? ra : 0;
-        const int r1 = j == jb ? rb : L.rows;
-        const KJob job = s_jobs[j];
-        if (j == ja)
-            xw = lut_segment_k<true>(job.k, hb, make_seg(L, job, slice, r0, r1),
-                                     make_src<DOWN>(L, job, slice), 0.f);
-        else if (r0 < r1)
-            xw = lut_segment_k<false>(job.k, hb, make_seg(L, job, slice, r0, r1), LutSrc{}, xw);
-    }
+    wg_range(s_jobs, L.n_jobs, L.rows, L.n_wgq, L.map, L.wpg, q, s_cum, s_range);
+    const MatArgs M = mat_of(L);
+    const int j0 = min(max(s_range[0], 0), L.n_jobs - 1);
+    const KJob& first = s_jobs[j0];
+    const LutSrc src = DOWN ? src_h(L.gu, L.gu_smax, L.inter, first, first.src, slice)
+                            : src_x(L.x + size_t(first.src) * L.x_stride, slice);
+    run_range(hb, s_jobs, L.n_jobs, M, slice, s_range, src);
 }
 
 __global__ __launch_bounds__(kBlock) void sum_slices_kernel(const float* __restrict__ part,
