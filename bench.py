@@ -57,6 +57,25 @@ def gateup_bytes(wl, kk):
     return b + wl.hidden * 4
 
 
+def copy_ceiling(torch, stream, nbytes=1 << 30, reps=5):
+    """A plain elementwise kernel of known traffic (read nbytes, write
+    nbytes, fp32 negation) on the same stream: the HBM rate this chip reaches
+    on a pure stream, and the reference for the per-dispatch HBM counters."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").normal_()
+    b = torch.empty_like(a)
+    torch.neg(a, out=b)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        torch.neg(a, out=b)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    del a, b
+    return {"kernel": "torch.neg fp32, 1 GiB read + 1 GiB written", "us": round(ms * 1e3, 1),
+            "GBs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(wl, plans, budget_s):
     """The oracle, untouched, on a bounded sample: the first token's 10
     experts, every matrix restricted to its first 256 rows, repeated until
@@ -169,6 +188,9 @@ def main():
     ms = el / args.steps * 1e3
     log(f"timed {args.steps} steps: {ms:.4f} ms/step, {gbs:.1f} GB/s")
 
+    ceiling = copy_ceiling(torch, stream)
+    log(f"stream ceiling: {ceiling['GBs']} GB/s ({ceiling['kernel']})")
+
     # roofline pass: HIP events around each stage on the library's stream
     evs = []
     for s in steps:
@@ -204,7 +226,10 @@ def main():
                      "combine": round(cb_ms.mean() * 1e3, 2)},
         "roofline": {"bound": "hbm", "kernel": "gateup", "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(gu_b.mean()),
+                     "launch_us": round(gu_ms.mean() * 1e3, 2)},
+        "stream_ceiling": ceiling,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -704,43 +704,66 @@ struct JobSpec {                       // a LUT job before it is packed into a l
 };
 }  // namespace
 
-// Workgroups per job for the per-job map: n_total split by cost (largest
-// remainder), at least one each.
-static void assign_wg0(std::vector<JobSpec>& js, size_t j0, size_t j1, int n_total, KLaunch& L) {
-    const size_t n = j1 - j0;
-    n_total = std::max<int>(n_total, int(n));
+// Row cuts of a launch (KLaunch::start), contiguous: the cost of all rows in
+// order is split into n_wgq equal parts, each cut at an even row of its job.
+static void set_starts_contig(KLaunch& L, int n_wgq) {
+    const int n = L.n_jobs, rows = L.rows, pairs = (rows + 1) / 2;
+    std::vector<int64_t> pc(n), before(n + 1, 0);
+    for (int j = 0; j < n; ++j) {
+        pc[j] = 2 * lut_row_cost(L.job[j].k, L.wpg);
+        before[j + 1] = before[j] + pc[j] * pairs;
+    }
+    const int64_t total = before[n];
+    L.start[0] = 0;
+    int j = 0;
+    for (int q = 1; q < n_wgq; ++q) {
+        const int64_t target = total * q / n_wgq;
+        while (j < n - 1 && before[j + 1] <= target) ++j;
+        const int64_t p = (target - before[j] + pc[j] - 1) / pc[j];
+        L.start[q] = j * rows + int(std::min<int64_t>(rows, 2 * p));
+    }
+    L.start[n_wgq] = n * rows;
+    L.n_wgq = n_wgq;
+}
+
+// Row cuts, one job per workgroup: n_total workgroups split among the jobs
+// by cost (largest remainder, at least one each); a job's workgroups split
+// its rows evenly at even rows.
+static void set_starts_per_job(KLaunch& L, const int64_t* cost, int n_total) {
+    const int n = L.n_jobs, rows = L.rows, pairs = (rows + 1) / 2;
+    n_total = std::min(kMaxLaunchWgq, std::max(n_total, n));
     double C = 0;
-    for (size_t j = j0; j < j1; ++j) C += double(js[j].cost);
+    for (int j = 0; j < n; ++j) C += double(cost[j]);
     std::vector<int> a(n);
     std::vector<double> share(n);
     int sum = 0;
-    for (size_t j = 0; j < n; ++j) {
-        share[j] = C > 0 ? n_total * double(js[j0 + j].cost) / C : double(n_total) / n;
+    for (int j = 0; j < n; ++j) {
+        share[j] = C > 0 ? n_total * double(cost[j]) / C : double(n_total) / n;
         a[j] = std::max(1, int(share[j]));
         sum += a[j];
     }
     while (sum > n_total) {
-        size_t b = 0;
-        for (size_t j = 1; j < n; ++j)
+        int b = 0;
+        for (int j = 1; j < n; ++j)
             if (a[j] > a[b]) b = j;
         if (a[b] <= 1) break;
         --a[b];
         --sum;
     }
     while (sum < n_total) {
-        size_t b = 0;
-        for (size_t j = 1; j < n; ++j)
+        int b = 0;
+        for (int j = 1; j < n; ++j)
             if (share[j] - a[j] > share[b] - a[b]) b = j;
         ++a[b];
         ++sum;
     }
     int w = 0;
-    for (size_t j = 0; j < n; ++j) {
-        L.job[j] = js[j0 + j].job;
-        L.job[j].wg0 = w;
+    for (int j = 0; j < n; ++j) {
+        for (int c = 0; c < a[j]; ++c)
+            L.start[w + c] = j * rows + std::min(rows, 2 * int(int64_t(c) * pairs / a[j]));
         w += a[j];
     }
-    L.n_jobs = int(n);
+    L.start[w] = n * rows;
     L.n_wgq = w;
 }
 
@@ -750,23 +773,24 @@ static void pack_launches(std::vector<JobSpec>& js, const KLaunch& proto, bool c
                           std::vector<KLaunch>& out) {
     int64_t all = 0;
     for (auto& j : js) all += j.cost;
-    const int target = std::max(1, lut_wg_target() / proto.S);
+    const int target = std::max(1, std::min(kMaxLaunchWgq, lut_wg_target() / proto.S));
     for (size_t j0 = 0; j0 < js.size(); j0 += kMaxLaunchJobs) {
         const size_t j1 = std::min(js.size(), j0 + kMaxLaunchJobs);
         int64_t part = 0;
-        for (size_t j = j0; j < j1; ++j) part += js[j].cost;
+        std::vector<int64_t> cost;
+        for (size_t j = j0; j < j1; ++j) {
+            part += js[j].cost;
+            cost.push_back(js[j].cost);
+        }
         const int n = std::max(1, int(std::lround(double(target) * double(part) / double(all))));
         out.push_back(proto);
         KLaunch& L = out.back();
-        if (contig) {
-            L.map = kMapContig;
-            L.n_jobs = int(j1 - j0);
-            for (size_t j = j0; j < j1; ++j) L.job[j - j0] = js[j].job;
-            L.n_wgq = n;
-        } else {
-            L.map = kMapPerJob;
-            assign_wg0(js, j0, j1, n, L);
-        }
+        L.n_jobs = int(j1 - j0);
+        for (size_t j = j0; j < j1; ++j) L.job[j - j0] = js[j].job;
+        if (contig)
+            set_starts_contig(L, std::min(n, kMaxLaunchWgq));
+        else
+            set_starts_per_job(L, cost.data(), n);
     }
 }
 
@@ -814,7 +838,6 @@ pm_status gemv_lut(pm_matrix_shape s, int k, const uint32_t* d_planes, size_t ps
     L.wpg = s.group / 32;
     L.out_stride = s.rows;
     L.x_stride = 0;
-    L.map = kMapContig;
     L.n_jobs = 1;
     KJob& jb = L.job[0];
     jb.planes = d_planes;
@@ -828,8 +851,8 @@ pm_status gemv_lut(pm_matrix_shape s, int k, const uint32_t* d_planes, size_t ps
         if (r) return r;
     }
     // workgroups per slice: enough to fill the device, at least 32 rows each
-    const int target = std::max(1, lut_wg_target() / S);
-    L.n_wgq = std::max(1, std::min(target, (s.rows + 31) / 32));
+    const int target = std::max(1, std::min(kMaxLaunchWgq, lut_wg_target() / S));
+    set_starts_contig(L, std::max(1, std::min(target, (s.rows + 31) / 32)));
     HIP_TRY(launch_lut(L, false, st));
     if (S > 1) HIP_TRY(launch_sum_slices(jb.out, S, s.rows, d_y, st));
     return PM_OK;

@@ -80,31 +80,38 @@ constexpr int kSliceCols = 1024;   // columns of x covered by one LUT
 constexpr int kLutMaxK = 5;        // largest prefix read through the LUT path
 
 // LUT-path launch description, passed as kernel arguments (no upload).
-constexpr int kMaxLaunchJobs = 96;
+constexpr int kMaxLaunchJobs = 64;
 struct KJob {                      // one matrix of one use
     const uint32_t* planes;        // plane 0, row 0
     const float* lvk;              // depth-k nodes
     float* out;                    // row r, slice s -> out[s * out_stride + r]
-    int32_t wg0;                   // per-job map: first workgroup (per slice) of the job
+    int32_t pad;
     int16_t src;                   // gate/up: token; down: use
     int8_t k;
     uint8_t gsl;                   // down: gate slices (bits 0-3), up slices (bits 4-7)
 };
-enum { kMapContig = 0, kMapPerJob = 1 };
+// One LUT launch: n_wgq * S workgroups.  The rows of the jobs are numbered
+// as one sequence (row r of job j is g = j * rows + r); workgroup q of every
+// slice runs g in [start[q], start[q + 1]), cut by the host so that the work
+// is balanced.  Scalars come first so that the fields every workgroup reads
+// at its start share one cache line.
+constexpr int kMaxLaunchWgq = 256;
 struct KLaunch {
-    KJob job[kMaxLaunchJobs];
     const float* x;                // gate/up: activation of token t at x + t * x_stride
     const float* gu;               // down: gate/up partials [use][2][gu_smax][inter]
     uint64_t pstride;              // words between planes
-    int32_t n_jobs, n_wgq, S, map; // jobs, workgroups per slice, slices, row map
-    int32_t rows, W, wpg, out_stride;
-    int32_t x_stride, gu_smax, inter, pad;
+    int32_t n_jobs, n_wgq, S, rows;
+    int32_t W, wpg, out_stride, x_stride;
+    int32_t gu_smax, inter, pad0, pad1;
+    int32_t start[kMaxLaunchWgq + 2];
+    KJob job[kMaxLaunchJobs];
 };
+static_assert(sizeof(KLaunch) <= 4096, "kernel arguments are limited to 4 KiB");
 // Cost of one row-slice when rows are split among workgroups: its execution
 // time, dominated by the 2^k - 1 mask lookups per word plus a fixed per-row
 // share (loads, reduction, store); k = 1 rows carry a larger fixed share.
-// Measured on gfx950 (workgroup durations per prefix), in arbitrary integer
-// units so every workgroup splits alike.
+// Measured on gfx950 with the layer's rows streamed from HBM (workgroup
+// durations per prefix), in integer units.
 __host__ __device__ inline int64_t lut_row_cost(int k, int /*wpg*/) {
     return k == 1 ? 400 : 220 + 75 * ((int64_t(1) << k) - 1);
 }

@@ -75,6 +75,20 @@ __device__ inline float wave_sum(float v) {
 
 __device__ inline float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
+// Values the whole wave shares, made explicit so that they live in scalar
+// registers: arguments of out-of-line functions and values read from LDS
+// arrive in vector registers.
+__device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline uint64_t uni64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+    return (uint64_t(hi) << 32) | lo;
+}
+template <class T>
+__device__ inline T* uni_ptr(T* p) {
+    return reinterpret_cast<T*>(uni64(reinterpret_cast<uint64_t>(p)));
+}
+
 // ---------------------------------------------------------------- LUT path
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) float lds_float;
@@ -282,15 +296,17 @@ constexpr int lut_unroll() {
 #endif
 }
 
-// One job segment as plain values: the lane's word and block table in row 0.
+// One job segment: the slice's first word and first block table in row 0
+// (shared by the wave), and the lane's offsets from them.
 struct Seg {
-    const uint32_t* pw;    // plane 0, row 0, this lane's word
-    const float* tab;      // depth-k table of this lane's block, row 0
+    const uint32_t* pw;    // plane 0, row 0, first word of the slice
+    const float* tab;      // depth-k table of the slice's first block, row 0
     float* out;            // outputs of this slice
     uint64_t pstride;      // words between planes
     int W;                 // words per row
     int tab_row;           // floats between tables of consecutive rows
     int r0, r1;            // rows [r0, r1)
+    int wo, to;            // lane offsets: words (l + (lane >> 5) * W), table floats
 };
 
 // A batch: U row pairs of this wave, pairs p, p + kLutWaves, ... (rows 2p + hw).
@@ -300,34 +316,40 @@ struct Batch {
     int row[U];
 };
 
+// Loads are unconditional (a row outside the segment reloads a row inside
+// it and is not stored), so that the batch is straight-line code and the
+// wait for batch A does not also wait for batch B's loads in flight.
 template <int K, int U>
 __device__ inline void batch_load(Batch<K, U>& B, const Seg& sg, int p, int p1, int hw) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int pp = p + u * kLutWaves;
+        const int pp = min(p + u * kLutWaves, p1 - 1);      // wave-uniform
         const int row = 2 * pp + hw;
-        if (pp < p1 && row >= sg.r0 && row < sg.r1) {
-            B.row[u] = row;
-            lut_load<K>(B.in[u], sg.pw + size_t(row) * sg.W, sg.tab + size_t(row) * sg.tab_row,
-                        sg.pstride);
-        } else {
-            B.row[u] = -1;
-#pragma unroll
-            for (int q = 0; q < K; ++q) B.in[u].w[q] = 0u;
-#pragma unroll
-            for (int q = 0; q < (1 << K); ++q) B.in[u].tab[q] = 0.f;
-        }
+        const bool ok = p + u * kLutWaves < p1 && row >= sg.r0 && row < sg.r1;
+        B.row[u] = ok ? row : -1;
+        // the pair's first row from the shared bases, then the lane's offset;
+        // a half outside [r0, r1) reads its neighbour row (not stored)
+        const int fix = row < sg.r0 ? 1 : row >= sg.r1 ? -1 : 0;
+        const size_t r2 = size_t(2 * pp);
+        lut_load<K>(B.in[u], sg.pw + r2 * sg.W + (sg.wo + fix * sg.W),
+                    sg.tab + r2 * sg.tab_row + (sg.to + (hw + fix) * sg.tab_row), sg.pstride);
     }
 }
 
+// The rows of a batch are computed and reduced as one straight-line block
+// (their lookups and reductions interleave), and stored after it.
 template <int K, int U>
 __device__ inline void batch_compute(const Batch<K, U>& B, const Seg& sg, float xw, uint32_t b0,
                                      uint32_t b1, int l) {
+    float acc[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        float acc = lut_row<K>(B.in[u].w, B.in[u].tab, xw, b0, b1);
-        acc = half_sum(acc);
-        if (l == 31 && B.row[u] >= 0) ((g_f32_out*)sg.out)[B.row[u]] = acc;
+    for (int u = 0; u < U; ++u) acc[u] = lut_row<K>(B.in[u].w, B.in[u].tab, xw, b0, b1);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] = half_sum(acc[u]);
+    if (l == 31) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (B.row[u] >= 0) ((g_f32_out*)sg.out)[B.row[u]] = acc[u];
     }
 }
 
@@ -347,12 +369,16 @@ struct LutSrc {
 template <int K, bool FIRST>
 __device__ __noinline__ float lut_segment(lds_float* hbuf, const uint32_t* pw, const float* tab,
                                           float* out, uint64_t pstride, int W, int tab_row,
-                                          int r0, int r1, const float* x, const float* pg,
-                                          const float* pu, int ngnu, int hstride, float xw) {
+                                          int wpg, int r0, int r1, const float* x,
+                                          const float* pg, const float* pu, int ngnu,
+                                          int hstride, float xw) {
     constexpr int U = lut_unroll<K>();
-    const Seg sg{pw, tab, out, pstride, W, tab_row, r0, r1};
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int tid = threadIdx.x, wave = uni(tid / kWave), lane = tid % kWave;
     const int hw = lane >> 5, l = lane & 31;
+    Seg sg{uni_ptr(pw), uni_ptr(tab), uni_ptr(out), uni64(pstride), uni(W), uni(tab_row),
+           uni(r0), uni(r1), 0, 0};
+    sg.wo = l + hw * sg.W;
+    sg.to = (l / wpg) << K;
     const uint32_t b0 = uint32_t(l) << 2, b1 = b0 | 0x10000u;
     const int p1 = (sg.r1 + 1) >> 1;
     constexpr int step = kLutWaves * U;
@@ -366,25 +392,31 @@ __device__ __noinline__ float lut_segment(lds_float* hbuf, const uint32_t* pw, c
 #pragma unroll
         for (int t = 0; t < 4; ++t) xw += lds_at(lut_addr(4 * l + t, 255));
     }
+    // the scheduling barriers keep each batch's loads ahead of the other
+    // batch's arithmetic (hoisting that arithmetic would make the loads wait)
     while (p < p1) {
         batch_load<K, U>(B, sg, p + step, p1, hw);
+        __builtin_amdgcn_sched_barrier(0);
         batch_compute<K, U>(A, sg, xw, b0, b1, l);
+        __builtin_amdgcn_sched_barrier(0);
         p += step;
         if (p >= p1) break;
         batch_load<K, U>(A, sg, p + step, p1, hw);
+        __builtin_amdgcn_sched_barrier(0);
         batch_compute<K, U>(B, sg, xw, b0, b1, l);
+        __builtin_amdgcn_sched_barrier(0);
         p += step;
     }
     return xw;
 }
 
 template <bool FIRST>
-__device__ inline float lut_segment_k(int k, lds_float* hbuf, const Seg& sg, const LutSrc& src,
-                                      float xw) {
+__device__ inline float lut_segment_k(int k, lds_float* hbuf, const Seg& sg, int wpg,
+                                      const LutSrc& src, float xw) {
     const int ngnu = src.ng | (src.nu << 4);
 #define PM_SEG(KK)                                                                            \
-    lut_segment<KK, FIRST>(hbuf, sg.pw, sg.tab, sg.out, sg.pstride, sg.W, sg.tab_row, sg.r0, \
-                           sg.r1, src.x, src.pg, src.pu, ngnu, src.stride, xw)
+    lut_segment<KK, FIRST>(hbuf, sg.pw, sg.tab, sg.out, sg.pstride, sg.W, sg.tab_row, wpg,   \
+                           sg.r0, sg.r1, src.x, src.pg, src.pu, ngnu, src.stride, xw)
     switch (k) {
         case 1: return PM_SEG(1);
         case 2: return PM_SEG(2);
@@ -408,17 +440,17 @@ __device__ inline MatArgs mat_of(const KLaunch& L) {
 
 // The segment description of job jb, rows [r0, r1), for this lane.
 __device__ inline Seg make_seg(const MatArgs& M, const KJob& jb, int slice, int r0, int r1) {
-    const int l = threadIdx.x & 31;
-    const int wi = (kSliceCols / 32) * slice + l;
+    const int w0 = (kSliceCols / 32) * slice;
     Seg sg;
-    sg.pw = jb.planes + wi;
-    sg.tab = jb.lvk + (size_t(wi / M.wpg) << jb.k);
+    sg.pw = jb.planes + w0;
+    sg.tab = jb.lvk + (size_t(w0 / M.wpg) << jb.k);
     sg.out = jb.out + size_t(slice) * M.out_stride;
     sg.pstride = M.pstride;
     sg.W = M.W;
     sg.tab_row = (M.W / M.wpg) << jb.k;
     sg.r0 = r0;
     sg.r1 = r1;
+    sg.wo = sg.to = 0;
     return sg;
 }
 
@@ -441,116 +473,36 @@ __device__ inline LutSrc src_h(const float* gu, int gu_smax, int inter, const KJ
     return r;
 }
 
-// The rows of this workgroup, found by all threads at once (one job each;
-// the jobs' costs are prefix-summed in LDS) instead of a serial walk over the
-// argument block, whose every step would be a dependent memory read.
-//   per-job map: job j with wg0[j] <= q < wg0[j+1], its chunk of rows;
-//   contiguous map: cost [q C / n, (q+1) C / n) of the jobs' rows taken in
-//   order (rows * lut_row_cost each), cut at even rows; neighbouring
-//   workgroups evaluate the same integer expressions, so ranges meet exactly.
-// Result in r[0..3] = (ja, ra, jb, rb): rows from (ja, ra) to (jb, rb).
-__device__ inline void wg_range(const KJob* jobs, int n, int rows, int n_wgq, int map, int wpg,
-                                int q, int64_t* s_cum, int* r) {
-    const int tid = threadIdx.x;
-    const int pairs = (rows + 1) >> 1;
-    if (tid == 0) {             // empty unless a job claims this workgroup
-        r[0] = n;
-        r[1] = 0;
-        r[2] = -1;
-        r[3] = 0;
-    }
-    __syncthreads();
-    if (map == kMapPerJob) {
-        if (tid < n) {
-            const int lo = jobs[tid].wg0;
-            const int hi = tid + 1 < n ? jobs[tid + 1].wg0 : n_wgq;
-            if (lo <= q && q < hi) {
-                const int c = q - lo, m = hi - lo;
-                r[0] = r[2] = tid;
-                r[1] = 2 * int(int64_t(c) * pairs / m);
-                r[3] = min(rows, 2 * int(int64_t(c + 1) * pairs / m));
-            }
-        }
-        __syncthreads();
-        return;
-    }
-    // inclusive prefix sum of the job costs (Hillis-Steele in LDS)
-    int64_t pc = 0;
-    if (tid < n) pc = 2 * lut_row_cost(jobs[tid].k, wpg);
-    if (tid < kMaxLaunchJobs) s_cum[tid] = tid < n ? pc * pairs : 0;
-    __syncthreads();
-    for (int d = 1; d < kMaxLaunchJobs; d <<= 1) {
-        int64_t add = 0;
-        if (tid < kMaxLaunchJobs && tid >= d) add = s_cum[tid - d];
-        __syncthreads();
-        if (tid < kMaxLaunchJobs) s_cum[tid] += add;
-        __syncthreads();
-    }
-    const int64_t total = s_cum[kMaxLaunchJobs - 1];
-    if (tid < n) {
-        const int64_t after = s_cum[tid], before = after - pc * pairs;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int qq = q + e;
-            if (qq <= 0) {
-                if (tid == 0) { r[2 * e] = 0; r[2 * e + 1] = 0; }
-            } else if (qq >= n_wgq) {
-                if (tid == n - 1) { r[2 * e] = n - 1; r[2 * e + 1] = rows; }
-            } else {
-                const int64_t target = total * qq / n_wgq;
-                if (before <= target && (target < after || tid == n - 1)) {
-                    const int64_t p = (target - before + pc - 1) / pc;
-                    r[2 * e] = tid;
-                    r[2 * e + 1] = int(min(int64_t(rows), 2 * p));
-                }
-            }
-        }
-    }
-    __syncthreads();
-}
-
-// Run the rows of range (ja, ra) .. (jb, rb) of jobs[], the first segment
-// building the LUT from `first_src`.  All threads of the workgroup take part.
-__device__ inline void run_range(lds_float* hb, const KJob* jobs, int n_jobs, const MatArgs& M,
-                                 int slice, const int* rg, const LutSrc& first_src) {
-    int ja = rg[0], ra = rg[1];
-    const int jb = rg[2], rb = rg[3];
-    if (ra >= M.rows) {         // the start lies at the end of a job
-        ++ja;
-        ra = 0;
-    }
-    if (ja >= n_jobs || ja > jb || (ja == jb && ra >= rb)) return;
-    float xw = 0.f;
-    for (int j = ja; j <= jb; ++j) {
-        const int r0 = j == ja ? ra : 0;
-        const int r1 = j == jb ? rb : M.rows;
-        const KJob job = jobs[j];
-        if (j == ja)
-            xw = lut_segment_k<true>(job.k, hb, make_seg(M, job, slice, r0, r1), first_src, 0.f);
-        else if (r0 < r1)
-            xw = lut_segment_k<false>(job.k, hb, make_seg(M, job, slice, r0, r1), LutSrc{}, xw);
-    }
-}
-
+// Rows g0 .. g1-1 of the launch's row sequence (row r of job j is
+// j * rows + r), the first segment building the LUT from its job's source.
+// Every value here is the same across the workgroup; the job descriptions
+// are read straight from the argument block.
 template <bool DOWN>
 __global__ __launch_bounds__(kLutThreads) void lut_kernel(const KLaunch L) {
     // one LDS object: the table at address 0 (lut_sum relies on it), then
     // the padded h of the down stage
     __shared__ __attribute__((aligned(16))) char lds_buf[kLutBytes + (DOWN ? kHbufBytes : 0)];
-    __shared__ KJob s_jobs[kMaxLaunchJobs];
-    __shared__ int64_t s_cum[kMaxLaunchJobs];
-    __shared__ int s_range[4];
     lds_float* hb = (lds_float*)(lds_buf + kLutBytes);
-    // the job table in one parallel read of the argument block
-    if (int(threadIdx.x) < L.n_jobs) s_jobs[threadIdx.x] = L.job[threadIdx.x];
     const int slice = blockIdx.x % L.S, q = blockIdx.x / L.S;
-    wg_range(s_jobs, L.n_jobs, L.rows, L.n_wgq, L.map, L.wpg, q, s_cum, s_range);
+    const int g0 = L.start[q], g1 = L.start[q + 1];
+    if (g0 >= g1) return;
+    const int rows = L.rows;
+    const int ja = g0 / rows, ra = g0 - ja * rows;
+    const int jl = (g1 - 1) / rows, rl = g1 - jl * rows;
     const MatArgs M = mat_of(L);
-    const int j0 = min(max(s_range[0], 0), L.n_jobs - 1);
-    const KJob& first = s_jobs[j0];
-    const LutSrc src = DOWN ? src_h(L.gu, L.gu_smax, L.inter, first, first.src, slice)
-                            : src_x(L.x + size_t(first.src) * L.x_stride, slice);
-    run_range(hb, s_jobs, L.n_jobs, M, slice, s_range, src);
+    float xw = 0.f;
+    for (int j = ja; j <= jl; ++j) {
+        const KJob job = L.job[j];
+        const int r0 = j == ja ? ra : 0, r1 = j == jl ? rl : rows;
+        const Seg sg = make_seg(M, job, slice, r0, r1);
+        if (j == ja) {
+            const LutSrc src = DOWN ? src_h(L.gu, L.gu_smax, L.inter, job, job.src, slice)
+                                    : src_x(L.x + size_t(job.src) * L.x_stride, slice);
+            xw = lut_segment_k<true>(job.k, hb, sg, M.wpg, src, 0.f);
+        } else {
+            xw = lut_segment_k<false>(job.k, hb, sg, M.wpg, LutSrc{}, xw);
+        }
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void sum_slices_kernel(const float* __restrict__ part,
