@@ -26,6 +26,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s (% of peak) + expert-GEMVs/s at avg 2.5-bit prefixes"
 PEAK_HBM_GBS = 8000.0
+# Device code whose HBM traffic the counters below describe.
+KERNEL_SOURCES = ("bitplane_quantized_expert_amd/csrc/pm_kernels.hip",
+                  "bitplane_quantized_expert_amd/csrc/pm_internal.h")
+# HBM bytes per gate/up launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
+# passes of this benchmark, each scaled by the same counter on the 1 GiB
+# negation kernel (see --summarize-counters); reported only while the kernel
+# sources still have this digest.
+TRAFFIC = {"sources_sha256": "9618b6e7811411e9a4b042c5fa3f2e84e16b51d3660978ed9d42371cf3af91b6",
+           "bytes_per_launch": 48516078}
 
 
 def log(msg):
@@ -55,6 +64,64 @@ def gateup_bytes(wl, kk):
         for m in range(2):
             b += matrix_bytes(wl.inter, wl.hidden, wl.group, int(k3[m]))
     return b + wl.hidden * 4
+
+
+def sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def summarize_counters(fetch_csv, write_csv, stats_csv):
+    """Markdown summary of rocprofv3 runs of this benchmark: per-kernel mean
+    duration (kernel trace) and HBM bytes per dispatch (FETCH_SIZE and
+    WRITE_SIZE in KiB, each scaled by its reading on the 1 GiB negation
+    kernel, which reads and writes exactly 1 GiB)."""
+    import csv
+
+    def per_kernel(path, col="Counter_Value"):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            out.setdefault(r["Kernel_Name"], []).append(float(r[col]))
+        return out
+
+    def short(name):
+        for key, lab in (("lut_kernel<false>", "lut_kernel<false> (gate/up)"),
+                         ("lut_kernel<true>", "lut_kernel<true> (down)"),
+                         ("combine_k_kernel", "combine_k_kernel"), ("neg_kernel", "torch.neg 1 GiB")):
+            if key in name:
+                return lab
+        return None
+
+    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+    ref = 1 << 20                                    # KiB in 1 GiB
+    cal_f = ref / np.mean(next(v for k, v in fetch.items() if "neg_kernel" in k))
+    cal_w = ref / np.mean(next(v for k, v in write.items() if "neg_kernel" in k))
+    lines = ["| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM MB/dispatch (scaled) |",
+             "|---|---|---|---|---|"]
+    gate_up = None
+    for k in fetch:
+        lab = short(k)
+        if lab is None or k not in write:
+            continue
+        f, w = float(np.mean(fetch[k])), float(np.mean(write[k]))
+        mb = (f * cal_f + w * cal_w) * 1024 / 1e6
+        if "gate/up" in lab:
+            gate_up = (f * cal_f + w * cal_w) * 1024
+        lines.append(f"| {lab} | {len(fetch[k])} | {f:.1f} | {w:.1f} | {mb:.2f} |")
+    lines += ["", f"Scale factors: FETCH_SIZE x{cal_f:.3f}, WRITE_SIZE x{cal_w:.3f}.", "",
+              "| kernel | calls | mean us | min us | max us |", "|---|---|---|---|---|"]
+    for r in csv.DictReader(open(stats_csv)):
+        lab = short(r["Name"])
+        if lab:
+            lines.append(f"| {lab} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", f"gate/up HBM bytes per launch: {gate_up:.0f}",
+              f"kernel sources sha256: {sources_digest()}"]
+    return "\n".join(lines)
 
 
 def copy_ceiling(torch, stream, nbytes=1 << 30, reps=5):
@@ -125,7 +192,12 @@ def main():
     ap.add_argument("--experts", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV"),
+                    help="print a summary of rocprofv3 outputs of this benchmark and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the path is built and timed on a single MI355X)", file=sys.stderr)
@@ -180,13 +252,15 @@ def main():
     t0 = time.perf_counter()
     for s in range(args.warmup, total):
         run(s)
+    issued = time.perf_counter() - t0
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     steps = range(args.warmup, total)
     nbytes = sum(step_bytes(wl, k3[s]) for s in steps)
     gbs = nbytes / el / 1e9
     ms = el / args.steps * 1e3
-    log(f"timed {args.steps} steps: {ms:.4f} ms/step, {gbs:.1f} GB/s")
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step, {gbs:.1f} GB/s "
+        f"(host issue {issued / args.steps * 1e6:.1f} us/step)")
 
     ceiling = copy_ceiling(torch, stream)
     log(f"stream ceiling: {ceiling['GBs']} GB/s ({ceiling['kernel']})")
@@ -221,12 +295,15 @@ def main():
                    "inter": wl.inter, "group": wl.group, "top_k": wl.top_k, "batch": 1,
                    "mean_k": round(float(kk[args.warmup:].mean()), 4), "pool_experts": n_exp},
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "host_issue_us_per_step": round(issued / args.steps * 1e6, 2),
         "expert_gemvs_per_s": round(3 * wl.top_k * args.steps / el, 1),
         "stage_us": {"gateup": round(gu_ms.mean() * 1e3, 2), "down": round(dn_ms.mean() * 1e3, 2),
                      "combine": round(cb_ms.mean() * 1e3, 2)},
         "roofline": {"bound": "hbm", "kernel": "gateup", "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": (TRAFFIC["bytes_per_launch"]
+                                 if TRAFFIC["sources_sha256"] == sources_digest() else None),
                      "bytes_per_launch": int(gu_b.mean()),
                      "launch_us": round(gu_ms.mean() * 1e3, 2)},
         "stream_ceiling": ceiling,

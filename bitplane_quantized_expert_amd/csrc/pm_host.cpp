@@ -1171,8 +1171,15 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
             sl.pending = false;
         }
     }
-    if (s->profiling) HIP_TRY(hipEventRecord(s->prof[0], compute));
-    for (const KLaunch& L : L_gu[0]) HIP_TRY(launch_lut(L, false, compute));
+    // a gate/up stage of one LUT launch is timed by the launch itself
+    const bool gu_single = L_gu[0].size() == 1 && d_gu0 == 0 && n_res == n_items;
+    if (s->profiling && !gu_single) HIP_TRY(hipEventRecord(s->prof[0], compute));
+    for (const KLaunch& L : L_gu[0]) {
+        if (s->profiling && gu_single)
+            HIP_TRY(launch_lut(L, false, compute, s->prof[0], s->prof[1]));
+        else
+            HIP_TRY(launch_lut(L, false, compute));
+    }
     if (d_gu0) HIP_TRY(launch_direct_gateup(g, ddir, int(d_gu0), duses, dlist, d_x, P, compute));
     if (n_res < n_items) {
         for (int i = n_res; i < n_items; ++i) {
@@ -1185,7 +1192,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
             HIP_TRY(launch_direct_gateup(g, ddir + d_gu0, int(d_gu1), duses, dlist, d_x, P,
                                          compute));
     }
-    if (s->profiling) HIP_TRY(hipEventRecord(s->prof[1], compute));
+    if (s->profiling && !gu_single) HIP_TRY(hipEventRecord(s->prof[1], compute));
     if (!dir_dn.empty()) {
         HIP_TRY(launch_swiglu(duses, n_uses, P, g.inter, compute));
         HIP_TRY(launch_direct_down(g, ddir + d_gu0 + d_gu1, int(dir_dn.size()), duses, dlist, P,

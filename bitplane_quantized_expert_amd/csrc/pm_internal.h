@@ -135,7 +135,9 @@ hipError_t launch_gemv_fp16(int rows, int cols, const uint16_t* w, const float* 
 // LUT path: n_wgq * S workgroups of 512 threads, about 132 KiB of LDS each.
 // Gate/up (down == false): the activation slice comes from L.x; down: h of
 // use src, formed from the gate/up partials L.gu.
-hipError_t launch_lut(const KLaunch& L, bool down, hipStream_t st);
+// t0 / t1: if given, the launch's own start and stop events.
+hipError_t launch_lut(const KLaunch& L, bool down, hipStream_t st, hipEvent_t t0 = nullptr,
+                      hipEvent_t t1 = nullptr);
 // Combine with the weights in the kernel arguments: tokens t0 .. t0+n-1.
 constexpr int kMaxLaunchUses = 128;
 struct KCombine {

@@ -23,6 +23,7 @@
 // All sums run in a fixed order (DPP row reductions, slices and slots in
 // index order), so every output is deterministic.
 #include <hip/hip_fp16.h>
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "pm_internal.h"
@@ -814,13 +815,20 @@ hipError_t launch_gemv(int rows, int cols, int group, int k, const uint32_t* pla
     return hipGetLastError();
 }
 
-hipError_t launch_lut(const KLaunch& L, bool down, hipStream_t st) {
+hipError_t launch_lut(const KLaunch& L, bool down, hipStream_t st, hipEvent_t t0,
+                      hipEvent_t t1) {
     if (L.n_jobs == 0 || L.n_wgq == 0) return hipSuccess;
     const dim3 grid(unsigned(L.n_wgq * L.S));
-    if (down)
+    if (t0 || t1) {
+        if (down)
+            hipExtLaunchKernelGGL(lut_kernel<true>, grid, dim3(kLutThreads), 0, st, t0, t1, 0, L);
+        else
+            hipExtLaunchKernelGGL(lut_kernel<false>, grid, dim3(kLutThreads), 0, st, t0, t1, 0, L);
+    } else if (down) {
         hipLaunchKernelGGL(lut_kernel<true>, grid, dim3(kLutThreads), 0, st, L);
-    else
+    } else {
         hipLaunchKernelGGL(lut_kernel<false>, grid, dim3(kLutThreads), 0, st, L);
+    }
     return hipGetLastError();
 }
 
