@@ -266,7 +266,8 @@ extern "C" pm_status pm_expert_gemv(pm_matrix_shape s, int k, const uint32_t* d_
     if (st) return st;
     if (s.rows == 0) return PM_OK;
     if (s.cols > 0 && !d_x) return fail(PM_ERR_ARG, "null x");
-    if (k <= kLutMaxK && s.cols > 0 && s.cols % kSliceCols == 0 && kSliceCols % s.group == 0)
+    if (k <= kLutMaxK && s.cols > 0 && s.cols % kSliceCols == 0 && kSliceCols % s.group == 0 &&
+        s.rows % 2 == 0)
         return gemv_lut(s, k, d_planes, pstride, d_levels, d_x, d_y, (hipStream_t)stream);
     HIP_TRY(launch_gemv(s.rows, s.cols, s.group, k, d_planes, pstride, d_levels, d_x, d_y,
                         (hipStream_t)stream));
@@ -986,9 +987,11 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
 
     // ---- path of every (use, matrix): LUT for an unshared expert at k <= 5
     // when the columns split into 1024-column slices (at most 15), else direct
+    // the LUT path takes rows in pairs: an even number of rows per matrix
     const bool gu_lut_shape = g.hidden % kSliceCols == 0 && kSliceCols % g.group == 0 &&
-                              g.hidden / kSliceCols <= 15;
-    const bool dn_lut_shape = g.inter % kSliceCols == 0 && kSliceCols % g.group == 0;
+                              g.hidden / kSliceCols <= 15 && g.inter % 2 == 0;
+    const bool dn_lut_shape = g.inter % kSliceCols == 0 && kSliceCols % g.group == 0 &&
+                              g.hidden % 2 == 0;
     const int S_gu = gu_lut_shape ? g.hidden / kSliceCols : 1;
     const int S_dn = dn_lut_shape ? g.inter / kSliceCols : 1;
     for (int d = 0; d < n_items; ++d) {

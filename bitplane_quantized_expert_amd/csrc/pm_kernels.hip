@@ -267,19 +267,21 @@ struct LutRowIn {
 };
 
 template <int K>
-__device__ inline void lut_load(LutRowIn<K>& in, const uint32_t* pw, const float* t,
-                                uint64_t pstride) {
-    g_u32* gw = (g_u32*)pw;
+__device__ inline void lut_load(LutRowIn<K>& in, const uint32_t* pw, uint32_t wo,
+                                const float* t, uint32_t to, uint64_t pstride) {
+    // wave-uniform bases, the lane's byte offset added last
 #pragma unroll
-    for (int p = 0; p < K; ++p) in.w[p] = __builtin_nontemporal_load(gw + p * pstride);
+    for (int p = 0; p < K; ++p)
+        in.w[p] = *(g_u32*)(reinterpret_cast<const char*>(pw + p * pstride) + wo);
+    const char* tb = reinterpret_cast<const char*>(t) + to;
     if constexpr (K == 1) {
-        const f32x2 a = *(g_f32x2*)t;
+        const f32x2 a = *(g_f32x2*)tb;
         in.tab[0] = a.x;
         in.tab[1] = a.y;
     } else {
 #pragma unroll
         for (int i = 0; i < (1 << K); i += 4) {
-            const f32x4 a = *(g_f32x4*)(t + i);
+            const f32x4 a = *(g_f32x4*)(tb + 4 * i);
             in.tab[i] = a.x;
             in.tab[i + 1] = a.y;
             in.tab[i + 2] = a.z;
@@ -298,7 +300,9 @@ constexpr int lut_unroll() {
 }
 
 // One job segment: the slice's first word and first block table in row 0
-// (shared by the wave), and the lane's offsets from them.
+// (shared by the wave), and the lane's byte offsets from them.  The LUT path
+// takes an even number of rows per matrix and cuts segments at even rows, so
+// every row pair of a segment lies inside it.
 struct Seg {
     const uint32_t* pw;    // plane 0, row 0, first word of the slice
     const float* tab;      // depth-k table of the slice's first block, row 0
@@ -306,34 +310,36 @@ struct Seg {
     uint64_t pstride;      // words between planes
     int W;                 // words per row
     int tab_row;           // floats between tables of consecutive rows
-    int r0, r1;            // rows [r0, r1)
-    int wo, to;            // lane offsets: words (l + (lane >> 5) * W), table floats
+    int r0, r1;            // rows [r0, r1), both even
+    uint32_t wo, to, oo;   // lane byte offsets: word, table, output
 };
 
 // A batch: U row pairs of this wave, pairs p, p + kLutWaves, ... (rows 2p + hw).
 template <int K, int U>
 struct Batch {
     LutRowIn<K> in[U];
-    int row[U];
+    int pp[U];             // pair index (wave-uniform)
+    bool ok[U];            // the pair lies in the segment (wave-uniform)
 };
 
-// Loads are unconditional (a row outside the segment reloads a row inside
-// it and is not stored), so that the batch is straight-line code and the
-// wait for batch A does not also wait for batch B's loads in flight.
+template <class T>
+__device__ inline const T* at_bytes(const T* base, uint32_t off) {
+    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
+}
+
+// Loads are unconditional (a pair past the segment reloads its last pair
+// and is not stored), so that the batch is straight-line code; every
+// address is a wave-uniform base plus the lane's fixed byte offset.
 template <int K, int U>
-__device__ inline void batch_load(Batch<K, U>& B, const Seg& sg, int p, int p1, int hw) {
+__device__ inline void batch_load(Batch<K, U>& B, const Seg& sg, int p, int p1) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int pp = min(p + u * kLutWaves, p1 - 1);      // wave-uniform
-        const int row = 2 * pp + hw;
-        const bool ok = p + u * kLutWaves < p1 && row >= sg.r0 && row < sg.r1;
-        B.row[u] = ok ? row : -1;
-        // the pair's first row from the shared bases, then the lane's offset;
-        // a half outside [r0, r1) reads its neighbour row (not stored)
-        const int fix = row < sg.r0 ? 1 : row >= sg.r1 ? -1 : 0;
-        const size_t r2 = size_t(2 * pp);
-        lut_load<K>(B.in[u], sg.pw + r2 * sg.W + (sg.wo + fix * sg.W),
-                    sg.tab + r2 * sg.tab_row + (sg.to + (hw + fix) * sg.tab_row), sg.pstride);
+        const int q = p + u * kLutWaves;
+        const int pp = min(q, p1 - 1);
+        B.pp[u] = pp;
+        B.ok[u] = q < p1;
+        lut_load<K>(B.in[u], sg.pw + size_t(2 * pp) * sg.W, sg.wo,
+                    sg.tab + size_t(2 * pp) * sg.tab_row, sg.to, sg.pstride);
     }
 }
 
@@ -347,11 +353,10 @@ __device__ inline void batch_compute(const Batch<K, U>& B, const Seg& sg, float 
     for (int u = 0; u < U; ++u) acc[u] = lut_row<K>(B.in[u].w, B.in[u].tab, xw, b0, b1);
 #pragma unroll
     for (int u = 0; u < U; ++u) acc[u] = half_sum(acc[u]);
-    if (l == 31) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (B.row[u] >= 0) ((g_f32_out*)sg.out)[B.row[u]] = acc[u];
-    }
+    for (int u = 0; u < U; ++u)
+        if (B.ok[u] && l == 31)
+            *(g_f32_out*)at_bytes(sg.out + 2 * B.pp[u], sg.oo) = acc[u];
 }
 
 // Where the LUT of a workgroup comes from (see build_lut).
@@ -377,15 +382,16 @@ __device__ __noinline__ float lut_segment(lds_float* hbuf, const uint32_t* pw, c
     const int tid = threadIdx.x, wave = uni(tid / kWave), lane = tid % kWave;
     const int hw = lane >> 5, l = lane & 31;
     Seg sg{uni_ptr(pw), uni_ptr(tab), uni_ptr(out), uni64(pstride), uni(W), uni(tab_row),
-           uni(r0), uni(r1), 0, 0};
-    sg.wo = l + hw * sg.W;
-    sg.to = (l / wpg) << K;
+           uni(r0), uni(r1), 0, 0, 0};
+    sg.wo = uint32_t(l + hw * sg.W) * 4u;
+    sg.to = uint32_t(hw * sg.tab_row + ((l / wpg) << K)) * 4u;
+    sg.oo = uint32_t(hw) * 4u;
     const uint32_t b0 = uint32_t(l) << 2, b1 = b0 | 0x10000u;
     const int p1 = (sg.r1 + 1) >> 1;
     constexpr int step = kLutWaves * U;
     int p = (sg.r0 >> 1) + wave;
     Batch<K, U> A, B;
-    batch_load<K, U>(A, sg, p, p1, hw);
+    batch_load<K, U>(A, sg, p, p1);
     if constexpr (FIRST) {
         build_lut(hbuf, x, pg, pu, ngnu & 15, ngnu >> 4, hstride);
         __syncthreads();
@@ -396,13 +402,13 @@ __device__ __noinline__ float lut_segment(lds_float* hbuf, const uint32_t* pw, c
     // the scheduling barriers keep each batch's loads ahead of the other
     // batch's arithmetic (hoisting that arithmetic would make the loads wait)
     while (p < p1) {
-        batch_load<K, U>(B, sg, p + step, p1, hw);
+        batch_load<K, U>(B, sg, p + step, p1);
         __builtin_amdgcn_sched_barrier(0);
         batch_compute<K, U>(A, sg, xw, b0, b1, l);
         __builtin_amdgcn_sched_barrier(0);
         p += step;
         if (p >= p1) break;
-        batch_load<K, U>(A, sg, p + step, p1, hw);
+        batch_load<K, U>(A, sg, p + step, p1);
         __builtin_amdgcn_sched_barrier(0);
         batch_compute<K, U>(B, sg, xw, b0, b1, l);
         __builtin_amdgcn_sched_barrier(0);
@@ -451,7 +457,7 @@ __device__ inline Seg make_seg(const MatArgs& M, const KJob& jb, int slice, int 
     sg.tab_row = (M.W / M.wpg) << jb.k;
     sg.r0 = r0;
     sg.r1 = r1;
-    sg.wo = sg.to = 0;
+    sg.wo = sg.to = sg.oo = 0;
     return sg;
 }
 
