@@ -1047,7 +1047,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     gu_proto.W = g.hidden / 32;
     gu_proto.wpg = g.group / 32;
     gu_proto.out_stride = g.inter;
-    gu_proto.x_stride = g.hidden;
+    gu_proto.x_stride = n_tokens == 1 ? 0 : g.hidden;     // 0: one activation for all jobs
     KLaunch dn_proto{};
     dn_proto.gu = P.gu;
     dn_proto.gu_smax = S_gu;

@@ -98,6 +98,7 @@ struct KJob {                      // one matrix of one use
 constexpr int kMaxLaunchWgq = 256;
 struct KLaunch {
     const float* x;                // gate/up: activation of token t at x + t * x_stride
+                                   // (x_stride 0: every job reads x itself)
     const float* gu;               // down: gate/up partials [use][2][gu_smax][inter]
     uint64_t pstride;              // words between planes
     int32_t n_jobs, n_wgq, S, rows;

@@ -197,8 +197,20 @@ __device__ inline float lut_row(const uint32_t (&w)[K], const float (&tab)[1 << 
 // nu slices), `stride` floats apart.  Sums with a zero term are exact.  h is
 // staged with one pad word per 32 so that the chunk-wise reads hit 32
 // different banks.
+// A thread's eight activation values of its chunk, loaded ahead of time (a
+// vector type, so that it travels in registers into out-of-line calls).
+typedef float X8 __attribute__((ext_vector_type(8)));
+
+__device__ inline X8 load_x8(const float* x) {
+    const int tid = threadIdx.x;
+    const int c8 = 8 * (4 * (tid & 31) + ((tid >> 5) & 3));
+    const f32x4 a = *(g_f32x4*)(x + c8);
+    const f32x4 b = *(g_f32x4*)(x + c8 + 4);
+    return X8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+}
+
 __device__ inline void build_lut(lds_float* hbuf, const float* x, const float* pg,
-                                 const float* pu, int ng, int nu, int stride) {
+                                 const float* pu, int ng, int nu, int stride, const X8& xv) {
     constexpr int kQ = kLutThreads / 128;          // q values spread over threads
     constexpr int kPer = 8 / kQ;                   // q values per thread
     const int tid = threadIdx.x;
@@ -237,11 +249,14 @@ __device__ inline void build_lut(lds_float* hbuf, const float* x, const float* p
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = hbuf[c8 + i + ((c8 + i) >> 5)];
-    } else {
+    } else if (x) {
         const f32x4 a = *(g_f32x4*)(x + c8);
         const f32x4 b = *(g_f32x4*)(x + c8 + 4);
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
         v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = xv[i];
     }
     const int c = 4 * l + t;
     float sub[32];
@@ -361,10 +376,11 @@ __device__ inline void batch_compute(const Batch<K, U>& B, const Seg& sg, float 
 
 // Where the LUT of a workgroup comes from (see build_lut).
 struct LutSrc {
-    const float* x;
+    const float* x;        // null with pg null: the values are in xv
     const float* pg;
     const float* pu;
     int ng, nu, stride;
+    X8 xv;
 };
 
 // Rows [r0, r1) of one job for this wave, double-buffered: the next batch is
@@ -377,7 +393,7 @@ __device__ __noinline__ float lut_segment(lds_float* hbuf, const uint32_t* pw, c
                                           float* out, uint64_t pstride, int W, int tab_row,
                                           int wpg, int r0, int r1, const float* x,
                                           const float* pg, const float* pu, int ngnu,
-                                          int hstride, float xw) {
+                                          int hstride, X8 xv, float xw) {
     constexpr int U = lut_unroll<K>();
     const int tid = threadIdx.x, wave = uni(tid / kWave), lane = tid % kWave;
     const int hw = lane >> 5, l = lane & 31;
@@ -393,7 +409,7 @@ __device__ __noinline__ float lut_segment(lds_float* hbuf, const uint32_t* pw, c
     Batch<K, U> A, B;
     batch_load<K, U>(A, sg, p, p1);
     if constexpr (FIRST) {
-        build_lut(hbuf, x, pg, pu, ngnu & 15, ngnu >> 4, hstride);
+        build_lut(hbuf, x, pg, pu, ngnu & 15, ngnu >> 4, hstride, xv);
         __syncthreads();
         xw = 0.f;
 #pragma unroll
@@ -423,7 +439,7 @@ __device__ inline float lut_segment_k(int k, lds_float* hbuf, const Seg& sg, int
     const int ngnu = src.ng | (src.nu << 4);
 #define PM_SEG(KK)                                                                            \
     lut_segment<KK, FIRST>(hbuf, sg.pw, sg.tab, sg.out, sg.pstride, sg.W, sg.tab_row, wpg,   \
-                           sg.r0, sg.r1, src.x, src.pg, src.pu, ngnu, src.stride, xw)
+                           sg.r0, sg.r1, src.x, src.pg, src.pu, ngnu, src.stride, src.xv, xw)
     switch (k) {
         case 1: return PM_SEG(1);
         case 2: return PM_SEG(2);
@@ -491,6 +507,11 @@ __global__ __launch_bounds__(kLutThreads) void lut_kernel(const KLaunch L) {
     __shared__ __attribute__((aligned(16))) char lds_buf[kLutBytes + (DOWN ? kHbufBytes : 0)];
     lds_float* hb = (lds_float*)(lds_buf + kLutBytes);
     const int slice = blockIdx.x % L.S, q = blockIdx.x / L.S;
+    // one activation for the whole launch (x_stride 0): its slice is loaded
+    // before the row range is known
+    X8 xpre{};
+    const bool pre = !DOWN && L.x_stride == 0;
+    if (pre) xpre = load_x8(L.x + kSliceCols * slice);
     const int g0 = L.start[q], g1 = L.start[q + 1];
     if (g0 >= g1) return;
     const int rows = L.rows;
@@ -503,8 +524,12 @@ __global__ __launch_bounds__(kLutThreads) void lut_kernel(const KLaunch L) {
         const int r0 = j == ja ? ra : 0, r1 = j == jl ? rl : rows;
         const Seg sg = make_seg(M, job, slice, r0, r1);
         if (j == ja) {
-            const LutSrc src = DOWN ? src_h(L.gu, L.gu_smax, L.inter, job, job.src, slice)
-                                    : src_x(L.x + size_t(job.src) * L.x_stride, slice);
+            LutSrc src = DOWN ? src_h(L.gu, L.gu_smax, L.inter, job, job.src, slice)
+                              : src_x(L.x + size_t(job.src) * L.x_stride, slice);
+            if (pre) {
+                src.x = nullptr;
+                src.xv = xpre;
+            }
             xw = lut_segment_k<true>(job.k, hb, sg, M.wpg, src, 0.f);
         } else {
             xw = lut_segment_k<false>(job.k, hb, sg, M.wpg, LutSrc{}, xw);
