@@ -256,6 +256,15 @@ static pm_status check_matrix_call(pm_matrix_shape s, int k, const void* planes,
     return PM_OK;
 }
 
+// The LUT kernels address planes and tables with 32-bit byte offsets from a
+// slice's base: planes 0..k-1 and the depth-k tables of one matrix must fit.
+static bool lut_offsets_fit(pm_matrix_shape s, int k, size_t pstride) {
+    const uint64_t lim = uint64_t(1) << 31;
+    const uint64_t planes = (uint64_t(k - 1) * pstride + uint64_t(s.rows) * (s.cols / 32)) * 4;
+    const uint64_t tables = uint64_t(s.rows) * (s.cols / s.group) * (uint64_t(1) << k) * 4;
+    return planes < lim && tables < lim;
+}
+
 pm_status gemv_lut(pm_matrix_shape s, int k, const uint32_t* d_planes, size_t pstride,
                    const float* d_levels, const float* d_x, float* d_y, hipStream_t st);
 
@@ -266,8 +275,8 @@ extern "C" pm_status pm_expert_gemv(pm_matrix_shape s, int k, const uint32_t* d_
     if (st) return st;
     if (s.rows == 0) return PM_OK;
     if (s.cols > 0 && !d_x) return fail(PM_ERR_ARG, "null x");
-    if (k <= kLutMaxK && s.cols > 0 && s.cols % kSliceCols == 0 && kSliceCols % s.group == 0 &&
-        s.rows % 2 == 0)
+    if (k <= kLutMaxK && s.cols > 0 && s.cols % kSliceCols == 0 && s.group == kLutGroup &&
+        s.rows % 2 == 0 && lut_offsets_fit(s, k, pstride))
         return gemv_lut(s, k, d_planes, pstride, d_levels, d_x, d_y, (hipStream_t)stream);
     HIP_TRY(launch_gemv(s.rows, s.cols, s.group, k, d_planes, pstride, d_levels, d_x, d_y,
                         (hipStream_t)stream));
@@ -987,10 +996,11 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
 
     // ---- path of every (use, matrix): LUT for an unshared expert at k <= 5
     // when the columns split into 1024-column slices (at most 15), else direct
-    // the LUT path takes rows in pairs: an even number of rows per matrix
-    const bool gu_lut_shape = g.hidden % kSliceCols == 0 && kSliceCols % g.group == 0 &&
+    // the LUT path takes rows in pairs (an even number of rows per matrix)
+    // and blocks of kLutGroup inputs
+    const bool gu_lut_shape = g.hidden % kSliceCols == 0 && g.group == kLutGroup &&
                               g.hidden / kSliceCols <= 15 && g.inter % 2 == 0;
-    const bool dn_lut_shape = g.inter % kSliceCols == 0 && kSliceCols % g.group == 0 &&
+    const bool dn_lut_shape = g.inter % kSliceCols == 0 && g.group == kLutGroup &&
                               g.hidden % 2 == 0;
     const int S_gu = gu_lut_shape ? g.hidden / kSliceCols : 1;
     const int S_dn = dn_lut_shape ? g.inter / kSliceCols : 1;
@@ -999,7 +1009,10 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         for (int u : item_uses[d]) {
             for (int m = 0; m < 3; ++m) {
                 const bool shape_ok = m < 2 ? gu_lut_shape : dn_lut_shape;
-                const bool lut = alone && shape_ok && uses[u].k[m] <= kLutMaxK;
+                const pm_matrix_shape ms = m < 2 ? pm_matrix_shape{g.inter, g.hidden, g.group}
+                                                 : pm_matrix_shape{g.hidden, g.inter, g.group};
+                const bool lut = alone && shape_ok && uses[u].k[m] <= kLutMaxK &&
+                                 lut_offsets_fit(ms, uses[u].k[m], g.plane_words);
                 uses[u].direct[m] = lut ? 0 : 1;
                 uses[u].slices[m] = lut ? (m < 2 ? S_gu : S_dn) : 1;
             }

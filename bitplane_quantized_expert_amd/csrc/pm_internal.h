@@ -77,6 +77,8 @@ struct Partials {
 };
 
 constexpr int kSliceCols = 1024;   // columns of x covered by one LUT
+// Block size of the LUT path: the four lanes of a block share its table.
+constexpr int kLutGroup = 128;
 constexpr int kLutMaxK = 5;        // largest prefix read through the LUT path
 
 // LUT-path launch description, passed as kernel arguments (no upload).

@@ -156,14 +156,51 @@ struct PrefixMasks<K, K, V> {
     }
 };
 
+// Floats of a block's depth-K table held by each lane of the block's four
+// lanes (a block is 128 inputs, four 32-bit words): lane q of the quad holds
+// values q*NQ .. q*NQ + NQ - 1 (K = 1: lane q holds value q & 1).
+template <int K>
+constexpr int quad_share() {
+    return (1 << K) >= 4 ? (1 << K) / 4 : 1;
+}
+
+// Node value V of this lane's block, from the quad lane that holds it.
+template <int K, int V>
+__device__ inline float quad_node(const float (&tq)[quad_share<K>()]) {
+    constexpr int NQ = quad_share<K>();
+    constexpr int owner = K == 1 ? V : V / NQ;
+    constexpr int j = K == 1 ? 0 : V % NQ;
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, tq[j]), owner * 0x55, 0xF, 0xF,
+                                        true));
+}
+
+// Bucket V's term of one row: its sum S from the four chunk lookups (in chunk
+// order), taken off the running remainder, times node V.
+template <int K, int V>
+__device__ inline void lut_term(const float* r, const float (&tq)[quad_share<K>()], float& acc,
+                                float& last) {
+    if constexpr (V < (1 << K) - 1) {
+        float S = r[4 * V];
+        S += r[4 * V + 1];
+        S += r[4 * V + 2];
+        S += r[4 * V + 3];
+        last -= S;
+        acc = fmaf(quad_node<K, V>(tq), S, acc);
+        lut_term<K, V + 1>(r, tq, acc, last);
+    } else {
+        acc = fmaf(quad_node<K, V>(tq), last, acc);
+    }
+}
+
 // One row's contribution of this lane's word at prefix K:
 // sum_v node(v) * S_v, S_v = sum of x where the prefix is v.  All lookups of
 // the row are issued before any is consumed, so one LDS round trip covers the
-// row; then the bucket sums are formed in v order (each from its four chunk
-// sums in chunk order) and the last bucket by subtraction.
+// row; then the bucket sums are formed in v order and the last bucket, by
+// subtraction, from the word's total xw.
 template <int K>
-__device__ inline float lut_row(const uint32_t (&w)[K], const float (&tab)[1 << K], float xw,
-                                uint32_t b0, uint32_t b1) {
+__device__ inline float lut_row(const uint32_t (&w)[K], const float (&tq)[quad_share<K>()],
+                                float xw, uint32_t b0, uint32_t b1) {
     constexpr int N = (1 << K) - 1;
     uint32_t m[N];
     PrefixMasks<K, 0, 0>::go(w, 0xFFFFFFFFu, m);
@@ -176,16 +213,8 @@ __device__ inline float lut_row(const uint32_t (&w)[K], const float (&tab)[1 << 
         r[4 * v + 3] = lds_at(__builtin_amdgcn_perm(b1, m[v], 0x0C060304u) + 128);
     }
     float acc = 0.f, last = xw;
-#pragma unroll
-    for (int v = 0; v < N; ++v) {
-        float S = r[4 * v];
-        S += r[4 * v + 1];
-        S += r[4 * v + 2];
-        S += r[4 * v + 3];
-        last -= S;
-        acc = fmaf(tab[v], S, acc);
-    }
-    return fmaf(tab[N], last, acc);
+    lut_term<K, 0>(r, tq, acc, last);
+    return acc;
 }
 
 // The activation slice of this workgroup into the LUT.  Thread tid owns
@@ -278,31 +307,30 @@ __device__ inline void build_lut(lds_float* hbuf, const float* x, const float* p
 template <int K>
 struct LutRowIn {
     uint32_t w[K];
-    float tab[1 << K];
+    float tq[quad_share<K>()];
 };
 
+// Buffer resource over `bytes` bytes from p: loads through it take a
+// wave-uniform byte offset (scalar) plus the lane's byte offset, and return 0
+// past the end.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), 0x00020000);
+}
+
+// One row pair's inputs for this lane: its word of planes 0..K-1 and its
+// share of its block's depth-K table.  prow / trow: the pair's wave-uniform
+// byte offsets into the plane and table buffers; wo / to: the lane's.
 template <int K>
-__device__ inline void lut_load(LutRowIn<K>& in, const uint32_t* pw, uint32_t wo,
-                                const float* t, uint32_t to, uint64_t pstride) {
-    // wave-uniform bases, the lane's byte offset added last
+__device__ inline void lut_load(LutRowIn<K>& in, __amdgpu_buffer_rsrc_t rp, __amdgpu_buffer_rsrc_t rt,
+                                uint32_t wo, uint32_t to, uint32_t prow, uint32_t trow,
+                                uint32_t pbytes) {
 #pragma unroll
     for (int p = 0; p < K; ++p)
-        in.w[p] = *(g_u32*)(reinterpret_cast<const char*>(pw + p * pstride) + wo);
-    const char* tb = reinterpret_cast<const char*>(t) + to;
-    if constexpr (K == 1) {
-        const f32x2 a = *(g_f32x2*)tb;
-        in.tab[0] = a.x;
-        in.tab[1] = a.y;
-    } else {
+        in.w[p] = uint32_t(__builtin_amdgcn_raw_buffer_load_b32(rp, int(wo), int(prow + p * pbytes), 0));
 #pragma unroll
-        for (int i = 0; i < (1 << K); i += 4) {
-            const f32x4 a = *(g_f32x4*)(tb + 4 * i);
-            in.tab[i] = a.x;
-            in.tab[i + 1] = a.y;
-            in.tab[i + 2] = a.z;
-            in.tab[i + 3] = a.w;
-        }
-    }
+    for (int j = 0; j < quad_share<K>(); ++j)
+        in.tq[j] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rt, int(to + 4 * j), int(trow), 0));
 }
 
 template <int K>
@@ -346,15 +374,16 @@ __device__ inline const T* at_bytes(const T* base, uint32_t off) {
 // and is not stored), so that the batch is straight-line code; every
 // address is a wave-uniform base plus the lane's fixed byte offset.
 template <int K, int U>
-__device__ inline void batch_load(Batch<K, U>& B, const Seg& sg, int p, int p1) {
+__device__ inline void batch_load(Batch<K, U>& B, const Seg& sg, __amdgpu_buffer_rsrc_t rp,
+                                  __amdgpu_buffer_rsrc_t rt, int p, int p1) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int q = p + u * kLutWaves;
         const int pp = min(q, p1 - 1);
         B.pp[u] = pp;
         B.ok[u] = q < p1;
-        lut_load<K>(B.in[u], sg.pw + size_t(2 * pp) * sg.W, sg.wo,
-                    sg.tab + size_t(2 * pp) * sg.tab_row, sg.to, sg.pstride);
+        lut_load<K>(B.in[u], rp, rt, sg.wo, sg.to, uint32_t(2 * pp * sg.W) * 4u,
+                    uint32_t(2 * pp * sg.tab_row) * 4u, uint32_t(sg.pstride) * 4u);
     }
 }
 
@@ -365,7 +394,7 @@ __device__ inline void batch_compute(const Batch<K, U>& B, const Seg& sg, float 
                                      uint32_t b1, int l) {
     float acc[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc[u] = lut_row<K>(B.in[u].w, B.in[u].tab, xw, b0, b1);
+    for (int u = 0; u < U; ++u) acc[u] = lut_row<K>(B.in[u].w, B.in[u].tq, xw, b0, b1);
 #pragma unroll
     for (int u = 0; u < U; ++u) acc[u] = half_sum(acc[u]);
 #pragma unroll
@@ -399,15 +428,21 @@ __device__ __noinline__ float lut_segment(lds_float* hbuf, const uint32_t* pw, c
     const int hw = lane >> 5, l = lane & 31;
     Seg sg{uni_ptr(pw), uni_ptr(tab), uni_ptr(out), uni64(pstride), uni(W), uni(tab_row),
            uni(r0), uni(r1), 0, 0, 0};
+    // planes 0..K-1 and the tables of the rows below r1
+    const __amdgpu_buffer_rsrc_t rp =
+        buffer_of(sg.pw, uint32_t(((K - 1) * sg.pstride + uint64_t(sg.r1) * sg.W) * 4));
+    const __amdgpu_buffer_rsrc_t rt = buffer_of(sg.tab, uint32_t(uint64_t(sg.r1) * sg.tab_row * 4));
     sg.wo = uint32_t(l + hw * sg.W) * 4u;
-    sg.to = uint32_t(hw * sg.tab_row + ((l / wpg) << K)) * 4u;
+    // the lane's quad share of its block's table (four lanes per block)
+    sg.to = uint32_t(hw * sg.tab_row + ((l >> 2) << K) +
+                     (K == 1 ? (l & 1) : (l & 3) * quad_share<K>())) * 4u;
     sg.oo = uint32_t(hw) * 4u;
     const uint32_t b0 = uint32_t(l) << 2, b1 = b0 | 0x10000u;
     const int p1 = (sg.r1 + 1) >> 1;
     constexpr int step = kLutWaves * U;
     int p = (sg.r0 >> 1) + wave;
     Batch<K, U> A, B;
-    batch_load<K, U>(A, sg, p, p1);
+    batch_load<K, U>(A, sg, rp, rt, p, p1);
     if constexpr (FIRST) {
         build_lut(hbuf, x, pg, pu, ngnu & 15, ngnu >> 4, hstride, xv);
         __syncthreads();
@@ -418,13 +453,13 @@ __device__ __noinline__ float lut_segment(lds_float* hbuf, const uint32_t* pw, c
     // the scheduling barriers keep each batch's loads ahead of the other
     // batch's arithmetic (hoisting that arithmetic would make the loads wait)
     while (p < p1) {
-        batch_load<K, U>(B, sg, p + step, p1);
+        batch_load<K, U>(B, sg, rp, rt, p + step, p1);
         __builtin_amdgcn_sched_barrier(0);
         batch_compute<K, U>(A, sg, xw, b0, b1, l);
         __builtin_amdgcn_sched_barrier(0);
         p += step;
         if (p >= p1) break;
-        batch_load<K, U>(A, sg, p + step, p1);
+        batch_load<K, U>(A, sg, rp, rt, p + step, p1);
         __builtin_amdgcn_sched_barrier(0);
         batch_compute<K, U>(B, sg, xw, b0, b1, l);
         __builtin_amdgcn_sched_barrier(0);
