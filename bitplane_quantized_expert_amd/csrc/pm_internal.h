@@ -135,7 +135,7 @@ hipError_t launch_dequant(int rows, int cols, int group, int k, const uint32_t* 
 hipError_t launch_gemv_fp16(int rows, int cols, const uint16_t* w, const float* x, float* y,
                             hipStream_t st);
 
-// LUT path: n_wgq * S workgroups of 512 threads, about 132 KiB of LDS each.
+// LUT path: n_wgq * S workgroups of 1024 threads, about 132 KiB of LDS each.
 // Gate/up (down == false): the activation slice comes from L.x; down: h of
 // use src, formed from the gate/up partials L.gu.
 // t0 / t1: if given, the launch's own start and stop events.

@@ -36,7 +36,7 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kRowsPerBlock = kBlock / kWave;
 #ifndef PM_LUT_THREADS
-#define PM_LUT_THREADS 512
+#define PM_LUT_THREADS 1024
 #endif
 constexpr int kLutThreads = PM_LUT_THREADS;
 constexpr int kLutWaves = kLutThreads / kWave;
@@ -336,7 +336,7 @@ __device__ inline void lut_load(LutRowIn<K>& in, __amdgpu_buffer_rsrc_t rp, __am
 template <int K>
 constexpr int lut_unroll() {
 #if PM_LUT_THREADS == 1024
-    return K == 1 ? 4 : K == 2 ? 2 : K == 3 ? 2 : 1;
+    return K == 1 ? 4 : K == 2 ? 2 : 1;
 #else
     return K == 1 ? 8 : K == 2 ? 4 : K == 3 ? 3 : K == 4 ? 2 : 1;
 #endif
