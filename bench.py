@@ -184,6 +184,200 @@ def cpu_baseline(wl, plans, budget_s):
             "expert_gemvs_per_s": round(len(mats) * reps / el * (rows / 1024) / 1.0, 3)}
 
 
+def route_steps(pm, synth, wl, layer, steps, token=0, kfix=None, n_exp=None):
+    """Product routing and allocation of `steps` fresh tokens of one layer:
+    ids int32 [steps][top_k], w fp32, k uint8-ish [steps][top_k][3]."""
+    err = synth.error_profiles(wl.seed, wl.cfg, layer, wl.n_experts)
+    logits = np.stack([synth.router_logits(wl.seed, wl.cfg, layer, token, wl.n_experts, step=s)
+                       for s in steps])
+    if n_exp is not None and n_exp < wl.n_experts:
+        logits[:, n_exp:] = -np.inf
+    ids, w = pm.pm_route_topk(logits, wl.top_k)
+    if kfix is None:
+        kk = pm.pm_allocate_bits(ids, w, err, wl.budget)
+    else:
+        kk = np.full(ids.shape, kfix, np.int32)
+    return ids, w, np.repeat(kk[:, :, None], 3, axis=2)
+
+
+def timed(torch, fn, n):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        fn(i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def bench_sixty_layers(args, torch, pm, synth, PoolFiller):
+    """One decode token through 60 independent layers (600 routed experts,
+    all resident): a step is the 60 layer calls, fresh x and logits per layer."""
+    wl = synth.WORKLOADS[2]
+    st = pm.pm_store_create(pm.eshape(wl.hidden, wl.inter, wl.group), wl.n_layers, wl.n_experts)
+    filler = PoolFiller(wl)
+    plan, nbytes = [], 0
+    for layer in range(wl.n_layers):
+        ids, w, k3 = route_steps(pm, synth, wl, layer, [0])
+        for i in ids[0]:
+            filler.fill(st, layer, int(i))
+        x = torch.from_numpy(synth.activation(wl.seed, wl.cfg, layer, 0, wl.hidden)[None]).cuda()
+        plan.append((layer, ids, w, k3, x))
+        nbytes += step_bytes(wl, k3[0])
+    torch.cuda.synchronize()
+    log(f"60-layer pool ready ({wl.n_layers * wl.top_k} experts)")
+    y = torch.empty((1, wl.hidden), dtype=torch.float32, device="cuda")
+
+    def token(_):
+        for layer, ids, w, k3, x in plan:
+            pm.pm_moe_token_forward(st, layer, ids, w, k3, x, y)
+
+    timed(torch, token, max(2, args.warmup // 10))
+    n = max(5, args.steps // 10)
+    el = timed(torch, token, n)
+    st.close()
+    ms = el / n * 1e3
+    return {"workload": wl.name, "ms_per_token": round(ms, 4),
+            "GBs": round(nbytes * n / el / 1e9, 1),
+            "expert_gemvs_per_s": round(3 * wl.top_k * wl.n_layers * n / el, 1),
+            "bytes_per_token": nbytes}
+
+
+def bench_precisions(args, torch, pm, synth, PoolFiller):
+    """The one-layer step at k = 4, k = 8 and the mixed draw, each beside the
+    materialize-then-GEMV comparator (the 30 matrices dequantized to fp16 in
+    HBM, then an fp16-weight GEMV each)."""
+    wl = synth.WORKLOADS[3]
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    st = pm.pm_store_create(e, 1, wl.n_experts)
+    filler = PoolFiller(wl)
+    for i in range(wl.n_experts):
+        filler.fill(st, 0, i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    pw = pm.pm_expert_plane_words(e)
+    offs = [pm.pm_expert_matrix_offsets(e, m) for m in range(3)]
+    w16 = torch.empty(wl.hidden * wl.inter, dtype=torch.int16, device="cuda")
+    yv = torch.empty(wl.hidden, dtype=torch.float32, device="cuda")
+    out = {}
+    total = args.warmup + args.steps
+    for label, kfix in (("k4", 4), ("k8", 8), ("mixed", None)):
+        ids, w, k3 = route_steps(pm, synth, wl, 0, range(total), kfix=kfix)
+        x = torch.from_numpy(np.stack([synth.activation(wl.seed, wl.cfg, 0, 0, wl.hidden, step=s)
+                                       for s in range(total)])).cuda()
+        hx = torch.randn(wl.inter, device="cuda")
+        y = torch.empty_like(x)
+
+        def direct(i, s0=args.warmup):
+            s = s0 + i
+            pm.pm_moe_token_forward(st, 0, ids[s:s + 1], w[s:s + 1], k3[s:s + 1], x[s:s + 1],
+                                    y[s:s + 1], stream)
+
+        def materialize(i, s0=args.warmup):
+            s = s0 + i
+            for j in range(wl.top_k):
+                pp, lp = pm.pm_store_slot(st, 0, int(ids[s][j]))
+                for m in range(3):
+                    po, lo, sh = offs[m]
+                    pm.pm_materialize_fp16(sh, int(k3[s][j][m]), pp + 4 * po, pw, lp + 4 * lo,
+                                           w16, stream)
+                    pm.pm_gemv_fp16(sh, w16, x[s] if m < 2 else hx, yv, stream)
+
+        n = args.steps
+        timed(torch, lambda i: direct(i, 0), min(args.warmup, 20))
+        el_d = timed(torch, direct, n)
+        nm = max(5, n // 10)
+        timed(torch, lambda i: materialize(i, 0), 2)
+        el_m = timed(torch, materialize, nm)
+        b = np.mean([step_bytes(wl, k3[args.warmup + i]) for i in range(n)])
+        bm = np.mean([step_bytes(wl, k3[args.warmup + i]) for i in range(nm)]) + \
+            3 * wl.top_k * wl.hidden * wl.inter * 4
+        out[label] = {"direct_us": round(el_d / n * 1e6, 2), "direct_GBs": round(b * n / el_d / 1e9, 1),
+                      "materialize_us": round(el_m / nm * 1e6, 2),
+                      "materialize_GBs": round(bm * nm / el_m / 1e9, 1),
+                      "speedup": round((el_m / nm) / (el_d / n), 2), "bytes_per_step": int(b)}
+        log(f"{label}: {out[label]}")
+    st.close()
+    return {"workload": wl.name, "results": out}
+
+
+def bench_batch_topup(args, torch, pm, synth, PoolFiller):
+    """B = 8 tokens per step, experts grouped; before each step 20% of the
+    distinct experts (kmax >= 2) are cut back to a shorter resident prefix and
+    the step tops them up from pinned host memory on the store's side stream."""
+    wl = synth.WORKLOADS[4]
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    st = pm.pm_store_create(e, 1, wl.n_experts)
+    filler = PoolFiller(wl)
+    pw = pm.pm_expert_plane_words(e)
+    # pinned host sources: every expert's planes; levels stay resident (the
+    # store never reads a host levels source once its levels are on the device)
+    hplanes = torch.empty((wl.n_experts, 8 * pw), dtype=torch.int32, pin_memory=True)
+    hlevels = torch.empty(pm.pm_expert_levels_floats(e), dtype=torch.float32, pin_memory=True)
+    for i in range(wl.n_experts):
+        filler.fill(st, 0, i)
+        hplanes[i].copy_(pm_slot_tensor(torch, pm, st, i, pw))
+        pm.pm_store_attach_host(st, 0, i, hplanes[i].data_ptr(), hlevels.data_ptr())
+    torch.cuda.synchronize()
+    total = args.warmup + args.steps
+    routes = [route_steps(pm, synth, wl, 0, range(total), token=t) for t in range(wl.n_tokens)]
+    ids = np.stack([r[0] for r in routes], 1)          # [steps][B][top_k]
+    w = np.stack([r[1] for r in routes], 1)
+    k3 = np.stack([r[2] for r in routes], 1)
+    x = torch.from_numpy(np.stack([np.stack([synth.activation(wl.seed, wl.cfg, 0, t, wl.hidden, step=s)
+                                             for t in range(wl.n_tokens)]) for s in range(total)])).cuda()
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    plans = []
+    for s in range(total):
+        distinct = sorted(set(int(i) for i in ids[s].reshape(-1)))
+        kmax = {i: int(k3[s][ids[s] == i].max()) for i in distinct}
+        cand = [i for i in distinct if kmax[i] >= 2]
+        pick = synth.words(wl.seed, synth.KIND_TRUNC, wl.cfg, 0, s, 0, len(cand)).argsort()
+        short = [cand[int(j)] for j in pick[:int(np.ceil(0.2 * len(distinct)))]]
+        r = synth.words(wl.seed, synth.KIND_TRUNC, wl.cfg, 0, s, 1, len(short))
+        plans.append([(i, 1 + int(r[j] % (kmax[i] - 1))) for j, i in enumerate(short)])
+    gemv_bytes = np.mean([sum(step_bytes(wl, k3[s][t]) for t in range(wl.n_tokens))
+                          for s in range(total)])
+    copies = []
+
+    def step(i, topup=True, s0=args.warmup):
+        s = s0 + i
+        if topup:
+            for e_, keep in plans[s]:
+                pm.pm_store_truncate(st, 0, e_, keep)
+        pm.pm_moe_token_forward(st, 0, ids[s], w[s], k3[s], x[s], y[s], stream,
+                                flags=pm.PM_AUTO_TOPUP)
+
+    n = args.steps
+    timed(torch, lambda i: step(i, True, 0), min(args.warmup, 10))
+    _, _, p0, b0 = pm.pm_store_copy_stats(st)
+    el = timed(torch, step, n)
+    _, _, p1, b1 = pm.pm_store_copy_stats(st)
+    el_res = timed(torch, lambda i: step(i, False), n)
+    st.close()
+    return {"workload": wl.name, "ms_per_step": round(el / n * 1e3, 4),
+            "ms_per_step_all_resident": round(el_res / n * 1e3, 4),
+            "gemv_GBs_all_resident": round(gemv_bytes * n / el_res / 1e9, 1),
+            "h2d_MB_per_step": round((b1 - b0) / n / 1e6, 2),
+            "h2d_GBs": round((b1 - b0) / el / 1e9, 2),
+            "planes_per_step": round((p1 - p0) / n, 2),
+            "expert_gemvs_per_s": round(3 * wl.top_k * wl.n_tokens * n / el, 1)}
+
+
+def pm_slot_tensor(torch, pm, st, expert, pw):
+    """The device planes of a store slot as a torch view (for copying out)."""
+    pp, _ = pm.pm_store_slot(st, 0, expert)
+    import ctypes
+    buf = torch.empty(8 * pw, dtype=torch.int32, device="cuda")
+    hip = ctypes.CDLL("libamdhip64.so")
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = hip.hipMemcpyAsync(ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(pp),
+                            ctypes.c_size_t(8 * pw * 4), 3, ctypes.c_void_p(stream))
+    if rc != 0:
+        raise RuntimeError(f"hipMemcpyAsync failed: {rc}")
+    return buf
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,6 +386,9 @@ def main():
     ap.add_argument("--experts", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="1", choices=["1", "2", "3", "4", "all"],
+                    help="1: the one-layer step (the reported line); 2: 60 layers; "
+                         "3: k = 4 / 8 / mixed against materialize; 4: B = 8 with top-ups")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV"),
                     help="print a summary of rocprofv3 outputs of this benchmark and exit")
     args = ap.parse_args()
@@ -211,6 +408,12 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+    if args.workload != "1":
+        extra = {"2": bench_sixty_layers, "3": bench_precisions, "4": bench_batch_topup}
+        for key in (["2", "3", "4"] if args.workload == "all" else [args.workload]):
+            res = extra[key](args, torch, pm, synth, PoolFiller)
+            print(json.dumps({"workload_result": res}), flush=True)
+        return 0
     wl = synth.WORKLOADS[1]
     n_exp = args.experts
     e = pm.eshape(wl.hidden, wl.inter, wl.group)

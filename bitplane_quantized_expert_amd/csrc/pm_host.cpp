@@ -275,6 +275,7 @@ extern "C" pm_status pm_expert_gemv(pm_matrix_shape s, int k, const uint32_t* d_
     if (st) return st;
     if (s.rows == 0) return PM_OK;
     if (s.cols > 0 && !d_x) return fail(PM_ERR_ARG, "null x");
+    if (reinterpret_cast<uintptr_t>(d_x) % 16) return fail(PM_ERR_ARG, "x not 16-byte aligned");
     if (k <= kLutMaxK && s.cols > 0 && s.cols % kSliceCols == 0 && s.group == kLutGroup &&
         s.rows % 2 == 0 && lut_offsets_fit(s, k, pstride))
         return gemv_lut(s, k, d_planes, pstride, d_levels, d_x, d_y, (hipStream_t)stream);
@@ -916,6 +917,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     if (n_tokens < 0 || top_k < 1) return fail(PM_ERR_ARG, "n_tokens=%d top_k=%d", n_tokens, top_k);
     if (n_tokens == 0) return PM_OK;
     if (!h_ids || !h_w || !h_k || !d_x || !d_y) return fail(PM_ERR_ARG, "null pointer");
+    if (reinterpret_cast<uintptr_t>(d_x) % 16) return fail(PM_ERR_ARG, "x not 16-byte aligned");
     if (top_k > kMaxLaunchUses)
         return fail(PM_ERR_ARG, "top_k=%d above %d", top_k, kMaxLaunchUses);
     hipStream_t compute = (hipStream_t)compute_v;

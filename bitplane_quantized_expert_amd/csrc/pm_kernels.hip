@@ -595,14 +595,24 @@ __device__ inline float row_dot_lane(const uint32_t* __restrict__ planes, size_t
         for (int p = 0; p < kBits; ++p)
             pw[p] = p < k ? planes[size_t(p) * pstride + size_t(o) * W + w] : 0u;
         const float* tab = lv_k + ((size_t(o) * nb_row + w / wpg) << k);
-        const float* xw = x + 32 * w;
-#pragma unroll 4
+        // the word's 32 activations as eight 16-byte loads (a lane's columns
+        // are contiguous; one value per load would touch 64 lines per load)
+        float xv[32];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const f32x4 a = *(g_f32x4*)(x + 32 * w + 4 * q);
+            xv[4 * q] = a.x;
+            xv[4 * q + 1] = a.y;
+            xv[4 * q + 2] = a.z;
+            xv[4 * q + 3] = a.w;
+        }
+#pragma unroll
         for (int j = 0; j < 32; ++j) {
             uint32_t v = 0;
 #pragma unroll
             for (int p = 0; p < kBits; ++p)
                 if (p < k) v = (v << 1) | ((pw[p] >> j) & 1u);
-            acc = fmaf(tab[v], xw[j], acc);
+            acc = fmaf(tab[v], xv[j], acc);
         }
     }
     return acc;

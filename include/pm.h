@@ -120,7 +120,8 @@ pm_status pm_encode_matrix_device(pm_matrix_shape s, const uint8_t* d_codes,
  * directly at a k-bit prefix, no decoded matrix is formed [Abs "directly
  * executes cached 1-8-bit prefixes without materializing full-precision
  * experts"; T c37].  Reads planes 0..k-1 and depth k only.
- *   d_x fp32 [cols], d_y fp32 [rows] (overwritten; cols == 0 gives zeros).
+ *   d_x fp32 [cols], 16-byte aligned; d_y fp32 [rows] (overwritten; cols == 0
+ *   gives zeros).
  *   Errors: PM_ERR_PREFIX (k), PM_ERR_SHAPE, PM_ERR_ARG (null pointer or
  *   plane_stride_words < rows*cols/32). */
 pm_status pm_expert_gemv(pm_matrix_shape s, int k, const uint32_t* d_planes,
@@ -208,7 +209,8 @@ pm_status pm_store_set_profile_events(pm_store* s, void* const* events, int n);
  * at its own prefix [Abs; T c25].
  *   h_ids int32 [n_tokens][top_k], h_w fp32 [n_tokens][top_k],
  *   h_k uint8 [n_tokens][top_k][3] -- host memory, read before return.
- *   d_x fp32 [n_tokens][hidden], d_y fp32 [n_tokens][hidden] (overwritten).
+ *   d_x fp32 [n_tokens][hidden] (16-byte aligned), d_y fp32 [n_tokens][hidden]
+ *   (overwritten).
  * flags: PM_AUTO_TOPUP tops up every short slot from its host source on the
  * store's side stream and makes `compute` wait for it (kernels of resident
  * experts are issued first); without it a short slot is PM_ERR_NOT_RESIDENT.
