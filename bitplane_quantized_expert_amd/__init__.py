@@ -80,6 +80,12 @@ SIGNATURES = {
     "pm_store_resident": (_I, [_P, _I, _I, _P]),
     "pm_store_copy_stats": (_I, [_P, _P, _P, _P, _P]),
     "pm_store_set_profile_events": (_I, [_P, _P, _I]),
+    "pm_cache_create": (_I, [_I, _c.c_int64, _I, _P]),
+    "pm_cache_destroy": (_I, [_P]),
+    "pm_cache_access": (_I, [_P, _I, _I, _P, _P]),
+    "pm_cache_replay": (_I, [_P, _P, _P, _Z]),
+    "pm_cache_resident": (_I, [_P, _I, _P]),
+    "pm_cache_stats": (_I, [_P, _P, _P, _P, _P, _P]),
     "pm_moe_token_forward": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _U32]),
     "pm_debug_unpack_prefix": (_I, [_MS, _I, _P, _Z, _P, _P]),
     "pm_debug_dequant": (_I, [_MS, _I, _P, _Z, _P, _P, _P]),
@@ -333,6 +339,69 @@ def pm_store_set_profile_events(store, events):
     arr = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
     store._profile_events = (events, arr)
     return _check(lib().pm_store_set_profile_events(store.handle, arr, len(events)))
+
+
+# ---------------------------------------------------------------- expert caches
+PM_CACHE_PREFIX = 0
+PM_CACHE_OBJECTS = 1
+
+
+class Cache:
+    """Owner of a pm_cache handle (pm_cache_destroy on close)."""
+
+    def __init__(self, n_experts, capacity_planes, policy=PM_CACHE_PREFIX):
+        h = ctypes.c_void_p()
+        _check(lib().pm_cache_create(n_experts, capacity_planes, policy, ctypes.byref(h)))
+        self.handle = h.value
+
+    def close(self):
+        if self.handle:
+            lib().pm_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def pm_cache_create(n_experts, capacity_planes, policy=PM_CACHE_PREFIX):
+    return Cache(n_experts, capacity_planes, policy)
+
+
+def pm_cache_destroy(cache):
+    cache.close()
+
+
+def pm_cache_access(cache, expert, k):
+    """(first, count): the 1-based planes this access reads."""
+    a, b = ctypes.c_int(), ctypes.c_int()
+    _check(lib().pm_cache_access(cache.handle, expert, k, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def pm_cache_replay(cache, experts, ks):
+    """experts, ks: int32 numpy arrays of one length (host)."""
+    experts = np.ascontiguousarray(experts, dtype=np.int32)
+    ks = np.ascontiguousarray(ks, dtype=np.int32)
+    if experts.shape != ks.shape or experts.ndim != 1:
+        raise ValueError("experts and ks must be 1-D arrays of one length")
+    return _check(lib().pm_cache_replay(cache.handle, _hptr(experts), _hptr(ks), experts.size))
+
+
+def pm_cache_resident(cache, expert):
+    r = ctypes.c_int()
+    _check(lib().pm_cache_resident(cache.handle, expert, ctypes.byref(r)))
+    return r.value
+
+
+def pm_cache_stats(cache):
+    """dict of accesses, hits, partial, planes_read, planes_held."""
+    v = [ctypes.c_uint64() for _ in range(4)] + [ctypes.c_int64()]
+    _check(lib().pm_cache_stats(cache.handle, *[ctypes.byref(x) for x in v]))
+    return dict(zip(("accesses", "hits", "partial", "planes_read", "planes_held"),
+                    (x.value for x in v)))
 
 
 def pm_moe_token_forward(store, layer, ids, w, k, d_x, d_y, stream=None, flags=0):

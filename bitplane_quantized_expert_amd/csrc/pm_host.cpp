@@ -13,6 +13,7 @@
 #include <string>
 #include <vector>
 
+#include "pm_error.h"
 #include "pm_internal.h"
 
 using namespace pm;
@@ -20,7 +21,7 @@ using namespace pm;
 // ---------------------------------------------------------------- errors
 static thread_local std::string g_last_error;
 
-static pm_status fail(pm_status st, const char* fmt, ...) {
+pm_status pm::failf(pm_status st, const char* fmt, ...) {
     char buf[512];
     va_list ap;
     va_start(ap, fmt);
@@ -31,7 +32,7 @@ static pm_status fail(pm_status st, const char* fmt, ...) {
 }
 
 static pm_status hip_fail(hipError_t e, const char* what) {
-    return fail(PM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return failf(PM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
 #define HIP_TRY(expr)                                           \
@@ -51,7 +52,7 @@ static bool shape_ok(pm_matrix_shape s) {
 
 static pm_status check_shape(pm_matrix_shape s) {
     if (!shape_ok(s))
-        return fail(PM_ERR_SHAPE,
+        return failf(PM_ERR_SHAPE,
                     "shape rows=%d cols=%d group=%d: need rows>=0, group a positive "
                     "multiple of 32, cols a multiple of group",
                     s.rows, s.cols, s.group);
@@ -59,7 +60,7 @@ static pm_status check_shape(pm_matrix_shape s) {
 }
 
 static pm_status check_k(int k) {
-    if (k < 1 || k > kBits) return fail(PM_ERR_PREFIX, "prefix k=%d outside 1..8", k);
+    if (k < 1 || k > kBits) return failf(PM_ERR_PREFIX, "prefix k=%d outside 1..8", k);
     return PM_OK;
 }
 
@@ -96,8 +97,8 @@ extern "C" size_t pm_expert_levels_floats(pm_expert_shape e) {
 }
 extern "C" pm_status pm_expert_matrix_offsets(pm_expert_shape e, int m, size_t* pw, size_t* lf,
                                               pm_matrix_shape* shape_out) {
-    if (!expert_ok(e)) return fail(PM_ERR_SHAPE, "invalid expert shape");
-    if (m < 0 || m > 2) return fail(PM_ERR_ARG, "matrix index %d outside 0..2", m);
+    if (!expert_ok(e)) return failf(PM_ERR_SHAPE, "invalid expert shape");
+    if (m < 0 || m > 2) return failf(PM_ERR_ARG, "matrix index %d outside 0..2", m);
     size_t p = 0, l = 0;
     for (int i = 0; i < m; ++i) {
         p += pm_plane_words(matrix_of(e, i));
@@ -138,7 +139,7 @@ static pm_status encode_host(pm_matrix_shape s, const uint8_t* codes, const floa
         const float* lf = leaves + b * kLeaves;
         for (int v = 1; v < kLeaves; ++v)
             if (!(lf[v - 1] <= lf[v]))
-                return fail(PM_ERR_ARG, "leaves of block %zu are not ascending at %d", b, v);
+                return failf(PM_ERR_ARG, "leaves of block %zu are not ascending at %d", b, v);
     }
     for (int p = 0; p < kBits; ++p) {
         for (int o = 0; o < s.rows; ++o) {
@@ -198,9 +199,9 @@ extern "C" pm_status pm_encode_matrix(pm_matrix_shape s, const uint8_t* codes,
     if (st) return st;
     if (s.rows == 0 || s.cols == 0) return PM_OK;
     if (!codes || !leaves || !planes_out || !levels_out)
-        return fail(PM_ERR_ARG, "pm_encode_matrix: null pointer");
+        return failf(PM_ERR_ARG, "pm_encode_matrix: null pointer");
     if (pstride < pm_plane_words(s))
-        return fail(PM_ERR_ARG, "plane stride %zu below plane size %zu", pstride,
+        return failf(PM_ERR_ARG, "plane stride %zu below plane size %zu", pstride,
                     pm_plane_words(s));
     return encode_host(s, codes, leaves, counts, planes_out, pstride, levels_out);
 }
@@ -209,9 +210,9 @@ extern "C" pm_status pm_encode_expert(pm_expert_shape e, const uint8_t* const co
                                       const float* const leaves[3],
                                       const uint32_t* const counts[3], uint32_t* planes_out,
                                       float* levels_out) {
-    if (!expert_ok(e)) return fail(PM_ERR_SHAPE, "invalid expert shape");
+    if (!expert_ok(e)) return failf(PM_ERR_SHAPE, "invalid expert shape");
     if (!codes || !leaves || !planes_out || !levels_out)
-        return fail(PM_ERR_ARG, "pm_encode_expert: null pointer");
+        return failf(PM_ERR_ARG, "pm_encode_expert: null pointer");
     const size_t pw = pm_expert_plane_words(e);
     for (int m = 0; m < 3; ++m) {
         size_t po, lo;
@@ -232,9 +233,9 @@ extern "C" pm_status pm_encode_matrix_device(pm_matrix_shape s, const uint8_t* d
     if (st) return st;
     if (s.rows == 0 || s.cols == 0) return PM_OK;
     if (!d_codes || !d_leaves || !d_planes || !d_levels)
-        return fail(PM_ERR_ARG, "pm_encode_matrix_device: null pointer");
+        return failf(PM_ERR_ARG, "pm_encode_matrix_device: null pointer");
     if (pstride < pm_plane_words(s))
-        return fail(PM_ERR_ARG, "plane stride %zu below plane size %zu", pstride,
+        return failf(PM_ERR_ARG, "plane stride %zu below plane size %zu", pstride,
                     pm_plane_words(s));
     HIP_TRY(launch_encode_device(s.rows, s.cols, s.group, d_codes, d_leaves, d_counts,
                                  d_planes, pstride, d_levels, (hipStream_t)stream));
@@ -249,9 +250,9 @@ static pm_status check_matrix_call(pm_matrix_shape s, int k, const void* planes,
     st = check_k(k);
     if (st) return st;
     if (s.rows == 0) return PM_OK;
-    if (!planes || !a || !b) return fail(PM_ERR_ARG, "null device pointer");
+    if (!planes || !a || !b) return failf(PM_ERR_ARG, "null device pointer");
     if (pstride < pm_plane_words(s))
-        return fail(PM_ERR_ARG, "plane stride %zu below plane size %zu", pstride,
+        return failf(PM_ERR_ARG, "plane stride %zu below plane size %zu", pstride,
                     pm_plane_words(s));
     return PM_OK;
 }
@@ -274,8 +275,8 @@ extern "C" pm_status pm_expert_gemv(pm_matrix_shape s, int k, const uint32_t* d_
     pm_status st = check_matrix_call(s, k, d_planes, pstride, d_levels, d_y);
     if (st) return st;
     if (s.rows == 0) return PM_OK;
-    if (s.cols > 0 && !d_x) return fail(PM_ERR_ARG, "null x");
-    if (reinterpret_cast<uintptr_t>(d_x) % 16) return fail(PM_ERR_ARG, "x not 16-byte aligned");
+    if (s.cols > 0 && !d_x) return failf(PM_ERR_ARG, "null x");
+    if (reinterpret_cast<uintptr_t>(d_x) % 16) return failf(PM_ERR_ARG, "x not 16-byte aligned");
     if (k <= kLutMaxK && s.cols > 0 && s.cols % kSliceCols == 0 && s.group == kLutGroup &&
         s.rows % 2 == 0 && lut_offsets_fit(s, k, pstride))
         return gemv_lut(s, k, d_planes, pstride, d_levels, d_x, d_y, (hipStream_t)stream);
@@ -321,7 +322,7 @@ extern "C" pm_status pm_gemv_fp16(pm_matrix_shape s, const uint16_t* d_w, const 
     pm_status st = check_shape(s);
     if (st) return st;
     if (s.rows == 0) return PM_OK;
-    if (!d_y || (s.cols > 0 && (!d_w || !d_x))) return fail(PM_ERR_ARG, "null device pointer");
+    if (!d_y || (s.cols > 0 && (!d_w || !d_x))) return failf(PM_ERR_ARG, "null device pointer");
     HIP_TRY(launch_gemv_fp16(s.rows, s.cols, d_w, d_x, d_y, (hipStream_t)stream));
     return PM_OK;
 }
@@ -330,16 +331,16 @@ extern "C" pm_status pm_gemv_fp16(pm_matrix_shape s, const uint16_t* d_w, const 
 extern "C" pm_status pm_route_topk(int n_tokens, int n_experts, int top_k, const float* logits,
                                    int32_t* ids_out, float* w_out) {
     if (n_tokens < 0 || n_experts < 1 || top_k < 1 || top_k > n_experts)
-        return fail(PM_ERR_ARG, "route: n_tokens=%d n_experts=%d top_k=%d", n_tokens,
+        return failf(PM_ERR_ARG, "route: n_tokens=%d n_experts=%d top_k=%d", n_tokens,
                     n_experts, top_k);
     if (n_tokens == 0) return PM_OK;
-    if (!logits || !ids_out || !w_out) return fail(PM_ERR_ARG, "route: null pointer");
+    if (!logits || !ids_out || !w_out) return failf(PM_ERR_ARG, "route: null pointer");
     std::vector<int32_t> order(n_experts);
     std::vector<double> ex(top_k);
     for (int t = 0; t < n_tokens; ++t) {
         const float* l = logits + size_t(t) * n_experts;
         for (int e = 0; e < n_experts; ++e) {
-            if (std::isnan(l[e])) return fail(PM_ERR_ARG, "route: NaN logit");
+            if (std::isnan(l[e])) return failf(PM_ERR_ARG, "route: NaN logit");
             order[e] = e;
         }
         std::partial_sort(order.begin(), order.begin() + top_k, order.end(),
@@ -394,20 +395,20 @@ extern "C" pm_status pm_allocate_bits(int n_tokens, int top_k, const int32_t* id
                                       const float* w, int n_experts, const double* err,
                                       int budget, uint8_t* k_out) {
     if (n_tokens < 0 || top_k < 1 || n_experts < 1)
-        return fail(PM_ERR_ARG, "allocate: n_tokens=%d top_k=%d n_experts=%d", n_tokens, top_k,
+        return failf(PM_ERR_ARG, "allocate: n_tokens=%d top_k=%d n_experts=%d", n_tokens, top_k,
                     n_experts);
     if (budget < top_k || budget > kBits * top_k)
-        return fail(PM_ERR_ARG, "allocate: budget %d outside [%d, %d]", budget, top_k,
+        return failf(PM_ERR_ARG, "allocate: budget %d outside [%d, %d]", budget, top_k,
                     kBits * top_k);
     if (n_tokens == 0) return PM_OK;
-    if (!ids || !w || !err || !k_out) return fail(PM_ERR_ARG, "allocate: null pointer");
+    if (!ids || !w || !err || !k_out) return failf(PM_ERR_ARG, "allocate: null pointer");
     std::vector<double> prof(size_t(top_k) * kBits);
     std::vector<int> b(top_k);
     for (int t = 0; t < n_tokens; ++t) {
         for (int j = 0; j < top_k; ++j) {
             const int32_t e = ids[size_t(t) * top_k + j];
             if (e < 0 || e >= n_experts)
-                return fail(PM_ERR_ARG, "allocate: expert id %d outside 0..%d", e,
+                return failf(PM_ERR_ARG, "allocate: expert id %d outside 0..%d", e,
                             n_experts - 1);
             convex_profile(err + size_t(e) * kBits, &prof[size_t(j) * kBits]);
             b[j] = 1;
@@ -479,9 +480,9 @@ struct pm_store {
 };
 
 static pm_status slot_of(const pm_store* s, int layer, int expert, size_t* idx) {
-    if (!s) return fail(PM_ERR_ARG, "null store");
+    if (!s) return failf(PM_ERR_ARG, "null store");
     if (layer < 0 || layer >= s->n_layers || expert < 0 || expert >= s->n_experts)
-        return fail(PM_ERR_ARG, "slot (%d, %d) outside %d layers x %d experts", layer, expert,
+        return failf(PM_ERR_ARG, "slot (%d, %d) outside %d layers x %d experts", layer, expert,
                     s->n_layers, s->n_experts);
     *idx = size_t(layer) * s->n_experts + expert;
     return PM_OK;
@@ -493,17 +494,17 @@ static pm_status ensure_slot(pm_store* s, Slot& sl) {
     const size_t pad = (pbytes + 255) & ~size_t(255);
     const size_t total = pad + s->level_bytes;
     if (s->capacity && s->used + total > s->capacity)
-        return fail(PM_ERR_OOM, "store capacity %zu bytes exceeded (%zu used, %zu more)",
+        return failf(PM_ERR_OOM, "store capacity %zu bytes exceeded (%zu used, %zu more)",
                     s->capacity, s->used, total);
     char* mem = nullptr;
     if (s->host_fake) {
         mem = static_cast<char*>(std::calloc(total, 1));
-        if (!mem) return fail(PM_ERR_OOM, "host allocation of %zu bytes failed", total);
+        if (!mem) return failf(PM_ERR_OOM, "host allocation of %zu bytes failed", total);
     } else {
         hipError_t e = hipMalloc(&mem, total);
         if (e != hipSuccess) {
             (void)hipGetLastError();
-            return fail(PM_ERR_OOM, "hipMalloc of %zu bytes failed: %s", total,
+            return failf(PM_ERR_OOM, "hipMalloc of %zu bytes failed: %s", total,
                         hipGetErrorString(e));
         }
         HIP_TRY(hipEventCreateWithFlags(&sl.ready, hipEventDisableTiming));
@@ -518,11 +519,11 @@ static pm_status ensure_slot(pm_store* s, Slot& sl) {
 
 extern "C" pm_status pm_store_create(pm_expert_shape e, int n_layers, int n_experts,
                                      size_t capacity, uint32_t flags, pm_store** out) {
-    if (!out) return fail(PM_ERR_ARG, "null output pointer");
+    if (!out) return failf(PM_ERR_ARG, "null output pointer");
     *out = nullptr;
-    if (!expert_ok(e)) return fail(PM_ERR_SHAPE, "invalid expert shape");
-    if (n_layers < 1 || n_experts < 1) return fail(PM_ERR_ARG, "empty store");
-    if (flags & ~uint32_t(PM_STORE_HOST_FAKE)) return fail(PM_ERR_ARG, "unknown store flags");
+    if (!expert_ok(e)) return failf(PM_ERR_SHAPE, "invalid expert shape");
+    if (n_layers < 1 || n_experts < 1) return failf(PM_ERR_ARG, "empty store");
+    if (flags & ~uint32_t(PM_STORE_HOST_FAKE)) return failf(PM_ERR_ARG, "unknown store flags");
     pm_store* s = new pm_store();
     s->shape = e;
     s->geom = make_geom(e);
@@ -587,8 +588,8 @@ extern "C" pm_status pm_store_set_resident(pm_store* s, int layer, int expert, i
     size_t i;
     pm_status st = slot_of(s, layer, expert, &i);
     if (st) return st;
-    if (r < 0 || r > kBits) return fail(PM_ERR_PREFIX, "resident prefix %d outside 0..8", r);
-    if (!s->slots[i].planes) return fail(PM_ERR_STATE, "slot (%d, %d) has no memory", layer, expert);
+    if (r < 0 || r > kBits) return failf(PM_ERR_PREFIX, "resident prefix %d outside 0..8", r);
+    if (!s->slots[i].planes) return failf(PM_ERR_STATE, "slot (%d, %d) has no memory", layer, expert);
     s->slots[i].resident = r;
     s->slots[i].levels_ready = true;
     s->slots[i].pending = false;
@@ -600,7 +601,7 @@ extern "C" pm_status pm_store_attach_host(pm_store* s, int layer, int expert,
     size_t i;
     pm_status st = slot_of(s, layer, expert, &i);
     if (st) return st;
-    if (!h_planes || !h_levels) return fail(PM_ERR_ARG, "null host source");
+    if (!h_planes || !h_levels) return failf(PM_ERR_ARG, "null host source");
     s->slots[i].h_planes = h_planes;
     s->slots[i].h_levels = h_levels;
     return PM_OK;
@@ -612,7 +613,7 @@ static pm_status topup_slot(pm_store* s, Slot& sl, int k, hipStream_t side) {
         s->last_count = 0;
         return PM_OK;
     }
-    if (!sl.h_planes || !sl.h_levels) return fail(PM_ERR_STATE, "slot has no host source");
+    if (!sl.h_planes || !sl.h_levels) return failf(PM_ERR_STATE, "slot has no host source");
     pm_status st = ensure_slot(s, sl);
     if (st) return st;
     const int first = sl.resident;
@@ -655,7 +656,7 @@ extern "C" pm_status pm_store_truncate(pm_store* s, int layer, int expert, int k
     size_t i;
     pm_status st = slot_of(s, layer, expert, &i);
     if (st) return st;
-    if (keep < 0 || keep > kBits) return fail(PM_ERR_PREFIX, "keep %d outside 0..8", keep);
+    if (keep < 0 || keep > kBits) return failf(PM_ERR_PREFIX, "keep %d outside 0..8", keep);
     s->slots[i].resident = std::min(s->slots[i].resident, keep);
     return PM_OK;
 }
@@ -664,14 +665,14 @@ extern "C" pm_status pm_store_resident(const pm_store* s, int layer, int expert,
     size_t i;
     pm_status st = slot_of(s, layer, expert, &i);
     if (st) return st;
-    if (!r_out) return fail(PM_ERR_ARG, "null output pointer");
+    if (!r_out) return failf(PM_ERR_ARG, "null output pointer");
     *r_out = s->slots[i].resident;
     return PM_OK;
 }
 
 extern "C" pm_status pm_store_copy_stats(const pm_store* s, int* last_first, int* last_count,
                                          uint64_t* total_planes, uint64_t* total_bytes) {
-    if (!s) return fail(PM_ERR_ARG, "null store");
+    if (!s) return failf(PM_ERR_ARG, "null store");
     if (last_first) *last_first = s->last_first;
     if (last_count) *last_count = s->last_count;
     if (total_planes) *total_planes = s->total_planes;
@@ -680,12 +681,12 @@ extern "C" pm_status pm_store_copy_stats(const pm_store* s, int* last_first, int
 }
 
 extern "C" pm_status pm_store_set_profile_events(pm_store* s, void* const* events, int n) {
-    if (!s) return fail(PM_ERR_ARG, "null store");
+    if (!s) return failf(PM_ERR_ARG, "null store");
     if (n == 0) {
         s->profiling = false;
         return PM_OK;
     }
-    if (n < 4 || !events) return fail(PM_ERR_ARG, "need 4 events");
+    if (n < 4 || !events) return failf(PM_ERR_ARG, "need 4 events");
     for (int i = 0; i < 4; ++i) s->prof[i] = (hipEvent_t)events[i];
     s->profiling = true;
     return PM_OK;
@@ -828,7 +829,7 @@ static pm_status gemv_partials(hipStream_t st, size_t n, float** out) {
         hipError_t e = hipMalloc(&b.p, n * sizeof(float));
         if (e != hipSuccess) {
             (void)hipGetLastError();
-            return fail(PM_ERR_OOM, "GEMV workspace allocation failed: %s", hipGetErrorString(e));
+            return failf(PM_ERR_OOM, "GEMV workspace allocation failed: %s", hipGetErrorString(e));
         }
         b.n = n;
     }
@@ -884,7 +885,7 @@ static pm_status ensure_workspace(pm_store* s, size_t floats, size_t list_bytes)
         hipError_t e = hipMalloc(&w.d_buf, n * sizeof(float));
         if (e != hipSuccess) {
             (void)hipGetLastError();
-            return fail(PM_ERR_OOM, "workspace allocation failed: %s", hipGetErrorString(e));
+            return failf(PM_ERR_OOM, "workspace allocation failed: %s", hipGetErrorString(e));
         }
         w.d_floats = n;
     }
@@ -910,16 +911,16 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
                                           const int32_t* h_ids, const float* h_w,
                                           const uint8_t* h_k, const float* d_x, float* d_y,
                                           void* compute_v, uint32_t flags) {
-    if (!s) return fail(PM_ERR_ARG, "null store");
-    if (s->host_fake) return fail(PM_ERR_STATE, "a host-backed store cannot compute");
-    if (flags & ~uint32_t(PM_AUTO_TOPUP)) return fail(PM_ERR_ARG, "unknown forward flags");
-    if (layer < 0 || layer >= s->n_layers) return fail(PM_ERR_ARG, "layer %d outside store", layer);
-    if (n_tokens < 0 || top_k < 1) return fail(PM_ERR_ARG, "n_tokens=%d top_k=%d", n_tokens, top_k);
+    if (!s) return failf(PM_ERR_ARG, "null store");
+    if (s->host_fake) return failf(PM_ERR_STATE, "a host-backed store cannot compute");
+    if (flags & ~uint32_t(PM_AUTO_TOPUP)) return failf(PM_ERR_ARG, "unknown forward flags");
+    if (layer < 0 || layer >= s->n_layers) return failf(PM_ERR_ARG, "layer %d outside store", layer);
+    if (n_tokens < 0 || top_k < 1) return failf(PM_ERR_ARG, "n_tokens=%d top_k=%d", n_tokens, top_k);
     if (n_tokens == 0) return PM_OK;
-    if (!h_ids || !h_w || !h_k || !d_x || !d_y) return fail(PM_ERR_ARG, "null pointer");
-    if (reinterpret_cast<uintptr_t>(d_x) % 16) return fail(PM_ERR_ARG, "x not 16-byte aligned");
+    if (!h_ids || !h_w || !h_k || !d_x || !d_y) return failf(PM_ERR_ARG, "null pointer");
+    if (reinterpret_cast<uintptr_t>(d_x) % 16) return failf(PM_ERR_ARG, "x not 16-byte aligned");
     if (top_k > kMaxLaunchUses)
-        return fail(PM_ERR_ARG, "top_k=%d above %d", top_k, kMaxLaunchUses);
+        return failf(PM_ERR_ARG, "top_k=%d above %d", top_k, kMaxLaunchUses);
     hipStream_t compute = (hipStream_t)compute_v;
     const Geom& g = s->geom;
 
@@ -934,13 +935,13 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
             const int u = t * top_k + j;
             const int e = h_ids[u];
             if (e < 0 || e >= s->n_experts)
-                return fail(PM_ERR_ARG, "ids[%d][%d]=%d outside 0..%d", t, j, e, s->n_experts - 1);
-            if (!std::isfinite(h_w[u])) return fail(PM_ERR_ARG, "w[%d][%d] not finite", t, j);
+                return failf(PM_ERR_ARG, "ids[%d][%d]=%d outside 0..%d", t, j, e, s->n_experts - 1);
+            if (!std::isfinite(h_w[u])) return failf(PM_ERR_ARG, "w[%d][%d] not finite", t, j);
             Use& us = uses[u];
             for (int m = 0; m < 3; ++m) {
                 const int k = h_k[size_t(u) * 3 + m];
                 if (k < 1 || k > kBits)
-                    return fail(PM_ERR_PREFIX, "k[%d][%d][%d]=%d outside 1..8", t, j, m, k);
+                    return failf(PM_ERR_PREFIX, "k[%d][%d][%d]=%d outside 1..8", t, j, m, k);
                 us.k[m] = k;
             }
             us.w = h_w[u];
@@ -964,7 +965,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     std::vector<std::array<int, 3>> kmax(n_items, {0, 0, 0});
     for (int d = 0; d < n_items; ++d) {
         if (int(item_uses[d].size()) > max_uses_per_item())
-            return fail(PM_ERR_ARG, "expert %d is used %zu times; at most %d per call",
+            return failf(PM_ERR_ARG, "expert %d is used %zu times; at most %d per call",
                         item_expert[d], item_uses[d].size(), max_uses_per_item());
         for (int u : item_uses[d])
             for (int m = 0; m < 3; ++m) kmax[d][m] = std::max(kmax[d][m], uses[u].k[m]);
@@ -977,11 +978,11 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         const bool ok = sl.planes && sl.levels_ready && sl.resident >= kneed[d];
         if (!ok) {
             if (!(flags & PM_AUTO_TOPUP))
-                return fail(PM_ERR_NOT_RESIDENT,
+                return failf(PM_ERR_NOT_RESIDENT,
                             "expert (%d, %d) holds %d planes, %d requested", layer,
                             item_expert[d], sl.planes ? sl.resident : 0, kneed[d]);
             if (!sl.h_planes || !sl.h_levels)
-                return fail(PM_ERR_STATE, "expert (%d, %d) is short and has no host source",
+                return failf(PM_ERR_STATE, "expert (%d, %d) is short and has no host source",
                             layer, item_expert[d]);
             late[d] = 1;
         }

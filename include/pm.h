@@ -200,6 +200,41 @@ pm_status pm_store_copy_stats(const pm_store* s, int* last_first, int* last_coun
  * n = 0 switches it off. */
 pm_status pm_store_set_profile_events(pm_store* s, void* const* events, int n);
 
+/* ---------------------------------------------------------------- expert caches
+ * Replacement decisions for an expert cache whose capacity is counted in
+ * planes (one plane = one bit of every index of one expert), for trace
+ * replay and for a caller that drives pm_store_topup / pm_store_truncate.
+ * Host only; no device memory.
+ *   PM_CACHE_PREFIX  one state per expert: its resident planes are a prefix
+ *     1..r.  An access at k reads only planes r+1..k; a deeper resident prefix
+ *     serves a shallower request [T c13, c35].  The access then refreshes
+ *     planes k, k-1, .., 1 in that order, so an expert's deeper planes are
+ *     always older and leave first [T c35]; eviction takes the least recently
+ *     used plane of any other expert, always the deepest plane of its expert.
+ *   PM_CACHE_OBJECTS the independent-object baseline [T c11]: every (expert,
+ *     k) is its own LRU entry of k planes and serves only requests at k.
+ * Under both, a request deeper than the whole capacity is read and not kept.
+ * Experts are 0..n_experts-1 (a caller numbers layer * n_experts + expert);
+ * k in 1..8 (else PM_ERR_PREFIX from pm_cache_access). */
+typedef struct pm_cache pm_cache;
+enum { PM_CACHE_PREFIX = 0, PM_CACHE_OBJECTS = 1 };
+pm_status pm_cache_create(int n_experts, int64_t capacity_planes, int policy,
+                          pm_cache** out);
+pm_status pm_cache_destroy(pm_cache* c);
+/* One access: *first (1-based) and *count are the planes it reads (count 0
+ * on a hit, with *first = k + 1). */
+pm_status pm_cache_access(pm_cache* c, int expert, int k, int* first, int* count);
+/* n accesses from host arrays; the whole trace is checked (PM_ERR_ARG) before
+ * the first access. */
+pm_status pm_cache_replay(pm_cache* c, const int32_t* experts, const int32_t* ks, size_t n);
+/* Planes of the expert now held: the prefix r (PREFIX) or the largest k of
+ * its resident entries (OBJECTS); 0 if none. */
+pm_status pm_cache_resident(const pm_cache* c, int expert, int* out);
+/* Running totals (any output may be null): accesses, full hits, partial hits
+ * (PREFIX: some planes resident, more read), planes read, planes held. */
+pm_status pm_cache_stats(const pm_cache* c, uint64_t* accesses, uint64_t* hits,
+                         uint64_t* partial, uint64_t* planes_read, int64_t* planes_held);
+
 /* ---------------------------------------------------------------- MoE layer
  * One MoE layer for n_tokens tokens:
  *   y[t] = sum_j w[t][j] * W_down(k2) (silu(W_gate(k0) x[t]) * W_up(k1) x[t])

@@ -296,6 +296,102 @@ def missing_planes(resident, k):
 
 
 # ---------------------------------------------------------------------------
+# Expert caches of limited capacity, counted in planes  ([T] c11, c13, c35)
+# ---------------------------------------------------------------------------
+class PrefixPlaneCache:
+    """One shared state per expert: its resident planes form a prefix 1..r.
+
+    An access of expert e at k bits reads the missing planes r+1..k ([T] c35:
+    3 resident and 5 requested reads planes 4 and 5; 5 resident and 3
+    requested reads nothing) and refreshes planes k, k-1, .., 1 in that
+    order, so that an expert's deeper planes are always older than its
+    shallower ones and age out first ([T] c35).  Eviction takes the least
+    recently used plane over all experts, which is then always the deepest
+    resident plane of its expert, so every resident set stays a prefix.
+    Planes needed by the access itself are never evicted for it; a request
+    deeper than the whole capacity is read and not kept.
+
+    Plain reference implementation: a list of (expert, plane) from least to
+    most recently used."""
+
+    def __init__(self, capacity_planes):
+        self.cap = int(capacity_planes)
+        self.order = []                 # [(expert, plane)], oldest first
+        self.res = {}                   # expert -> resident prefix r
+        self.accesses = self.hits = self.partial = self.planes_read = 0
+
+    def resident(self, e):
+        return self.res.get(e, 0)
+
+    def _touch(self, e, p):
+        if (e, p) in self.order:
+            self.order.remove((e, p))
+        self.order.append((e, p))
+
+    def access(self, e, k):
+        """Planes (1-based) read for this access."""
+        self.accesses += 1
+        r = self.resident(e)
+        if r >= k:
+            self.hits += 1
+            for p in range(k, 0, -1):
+                self._touch(e, p)
+            return []
+        if r > 0:
+            self.partial += 1
+        read = list(range(r + 1, k + 1))
+        self.planes_read += len(read)
+        if k > self.cap:                # cannot be held: read, keep nothing new
+            for p in range(r, 0, -1):
+                self._touch(e, p)
+            return read
+        # room for the missing planes; the victim is the oldest plane of any
+        # expert but e (e's planes 1..r are about to be refreshed)
+        while len(self.order) + (k - r) > self.cap:
+            victim = next(x for x in self.order if x[0] != e)
+            self.order.remove(victim)
+            ve, vp = victim
+            assert vp == self.res[ve], "an evicted plane must be its expert's deepest"
+            self.res[ve] = vp - 1
+            if self.res[ve] == 0:
+                del self.res[ve]
+        for p in range(k, 0, -1):
+            self._touch(e, p)
+        self.res[e] = k
+        return read
+
+
+class ObjectCache:
+    """The independent-object baseline ([T] c11): every (expert, bit-width)
+    is its own cache entry of k planes, so a resident 2-bit copy cannot serve
+    a 4-bit request.  LRU over entries; a request larger than the capacity is
+    read and not kept."""
+
+    def __init__(self, capacity_planes):
+        self.cap = int(capacity_planes)
+        self.order = []                 # [(expert, k)], oldest first
+        self.used = 0
+        self.accesses = self.hits = self.partial = self.planes_read = 0
+
+    def access(self, e, k):
+        self.accesses += 1
+        if (e, k) in self.order:
+            self.hits += 1
+            self.order.remove((e, k))
+            self.order.append((e, k))
+            return []
+        self.planes_read += k
+        if k > self.cap:
+            return list(range(1, k + 1))
+        while self.used + k > self.cap:
+            _, vk = self.order.pop(0)
+            self.used -= vk
+        self.order.append((e, k))
+        self.used += k
+        return list(range(1, k + 1))
+
+
+# ---------------------------------------------------------------------------
 # One MoE layer for a batch of tokens
 # ---------------------------------------------------------------------------
 def moe_forward(experts, ids, w, k, x):

@@ -21,6 +21,9 @@ forms, read plainly):
     the leaves strictly ascending without a sort.
   * codes: independent uniform bytes (every bitplane is fair coin flips).
   * x and router logits: N(0, 1) by Box-Muller, fp64 then rounded to fp32.
+  * routing traces for cache replay: per-layer Zipf popularity over a seeded
+    rank permutation, logits -s ln(rank) plus Gumbel noise (see
+    zipf_router_logits); independent across tokens.
   * error profiles: err_e(b) = s_e * 4**(-b), s_e = exp(sigma * z_e),
     z_e ~ N(0, 1), sigma = 1 -- a convex stand-in for the offline profiles
     measured on trained weights.
@@ -80,6 +83,8 @@ KIND_PROFILE = 5
 KIND_KDRAW = 6
 KIND_POISON = 7
 KIND_TRUNC = 8
+KIND_ZIPF = 9
+KIND_RANK = 10
 
 
 def stream_key(seed: int, kind: int, cfg: int, layer: int, unit: int, matrix: int):
@@ -196,6 +201,28 @@ def router_logits(seed, cfg, layer, token, n_experts, step=0):
     """fp32 [n_experts] N(0,1) router logits of one token (per step)."""
     key = stream_key(seed, KIND_LOGITS, cfg, layer, token, 0)
     return normals(key, n_experts, extra=step).astype(np.float32)
+
+
+def expert_popularity_rank(seed, cfg, layer, n_experts):
+    """int64 [n_experts]: the 1-based popularity rank of every expert of one
+    layer, a seeded permutation (stable argsort of Philox words)."""
+    key = stream_key(seed, KIND_RANK, cfg, layer, 0, 0)
+    w = philox_words(key, 0, (n_experts + 3) // 4)[:n_experts]
+    rank = np.empty(n_experts, np.int64)
+    rank[np.argsort(w, kind="stable")] = np.arange(1, n_experts + 1)
+    return rank
+
+
+def zipf_router_logits(seed, cfg, layer, token, n_experts, s=1.0, step=0):
+    """fp32 [n_experts] router logits of one token for a synthetic routing
+    trace with Zipf popularity: -s * ln(rank_e) + G_e, G_e standard Gumbel
+    (-ln(-ln u)).  Their top-k is a draw of k distinct experts without
+    replacement with probabilities proportional to rank^-s (the Gumbel-top-k
+    trick: Kool, van Hoof and Welling, ICML 2019)."""
+    rank = expert_popularity_rank(seed, cfg, layer, n_experts)
+    key = stream_key(seed, KIND_ZIPF, cfg, layer, token, 0)
+    u = uniform_01(philox_words(key, 0, (n_experts + 3) // 4, extra=step)[:n_experts])
+    return (-s * np.log(rank.astype(np.float64)) - np.log(-np.log(u))).astype(np.float32)
 
 
 PROFILE_SIGMA = 1.0

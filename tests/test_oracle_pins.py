@@ -385,3 +385,70 @@ def test_moe_onehot_weight_is_single_expert(tiny_expert):
     r = oracle.expert_ffn(enc, 2, 3, 4, x)
     assert np.array_equal(y[0], r["y"])
     assert np.array_equal(s[0], r["Sy"])
+
+
+def test_plane_cache_pages_examples():
+    """[T] c13, c35: the pages' residency examples through the cache."""
+    c = oracle.PrefixPlaneCache(64)
+    assert c.access(7, 3) == [1, 2, 3]
+    assert c.access(7, 5) == [4, 5]          # 3 resident, 5 requested
+    assert c.access(7, 3) == []              # 5 resident, 3 requested
+    assert c.resident(7) == 5
+    d = oracle.PrefixPlaneCache(64)
+    d.access(9, 2)
+    assert d.access(9, 4) == [3, 4]          # only the missing part
+    o = oracle.ObjectCache(64)
+    o.access(17, 2)
+    assert o.access(17, 4) == [1, 2, 3, 4]   # [T] c11: 2-bit copy does not help
+    assert o.access(17, 2) == []
+
+
+def test_plane_cache_golden_trace():
+    """A hand-worked eviction trace: deepest planes age out first."""
+    g = load("plane_cache_trace.json")
+    c = oracle.PrefixPlaneCache(g["capacity"])
+    o = oracle.ObjectCache(g["capacity"])
+    for (e, k), want, res in zip(g["trace"], g["prefix"]["reads"], g["prefix"]["resident_after"]):
+        assert c.access(e, k) == want
+        assert {str(x): r for x, r in c.res.items()} == res
+    assert (c.planes_read, c.hits, c.partial) == (g["prefix"]["planes_read"], g["prefix"]["hits"],
+                                                  g["prefix"]["partial"])
+    for (e, k), want in zip(g["trace"], g["objects"]["reads"]):
+        assert o.access(e, k) == want
+    assert (o.planes_read, o.hits) == (g["objects"]["planes_read"], g["objects"]["hits"])
+
+
+def test_plane_cache_unbounded_closed_forms():
+    """With room for everything nothing is evicted: the prefix cache reads
+    each expert's deepest requested prefix once, the object cache each
+    distinct (expert, k) once."""
+    rng = np.random.default_rng(3)
+    trace = [(int(e), int(k)) for e, k in zip(rng.integers(0, 20, 400), rng.integers(1, 9, 400))]
+    c = oracle.PrefixPlaneCache(10 ** 6)
+    o = oracle.ObjectCache(10 ** 6)
+    for e, k in trace:
+        c.access(e, k)
+        o.access(e, k)
+    deepest = {}
+    for e, k in trace:
+        deepest[e] = max(deepest.get(e, 0), k)
+    assert c.planes_read == sum(deepest.values())
+    assert o.planes_read == sum(k for _, k in set(trace))
+
+
+def test_plane_cache_invariants_small_capacity():
+    """Resident sets stay prefixes within the capacity, and never does the
+    prefix cache read more planes than the object cache on the same trace
+    with the same capacity when every request is at one fixed width."""
+    rng = np.random.default_rng(4)
+    trace = [(int(e), 4) for e in rng.zipf(1.3, 600) % 40]
+    c = oracle.PrefixPlaneCache(48)
+    o = oracle.ObjectCache(48)
+    for e, k in trace:
+        c.access(e, k)
+        o.access(e, k)
+        assert sum(c.res.values()) == len(c.order) <= 48
+        assert all(1 <= r <= 8 for r in c.res.values())
+    # at one fixed width both policies hold the same whole experts in the
+    # same order: identical reads
+    assert c.planes_read == o.planes_read

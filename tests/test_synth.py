@@ -46,3 +46,20 @@ def test_uniform_k_range():
     k = synth.uniform_k(3, 0, 0, 0, 4000)
     assert k.min() == 1 and k.max() == 8
     assert np.all(np.bincount(k)[1:] > 350)
+
+
+def test_zipf_trace_draws_by_rank():
+    rank = synth.expert_popularity_rank(3, 1, 7, 512)
+    assert sorted(rank.tolist()) == list(range(1, 513))
+    n = 4000
+    top = np.array([int(np.argmax(synth.zipf_router_logits(3, 1, 7, t % 4096, 512, 1.0,
+                                                            step=t // 4096)))
+                    for t in range(n)])
+    # Gumbel-max: the top expert is rank r with probability r^-1 / H_512
+    h = np.sum(1.0 / np.arange(1, 513))
+    for r in (1, 2, 5):
+        p = 1.0 / r / h
+        got = np.mean(rank[top] == r)
+        assert abs(got - p) <= 4.0 * np.sqrt(p * (1 - p) / n)
+    again = synth.zipf_router_logits(3, 1, 7, 11, 512, 1.0)
+    assert np.array_equal(again, synth.zipf_router_logits(3, 1, 7, 11, 512, 1.0))
