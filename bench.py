@@ -364,6 +364,61 @@ def bench_batch_topup(args, torch, pm, synth, PoolFiller):
             "expert_gemvs_per_s": round(3 * wl.top_k * wl.n_tokens * n / el, 1)}
 
 
+CACHE_TOKENS = 500
+CACHE_ZIPF_S = 1.0
+CACHE_GIB = (12, 24, 48)
+
+
+def bench_cache_replay(args, pm, synth):
+    """Replay of a synthetic decode trace through the expert caches (host
+    only).  Shapes of the 60-layer workload: 512 experts per layer, top-10,
+    500 tokens from a cold cache; expert popularity per layer is Zipf (s = 1)
+    over a seeded rank order, tokens are independent; the allocator picks the
+    prefixes at a mean of 2.5 bits.  A plane of one expert (gate, up and down)
+    is hidden * inter * 3 / 8 bytes = 1.5 MiB.  Policies: fixed 4 and fixed 3
+    bits (one width per expert, so both caches behave alike), the
+    independent-object cache at the allocator's widths, and the plane-aging
+    prefix cache at the same widths, at 12, 24 and 48 GiB."""
+    wl = synth.WORKLOADS[2]
+    L, E, K, T = wl.n_layers, wl.n_experts, wl.top_k, CACHE_TOKENS
+    t0 = time.perf_counter()
+    ex = np.zeros((T, L, K), np.int32)
+    kk = np.zeros((T, L, K), np.int32)
+    for layer in range(L):
+        lg = np.stack([synth.zipf_router_logits(wl.seed, wl.cfg, layer, t, E, CACHE_ZIPF_S)
+                       for t in range(T)])
+        ids, w = pm.pm_route_topk(lg, K)
+        ex[:, layer] = ids + layer * E
+        kk[:, layer] = pm.pm_allocate_bits(ids, w, synth.error_profiles(wl.seed, wl.cfg, layer, E),
+                                           wl.budget)
+    log(f"cache trace: {T * L * K} accesses, mean k {kk.mean():.3f} "
+        f"({time.perf_counter() - t0:.1f} s)")
+    e, k = ex.reshape(-1), kk.reshape(-1)
+    plane_bytes = wl.hidden * wl.inter * 3 // 8
+    runs = (("fixed4", pm.PM_CACHE_PREFIX, np.full_like(k, 4)),
+            ("fixed3", pm.PM_CACHE_PREFIX, np.full_like(k, 3)),
+            ("dynamic2.5_objects", pm.PM_CACHE_OBJECTS, k),
+            ("dynamic2.5_prefix", pm.PM_CACHE_PREFIX, k))
+    out = []
+    for gib in CACHE_GIB:
+        cap = (gib << 30) // plane_bytes
+        for name, policy, ks in runs:
+            c = pm.pm_cache_create(L * E, cap, policy)
+            t1 = time.perf_counter()
+            pm.pm_cache_replay(c, e, ks)
+            dt = time.perf_counter() - t1
+            st = pm.pm_cache_stats(c)
+            out.append({"cache_GiB": gib, "policy": name,
+                        "hit_pct": round(100 * st["hits"] / st["accesses"], 2),
+                        "partial_pct": round(100 * st["partial"] / st["accesses"], 2),
+                        "planes_read_per_token": round(st["planes_read"] / T, 1),
+                        "GiB_read_per_token": round(st["planes_read"] * plane_bytes / T / 2**30, 3),
+                        "replay_M_accesses_per_s": round(st["accesses"] / dt / 1e6, 1)})
+            c.close()
+    return {"workload": f"cache-replay-{L}layers-e{E}-top{K}-{T}tokens-zipf{CACHE_ZIPF_S}-k2.5",
+            "plane_MiB": plane_bytes / 2**20, "results": out}
+
+
 def pm_slot_tensor(torch, pm, st, expert, pw):
     """The device planes of a store slot as a torch view (for copying out)."""
     pp, _ = pm.pm_store_slot(st, 0, expert)
@@ -386,9 +441,10 @@ def main():
     ap.add_argument("--experts", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="1", choices=["1", "2", "3", "4", "all"],
+    ap.add_argument("--workload", default="1", choices=["1", "2", "3", "4", "cache", "all"],
                     help="1: the one-layer step (the reported line); 2: 60 layers; "
-                         "3: k = 4 / 8 / mixed against materialize; 4: B = 8 with top-ups")
+                         "3: k = 4 / 8 / mixed against materialize; 4: B = 8 with top-ups; "
+                         "cache: Zipf trace replay through the expert caches (host only)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV"),
                     help="print a summary of rocprofv3 outputs of this benchmark and exit")
     args = ap.parse_args()
@@ -399,6 +455,12 @@ def main():
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the path is built and timed on a single MI355X)", file=sys.stderr)
         return 2
+    if args.workload in ("cache", "all"):
+        import bitplane_quantized_expert_amd as pm
+        import synth
+        print(json.dumps({"workload_result": bench_cache_replay(args, pm, synth)}), flush=True)
+        if args.workload == "cache":
+            return 0
 
     import torch
     import bitplane_quantized_expert_amd as pm
