@@ -424,3 +424,48 @@ def within_tolerance(got, want, scale, rel=1e-4, abs_=1e-6):
     """The acceptance bound |got - want| <= rel * scale + abs_ per output."""
     got = np.asarray(got, dtype=np.float64)
     return np.abs(got - want) <= rel * np.asarray(scale) + abs_
+
+
+class DownwardCache:
+    """The middle option the pages name and never measure ([T] c51): copies
+    of different widths are still separate encodings, but a resident copy of
+    width r serves every request at k <= r with no I/O (downward reuse), and a
+    request at k > r reads a fresh k-bit copy in full, which replaces the old
+    one (promotion).  One copy per expert at most; LRU over the copies, which
+    are evicted whole.  The superseded copy is dropped before room is made.
+    A request larger than the capacity is read and not kept; the resident
+    copy then stays and is refreshed."""
+
+    def __init__(self, capacity_planes):
+        self.cap = int(capacity_planes)
+        self.order = []                 # [expert], oldest first
+        self.width = {}                 # expert -> width of its copy
+        self.used = 0
+        self.accesses = self.hits = self.partial = self.planes_read = 0
+
+    def resident(self, e):
+        return self.width.get(e, 0)
+
+    def access(self, e, k):
+        self.accesses += 1
+        r = self.resident(e)
+        if r >= k:
+            self.hits += 1
+            self.order.remove(e)
+            self.order.append(e)
+            return []
+        self.planes_read += k
+        if k > self.cap:
+            if r:
+                self.order.remove(e)
+                self.order.append(e)
+            return list(range(1, k + 1))
+        if r:
+            self.order.remove(e)
+            self.used -= self.width.pop(e)
+        while self.used + k > self.cap:
+            self.used -= self.width.pop(self.order.pop(0))
+        self.order.append(e)
+        self.width[e] = k
+        self.used += k
+        return list(range(1, k + 1))

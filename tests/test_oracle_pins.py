@@ -452,3 +452,62 @@ def test_plane_cache_invariants_small_capacity():
     # at one fixed width both policies hold the same whole experts in the
     # same order: identical reads
     assert c.planes_read == o.planes_read
+
+
+def test_downward_cache_pages_example():
+    """[T] c51: a resident higher-precision copy serves lower requests and is
+    promoted (read anew in full) when a request needs more."""
+    d = oracle.DownwardCache(64)
+    assert d.access(17, 4) == [1, 2, 3, 4]
+    assert d.access(17, 2) == []              # served from the 4-bit copy
+    assert d.access(17, 6) == [1, 2, 3, 4, 5, 6]
+    assert d.access(17, 3) == [] and d.resident(17) == 6 and d.used == 6
+
+
+def test_downward_cache_golden_traces():
+    g = load("plane_cache_downward_trace.json")
+    d = oracle.DownwardCache(g["capacity"])
+    for (e, k), want, wd in zip(g["trace"], g["downward"]["reads"], g["downward"]["width_after"]):
+        assert d.access(e, k) == want
+        assert {str(x): r for x, r in d.width.items()} == wd
+    assert (d.planes_read, d.hits) == (g["downward"]["planes_read"], g["downward"]["hits"])
+    c = oracle.PrefixPlaneCache(g["capacity"])
+    for (e, k), want, res in zip(g["trace"], g["prefix"]["reads"], g["prefix"]["resident_after"]):
+        assert c.access(e, k) == want
+        assert {str(x): r for x, r in c.res.items()} == res
+    assert (c.planes_read, c.hits, c.partial) == (g["prefix"]["planes_read"], g["prefix"]["hits"],
+                                                  g["prefix"]["partial"])
+    o = oracle.ObjectCache(g["capacity"])
+    for (e, k), want in zip(g["trace"], g["objects"]["reads"]):
+        assert o.access(e, k) == want
+    assert (o.planes_read, o.hits) == (g["objects"]["planes_read"], g["objects"]["hits"])
+    first = load("plane_cache_trace.json")
+    d = oracle.DownwardCache(first["capacity"])
+    for (e, k), want in zip(first["trace"], g["first_trace_downward"]["reads"]):
+        assert d.access(e, k) == want
+    assert d.planes_read == g["first_trace_downward"]["planes_read"]
+
+
+def test_downward_cache_closed_forms_and_invariants():
+    """Unbounded: an expert costs k at every access that exceeds all its
+    earlier requests.  At one fixed width it is the object cache."""
+    rng = np.random.default_rng(5)
+    trace = [(int(e), int(k)) for e, k in zip(rng.integers(0, 20, 400), rng.integers(1, 9, 400))]
+    d = oracle.DownwardCache(10 ** 6)
+    for e, k in trace:
+        d.access(e, k)
+    best, want = {}, 0
+    for e, k in trace:
+        if k > best.get(e, 0):
+            want += k
+            best[e] = k
+    assert d.planes_read == want
+    fixed = [(int(e), 3) for e in rng.zipf(1.3, 600) % 40]
+    d, o = oracle.DownwardCache(30), oracle.ObjectCache(30)
+    for e, k in fixed:
+        assert d.access(e, k) == o.access(e, k)
+    small = oracle.DownwardCache(10)
+    for e, k in trace:
+        small.access(e, k)
+        assert small.used == sum(small.width.values()) <= 10
+        assert sorted(small.order) == sorted(small.width)
