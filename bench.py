@@ -376,9 +376,9 @@ def bench_cache_replay(args, pm, synth):
     over a seeded rank order, tokens are independent; the allocator picks the
     prefixes at a mean of 2.5 bits.  A plane of one expert (gate, up and down)
     is hidden * inter * 3 / 8 bytes = 1.5 MiB.  Policies: fixed 4 and fixed 3
-    bits (one width per expert, so both caches behave alike), the
-    independent-object cache at the allocator's widths, and the plane-aging
-    prefix cache at the same widths, at 12, 24 and 48 GiB."""
+    bits (one width per expert, so all caches behave alike), then at the
+    allocator's widths the independent-object cache, the downward-reuse cache
+    and the plane-aging prefix cache, at 12, 24 and 48 GiB."""
     wl = synth.WORKLOADS[2]
     L, E, K, T = wl.n_layers, wl.n_experts, wl.top_k, CACHE_TOKENS
     t0 = time.perf_counter()
@@ -398,6 +398,7 @@ def bench_cache_replay(args, pm, synth):
     runs = (("fixed4", pm.PM_CACHE_PREFIX, np.full_like(k, 4)),
             ("fixed3", pm.PM_CACHE_PREFIX, np.full_like(k, 3)),
             ("dynamic2.5_objects", pm.PM_CACHE_OBJECTS, k),
+            ("dynamic2.5_downward", pm.PM_CACHE_DOWNWARD, k),
             ("dynamic2.5_prefix", pm.PM_CACHE_PREFIX, k))
     out = []
     for gib in CACHE_GIB:

@@ -344,6 +344,7 @@ def pm_store_set_profile_events(store, events):
 # ---------------------------------------------------------------- expert caches
 PM_CACHE_PREFIX = 0
 PM_CACHE_OBJECTS = 1
+PM_CACHE_DOWNWARD = 2
 
 
 class Cache:

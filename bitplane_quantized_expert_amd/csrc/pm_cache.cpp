@@ -1,8 +1,8 @@
 // Expert caches of limited capacity counted in planes: the plane-aging prefix
-// cache and the independent-object baseline ("PagedMoE: Cross-Precision Expert
-// Caching for SSD-Resident MoE Inference", podcast transcript, cues 11, 13
-// and 35).  Host code; the replacement decisions only (the copies are the
-// plane store's).
+// cache, the independent-object baseline and the downward-reuse middle option
+// ("PagedMoE: Cross-Precision Expert Caching for SSD-Resident MoE Inference",
+// podcast transcript, cues 11, 13, 35 and 51).  Host code; the replacement
+// decisions only (the copies are the plane store's).
 #include <cstdint>
 #include <vector>
 
@@ -47,9 +47,11 @@ struct pm_cache {
     int n_experts;
     int64_t cap;                       // planes
     int policy;
-    Lru lru;                           // node = expert * 8 + (plane or width) - 1
-    std::vector<int8_t> res;           // prefix policy: resident prefix per expert
-    int64_t used = 0;                  // object policy: planes held
+    // node = expert * 8 + (plane or width) - 1; the downward policy uses
+    // node expert * 8 for the expert's one copy
+    Lru lru;
+    std::vector<int8_t> res;           // prefix: resident prefix; downward: copy width
+    int64_t used = 0;                  // object and downward policies: planes held
     uint64_t accesses = 0, hits = 0, partial = 0, planes_read = 0;
 
     pm_cache(int n, int64_t c, int p)
@@ -115,6 +117,49 @@ void access_object(pm_cache* c, int e, int k, int* first, int* count) {
     c->used += k;
 }
 
+// Downward policy: one copy per expert; a copy of width r >= k serves the
+// request, a wider request reads a fresh copy in full and replaces it.
+void access_downward(pm_cache* c, int e, int k, int* first, int* count) {
+    const int32_t node = e * kPlanes;
+    const int r = c->res[e];
+    if (r >= k) {
+        ++c->hits;
+        c->lru.push_back(node);
+        *first = k + 1;
+        *count = 0;
+        return;
+    }
+    *first = 1;
+    *count = k;
+    c->planes_read += uint64_t(k);
+    if (k > c->cap) {                  // read, not kept; the old copy stays
+        if (r) c->lru.push_back(node);
+        return;
+    }
+    if (r) {                           // superseded before room is made
+        c->lru.unlink(node);
+        c->used -= r;
+    }
+    while (c->used + k > c->cap) {
+        const int32_t v = c->lru.head;
+        c->lru.unlink(v);
+        c->used -= c->res[v / kPlanes];
+        c->res[v / kPlanes] = 0;
+    }
+    c->lru.push_back(node);
+    c->used += k;
+    c->res[e] = int8_t(k);
+}
+
+void access(pm_cache* c, int e, int k, int* first, int* count) {
+    if (c->policy == PM_CACHE_PREFIX)
+        access_prefix(c, e, k, first, count);
+    else if (c->policy == PM_CACHE_OBJECTS)
+        access_object(c, e, k, first, count);
+    else
+        access_downward(c, e, k, first, count);
+}
+
 }  // namespace
 
 extern "C" pm_status pm_cache_create(int n_experts, int64_t capacity_planes, int policy,
@@ -123,7 +168,7 @@ extern "C" pm_status pm_cache_create(int n_experts, int64_t capacity_planes, int
     *out = nullptr;
     if (n_experts <= 0 || n_experts > (1 << 27) || capacity_planes < 0)
         return pm::failf(PM_ERR_ARG, "bad expert count or capacity");
-    if (policy != PM_CACHE_PREFIX && policy != PM_CACHE_OBJECTS)
+    if (policy != PM_CACHE_PREFIX && policy != PM_CACHE_OBJECTS && policy != PM_CACHE_DOWNWARD)
         return pm::failf(PM_ERR_ARG, "unknown cache policy %d", policy);
     *out = new pm_cache(n_experts, capacity_planes, policy);
     return PM_OK;
@@ -139,10 +184,7 @@ extern "C" pm_status pm_cache_access(pm_cache* c, int expert, int k, int* first,
     if (expert < 0 || expert >= c->n_experts) return pm::failf(PM_ERR_ARG, "expert out of range");
     if (k < 1 || k > kPlanes) return pm::failf(PM_ERR_PREFIX, "k = %d outside 1..8", k);
     ++c->accesses;
-    if (c->policy == PM_CACHE_PREFIX)
-        access_prefix(c, expert, k, first, count);
-    else
-        access_object(c, expert, k, first, count);
+    access(c, expert, k, first, count);
     return PM_OK;
 }
 
@@ -156,10 +198,7 @@ extern "C" pm_status pm_cache_replay(pm_cache* c, const int32_t* experts, const 
     int first, count;
     for (size_t i = 0; i < n; ++i) {
         ++c->accesses;
-        if (c->policy == PM_CACHE_PREFIX)
-            access_prefix(c, experts[i], ks[i], &first, &count);
-        else
-            access_object(c, experts[i], ks[i], &first, &count);
+        access(c, experts[i], ks[i], &first, &count);
     }
     return PM_OK;
 }
@@ -167,7 +206,7 @@ extern "C" pm_status pm_cache_replay(pm_cache* c, const int32_t* experts, const 
 extern "C" pm_status pm_cache_resident(const pm_cache* c, int expert, int* out) {
     if (!c || !out) return pm::failf(PM_ERR_ARG, "null argument");
     if (expert < 0 || expert >= c->n_experts) return pm::failf(PM_ERR_ARG, "expert out of range");
-    if (c->policy == PM_CACHE_PREFIX) {
+    if (c->policy != PM_CACHE_OBJECTS) {
         *out = c->res[expert];
     } else {
         int best = 0;

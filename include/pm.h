@@ -213,11 +213,15 @@ pm_status pm_store_set_profile_events(pm_store* s, void* const* events, int n);
  *     used plane of any other expert, always the deepest plane of its expert.
  *   PM_CACHE_OBJECTS the independent-object baseline [T c11]: every (expert,
  *     k) is its own LRU entry of k planes and serves only requests at k.
+ *   PM_CACHE_DOWNWARD the middle option [T c51]: copies are still separate
+ *     encodings, one per expert; a resident copy of width r serves requests
+ *     at k <= r, a wider request reads a k-plane copy in full and replaces it
+ *     (the old copy is dropped before room is made).  LRU over whole copies.
  * Under both, a request deeper than the whole capacity is read and not kept.
  * Experts are 0..n_experts-1 (a caller numbers layer * n_experts + expert);
  * k in 1..8 (else PM_ERR_PREFIX from pm_cache_access). */
 typedef struct pm_cache pm_cache;
-enum { PM_CACHE_PREFIX = 0, PM_CACHE_OBJECTS = 1 };
+enum { PM_CACHE_PREFIX = 0, PM_CACHE_OBJECTS = 1, PM_CACHE_DOWNWARD = 2 };
 pm_status pm_cache_create(int n_experts, int64_t capacity_planes, int policy,
                           pm_cache** out);
 pm_status pm_cache_destroy(pm_cache* c);
@@ -227,8 +231,8 @@ pm_status pm_cache_access(pm_cache* c, int expert, int k, int* first, int* count
 /* n accesses from host arrays; the whole trace is checked (PM_ERR_ARG) before
  * the first access. */
 pm_status pm_cache_replay(pm_cache* c, const int32_t* experts, const int32_t* ks, size_t n);
-/* Planes of the expert now held: the prefix r (PREFIX) or the largest k of
- * its resident entries (OBJECTS); 0 if none. */
+/* Planes of the expert now held: the prefix r (PREFIX), the largest k of its
+ * resident entries (OBJECTS) or its copy's width (DOWNWARD); 0 if none. */
 pm_status pm_cache_resident(const pm_cache* c, int expert, int* out);
 /* Running totals (any output may be null): accesses, full hits, partial hits
  * (PREFIX: some planes resident, more read), planes read, planes held. */

@@ -1,5 +1,6 @@
 """The library's expert caches (pm_cache_*) against the oracle's plane-aging
-prefix cache and independent-object cache: the hand-worked golden trace,
+prefix cache, independent-object cache and downward-reuse cache: the
+hand-worked golden traces,
 seeded random traces at many capacities and a Zipf routing trace with
 allocator-chosen prefixes.  Reads, residency and counters must agree exactly
 after every access.  Host only."""
@@ -20,12 +21,16 @@ def reads_of(first, count):
     return list(range(first, first + count))
 
 
+POLICIES = [pm.PM_CACHE_PREFIX, pm.PM_CACHE_OBJECTS, pm.PM_CACHE_DOWNWARD]
+
+
 def oracle_cache(policy, cap):
-    return oracle.PrefixPlaneCache(cap) if policy == pm.PM_CACHE_PREFIX else oracle.ObjectCache(cap)
+    return {pm.PM_CACHE_PREFIX: oracle.PrefixPlaneCache, pm.PM_CACHE_OBJECTS: oracle.ObjectCache,
+            pm.PM_CACHE_DOWNWARD: oracle.DownwardCache}[policy](cap)
 
 
 def oracle_resident(policy, oc, e):
-    if policy == pm.PM_CACHE_PREFIX:
+    if policy != pm.PM_CACHE_OBJECTS:
         return oc.resident(e)
     return max([k for (x, k) in oc.order if x == e], default=0)
 
@@ -63,9 +68,29 @@ def test_golden_trace():
         assert st["planes_read"] == g[key]["planes_read"] and st["hits"] == g[key]["hits"]
         if policy == pm.PM_CACHE_PREFIX:
             assert st["partial"] == g[key]["partial"]
+    d = pm.pm_cache_create(4, g["capacity"], pm.PM_CACHE_DOWNWARD)
+    g2 = json.load(open(os.path.join(GOLDEN, "plane_cache_downward_trace.json")))
+    for (e, k), want in zip(g["trace"], g2["first_trace_downward"]["reads"]):
+        assert reads_of(*pm.pm_cache_access(d, e, k)) == want
 
 
-@pytest.mark.parametrize("policy", [pm.PM_CACHE_PREFIX, pm.PM_CACHE_OBJECTS])
+def test_golden_downward_trace():
+    g = json.load(open(os.path.join(GOLDEN, "plane_cache_downward_trace.json")))
+    for policy, key in ((pm.PM_CACHE_PREFIX, "prefix"), (pm.PM_CACHE_OBJECTS, "objects"),
+                        (pm.PM_CACHE_DOWNWARD, "downward")):
+        c = pm.pm_cache_create(3, g["capacity"], policy)
+        for i, (e, k) in enumerate(g["trace"]):
+            assert reads_of(*pm.pm_cache_access(c, e, k)) == g[key]["reads"][i]
+            after = g[key].get("resident_after", g[key].get("width_after"))
+            if after is not None:
+                want = {int(x): r for x, r in after[i].items()}
+                assert {x: pm.pm_cache_resident(c, x) for x in range(3)} == \
+                    {x: want.get(x, 0) for x in range(3)}
+        st = pm.pm_cache_stats(c)
+        assert (st["planes_read"], st["hits"]) == (g[key]["planes_read"], g[key]["hits"])
+
+
+@pytest.mark.parametrize("policy", POLICIES)
 @pytest.mark.parametrize("cap", [0, 1, 3, 8, 9, 17, 40, 200])
 def test_random_traces_match_oracle(policy, cap):
     n_experts = 11
@@ -91,7 +116,7 @@ def zipf_allocated_trace(n_layers, n_experts, top_k, n_tokens, budget, s=1.0, cf
     return out
 
 
-@pytest.mark.parametrize("policy", [pm.PM_CACHE_PREFIX, pm.PM_CACHE_OBJECTS])
+@pytest.mark.parametrize("policy", POLICIES)
 def test_zipf_allocated_trace_matches_oracle(policy):
     trace = zipf_allocated_trace(2, 64, 4, 60, 10)
     c = pm.pm_cache_create(128, 90, policy)
@@ -145,7 +170,7 @@ def test_pages_examples():
 
 def test_errors_leave_state_unchanged():
     with pytest.raises(pm.PMError) as ei:
-        pm.pm_cache_create(4, 8, 7)
+        pm.pm_cache_create(4, 8, 3)
     assert ei.value.status == pm.PM_ERR_ARG
     with pytest.raises(pm.PMError):
         pm.pm_cache_create(0, 8)
