@@ -200,6 +200,99 @@ def encode_expert(leaves_codes, group, weighted=False):
 
 
 # ---------------------------------------------------------------------------
+# Encoder from fp32 weights  ([T] c19: per block, K-means learns 256 values,
+# which are sorted and become the leaves of the frequency-weighted tree)
+# ---------------------------------------------------------------------------
+KMEANS_ITERS = 25
+
+
+def kmeans_init(w, n):
+    """Starting centroids: the (2j+1)/(2n) quantiles of the block's weights,
+    j = 0..n-1, by the inverted empirical distribution (a sample value, no
+    interpolation).  Blocks of fewer than n weights repeat values."""
+    s = np.sort(np.asarray(w, dtype=np.float32))
+    g = s.size
+    idx = -(-(2 * np.arange(n) + 1) * g // (2 * n)) - 1          # ceil(q g) - 1
+    return s[idx].copy()
+
+
+def kmeans_assign(w, c):
+    """Index of the nearest centroid of every weight; distances |w - c| in
+    fp64 (exact for fp32 operands of similar scale); ties go to the lowest
+    index (argmin returns the first minimum)."""
+    d = np.abs(np.asarray(w, np.float64)[:, None] - np.asarray(c, np.float64)[None, :])
+    return d.argmin(axis=1)
+
+
+def kmeans_update(w, a, c):
+    """New centroids: the mean of each centroid's members, summed in
+    ascending order in fp64, divided by their count in fp64 and rounded to
+    fp32; a centroid without members keeps its value."""
+    w = np.asarray(w, np.float32)
+    out = np.array(c, dtype=np.float32, copy=True)
+    for j in range(out.size):
+        m = np.sort(w[a == j]).astype(np.float64)
+        if m.size:
+            out[j] = np.float32(np.add.accumulate(m)[-1] / m.size)
+    return out
+
+
+def kmeans_block(w, n=NLEAF, max_iters=KMEANS_ITERS):
+    """Lloyd's algorithm on one block: start at kmeans_init, then update and
+    re-assign until an update leaves the assignment unchanged or max_iters
+    updates have run.  Then the centroids are sorted ([T] c19) and the codes
+    renumbered (1-D Lloyd keeps them sorted already, so this is a no-op in
+    practice).
+    Returns (leaves fp32 [n] ascending, codes int64 [G], counts int64 [n],
+    updates run); codes are the nearest leaves of the weights."""
+    w = np.asarray(w, dtype=np.float32).reshape(-1)
+    c = kmeans_init(w, n)
+    a = kmeans_assign(w, c)
+    it = 0
+    while it < max_iters:
+        c = kmeans_update(w, a, c)
+        it += 1
+        a_new = kmeans_assign(w, c)
+        done = np.array_equal(a_new, a)
+        a = a_new
+        if done:
+            break
+    order = np.argsort(c, kind="stable")
+    rank = np.empty_like(order)
+    rank[order] = np.arange(order.size)
+    return c[order], rank[a], np.bincount(rank[a], minlength=n), it
+
+
+def encode_weights(W, group, max_iters=KMEANS_ITERS):
+    """Encoder from a dense fp32 matrix W [rows][cols] ([T] c19, c21, c25):
+    K-means per block of `group` inputs of one row, sorted leaves, the
+    count-weighted tree, bitplanes.  Returns dict(codes uint8, leaves fp32
+    [rows][nb][256], counts int64 [rows][nb][256], levels, planes)."""
+    W = np.asarray(W, dtype=np.float32)
+    rows, cols = W.shape
+    nb = cols // group
+    codes = np.empty((rows, cols), np.uint8)
+    leaves = np.empty((rows, nb, NLEAF), np.float32)
+    counts = np.empty((rows, nb, NLEAF), np.int64)
+    for o in range(rows):
+        for g in range(nb):
+            lv, cd, n, _ = kmeans_block(W[o, g * group:(g + 1) * group], NLEAF, max_iters)
+            codes[o, g * group:(g + 1) * group] = cd
+            leaves[o, g] = lv
+            counts[o, g] = n
+    return {"codes": codes, "leaves": leaves, "counts": counts,
+            "levels": tree_levels(leaves, counts), "planes": pack_planes(codes)}
+
+
+def relative_weight_error(W, planes, levels, k, group):
+    """||W - W_k||_F / ||W||_F in fp64, W_k the depth-k reconstruction
+    ([T] c23 reports this measure at 4 bits)."""
+    W = np.asarray(W, np.float64)
+    Wk = dequant(planes, levels, k, group).astype(np.float64)
+    return float(np.sqrt(np.sum((W - Wk) ** 2) / np.sum(W ** 2)))
+
+
+# ---------------------------------------------------------------------------
 # Routing  ([T] c4: a router picks a few experts per token, weights sum to 1)
 # ---------------------------------------------------------------------------
 def route(logits, top_k):

@@ -21,6 +21,7 @@ forms, read plainly):
     the leaves strictly ascending without a sort.
   * codes: independent uniform bytes (every bitplane is fair coin flips).
   * x and router logits: N(0, 1) by Box-Muller, fp64 then rounded to fp32.
+  * dense weights for the encoder: N(0, 0.02) by Box-Muller, rounded to fp32.
   * routing traces for cache replay: per-layer Zipf popularity over a seeded
     rank permutation, logits -s ln(rank) plus Gumbel noise (see
     zipf_router_logits); independent across tokens.
@@ -85,6 +86,7 @@ KIND_POISON = 7
 KIND_TRUNC = 8
 KIND_ZIPF = 9
 KIND_RANK = 10
+KIND_WEIGHTS = 11
 
 
 def stream_key(seed: int, kind: int, cfg: int, layer: int, unit: int, matrix: int):
@@ -195,6 +197,16 @@ def activation(seed, cfg, layer, token, n, step=0):
     """fp32 [n] N(0,1) activation of one token (per step)."""
     key = stream_key(seed, KIND_X, cfg, layer, token, 0)
     return normals(key, n, extra=step).astype(np.float32)
+
+
+WEIGHT_SIGMA = 0.02
+
+
+def weights(seed, cfg, layer, expert, matrix, rows, cols):
+    """fp32 [rows][cols] dense N(0, 0.02) weights of one matrix (the input of
+    the encoder from fp32 weights)."""
+    key = stream_key(seed, KIND_WEIGHTS, cfg, layer, expert, matrix)
+    return (WEIGHT_SIGMA * normals(key, rows * cols)).astype(np.float32).reshape(rows, cols)
 
 
 def router_logits(seed, cfg, layer, token, n_experts, step=0):

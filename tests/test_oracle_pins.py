@@ -511,3 +511,121 @@ def test_downward_cache_closed_forms_and_invariants():
         small.access(e, k)
         assert small.used == sum(small.width.values()) <= 10
         assert sorted(small.order) == sorted(small.width)
+
+
+# ---------------------------------------------------------------------------
+# Encoder from fp32 weights: K-means per block, sorted leaves, weighted tree
+# ---------------------------------------------------------------------------
+def test_kmeans_textbook_case():
+    """Two clumps, two centroids: the clump means, whatever the order."""
+    w = np.array([11.0, 1.0, 12.0, 2.0, 10.0, 3.0], np.float32)
+    c, a, n, it = oracle.kmeans_block(w, 2)
+    assert c.tolist() == [2.0, 11.0]
+    assert a.tolist() == [1, 0, 1, 0, 1, 0] and n.tolist() == [3, 3]
+
+
+def test_kmeans_init_is_the_inverted_cdf_quantile():
+    rng = np.random.default_rng(11)
+    for g in (6, 96, 128, 255, 256, 1000, 4096):
+        w = rng.normal(0, 0.02, g).astype(np.float32)
+        for n in (2, 16, 256):
+            q = (2 * np.arange(n) + 1) / (2 * n)
+            want = np.quantile(w, q, method="inverted_cdf").astype(np.float32)
+            assert np.array_equal(oracle.kmeans_init(w, n), want)
+
+
+def test_kmeans_matches_scipy_lloyd():
+    """scipy.cluster.vq.kmeans2 from the same start runs the same Lloyd
+    iterations (it keeps fp64 centroids; ours are rounded to fp32)."""
+    import warnings
+    from scipy.cluster.vq import kmeans2, vq
+    rng = np.random.default_rng(12)
+    for trial in range(6):
+        n = (4, 16, 32)[trial % 3]
+        w = rng.normal(0, 0.02, 400).astype(np.float32)
+        c, a, cnt, it = oracle.kmeans_block(w, n, max_iters=40)
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore")
+            ref, _ = kmeans2(w.astype(np.float64)[:, None],
+                             oracle.kmeans_init(w, n).astype(np.float64)[:, None],
+                             iter=it, minit="matrix", missing="warn")
+        ref = ref[:, 0]
+        assert np.all(np.abs(c - ref) <= 4e-7 * np.abs(ref) + 1e-12)
+        assert np.array_equal(a, vq(w.astype(np.float64)[:, None], ref[:, None])[0])
+
+
+def test_kmeans_fixed_point_exact_rationals():
+    """At convergence every weight sits on a nearest leaf (exact rational
+    distances, ties to the lower index) and every occupied leaf is its
+    members' mean to within one fp32 rounding."""
+    from fractions import Fraction
+    rng = np.random.default_rng(13)
+    w = rng.normal(0, 0.02, 300).astype(np.float32)
+    w[::7] = w[1]                                     # duplicates
+    c, a, cnt, it = oracle.kmeans_block(w, 16, max_iters=200)
+    assert it < 200
+    cf = [Fraction(float(v)) for v in c]
+    for x, j in zip(w, a):
+        d = [abs(Fraction(float(x)) - v) for v in cf]
+        assert j == d.index(min(d))
+    for j in range(16):
+        m = w[a == j]
+        assert cnt[j] == m.size
+        if m.size:
+            exact = sum(Fraction(float(v)) for v in m) / m.size
+            assert abs(Fraction(float(c[j])) - exact) <= Fraction(float(abs(np.spacing(c[j]))))
+
+
+def test_kmeans_objective_never_increases():
+    rng = np.random.default_rng(14)
+    w = rng.normal(0, 0.02, 2048).astype(np.float32)
+    sse = []
+    for t in range(0, 12):
+        if t == 0:
+            c = oracle.kmeans_init(w, 256)
+            a = oracle.kmeans_assign(w, c)
+        else:
+            c, a, _, _ = oracle.kmeans_block(w, 256, max_iters=t)
+        sse.append(float(np.sum((w.astype(np.float64) - c[a].astype(np.float64)) ** 2)))
+    assert all(sse[i + 1] <= sse[i] * (1 + 1e-9) for i in range(len(sse) - 1))
+    assert sse[-1] < sse[0]
+
+
+def test_kmeans_small_block_is_exact_and_leaves_sorted():
+    """A block of at most 256 distinct weights gets one leaf per weight: the
+    8-bit reconstruction is exact.  The leaves are ascending in every case."""
+    rng = np.random.default_rng(15)
+    for g in (32, 128, 256):
+        w = rng.normal(0, 0.02, g).astype(np.float32)
+        c, a, cnt, it = oracle.kmeans_block(w)
+        assert np.array_equal(c[a], w) and it == 1
+        assert np.all(np.diff(c) >= 0)
+    for g in (512, 1024):
+        w = np.round(rng.normal(0, 0.02, g) * 300).astype(np.float32) / 300   # many ties
+        c, a, cnt, it = oracle.kmeans_block(w)
+        assert np.all(np.diff(c) >= 0) and cnt.sum() == g
+
+
+def test_encoder_nodes_are_subtree_means():
+    """Whole encoder: the depth-k node of a block is the mean of the block's
+    weights whose code starts with that prefix (count-weighted tree over
+    K-means leaves), to within a few fp32 roundings of the members' scale;
+    the error shrinks with
+    k and is zero at 8 bits for blocks of at most 256 distinct weights."""
+    W = synth.weights(1, 0, 0, 0, 0, 4, 512)
+    enc = oracle.encode_weights(W, 256, max_iters=40)
+    for k in range(1, 9):
+        pre = enc["codes"].astype(np.int64) >> (8 - k)
+        for o in range(4):
+            for g in range(2):
+                blk = W[o, g * 256:(g + 1) * 256].astype(np.float64)
+                pb = pre[o, g * 256:(g + 1) * 256]
+                for v in np.unique(pb):
+                    got = float(enc["levels"][k][o, g, v])
+                    want = blk[pb == v].mean()
+                    # roundings of the fp32 leaves and parents, each at most
+                    # half an ulp of a value no larger than the members' scale
+                    scale = np.abs(blk[pb == v]).max()
+                    assert abs(got - want) <= 16 * 2.0 ** -24 * scale
+    err = [oracle.relative_weight_error(W, enc["planes"], enc["levels"], k, 256) for k in range(1, 9)]
+    assert all(err[i + 1] <= err[i] + 1e-12 for i in range(7)) and err[7] == 0.0
