@@ -219,7 +219,8 @@ def kmeans_init(w, n):
 def kmeans_assign(w, c):
     """Index of the nearest centroid of every weight; distances |w - c| in
     fp64 (exact for fp32 operands of similar scale); ties go to the lowest
-    index (argmin returns the first minimum)."""
+    index (argmin returns the first minimum), which for the ascending
+    centroids of kmeans_block is the lower value."""
     d = np.abs(np.asarray(w, np.float64)[:, None] - np.asarray(c, np.float64)[None, :])
     return d.argmin(axis=1)
 
@@ -238,11 +239,14 @@ def kmeans_update(w, a, c):
 
 
 def kmeans_block(w, n=NLEAF, max_iters=KMEANS_ITERS):
-    """Lloyd's algorithm on one block: start at kmeans_init, then update and
-    re-assign until an update leaves the assignment unchanged or max_iters
-    updates have run.  Then the centroids are sorted ([T] c19) and the codes
-    renumbered (1-D Lloyd keeps them sorted already, so this is a no-op in
-    practice).
+    """Lloyd's algorithm on one block: start at kmeans_init, then update,
+    sort the centroids ([T] c19 sorts the learned values; done after every
+    update, a relabelling, so that a tie between two values always goes to
+    the lower one) and re-assign, until an update leaves the assignment
+    unchanged or max_iters updates have run.  Sorting matters when starting
+    centroids repeat (blocks with many equal weights): the first of a run of
+    equal centroids can take members above the run and move past its empty
+    twins.  The final sort and renumbering below are then no-ops.
     Returns (leaves fp32 [n] ascending, codes int64 [G], counts int64 [n],
     updates run); codes are the nearest leaves of the weights."""
     w = np.asarray(w, dtype=np.float32).reshape(-1)
@@ -250,7 +254,7 @@ def kmeans_block(w, n=NLEAF, max_iters=KMEANS_ITERS):
     a = kmeans_assign(w, c)
     it = 0
     while it < max_iters:
-        c = kmeans_update(w, a, c)
+        c = np.sort(kmeans_update(w, a, c))
         it += 1
         a_new = kmeans_assign(w, c)
         done = np.array_equal(a_new, a)

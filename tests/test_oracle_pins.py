@@ -554,21 +554,29 @@ def test_kmeans_matches_scipy_lloyd():
         assert np.array_equal(a, vq(w.astype(np.float64)[:, None], ref[:, None])[0])
 
 
-def test_kmeans_fixed_point_exact_rationals():
+@pytest.mark.parametrize("case", ["duplicates", "coarse grid"])
+def test_kmeans_fixed_point_exact_rationals(case):
     """At convergence every weight sits on a nearest leaf (exact rational
-    distances, ties to the lower index) and every occupied leaf is its
-    members' mean to within one fp32 rounding."""
+    distances, ties to the lower index), the leaves ascend and every
+    occupied leaf is its members' mean to within one fp32 rounding.  The
+    coarse grid (many equal weights, so the 256 starting centroids repeat)
+    is the case where the per-update sort matters."""
     from fractions import Fraction
     rng = np.random.default_rng(13)
-    w = rng.normal(0, 0.02, 300).astype(np.float32)
-    w[::7] = w[1]                                     # duplicates
-    c, a, cnt, it = oracle.kmeans_block(w, 16, max_iters=200)
-    assert it < 200
+    if case == "duplicates":
+        w = rng.normal(0, 0.02, 300).astype(np.float32)
+        w[::7] = w[1]
+        n = 16
+    else:
+        w = (np.round(rng.normal(0, 0.02, 600) * 150) / 150).astype(np.float32)
+        n = 256
+    c, a, cnt, it = oracle.kmeans_block(w, n, max_iters=500)
+    assert it < 500 and np.all(np.diff(c) >= 0)
     cf = [Fraction(float(v)) for v in c]
-    for x, j in zip(w, a):
+    for x in np.unique(w):
         d = [abs(Fraction(float(x)) - v) for v in cf]
-        assert j == d.index(min(d))
-    for j in range(16):
+        assert np.all(a[w == x] == d.index(min(d)))
+    for j in range(n):
         m = w[a == j]
         assert cnt[j] == m.size
         if m.size:
