@@ -67,6 +67,7 @@ SIGNATURES = {
     "pm_encode_matrix": (_I, [_MS, _P, _P, _P, _P, _Z, _P]),
     "pm_encode_expert": (_I, [_ES, _P, _P, _P, _P, _P]),
     "pm_encode_matrix_device": (_I, [_MS, _P, _P, _P, _P, _Z, _P, _P]),
+    "pm_kmeans_codebook_device": (_I, [_MS, _P, _I, _P, _P, _P, _P, _P]),
     "pm_expert_gemv": (_I, [_MS, _I, _P, _Z, _P, _P, _P, _P]),
     "pm_route_topk": (_I, [_I, _I, _I, _P, _P, _P]),
     "pm_allocate_bits": (_I, [_I, _I, _P, _P, _I, _P, _I, _P]),
@@ -206,6 +207,13 @@ def pm_encode_matrix_device(s, d_codes, d_leaves, d_counts, d_planes, plane_stri
 
 
 # ---------------------------------------------------------------- GEMV and checks
+def pm_kmeans_codebook_device(s, d_w, max_iters, d_codes, d_leaves, d_counts, d_iters=None,
+                              stream=None):
+    return _check(lib().pm_kmeans_codebook_device(s, _dptr(d_w), max_iters, _dptr(d_codes),
+                                                  _dptr(d_leaves), _dptr(d_counts),
+                                                  _dptr(d_iters), _stream(stream)))
+
+
 def pm_expert_gemv(s, k, d_planes, plane_stride_words, d_levels, d_x, d_y, stream=None):
     return _check(lib().pm_expert_gemv(s, k, _dptr(d_planes), plane_stride_words,
                                        _dptr(d_levels), _dptr(d_x), _dptr(d_y),

@@ -13,6 +13,7 @@
 #include <string>
 #include <vector>
 
+#include "pm_encoder.h"
 #include "pm_error.h"
 #include "pm_internal.h"
 
@@ -239,6 +240,25 @@ extern "C" pm_status pm_encode_matrix_device(pm_matrix_shape s, const uint8_t* d
                     pm_plane_words(s));
     HIP_TRY(launch_encode_device(s.rows, s.cols, s.group, d_codes, d_leaves, d_counts,
                                  d_planes, pstride, d_levels, (hipStream_t)stream));
+    return PM_OK;
+}
+
+extern "C" pm_status pm_kmeans_codebook_device(pm_matrix_shape s, const float* d_w,
+                                               int max_iters, uint8_t* d_codes, float* d_leaves,
+                                               uint32_t* d_counts, int32_t* d_iters,
+                                               void* stream) {
+    pm_status st = check_shape(s);
+    if (st) return st;
+    if (s.group > kMaxKmeansGroup)
+        return failf(PM_ERR_SHAPE, "K-means block of %d weights above %d", s.group,
+                     kMaxKmeansGroup);
+    if (max_iters < 0) return failf(PM_ERR_ARG, "max_iters %d below 0", max_iters);
+    if (s.rows == 0 || s.cols == 0) return PM_OK;
+    if (!d_w || !d_codes || !d_leaves || !d_counts)
+        return failf(PM_ERR_ARG, "pm_kmeans_codebook_device: null pointer");
+    if (nblocks(s) > 0xFFFFFFFFu) return failf(PM_ERR_SHAPE, "more than 2^32-1 blocks");
+    HIP_TRY(launch_kmeans_device(s.rows, s.cols, s.group, d_w, max_iters, d_codes, d_leaves,
+                                 d_counts, d_iters, (hipStream_t)stream));
     return PM_OK;
 }
 

@@ -115,6 +115,27 @@ pm_status pm_encode_matrix_device(pm_matrix_shape s, const uint8_t* d_codes,
                                   uint32_t* d_planes_out, size_t plane_stride_words,
                                   float* d_levels_out, void* stream);
 
+/* Encoder from fp32 weights, first half [T c19: per block, K-means learns 256
+ * values, which are sorted and become the leaves of the tree].  For every
+ * block of `group` inputs of one row of d_w fp32 [rows][cols] (device), 1-D
+ * Lloyd's K-means with 256 centroids:
+ *   start   centroid j = the ceil((2j+1)*group/512)-th smallest weight;
+ *   assign  each weight to its nearest centroid, ties to the lowest index
+ *           (distances exact in fp64 for weights within 2^29 of each other);
+ *   update  each centroid with members = fp32 of their mean (fp64 sum in
+ *           ascending order, fp64 division); one without members stays;
+ *   stop    once an update changes no assignment, or after max_iters updates.
+ * Outputs (device): d_codes uint8 [rows][cols] (each weight's nearest leaf),
+ * d_leaves fp32 [rows][cols/group][256] ascending, d_counts uint32
+ * [rows][cols/group][256] (weights per leaf), d_iters int32 [blocks] (updates
+ * run; may be NULL).  Pass codes, leaves and counts to
+ * pm_encode_matrix_device for the planes and the count-weighted tree.
+ * group <= 4096 (else PM_ERR_SHAPE); max_iters >= 0.  Weights must be finite
+ * (other values give unspecified codes). */
+pm_status pm_kmeans_codebook_device(pm_matrix_shape s, const float* d_w, int max_iters,
+                                    uint8_t* d_codes, float* d_leaves, uint32_t* d_counts,
+                                    int32_t* d_iters, void* stream);
+
 /* ---------------------------------------------------------------- prefix GEMV
  * y[o] = sum_i node(k, o, i/group, prefix_k(o, i)) * x[i]: one matrix read
  * directly at a k-bit prefix, no decoded matrix is formed [Abs "directly

@@ -223,3 +223,19 @@ def test_validation_before_any_hip_call():
         pm.pm_route_topk(np.zeros((1, 4), np.float32), 5)
     # empty inputs are no-ops that touch nothing
     pm.pm_expert_gemv(pm.mshape(0, 64, 32), 3, None, 0, None, None, None)
+
+
+def test_kmeans_validation_before_any_hip_call():
+    with pytest.raises(pm.PMError) as ei:
+        pm.pm_kmeans_codebook_device(pm.mshape(2, 8192, 8192), 1, 25, 1, 1, 1)
+    assert ei.value.status == pm.PM_ERR_SHAPE
+    with pytest.raises(pm.PMError) as ei:
+        pm.pm_kmeans_codebook_device(pm.mshape(2, 128, 128), 1, -1, 1, 1, 1)
+    assert ei.value.status == pm.PM_ERR_ARG
+    with pytest.raises(pm.PMError) as ei:
+        pm.pm_kmeans_codebook_device(pm.mshape(2, 128, 128), 1, 5, None, 1, 1)
+    assert ei.value.status == pm.PM_ERR_ARG
+    with pytest.raises(pm.PMError) as ei:
+        pm.pm_kmeans_codebook_device(pm.mshape(2, 100, 50), 1, 5, 1, 1, 1)
+    assert ei.value.status == pm.PM_ERR_SHAPE
+    pm.pm_kmeans_codebook_device(pm.mshape(0, 128, 128), None, 5, None, None, None)
