@@ -364,6 +364,74 @@ def bench_batch_topup(args, torch, pm, synth, PoolFiller):
             "expert_gemvs_per_s": round(3 * wl.top_k * wl.n_tokens * n / el, 1)}
 
 
+ENCODE_ITERS = 25
+
+
+def bench_encode(args, torch, pm, synth):
+    """The encoder from fp32 weights on one expert (gate, up, down of hidden
+    4096 / intermediate 1024, dense N(0, 0.02) weights): K-means per block
+    (pm_kmeans_codebook_device) then planes and the count-weighted tree
+    (pm_encode_matrix_device), at group 128 (the stored format; a block of
+    128 weights gets one leaf per weight, so 7 and 8 bits are exact) and at
+    group 1024.  Reports the time per expert and the relative weight error
+    ||W - W_k|| / ||W|| for k = 1..8 (W_k decoded by pm_debug_dequant)."""
+    wl = synth.WORKLOADS[1]
+    shapes = [(wl.inter, wl.hidden), (wl.inter, wl.hidden), (wl.hidden, wl.inter)]
+    W = [torch.from_numpy(synth.weights(wl.seed, wl.cfg, 0, 0, m, r, c)).cuda()
+         for m, (r, c) in enumerate(shapes)]
+    stream = torch.cuda.current_stream()
+    out = []
+    for group in (128, 1024):
+        bufs = []
+        for (r, c), w in zip(shapes, W):
+            s = pm.mshape(r, c, group)
+            nb = r * (c // group)
+            bufs.append(dict(
+                s=s, w=w, nb=nb,
+                codes=torch.empty(r * c, dtype=torch.uint8, device="cuda"),
+                leaves=torch.empty(nb * 256, dtype=torch.float32, device="cuda"),
+                counts=torch.empty(nb * 256, dtype=torch.int32, device="cuda"),
+                its=torch.empty(nb, dtype=torch.int32, device="cuda"),
+                planes=torch.empty(8 * pm.pm_plane_words(s), dtype=torch.int32, device="cuda"),
+                levels=torch.empty(pm.pm_levels_floats(s), dtype=torch.float32, device="cuda")))
+
+        def encode():
+            for b in bufs:
+                pm.pm_kmeans_codebook_device(b["s"], b["w"], ENCODE_ITERS, b["codes"],
+                                             b["leaves"], b["counts"], b["its"], stream)
+                pm.pm_encode_matrix_device(b["s"], b["codes"], b["leaves"], b["counts"],
+                                           b["planes"], pm.pm_plane_words(b["s"]), b["levels"],
+                                           stream)
+
+        encode()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        t0.record(stream)
+        for _ in range(reps):
+            encode()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / reps
+        err = []
+        wk = [torch.empty_like(b["w"]) for b in bufs]
+        for k in range(1, 9):
+            num = den = 0.0
+            for b, d in zip(bufs, wk):
+                pm.pm_debug_dequant(b["s"], k, b["planes"], pm.pm_plane_words(b["s"]),
+                                    b["levels"], d, stream)
+                num += float(((b["w"].double() - d.double()) ** 2).sum())
+                den += float((b["w"].double() ** 2).sum())
+            err.append(round(100 * (num / den) ** 0.5, 3))
+        its = torch.cat([b["its"] for b in bufs]).double()
+        n_w = sum(r * c for r, c in shapes)
+        out.append({"group": group, "ms_per_expert": round(ms, 3),
+                    "M_weights_per_s": round(n_w / ms / 1e3, 1),
+                    "mean_iters": round(float(its.mean()), 2), "max_iters": int(its.max()),
+                    "rel_weight_error_pct_k1_to_k8": err})
+    return {"workload": "encode-expert-h4096-i1024-normal0.02-kmeans256", "results": out}
+
+
 CACHE_TOKENS = 500
 CACHE_ZIPF_S = 1.0
 CACHE_GIB = (12, 24, 48)
@@ -442,10 +510,12 @@ def main():
     ap.add_argument("--experts", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="1", choices=["1", "2", "3", "4", "cache", "all"],
+    ap.add_argument("--workload", default="1",
+                    choices=["1", "2", "3", "4", "cache", "encode", "all"],
                     help="1: the one-layer step (the reported line); 2: 60 layers; "
                          "3: k = 4 / 8 / mixed against materialize; 4: B = 8 with top-ups; "
-                         "cache: Zipf trace replay through the expert caches (host only)")
+                         "cache: Zipf trace replay through the expert caches (host only); "
+                         "encode: K-means encoder from fp32 weights")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV"),
                     help="print a summary of rocprofv3 outputs of this benchmark and exit")
     args = ap.parse_args()
@@ -472,8 +542,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         return 1
     if args.workload != "1":
-        extra = {"2": bench_sixty_layers, "3": bench_precisions, "4": bench_batch_topup}
-        for key in (["2", "3", "4"] if args.workload == "all" else [args.workload]):
+        extra = {"2": bench_sixty_layers, "3": bench_precisions, "4": bench_batch_topup,
+                 "encode": lambda a, t, p, s, _: bench_encode(a, t, p, s)}
+        for key in (["2", "3", "4", "encode"] if args.workload == "all" else [args.workload]):
             res = extra[key](args, torch, pm, synth, PoolFiller)
             print(json.dumps({"workload_result": res}), flush=True)
         return 0
