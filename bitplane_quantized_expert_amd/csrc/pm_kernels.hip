@@ -618,19 +618,96 @@ __device__ inline float row_dot_lane(const uint32_t* __restrict__ planes, size_t
     return acc;
 }
 
+// Group 128 and k >= 6: the depth-k tables dominate the bytes (8 << k per
+// 32-word run against k words of planes), and a per-weight gather straight
+// from global memory touches up to 64 cache lines per instruction.  Here a
+// wave takes a row in runs of 32 words (8 blocks, 1024 inputs); each lane
+// takes half a word.  The run's 8 tables are one contiguous range of the
+// level-major layout: they arrive as coalesced 16-byte loads (the next run's
+// issued while this one computes) and are written to the wave's own LDS
+// region, where every weight's node is read.  The wave alone writes and
+// reads its region, and LDS operations of one wave complete in order.
+constexpr int kRunWords = 32;
+constexpr int kRunTabFloatsMax = 8 << kBits;
+
+template <int K>
+__device__ inline float row_dot_lds(const uint32_t* __restrict__ planes, size_t pstride,
+                                    const float* __restrict__ rowtab, int o, int W,
+                                    const float* __restrict__ x, float* __restrict__ tabs,
+                                    int lane) {
+    constexpr int kRunFloats = 8 << K;
+    constexpr int kLoads = kRunFloats / (4 * kWave);
+    const int h = lane & 1;
+    const int runs = W / kRunWords;
+    f32x4 T[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) T[i] = *(g_f32x4*)(rowtab + 4 * (lane + kWave * i));
+    const float* bt = tabs + ((lane >> 3) << K);          // this lane's block of the run
+    float acc = 0.f;
+    for (int r = 0; r < runs; ++r) {
+        const int w = r * kRunWords + (lane >> 1);
+        uint32_t pw[K];
+#pragma unroll
+        for (int p = 0; p < K; ++p)
+            pw[p] = planes[size_t(p) * pstride + size_t(o) * W + w] >> (16 * h);
+        f32x4 xv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[q] = *(g_f32x4*)(x + 32 * w + 16 * h + 4 * q);
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) *(f32x4*)(tabs + 4 * (lane + kWave * i)) = T[i];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (r + 1 < runs) {
+#pragma unroll
+            for (int i = 0; i < kLoads; ++i)
+                T[i] = *(g_f32x4*)(rowtab + size_t(r + 1) * kRunFloats + 4 * (lane + kWave * i));
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int p = 0; p < K; ++p) v = (v << 1) | ((pw[p] >> j) & 1u);
+            acc = fmaf(bt[v], xv[j >> 2][j & 3], acc);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    return acc;
+}
+
+// This lane's share of row o at prefix k: the LDS-staged form where it
+// applies (group 128, k >= 6, whole runs, 16-byte aligned tables), else
+// row_dot_lane.  The choice is uniform over the wave.
+__device__ inline float row_dot(const uint32_t* __restrict__ planes, size_t pstride,
+                                const float* __restrict__ lv_k, int k, int o, int W, int wpg,
+                                const float* __restrict__ x, float* __restrict__ tabs,
+                                int lane) {
+    if (wpg == 4 && k >= 6 && W % kRunWords == 0) {
+        const float* rowtab = lv_k + ((size_t(o) * (W / 4)) << k);
+        if ((reinterpret_cast<uintptr_t>(rowtab) & 15) == 0 &&
+            (reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+            if (k == 6) return row_dot_lds<6>(planes, pstride, rowtab, o, W, x, tabs, lane);
+            if (k == 7) return row_dot_lds<7>(planes, pstride, rowtab, o, W, x, tabs, lane);
+            return row_dot_lds<8>(planes, pstride, rowtab, o, W, x, tabs, lane);
+        }
+    }
+    return row_dot_lane(planes, pstride, lv_k, k, o, W, wpg, x, lane);
+}
+
 __global__ __launch_bounds__(kBlock) void gemv_direct_kernel(int rows, int cols, int group, int k,
                                                              const uint32_t* __restrict__ planes,
                                                              size_t pstride,
                                                              const float* __restrict__ levels,
                                                              const float* __restrict__ x,
                                                              float* __restrict__ y) {
+    __shared__ float tabs[kRowsPerBlock][kRunTabFloatsMax];
     const int lane = threadIdx.x % kWave;
     const int o = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
     if (o >= rows) return;
     const int W = cols / 32;
     const size_t nb = size_t(rows) * (cols / group);
-    float acc = row_dot_lane(planes, pstride, levels + level_offset(nb, k), k, o, W, group / 32,
-                             x, lane);
+    float acc = row_dot(planes, pstride, levels + level_offset(nb, k), k, o, W, group / 32, x,
+                        tabs[threadIdx.x / kWave], lane);
     acc = wave_sum(acc);
     if (lane == kWave - 1) y[o] = acc;
 }
@@ -642,6 +719,7 @@ __global__ __launch_bounds__(kBlock) void direct_gateup_kernel(Geom g,
                                                                const int32_t* __restrict__ list,
                                                                const float* __restrict__ x,
                                                                Partials P) {
+    __shared__ float tabs[kRowsPerBlock][kRunTabFloatsMax];
     const Item it = items[blockIdx.x / bpi];
     const int lane = threadIdx.x % kWave;
     const int o = (blockIdx.x % bpi) * kRowsPerBlock + threadIdx.x / kWave;
@@ -655,9 +733,9 @@ __global__ __launch_bounds__(kBlock) void direct_gateup_kernel(Geom g,
         for (int m = 0; m < 2; ++m) {
             if (!us.direct[m]) continue;
             const int k = us.k[m];
-            float acc = row_dot_lane(it.planes + g.plane_off[m], g.plane_words,
-                                     it.levels + g.level_off[m] + level_offset(nb, k), k, o, W,
-                                     g.group / 32, xt, lane);
+            float acc = row_dot(it.planes + g.plane_off[m], g.plane_words,
+                                it.levels + g.level_off[m] + level_offset(nb, k), k, o, W,
+                                g.group / 32, xt, tabs[threadIdx.x / kWave], lane);
             acc = wave_sum(acc);
             if (lane == kWave - 1) P.gu[(size_t(u) * 2 + m) * P.gu_smax * g.inter + o] = acc;
         }
@@ -687,6 +765,7 @@ __global__ __launch_bounds__(kBlock) void direct_down_kernel(Geom g, const Item*
                                                              const Use* __restrict__ uses,
                                                              const int32_t* __restrict__ list,
                                                              Partials P) {
+    __shared__ float tabs[kRowsPerBlock][kRunTabFloatsMax];
     const Item it = items[blockIdx.x / bpi];
     const int lane = threadIdx.x % kWave;
     const int o = (blockIdx.x % bpi) * kRowsPerBlock + threadIdx.x / kWave;
@@ -698,9 +777,10 @@ __global__ __launch_bounds__(kBlock) void direct_down_kernel(Geom g, const Item*
         const Use us = uses[u];
         if (!us.direct[2]) continue;
         const int k = us.k[2];
-        float acc = row_dot_lane(it.planes + g.plane_off[2], g.plane_words,
-                                 it.levels + g.level_off[2] + level_offset(nb, k), k, o, W,
-                                 g.group / 32, P.h + size_t(u) * g.inter, lane);
+        float acc = row_dot(it.planes + g.plane_off[2], g.plane_words,
+                            it.levels + g.level_off[2] + level_offset(nb, k), k, o, W,
+                            g.group / 32, P.h + size_t(u) * g.inter, tabs[threadIdx.x / kWave],
+                            lane);
         acc = wave_sum(acc);
         if (lane == kWave - 1) P.y[size_t(u) * P.dn_smax * g.hidden + o] = acc;
     }
