@@ -629,12 +629,13 @@ __device__ inline float row_dot_lane(const uint32_t* __restrict__ planes, size_t
 // reads its region, and LDS operations of one wave complete in order.
 constexpr int kRunWords = 32;
 constexpr int kRunTabFloatsMax = 8 << kBits;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 template <int K>
-__device__ inline float row_dot_lds(const uint32_t* __restrict__ planes, size_t pstride,
-                                    const float* __restrict__ rowtab, int o, int W,
-                                    const float* __restrict__ x, float* __restrict__ tabs,
-                                    int lane) {
+__device__ __attribute__((always_inline)) inline float row_dot_lds(
+    const uint32_t* __restrict__ planes, size_t pstride, const float* __restrict__ rowtab, int o,
+    int W, const float* __restrict__ x, lds_f32* __restrict__ tabs, int lane) {
     constexpr int kRunFloats = 8 << K;
     constexpr int kLoads = kRunFloats / (4 * kWave);
     const int h = lane & 1;
@@ -642,7 +643,7 @@ __device__ inline float row_dot_lds(const uint32_t* __restrict__ planes, size_t 
     f32x4 T[kLoads];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) T[i] = *(g_f32x4*)(rowtab + 4 * (lane + kWave * i));
-    const float* bt = tabs + ((lane >> 3) << K);          // this lane's block of the run
+    const lds_f32* bt = tabs + ((lane >> 3) << K);        // this lane's block of the run
     float acc = 0.f;
     for (int r = 0; r < runs; ++r) {
         const int w = r * kRunWords + (lane >> 1);
@@ -654,7 +655,7 @@ __device__ inline float row_dot_lds(const uint32_t* __restrict__ planes, size_t 
 #pragma unroll
         for (int q = 0; q < 4; ++q) xv[q] = *(g_f32x4*)(x + 32 * w + 16 * h + 4 * q);
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) *(f32x4*)(tabs + 4 * (lane + kWave * i)) = T[i];
+        for (int i = 0; i < kLoads; ++i) *(lds_f32x4*)(tabs + 4 * (lane + kWave * i)) = T[i];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -678,10 +679,9 @@ __device__ inline float row_dot_lds(const uint32_t* __restrict__ planes, size_t 
 // This lane's share of row o at prefix k: the LDS-staged form where it
 // applies (group 128, k >= 6, whole runs, 16-byte aligned tables), else
 // row_dot_lane.  The choice is uniform over the wave.
-__device__ inline float row_dot(const uint32_t* __restrict__ planes, size_t pstride,
-                                const float* __restrict__ lv_k, int k, int o, int W, int wpg,
-                                const float* __restrict__ x, float* __restrict__ tabs,
-                                int lane) {
+__device__ __attribute__((always_inline)) inline float row_dot(
+    const uint32_t* __restrict__ planes, size_t pstride, const float* __restrict__ lv_k, int k,
+    int o, int W, int wpg, const float* __restrict__ x, lds_f32* __restrict__ tabs, int lane) {
     if (wpg == 4 && k >= 6 && W % kRunWords == 0) {
         const float* rowtab = lv_k + ((size_t(o) * (W / 4)) << k);
         if ((reinterpret_cast<uintptr_t>(rowtab) & 15) == 0 &&
@@ -707,7 +707,7 @@ __global__ __launch_bounds__(kBlock) void gemv_direct_kernel(int rows, int cols,
     const int W = cols / 32;
     const size_t nb = size_t(rows) * (cols / group);
     float acc = row_dot(planes, pstride, levels + level_offset(nb, k), k, o, W, group / 32, x,
-                        tabs[threadIdx.x / kWave], lane);
+                        (lds_f32*)tabs[threadIdx.x / kWave], lane);
     acc = wave_sum(acc);
     if (lane == kWave - 1) y[o] = acc;
 }
@@ -730,12 +730,13 @@ __global__ __launch_bounds__(kBlock) void direct_gateup_kernel(Geom g,
         const int u = list[it.use0 + q];
         const Use us = uses[u];
         const float* xt = x + size_t(us.tok) * g.hidden;
+#pragma unroll
         for (int m = 0; m < 2; ++m) {
             if (!us.direct[m]) continue;
             const int k = us.k[m];
             float acc = row_dot(it.planes + g.plane_off[m], g.plane_words,
                                 it.levels + g.level_off[m] + level_offset(nb, k), k, o, W,
-                                g.group / 32, xt, tabs[threadIdx.x / kWave], lane);
+                                g.group / 32, xt, (lds_f32*)tabs[threadIdx.x / kWave], lane);
             acc = wave_sum(acc);
             if (lane == kWave - 1) P.gu[(size_t(u) * 2 + m) * P.gu_smax * g.inter + o] = acc;
         }
@@ -779,7 +780,7 @@ __global__ __launch_bounds__(kBlock) void direct_down_kernel(Geom g, const Item*
         const int k = us.k[2];
         float acc = row_dot(it.planes + g.plane_off[2], g.plane_words,
                             it.levels + g.level_off[2] + level_offset(nb, k), k, o, W,
-                            g.group / 32, P.h + size_t(u) * g.inter, tabs[threadIdx.x / kWave],
+                            g.group / 32, P.h + size_t(u) * g.inter, (lds_f32*)tabs[threadIdx.x / kWave],
                             lane);
         acc = wave_sum(acc);
         if (lane == kWave - 1) P.y[size_t(u) * P.dn_smax * g.hidden + o] = acc;
