@@ -297,7 +297,7 @@ extern "C" pm_status pm_expert_gemv(pm_matrix_shape s, int k, const uint32_t* d_
     if (s.rows == 0) return PM_OK;
     if (s.cols > 0 && !d_x) return failf(PM_ERR_ARG, "null x");
     if (reinterpret_cast<uintptr_t>(d_x) % 16) return failf(PM_ERR_ARG, "x not 16-byte aligned");
-    if (k <= kLutMaxK && s.cols > 0 && s.cols % kSliceCols == 0 && s.group == kLutGroup &&
+    if (k <= kGemvLutMaxK && s.cols > 0 && s.cols % kSliceCols == 0 && s.group == kLutGroup &&
         s.rows % 2 == 0 && lut_offsets_fit(s, k, pstride))
         return gemv_lut(s, k, d_planes, pstride, d_levels, d_x, d_y, (hipStream_t)stream);
     HIP_TRY(launch_gemv(s.rows, s.cols, s.group, k, d_planes, pstride, d_levels, d_x, d_y,

@@ -79,7 +79,11 @@ struct Partials {
 constexpr int kSliceCols = 1024;   // columns of x covered by one LUT
 // Block size of the LUT path: the four lanes of a block share its table.
 constexpr int kLutGroup = 128;
-constexpr int kLutMaxK = 5;        // largest prefix read through the LUT path
+// Largest prefix read through the LUT path: in a layer forward (one launch
+// for all experts; larger prefixes add the direct launches) and in a single
+// GEMV (from k = 5 the staged-table direct path is faster).
+constexpr int kLutMaxK = 5;
+constexpr int kGemvLutMaxK = 4;
 
 // LUT-path launch description, passed as kernel arguments (no upload).
 constexpr int kMaxLaunchJobs = 64;

@@ -4,9 +4,9 @@
 // "directly executes cached 1-8-bit prefixes without materializing
 // full-precision experts"; T c25, c37]:
 //
-// LUT path (k <= 5; columns in slices of 1024).  The result of one block of
-// a row is sum_v node[v] * S_v, where S_v is the sum of x over the block's
-// weights whose prefix is v.  A weight word (32 inputs) has prefix v exactly
+// LUT path (k <= 5 in a layer, k <= 4 in a single GEMV; columns in slices of
+// 1024).  The result of one block of a row is sum_v node[v] * S_v, where S_v
+// is the sum of x over the block's weights whose prefix is v.  A weight word (32 inputs) has prefix v exactly
 // where the AND of the k plane words (each taken plain or inverted by the
 // bits of v) is set, and the sum of x under a 32-bit mask is four lookups in
 // a table of all 256 subset sums of each 8-input chunk of x (an activation
@@ -18,7 +18,8 @@
 //
 // Direct path (any k, any shape, an expert shared by several tokens read
 // once): per weight, the prefix is assembled from the k plane words and its
-// node read from the depth-k table.
+// node read from the depth-k table, which for group 128 and k >= 5 is first
+// staged in LDS (row_dot_lds).
 //
 // All sums run in a fixed order (DPP row reductions, slices and slots in
 // index order), so every output is deterministic.
@@ -618,7 +619,7 @@ __device__ inline float row_dot_lane(const uint32_t* __restrict__ planes, size_t
     return acc;
 }
 
-// Group 128 and k >= 6: the depth-k tables dominate the bytes (8 << k per
+// Group 128 and k >= 5: the depth-k tables dominate the bytes (8 << k per
 // 32-word run against k words of planes), and a per-weight gather straight
 // from global memory touches up to 64 cache lines per instruction.  Here a
 // wave takes a row in runs of 32 words (8 blocks, 1024 inputs); each lane
@@ -629,6 +630,7 @@ __device__ inline float row_dot_lane(const uint32_t* __restrict__ planes, size_t
 // reads its region, and LDS operations of one wave complete in order.
 constexpr int kRunWords = 32;
 constexpr int kRunTabFloatsMax = 8 << kBits;
+constexpr int kLdsMinK = 5;              // smallest k read through the staged tables
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
@@ -637,12 +639,17 @@ __device__ __attribute__((always_inline)) inline float row_dot_lds(
     const uint32_t* __restrict__ planes, size_t pstride, const float* __restrict__ rowtab, int o,
     int W, const float* __restrict__ x, lds_f32* __restrict__ tabs, int lane) {
     constexpr int kRunFloats = 8 << K;
-    constexpr int kLoads = kRunFloats / (4 * kWave);
+    // 16-byte pieces per lane; below k = 5 only the first lanes hold one
+    constexpr bool kPartial = kRunFloats < 4 * kWave;
+    constexpr int kLoads = kPartial ? 1 : kRunFloats / (4 * kWave);
+    const bool holds = !kPartial || lane < kRunFloats / 4;
     const int h = lane & 1;
     const int runs = W / kRunWords;
     f32x4 T[kLoads];
+    if (holds) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) T[i] = *(g_f32x4*)(rowtab + 4 * (lane + kWave * i));
+        for (int i = 0; i < kLoads; ++i) T[i] = *(g_f32x4*)(rowtab + 4 * (lane + kWave * i));
+    }
     const lds_f32* bt = tabs + ((lane >> 3) << K);        // this lane's block of the run
     float acc = 0.f;
     for (int r = 0; r < runs; ++r) {
@@ -654,12 +661,14 @@ __device__ __attribute__((always_inline)) inline float row_dot_lds(
         f32x4 xv[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) xv[q] = *(g_f32x4*)(x + 32 * w + 16 * h + 4 * q);
+        if (holds) {
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) *(lds_f32x4*)(tabs + 4 * (lane + kWave * i)) = T[i];
+            for (int i = 0; i < kLoads; ++i) *(lds_f32x4*)(tabs + 4 * (lane + kWave * i)) = T[i];
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (r + 1 < runs) {
+        if (holds && r + 1 < runs) {
 #pragma unroll
             for (int i = 0; i < kLoads; ++i)
                 T[i] = *(g_f32x4*)(rowtab + size_t(r + 1) * kRunFloats + 4 * (lane + kWave * i));
@@ -677,18 +686,22 @@ __device__ __attribute__((always_inline)) inline float row_dot_lds(
 }
 
 // This lane's share of row o at prefix k: the LDS-staged form where it
-// applies (group 128, k >= 6, whole runs, 16-byte aligned tables), else
+// applies (group 128, k >= 5, whole runs, 16-byte aligned tables), else
 // row_dot_lane.  The choice is uniform over the wave.
 __device__ __attribute__((always_inline)) inline float row_dot(
     const uint32_t* __restrict__ planes, size_t pstride, const float* __restrict__ lv_k, int k,
     int o, int W, int wpg, const float* __restrict__ x, lds_f32* __restrict__ tabs, int lane) {
-    if (wpg == 4 && k >= 6 && W % kRunWords == 0) {
+    if (wpg == 4 && k >= kLdsMinK && W % kRunWords == 0) {
         const float* rowtab = lv_k + ((size_t(o) * (W / 4)) << k);
         if ((reinterpret_cast<uintptr_t>(rowtab) & 15) == 0 &&
             (reinterpret_cast<uintptr_t>(x) & 15) == 0) {
-            if (k == 6) return row_dot_lds<6>(planes, pstride, rowtab, o, W, x, tabs, lane);
-            if (k == 7) return row_dot_lds<7>(planes, pstride, rowtab, o, W, x, tabs, lane);
-            return row_dot_lds<8>(planes, pstride, rowtab, o, W, x, tabs, lane);
+            static_assert(kLdsMinK == 5, "one case per staged k");
+            switch (k) {
+            case 5: return row_dot_lds<5>(planes, pstride, rowtab, o, W, x, tabs, lane);
+            case 6: return row_dot_lds<6>(planes, pstride, rowtab, o, W, x, tabs, lane);
+            case 7: return row_dot_lds<7>(planes, pstride, rowtab, o, W, x, tabs, lane);
+            default: return row_dot_lds<8>(planes, pstride, rowtab, o, W, x, tabs, lane);
+            }
         }
     }
     return row_dot_lane(planes, pstride, lv_k, k, o, W, wpg, x, lane);
