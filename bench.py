@@ -364,6 +364,41 @@ def bench_batch_topup(args, torch, pm, synth, PoolFiller):
             "expert_gemvs_per_s": round(3 * wl.top_k * wl.n_tokens * n / el, 1)}
 
 
+def bench_gemv_by_k(args, torch, pm, synth):
+    """pm_expert_gemv alone at k = 1..8 on two tall group-128 matrices
+    (16384 x 4096 and 32768 x 1024: 16 gate/up and 8 down matrices stacked),
+    planes and levels filled with random bits/values (the timing does not
+    depend on them).  Reports us per call and GB/s on planes 0..k-1 plus the
+    depth-k tables plus x."""
+    stream = torch.cuda.current_stream()
+    out = []
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.BASE_SEED)
+    for rows, cols in ((16384, 4096), (32768, 1024)):
+        s = pm.mshape(rows, cols, 128)
+        pw, lf = pm.pm_plane_words(s), pm.pm_levels_floats(s)
+        planes = torch.randint(-2**31, 2**31 - 1, (8 * pw,), dtype=torch.int32, device="cuda",
+                               generator=g)
+        levels = torch.randn(lf, device="cuda", generator=g)
+        x = torch.randn(cols, device="cuda", generator=g)
+        y = torch.empty(rows, device="cuda")
+        for k in range(1, 9):
+            for _ in range(3):
+                pm.pm_expert_gemv(s, k, planes, pw, levels, x, y, stream)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = 20
+            a.record(stream)
+            for _ in range(n):
+                pm.pm_expert_gemv(s, k, planes, pw, levels, x, y, stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / n * 1e3
+            by = rows * cols * k // 8 + rows * (cols // 128) * (1 << k) * 4 + cols * 4
+            out.append({"rows": rows, "cols": cols, "k": k, "us": round(us, 2),
+                        "GBs": round(by / us / 1e3, 1)})
+    return {"workload": "gemv-by-k-g128", "results": out}
+
+
 ENCODE_ITERS = 25
 
 
@@ -511,11 +546,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="1",
-                    choices=["1", "2", "3", "4", "cache", "encode", "all"],
+                    choices=["1", "2", "3", "4", "cache", "encode", "gemv", "all"],
                     help="1: the one-layer step (the reported line); 2: 60 layers; "
                          "3: k = 4 / 8 / mixed against materialize; 4: B = 8 with top-ups; "
                          "cache: Zipf trace replay through the expert caches (host only); "
-                         "encode: K-means encoder from fp32 weights")
+                         "encode: K-means encoder from fp32 weights; "
+                         "gemv: pm_expert_gemv alone at k = 1..8")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV"),
                     help="print a summary of rocprofv3 outputs of this benchmark and exit")
     args = ap.parse_args()
@@ -543,8 +579,10 @@ def main():
         return 1
     if args.workload != "1":
         extra = {"2": bench_sixty_layers, "3": bench_precisions, "4": bench_batch_topup,
-                 "encode": lambda a, t, p, s, _: bench_encode(a, t, p, s)}
-        for key in (["2", "3", "4", "encode"] if args.workload == "all" else [args.workload]):
+                 "encode": lambda a, t, p, s, _: bench_encode(a, t, p, s),
+                 "gemv": lambda a, t, p, s, _: bench_gemv_by_k(a, t, p, s)}
+        for key in (["2", "3", "4", "encode", "gemv"] if args.workload == "all"
+                    else [args.workload]):
             res = extra[key](args, torch, pm, synth, PoolFiller)
             print(json.dumps({"workload_result": res}), flush=True)
         return 0
