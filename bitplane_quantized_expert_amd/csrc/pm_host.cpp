@@ -738,70 +738,80 @@ struct JobSpec {                       // a LUT job before it is packed into a l
 
 // Row cuts of a launch (KLaunch::start), contiguous: the cost of all rows in
 // order is split into n_wgq equal parts, each cut at an even row of its job.
-static void set_starts_contig(KLaunch& L, int n_wgq) {
-    const int n = L.n_jobs, rows = L.rows, pairs = (rows + 1) / 2;
+// Cuts jobs j0 .. j1-1 of a launch into n_wg row ranges of about equal cost
+// (rows in pairs), writing L.start[w0 .. w0 + n_wg - 1].
+static void cut_jobs(KLaunch& L, int j0, int j1, int n_wg, int w0) {
+    const int n = j1 - j0, rows = L.rows, pairs = (rows + 1) / 2;
     std::vector<int64_t> pc(n), before(n + 1, 0);
     for (int j = 0; j < n; ++j) {
-        pc[j] = 2 * lut_row_cost(L.job[j].k, L.wpg);
+        pc[j] = 2 * lut_row_cost(L.job[j0 + j].k, L.wpg);
         before[j + 1] = before[j] + pc[j] * pairs;
     }
     const int64_t total = before[n];
-    L.start[0] = 0;
+    L.start[w0] = j0 * rows;
     int j = 0;
-    for (int q = 1; q < n_wgq; ++q) {
-        const int64_t target = total * q / n_wgq;
+    for (int q = 1; q < n_wg; ++q) {
+        const int64_t target = total * q / n_wg;
         while (j < n - 1 && before[j + 1] <= target) ++j;
         const int64_t p = (target - before[j] + pc[j] - 1) / pc[j];
-        L.start[q] = j * rows + int(std::min<int64_t>(rows, 2 * p));
+        L.start[w0 + q] = (j0 + j) * rows + int(std::min<int64_t>(rows, 2 * p));
     }
-    L.start[n_wgq] = n * rows;
-    L.n_wgq = n_wgq;
 }
 
-// Row cuts, one job per workgroup: n_total workgroups split among the jobs
-// by cost (largest remainder, at least one each); a job's workgroups split
-// its rows evenly at even rows.
-static void set_starts_per_job(KLaunch& L, const int64_t* cost, int n_total) {
-    const int n = L.n_jobs, rows = L.rows, pairs = (rows + 1) / 2;
-    n_total = std::min(kMaxLaunchWgq, std::max(n_total, n));
+// Workgroup ranges of a launch whose jobs come in runs of one source (one
+// activation table): every run gets whole workgroups, in proportion to its
+// cost (largest remainder, at least one each), and no workgroup spans two
+// runs, so a workgroup builds its table once.  One run: the whole launch is
+// cut by cost.
+static void set_starts_by_source(KLaunch& L, int n_total) {
+    const int n = L.n_jobs;
+    std::vector<int> r0;                       // first job of every run
+    for (int j = 0; j < n; ++j)
+        if (j == 0 || L.job[j].src != L.job[j - 1].src) r0.push_back(j);
+    const int R = int(r0.size());
+    r0.push_back(n);
+    n_total = std::min(kMaxLaunchWgq, std::max(n_total, R));
+    std::vector<double> cost(R, 0.0), share(R);
     double C = 0;
-    for (int j = 0; j < n; ++j) C += double(cost[j]);
-    std::vector<int> a(n);
-    std::vector<double> share(n);
+    for (int r = 0; r < R; ++r) {
+        for (int j = r0[r]; j < r0[r + 1]; ++j)
+            cost[r] += double(L.rows) * double(lut_row_cost(L.job[j].k, L.wpg));
+        C += cost[r];
+    }
+    std::vector<int> a(R);
     int sum = 0;
-    for (int j = 0; j < n; ++j) {
-        share[j] = C > 0 ? n_total * double(cost[j]) / C : double(n_total) / n;
-        a[j] = std::max(1, int(share[j]));
-        sum += a[j];
+    for (int r = 0; r < R; ++r) {
+        share[r] = C > 0 ? n_total * cost[r] / C : double(n_total) / R;
+        a[r] = std::max(1, int(share[r]));
+        sum += a[r];
     }
     while (sum > n_total) {
         int b = 0;
-        for (int j = 1; j < n; ++j)
-            if (a[j] > a[b]) b = j;
+        for (int r = 1; r < R; ++r)
+            if (a[r] > a[b]) b = r;
         if (a[b] <= 1) break;
         --a[b];
         --sum;
     }
     while (sum < n_total) {
         int b = 0;
-        for (int j = 1; j < n; ++j)
-            if (share[j] - a[j] > share[b] - a[b]) b = j;
+        for (int r = 1; r < R; ++r)
+            if (share[r] - a[r] > share[b] - a[b]) b = r;
         ++a[b];
         ++sum;
     }
     int w = 0;
-    for (int j = 0; j < n; ++j) {
-        for (int c = 0; c < a[j]; ++c)
-            L.start[w + c] = j * rows + std::min(rows, 2 * int(int64_t(c) * pairs / a[j]));
-        w += a[j];
+    for (int r = 0; r < R; ++r) {
+        cut_jobs(L, r0[r], r0[r + 1], a[r], w);
+        w += a[r];
     }
-    L.start[w] = n * rows;
+    L.start[w] = n * L.rows;
     L.n_wgq = w;
 }
 
-// Pack jobs into launches of at most kMaxLaunchJobs.  contig: one source for
-// all jobs (a workgroup may span several); else one job per workgroup.
-static void pack_launches(std::vector<JobSpec>& js, const KLaunch& proto, bool contig,
+// Pack jobs into launches of at most kMaxLaunchJobs, cut by source
+// (set_starts_by_source); jobs of one source should be adjacent.
+static void pack_launches(std::vector<JobSpec>& js, const KLaunch& proto,
                           std::vector<KLaunch>& out) {
     int64_t all = 0;
     for (auto& j : js) all += j.cost;
@@ -809,20 +819,13 @@ static void pack_launches(std::vector<JobSpec>& js, const KLaunch& proto, bool c
     for (size_t j0 = 0; j0 < js.size(); j0 += kMaxLaunchJobs) {
         const size_t j1 = std::min(js.size(), j0 + kMaxLaunchJobs);
         int64_t part = 0;
-        std::vector<int64_t> cost;
-        for (size_t j = j0; j < j1; ++j) {
-            part += js[j].cost;
-            cost.push_back(js[j].cost);
-        }
+        for (size_t j = j0; j < j1; ++j) part += js[j].cost;
         const int n = std::max(1, int(std::lround(double(target) * double(part) / double(all))));
         out.push_back(proto);
         KLaunch& L = out.back();
         L.n_jobs = int(j1 - j0);
         for (size_t j = j0; j < j1; ++j) L.job[j - j0] = js[j].job;
-        if (contig)
-            set_starts_contig(L, std::min(n, kMaxLaunchWgq));
-        else
-            set_starts_per_job(L, cost.data(), n);
+        set_starts_by_source(L, n);
     }
 }
 
@@ -884,7 +887,7 @@ pm_status gemv_lut(pm_matrix_shape s, int k, const uint32_t* d_planes, size_t ps
     }
     // workgroups per slice: enough to fill the device, at least 32 rows each
     const int target = std::max(1, std::min(kMaxLaunchWgq, lut_wg_target() / S));
-    set_starts_contig(L, std::max(1, std::min(target, (s.rows + 31) / 32)));
+    set_starts_by_source(L, std::max(1, std::min(target, (s.rows + 31) / 32)));
     HIP_TRY(launch_lut(L, false, st));
     if (S > 1) HIP_TRY(launch_sum_slices(jb.out, S, s.rows, d_y, st));
     return PM_OK;
@@ -1117,8 +1120,11 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
                 }
             }
         }
-        // one token: jobs may share workgroups; several tokens: one job each
-        pack_launches(js, gu_proto, n_tokens == 1, L_gu[grp]);
+        // jobs of one token share an activation table: keep them adjacent
+        std::stable_sort(js.begin(), js.end(), [](const JobSpec& a, const JobSpec& b) {
+            return a.job.src < b.job.src;
+        });
+        pack_launches(js, gu_proto, L_gu[grp]);
     }
     {
         std::vector<JobSpec> js;
@@ -1140,7 +1146,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
                 js.push_back(j);
             }
         }
-        pack_launches(js, dn_proto, false, L_dn);
+        pack_launches(js, dn_proto, L_dn);
     }
 
     if (s->have_last) HIP_TRY(hipStreamWaitEvent(compute, s->last_done, 0));

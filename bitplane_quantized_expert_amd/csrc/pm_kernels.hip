@@ -630,7 +630,10 @@ __device__ inline float row_dot_lane(const uint32_t* __restrict__ planes, size_t
 // reads its region, and LDS operations of one wave complete in order.
 constexpr int kRunWords = 32;
 constexpr int kRunTabFloatsMax = 8 << kBits;
-constexpr int kLdsMinK = 5;              // smallest k read through the staged tables
+#ifndef PM_LDS_MIN_K
+#define PM_LDS_MIN_K 1
+#endif
+constexpr int kLdsMinK = PM_LDS_MIN_K;   // smallest k read through the staged tables
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
@@ -695,8 +698,23 @@ __device__ __attribute__((always_inline)) inline float row_dot(
         const float* rowtab = lv_k + ((size_t(o) * (W / 4)) << k);
         if ((reinterpret_cast<uintptr_t>(rowtab) & 15) == 0 &&
             (reinterpret_cast<uintptr_t>(x) & 15) == 0) {
-            static_assert(kLdsMinK == 5, "one case per staged k");
             switch (k) {
+            case 1:
+                if constexpr (kLdsMinK <= 1)
+                    return row_dot_lds<1>(planes, pstride, rowtab, o, W, x, tabs, lane);
+                break;
+            case 2:
+                if constexpr (kLdsMinK <= 2)
+                    return row_dot_lds<2>(planes, pstride, rowtab, o, W, x, tabs, lane);
+                break;
+            case 3:
+                if constexpr (kLdsMinK <= 3)
+                    return row_dot_lds<3>(planes, pstride, rowtab, o, W, x, tabs, lane);
+                break;
+            case 4:
+                if constexpr (kLdsMinK <= 4)
+                    return row_dot_lds<4>(planes, pstride, rowtab, o, W, x, tabs, lane);
+                break;
             case 5: return row_dot_lds<5>(planes, pstride, rowtab, o, W, x, tabs, lane);
             case 6: return row_dot_lds<6>(planes, pstride, rowtab, o, W, x, tabs, lane);
             case 7: return row_dot_lds<7>(planes, pstride, rowtab, o, W, x, tabs, lane);
