@@ -757,20 +757,20 @@ __global__ __launch_bounds__(kBlock) void direct_gateup_kernel(Geom g,
     if (o >= g.inter) return;
     const int W = g.hidden / 32;
     const size_t nb = size_t(g.inter) * (g.hidden / g.group);
-    for (int q = 0; q < it.nuse; ++q) {
-        const int u = list[it.use0 + q];
-        const Use us = uses[u];
-        const float* xt = x + size_t(us.tok) * g.hidden;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            if (!us.direct[m]) continue;
-            const int k = us.k[m];
-            float acc = row_dot(it.planes + g.plane_off[m], g.plane_words,
-                                it.levels + g.level_off[m] + level_offset(nb, k), k, o, W,
-                                g.group / 32, xt, (lds_f32*)tabs[threadIdx.x / kWave], lane);
-            acc = wave_sum(acc);
-            if (lane == kWave - 1) P.gu[(size_t(u) * 2 + m) * P.gu_smax * g.inter + o] = acc;
-        }
+    // one (use, matrix) per step; fields read from memory by index, so no
+    // copy of the use record is indexed in registers
+    for (int qm = 0; qm < 2 * it.nuse; ++qm) {
+        const int m = qm & 1;
+        const int u = list[it.use0 + (qm >> 1)];
+        const Use* up = uses + u;
+        if (!up->direct[m]) continue;
+        const int k = up->k[m];
+        const float* xt = x + size_t(up->tok) * g.hidden;
+        float acc = row_dot(it.planes + g.plane_off[m], g.plane_words,
+                            it.levels + g.level_off[m] + level_offset(nb, k), k, o, W,
+                            g.group / 32, xt, (lds_f32*)tabs[threadIdx.x / kWave], lane);
+        acc = wave_sum(acc);
+        if (lane == kWave - 1) P.gu[(size_t(u) * 2 + m) * P.gu_smax * g.inter + o] = acc;
     }
 }
 
