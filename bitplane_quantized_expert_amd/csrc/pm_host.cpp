@@ -466,6 +466,7 @@ struct Slot {
     const float* h_levels = nullptr;
     hipEvent_t ready = nullptr;    // recorded after the slot's last top-up copy
     bool pending = false;          // a top-up is in flight on the side stream
+    uint64_t read_seq = 0;         // last forward that read the slot (0: none)
 };
 
 struct Workspace {
@@ -492,6 +493,12 @@ struct pm_store {
     hipStream_t side = nullptr;        // the store's own top-up stream
     hipEvent_t last_done = nullptr;    // end of the last forward
     bool have_last = false;
+    // Ends of recent forwards: forward n (n >= 1) records done[n % kDone].
+    // Forwards of one store complete in order, so a reused entry marks a
+    // later forward and waiting on it is still safe.
+    static constexpr int kDone = 8;
+    hipEvent_t done[kDone] = {};
+    uint64_t fwd_seq = 0;              // forwards issued
     Workspace ws;
     int last_first = -1, last_count = 0;
     uint64_t total_planes = 0, total_bytes = 0;
@@ -557,6 +564,8 @@ extern "C" pm_status pm_store_create(pm_expert_shape e, int n_layers, int n_expe
     if (!s->host_fake) {
         hipError_t er = hipStreamCreateWithFlags(&s->side, hipStreamNonBlocking);
         if (er == hipSuccess) er = hipEventCreateWithFlags(&s->last_done, hipEventDisableTiming);
+        for (int i = 0; i < pm_store::kDone && er == hipSuccess; ++i)
+            er = hipEventCreateWithFlags(&s->done[i], hipEventDisableTiming);
         if (er != hipSuccess) {
             pm_store_destroy(s);
             return hip_fail(er, "store stream/event creation");
@@ -586,6 +595,8 @@ extern "C" pm_status pm_store_destroy(pm_store* s) {
         for (hipEvent_t ev : w.ring_ev)
             if (ev) (void)hipEventDestroy(ev);
         if (s->last_done) (void)hipEventDestroy(s->last_done);
+        for (hipEvent_t ev : s->done)
+            if (ev) (void)hipEventDestroy(ev);
         if (s->side) (void)hipStreamDestroy(s->side);
     }
     delete s;
@@ -627,6 +638,14 @@ extern "C" pm_status pm_store_attach_host(pm_store* s, int layer, int expert,
     return PM_OK;
 }
 
+// Whether the last forward that read the slot may still run; *ev is the event
+// that marks its end (or a later forward's).
+static bool slot_reader_running(pm_store* s, const Slot& sl, hipEvent_t* ev) {
+    if (sl.read_seq == 0) return false;
+    *ev = s->done[sl.read_seq % pm_store::kDone];
+    return hipEventQuery(*ev) != hipSuccess;
+}
+
 static pm_status topup_slot(pm_store* s, Slot& sl, int k, hipStream_t side) {
     if (k <= sl.resident) {            // a resident deeper prefix serves it: no copy
         s->last_first = sl.resident;
@@ -643,8 +662,10 @@ static pm_status topup_slot(pm_store* s, Slot& sl, int k, hipStream_t side) {
         std::memcpy(sl.planes + size_t(first) * pw, sl.h_planes + size_t(first) * pw,
                     size_t(k - first) * s->plane_bytes);
     } else {
-        // the copy must not overwrite planes a previous forward may still read
-        if (s->have_last) HIP_TRY(hipStreamWaitEvent(side, s->last_done, 0));
+        // the copy must not overwrite planes a forward may still read: wait
+        // for the last forward that read this slot, unless it has finished
+        hipEvent_t reader = nullptr;
+        if (slot_reader_running(s, sl, &reader)) HIP_TRY(hipStreamWaitEvent(side, reader, 0));
         if (!sl.levels_ready)
             HIP_TRY(hipMemcpyAsync(sl.levels, sl.h_levels, s->level_bytes,
                                    hipMemcpyHostToDevice, side));
@@ -1151,12 +1172,21 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
 
     if (s->have_last) HIP_TRY(hipStreamWaitEvent(compute, s->last_done, 0));
 
-    // ---- top-ups (side stream) for late items
-    for (int i = n_res; i < n_items; ++i) {
-        const int d = order[i];
-        st = topup_slot(s, slot_of_item(d), kneed[d], s->side);
-        if (st) return st;
+    // ---- top-ups (side stream) for late items; copies that must wait for an
+    // earlier forward still reading their slot go last, so that the others
+    // start at once
+    const uint64_t seq = ++s->fwd_seq;
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int i = n_res; i < n_items; ++i) {
+            const int d = order[i];
+            Slot& sl = slot_of_item(d);
+            hipEvent_t ev = nullptr;
+            if (slot_reader_running(s, sl, &ev) != (pass == 1)) continue;
+            st = topup_slot(s, sl, kneed[d], s->side);
+            if (st) return st;
+        }
     }
+
 
     // ---- direct-path work list into the pinned ring, then to the device
     const Use* duses = nullptr;
@@ -1264,6 +1294,8 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     }
     if (s->profiling) HIP_TRY(hipEventRecord(s->prof[3], compute));
     HIP_TRY(hipEventRecord(s->last_done, compute));
+    HIP_TRY(hipEventRecord(s->done[seq % pm_store::kDone], compute));
+    for (int i = 0; i < n_items; ++i) slot_of_item(order[i]).read_seq = seq;
     s->have_last = true;
     return PM_OK;
 }

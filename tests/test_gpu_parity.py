@@ -517,3 +517,48 @@ def test_forward_batch8_grouped_with_topup():
         want, S = oc.token_layer(4, 0, ids[t], w[t], k[t], x[t], rows)
         assert_close(got[t][rows], want, S, f"token {t}")
     st.close()
+
+
+def test_topup_waits_for_an_earlier_reader():
+    """A top-up must not overwrite planes that an earlier forward, still
+    queued or running, reads.  The slot's host source holds another expert's
+    planes, so a copy that ran too early would change the first result."""
+    report("top-up ordering: forward, truncate, forward with top-up, no sync between")
+    wl = synth.WORKLOADS[0]
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    pw = pm.pm_expert_plane_words(e)
+    st = pm.pm_store_create(e, 1, 2)
+    filler = PoolFiller(wl)
+    filler.fill(st, 0, 0)
+    filler.fill(st, 0, 1)
+    torch.cuda.synchronize()
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    pp1, _ = pm.pm_store_slot(st, 0, 1)
+    _, lp0 = pm.pm_store_slot(st, 0, 0)
+    src_p = torch.empty(8 * pw, dtype=torch.int32, pin_memory=True)
+    src_l = torch.empty(pm.pm_expert_levels_floats(e), dtype=torch.float32, pin_memory=True)
+    assert hip.hipMemcpy(ctypes.c_void_p(src_p.data_ptr()), ctypes.c_void_p(pp1),
+                         ctypes.c_size_t(8 * pw * 4), 2) == 0
+    assert hip.hipMemcpy(ctypes.c_void_p(src_l.data_ptr()), ctypes.c_void_p(lp0),
+                         ctypes.c_size_t(src_l.numel() * 4), 2) == 0
+    pm.pm_store_attach_host(st, 0, 0, src_p.data_ptr(), src_l.data_ptr())
+    A = oracle.encode_expert(synth.expert_inputs(wl, 0, 0), wl.group)
+    B = oracle.encode_expert(synth.expert_inputs(wl, 0, 1), wl.group)
+    mixed = {"group": wl.group, "levels": A["levels"],
+             "planes": [np.concatenate([A["planes"][m][:1], B["planes"][m][1:]]) for m in range(3)]}
+    xs = [synth.activation(wl.seed, 0, 0, 0, wl.hidden, step=s) for s in range(2)]
+    ys = [torch.empty((1, wl.hidden), dtype=torch.float32, device="cuda") for _ in range(2)]
+    ids = np.array([[0]], np.int32)
+    w = np.array([[1.0]], np.float32)
+    k = np.array([[[4, 4, 4]]], np.uint8)
+    for rep in range(4):
+        pm.pm_moe_token_forward(st, 0, ids, w, k, dev(xs[0][None]), ys[0])
+        pm.pm_store_truncate(st, 0, 0, 1)
+        pm.pm_moe_token_forward(st, 0, ids, w, k, dev(xs[1][None]), ys[1], flags=pm.PM_AUTO_TOPUP)
+        torch.cuda.synchronize()
+        first = oracle.expert_ffn(A if rep == 0 else mixed, 4, 4, 4, xs[0])
+        second = oracle.expert_ffn(mixed, 4, 4, 4, xs[1])
+        assert_close(host(ys[0])[0], first["y"], first["Sy"], f"rep {rep}: earlier forward")
+        assert_close(host(ys[1])[0], second["y"], second["Sy"], f"rep {rep}: after top-up")
+    st.close()
