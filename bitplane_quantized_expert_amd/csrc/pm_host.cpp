@@ -491,14 +491,14 @@ struct pm_store {
     size_t plane_bytes, level_bytes;   // per plane chunk, per slot levels
     std::vector<Slot> slots;
     hipStream_t side = nullptr;        // the store's own top-up stream
-    hipEvent_t last_done = nullptr;    // end of the last forward
-    bool have_last = false;
-    // Ends of recent forwards: forward n (n >= 1) records done[n % kDone].
-    // Forwards of one store complete in order, so a reused entry marks a
-    // later forward and waiting on it is still safe.
+    // Ends of recent forwards: forward n (n >= 1) records done[n % kDone],
+    // its only event (one more event per forward costs the launch-bound layer
+    // step several microseconds).  Forwards of one store complete in order,
+    // so a reused entry marks a later forward and waiting on it is still safe.
     static constexpr int kDone = 8;
     hipEvent_t done[kDone] = {};
     uint64_t fwd_seq = 0;              // forwards issued
+    hipStream_t last_compute = nullptr;    // stream of the last forward
     Workspace ws;
     int last_first = -1, last_count = 0;
     uint64_t total_planes = 0, total_bytes = 0;
@@ -563,7 +563,6 @@ extern "C" pm_status pm_store_create(pm_expert_shape e, int n_layers, int n_expe
     s->slots.resize(size_t(n_layers) * n_experts);
     if (!s->host_fake) {
         hipError_t er = hipStreamCreateWithFlags(&s->side, hipStreamNonBlocking);
-        if (er == hipSuccess) er = hipEventCreateWithFlags(&s->last_done, hipEventDisableTiming);
         for (int i = 0; i < pm_store::kDone && er == hipSuccess; ++i)
             er = hipEventCreateWithFlags(&s->done[i], hipEventDisableTiming);
         if (er != hipSuccess) {
@@ -594,7 +593,6 @@ extern "C" pm_status pm_store_destroy(pm_store* s) {
         if (w.h_ring) (void)hipHostFree(w.h_ring);
         for (hipEvent_t ev : w.ring_ev)
             if (ev) (void)hipEventDestroy(ev);
-        if (s->last_done) (void)hipEventDestroy(s->last_done);
         for (hipEvent_t ev : s->done)
             if (ev) (void)hipEventDestroy(ev);
         if (s->side) (void)hipStreamDestroy(s->side);
@@ -1170,7 +1168,9 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         pack_launches(js, dn_proto, L_dn);
     }
 
-    if (s->have_last) HIP_TRY(hipStreamWaitEvent(compute, s->last_done, 0));
+    // forwards on one store run in order; on the same stream they already do
+    if (s->fwd_seq > 0 && compute != s->last_compute)
+        HIP_TRY(hipStreamWaitEvent(compute, s->done[s->fwd_seq % pm_store::kDone], 0));
 
     // ---- top-ups (side stream) for late items; copies that must wait for an
     // earlier forward still reading their slot go last, so that the others
@@ -1293,9 +1293,8 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         HIP_TRY(launch_combine_k(C, compute));
     }
     if (s->profiling) HIP_TRY(hipEventRecord(s->prof[3], compute));
-    HIP_TRY(hipEventRecord(s->last_done, compute));
     HIP_TRY(hipEventRecord(s->done[seq % pm_store::kDone], compute));
+    s->last_compute = compute;
     for (int i = 0; i < n_items; ++i) slot_of_item(order[i]).read_seq = seq;
-    s->have_last = true;
     return PM_OK;
 }
