@@ -491,14 +491,21 @@ struct pm_store {
     size_t plane_bytes, level_bytes;   // per plane chunk, per slot levels
     std::vector<Slot> slots;
     hipStream_t side = nullptr;        // the store's own top-up stream
-    // Ends of recent forwards: forward n (n >= 1) records done[n % kDone],
-    // its only event (one more event per forward costs the launch-bound layer
-    // step several microseconds).  Forwards of one store complete in order,
-    // so a reused entry marks a later forward and waiting on it is still safe.
+    // Ends of recent forwards: done[n % kDone] marks the end of forward n
+    // (n >= 1).  A forward records it only when the store has host sources
+    // (a top-up may need it); otherwise it is recorded later on the last
+    // forward's stream, when a forward on another stream or a top-up needs
+    // it, and then marks everything queued there so far.  Every queued event
+    // costs the launch-bound layer step about 3 us.  Forwards of one store
+    // complete in order, so an entry that marks a later forward than the one
+    // asked for is still safe to wait on.
     static constexpr int kDone = 8;
     hipEvent_t done[kDone] = {};
+    uint64_t done_seq[kDone] = {};     // the forward each entry marks the end of
     uint64_t fwd_seq = 0;              // forwards issued
+    uint64_t recorded_seq = 0;         // last forward whose end is recorded
     hipStream_t last_compute = nullptr;    // stream of the last forward
+    bool has_sources = false;          // some slot has a host source
     Workspace ws;
     int last_first = -1, last_count = 0;
     uint64_t total_planes = 0, total_bytes = 0;
@@ -633,14 +640,30 @@ extern "C" pm_status pm_store_attach_host(pm_store* s, int layer, int expert,
     if (!h_planes || !h_levels) return failf(PM_ERR_ARG, "null host source");
     s->slots[i].h_planes = h_planes;
     s->slots[i].h_levels = h_levels;
+    s->has_sources = true;
     return PM_OK;
+}
+
+// The event that marks the end of forward n (1 <= n <= fwd_seq) or of a later
+// forward: its own entry, else the latest recorded end if that is not earlier,
+// else an end recorded now on the last forward's stream.
+static hipEvent_t forward_end(pm_store* s, uint64_t n) {
+    const int e = int(n % pm_store::kDone);
+    if (s->done_seq[e] == n) return s->done[e];
+    if (s->recorded_seq >= n) return s->done[s->recorded_seq % pm_store::kDone];
+    const int f = int(s->fwd_seq % pm_store::kDone);
+    if (hipEventRecord(s->done[f], s->last_compute) == hipSuccess) {
+        s->done_seq[f] = s->fwd_seq;
+        s->recorded_seq = s->fwd_seq;
+    }
+    return s->done[f];
 }
 
 // Whether the last forward that read the slot may still run; *ev is the event
 // that marks its end (or a later forward's).
 static bool slot_reader_running(pm_store* s, const Slot& sl, hipEvent_t* ev) {
     if (sl.read_seq == 0) return false;
-    *ev = s->done[sl.read_seq % pm_store::kDone];
+    *ev = forward_end(s, sl.read_seq);
     return hipEventQuery(*ev) != hipSuccess;
 }
 
@@ -1170,12 +1193,11 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
 
     // forwards on one store run in order; on the same stream they already do
     if (s->fwd_seq > 0 && compute != s->last_compute)
-        HIP_TRY(hipStreamWaitEvent(compute, s->done[s->fwd_seq % pm_store::kDone], 0));
+        HIP_TRY(hipStreamWaitEvent(compute, forward_end(s, s->fwd_seq), 0));
 
     // ---- top-ups (side stream) for late items; copies that must wait for an
     // earlier forward still reading their slot go last, so that the others
     // start at once
-    const uint64_t seq = ++s->fwd_seq;
     for (int pass = 0; pass < 2; ++pass) {
         for (int i = n_res; i < n_items; ++i) {
             const int d = order[i];
@@ -1293,8 +1315,13 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         HIP_TRY(launch_combine_k(C, compute));
     }
     if (s->profiling) HIP_TRY(hipEventRecord(s->prof[3], compute));
-    HIP_TRY(hipEventRecord(s->done[seq % pm_store::kDone], compute));
+    const uint64_t seq = ++s->fwd_seq;
     s->last_compute = compute;
+    if (s->has_sources) {
+        HIP_TRY(hipEventRecord(s->done[seq % pm_store::kDone], compute));
+        s->done_seq[seq % pm_store::kDone] = seq;
+        s->recorded_seq = seq;
+    }
     for (int i = 0; i < n_items; ++i) slot_of_item(order[i]).read_seq = seq;
     return PM_OK;
 }

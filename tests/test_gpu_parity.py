@@ -519,11 +519,15 @@ def test_forward_batch8_grouped_with_topup():
     st.close()
 
 
-def test_topup_waits_for_an_earlier_reader():
+@pytest.mark.parametrize("attach_first", [True, False])
+def test_topup_waits_for_an_earlier_reader(attach_first):
     """A top-up must not overwrite planes that an earlier forward, still
     queued or running, reads.  The slot's host source holds another expert's
-    planes, so a copy that ran too early would change the first result."""
-    report("top-up ordering: forward, truncate, forward with top-up, no sync between")
+    planes, so a copy that ran too early would change the first result.
+    Attached after the first forward, the source finds that forward's end
+    unrecorded (a store without sources records none)."""
+    report(f"top-up ordering (source attached {'before' if attach_first else 'after'} "
+           "the first forward): forward, truncate, forward with top-up, no sync between")
     wl = synth.WORKLOADS[0]
     e = pm.eshape(wl.hidden, wl.inter, wl.group)
     pw = pm.pm_expert_plane_words(e)
@@ -542,20 +546,35 @@ def test_topup_waits_for_an_earlier_reader():
                          ctypes.c_size_t(8 * pw * 4), 2) == 0
     assert hip.hipMemcpy(ctypes.c_void_p(src_l.data_ptr()), ctypes.c_void_p(lp0),
                          ctypes.c_size_t(src_l.numel() * 4), 2) == 0
-    pm.pm_store_attach_host(st, 0, 0, src_p.data_ptr(), src_l.data_ptr())
+    if attach_first:
+        pm.pm_store_attach_host(st, 0, 0, src_p.data_ptr(), src_l.data_ptr())
     A = oracle.encode_expert(synth.expert_inputs(wl, 0, 0), wl.group)
     B = oracle.encode_expert(synth.expert_inputs(wl, 0, 1), wl.group)
     mixed = {"group": wl.group, "levels": A["levels"],
              "planes": [np.concatenate([A["planes"][m][:1], B["planes"][m][1:]]) for m in range(3)]}
     xs = [synth.activation(wl.seed, 0, 0, 0, wl.hidden, step=s) for s in range(2)]
     ys = [torch.empty((1, wl.hidden), dtype=torch.float32, device="cuda") for _ in range(2)]
+    # inputs on the device beforehand: a copy inside the loop would wait for
+    # the first forward and close the window this test is about
+    xd = [dev(x[None]) for x in xs]
+    torch.cuda.synchronize()
     ids = np.array([[0]], np.int32)
     w = np.array([[1.0]], np.float32)
     k = np.array([[[4, 4, 4]]], np.uint8)
+    # a few milliseconds of queued work ahead of the first forward: a copy
+    # that did not wait for it would land before it reads the planes
+    busy = torch.randn(4096, 4096, device="cuda")
     for rep in range(4):
-        pm.pm_moe_token_forward(st, 0, ids, w, k, dev(xs[0][None]), ys[0])
+        for _ in range(4):
+            busy = busy @ busy
+            busy = busy / busy.abs().max()
+        pm.pm_moe_token_forward(st, 0, ids, w, k, xd[0], ys[0],
+                                torch.cuda.current_stream())
+        if rep == 0 and not attach_first:
+            pm.pm_store_attach_host(st, 0, 0, src_p.data_ptr(), src_l.data_ptr())
         pm.pm_store_truncate(st, 0, 0, 1)
-        pm.pm_moe_token_forward(st, 0, ids, w, k, dev(xs[1][None]), ys[1], flags=pm.PM_AUTO_TOPUP)
+        pm.pm_moe_token_forward(st, 0, ids, w, k, xd[1], ys[1], torch.cuda.current_stream(),
+                                flags=pm.PM_AUTO_TOPUP)
         torch.cuda.synchronize()
         first = oracle.expert_ffn(A if rep == 0 else mixed, 4, 4, 4, xs[0])
         second = oracle.expert_ffn(mixed, 4, 4, 4, xs[1])
