@@ -399,6 +399,52 @@ def bench_gemv_by_k(args, torch, pm, synth):
     return {"workload": "gemv-by-k-g128", "results": out}
 
 
+BATCHES = (16, 64, 256)
+
+
+def bench_batches(args, torch, pm, synth, PoolFiller):
+    """Larger batches of one layer (512 experts, 4096/1024, group 128, top-10,
+    allocator prefixes at mean 2.5, all experts resident): the layer step for
+    B tokens through the single-use kernels (LUT per use; shared experts on
+    the direct path) and through the matrix-core path (PM_BATCH_MFMA: uses of
+    one (expert, matrix, k) tiled 16 at a time).  Fresh tokens every step."""
+    wl = synth.WORKLOADS[1]
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    st = pm.pm_store_create(e, 1, wl.n_experts)
+    filler = PoolFiller(wl)
+    for i in range(wl.n_experts):
+        filler.fill(st, 0, i)
+    torch.cuda.synchronize()
+    err = synth.error_profiles(wl.seed, wl.cfg, 0, wl.n_experts)
+    stream = torch.cuda.current_stream()
+    out = []
+    n_steps = 4
+    for B in BATCHES:
+        steps = []
+        for s_ in range(n_steps + 1):
+            lg = np.stack([synth.router_logits(wl.seed, wl.cfg, 0, t % 4096, wl.n_experts,
+                                               step=100 + s_) for t in range(B)])
+            ids, w = pm.pm_route_topk(lg, wl.top_k)
+            kk = pm.pm_allocate_bits(ids, w, err, wl.budget)
+            k3 = np.repeat(kk[:, :, None], 3, axis=2).astype(np.uint8)
+            x = torch.randn(B, wl.hidden, device="cuda")
+            steps.append((ids, w, k3, x, torch.empty_like(x)))
+        res = {"tokens": B}
+        for name, flags in (("single_use", 0), ("mfma", pm.PM_BATCH_MFMA)):
+            ids, w, k3, x, y = steps[0]
+            pm.pm_moe_token_forward(st, 0, ids, w, k3, x, y, stream, flags=flags)
+            el = timed(torch, lambda i: pm.pm_moe_token_forward(
+                st, 0, steps[1 + i][0], steps[1 + i][1], steps[1 + i][2], steps[1 + i][3],
+                steps[1 + i][4], stream, flags=flags), n_steps)
+            res[name + "_ms"] = round(el / n_steps * 1e3, 3)
+        res["tokens_per_s_mfma"] = round(B / (res["mfma_ms"] / 1e3), 1)
+        res["speedup"] = round(res["single_use_ms"] / res["mfma_ms"], 2)
+        log(f"B={B}: {res}")
+        out.append(res)
+    st.close()
+    return {"workload": "moe-layer-e512-h4096-i1024-g128-top10-k2.5-batches", "results": out}
+
+
 ENCODE_ITERS = 25
 
 
@@ -546,12 +592,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="1",
-                    choices=["1", "2", "3", "4", "cache", "encode", "gemv", "all"],
+                    choices=["1", "2", "3", "4", "cache", "encode", "gemv", "batch", "all"],
                     help="1: the one-layer step (the reported line); 2: 60 layers; "
                          "3: k = 4 / 8 / mixed against materialize; 4: B = 8 with top-ups; "
                          "cache: Zipf trace replay through the expert caches (host only); "
                          "encode: K-means encoder from fp32 weights; "
-                         "gemv: pm_expert_gemv alone at k = 1..8")
+                         "gemv: pm_expert_gemv alone at k = 1..8; "
+                         "batch: B = 16/64/256 through single-use kernels and matrix cores")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV"),
                     help="print a summary of rocprofv3 outputs of this benchmark and exit")
     args = ap.parse_args()
@@ -580,8 +627,9 @@ def main():
     if args.workload != "1":
         extra = {"2": bench_sixty_layers, "3": bench_precisions, "4": bench_batch_topup,
                  "encode": lambda a, t, p, s, _: bench_encode(a, t, p, s),
-                 "gemv": lambda a, t, p, s, _: bench_gemv_by_k(a, t, p, s)}
-        for key in (["2", "3", "4", "encode", "gemv"] if args.workload == "all"
+                 "gemv": lambda a, t, p, s, _: bench_gemv_by_k(a, t, p, s),
+                 "batch": bench_batches}
+        for key in (["2", "3", "4", "encode", "gemv", "batch"] if args.workload == "all"
                     else [args.workload]):
             res = extra[key](args, torch, pm, synth, PoolFiller)
             print(json.dumps({"workload_result": res}), flush=True)

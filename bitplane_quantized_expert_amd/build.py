@@ -21,7 +21,8 @@ HIPCC_FLAGS = [
 TARGETS = [
     (os.path.join(PKG, "libpm.so"),
      [os.path.join(PKG, "csrc", "pm_host.cpp"), os.path.join(PKG, "csrc", "pm_cache.cpp"),
-      os.path.join(PKG, "csrc", "pm_kernels.hip"), os.path.join(PKG, "csrc", "pm_encoder.hip")]),
+      os.path.join(PKG, "csrc", "pm_kernels.hip"), os.path.join(PKG, "csrc", "pm_encoder.hip"),
+      os.path.join(PKG, "csrc", "pm_mfma.hip")]),
     (os.path.join(ROOT, "synth", "libpmsynth.so"),
      [os.path.join(ROOT, "synth", "synth_device.hip")]),
 ]

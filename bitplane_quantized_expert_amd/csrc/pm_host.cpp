@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "pm_encoder.h"
+#include "pm_mfma.h"
 #include "pm_error.h"
 #include "pm_internal.h"
 
@@ -972,13 +973,151 @@ static pm_status ensure_workspace(pm_store* s, size_t floats, size_t list_bytes)
     return PM_OK;
 }
 
+// The end of a forward: its sequence number, its stream, the event a later
+// top-up may wait on (only when top-ups are possible) and the slots it read.
+static pm_status finish_forward(pm_store* s, hipStream_t compute, const std::vector<Slot*>& read) {
+    const uint64_t seq = ++s->fwd_seq;
+    s->last_compute = compute;
+    if (s->has_sources) {
+        HIP_TRY(hipEventRecord(s->done[seq % pm_store::kDone], compute));
+        s->done_seq[seq % pm_store::kDone] = seq;
+        s->recorded_seq = seq;
+    }
+    for (Slot* sl : read) sl->read_seq = seq;
+    return PM_OK;
+}
+
+// ---------------------------------------------------------------- batched forward, matrix cores
+// Uses that read one matrix of one expert at one prefix k form tiles of up to
+// 16 (mfma_kernel); one launch per stage and k, then SwiGLU and the combine
+// over all tokens.  Every use keeps its own prefix.
+static pm_status forward_mfma(pm_store* s, int layer, int n_tokens, int top_k,
+                              std::vector<Use>& uses, const std::vector<int>& item_expert,
+                              const std::vector<std::vector<int>>& item_uses,
+                              const std::vector<int>& kneed, const std::vector<char>& late,
+                              const float* d_x, float* d_y, hipStream_t compute) {
+    const Geom& g = s->geom;
+    const int n_uses = n_tokens * top_k, n_items = int(item_expert.size());
+    std::vector<Slot*> slot(n_items);
+    for (int d = 0; d < n_items; ++d)
+        slot[d] = &s->slots[size_t(layer) * s->n_experts + item_expert[d]];
+    for (Use& us : uses)
+        for (int m = 0; m < 3; ++m) {
+            us.direct[m] = 1;
+            us.slices[m] = 1;
+        }
+    // tiles of every stage (0 gate/up, 1 down) and prefix
+    const size_t nb_gu = size_t(g.inter) * (g.hidden / g.group);
+    const size_t nb_dn = size_t(g.hidden) * (g.inter / g.group);
+    std::vector<MTile> tiles[2][kBits + 1];
+    for (int d = 0; d < n_items; ++d) {
+        for (int m = 0; m < 3; ++m) {
+            const int stage = m < 2 ? 0 : 1;
+            for (int k = 1; k <= kBits; ++k) {
+                MTile t{};
+                t.planes = slot[d]->planes + g.plane_off[m];
+                t.lvk = slot[d]->levels + g.level_off[m] + level_offset(m < 2 ? nb_gu : nb_dn, k);
+                t.m = m;
+                for (int u : item_uses[d]) {
+                    if (uses[u].k[m] != k) continue;
+                    t.use[t.n++] = u;
+                    if (t.n == kMfmaTileUses) {
+                        tiles[stage][k].push_back(t);
+                        t.n = 0;
+                    }
+                }
+                if (t.n) tiles[stage][k].push_back(t);
+            }
+        }
+    }
+    size_t n_tiles = 0;
+    for (auto& st2 : tiles)
+        for (auto& v : st2) n_tiles += v.size();
+    const size_t fGU = align256(size_t(n_uses) * 2 * g.inter);
+    const size_t fH = align256(size_t(n_uses) * g.inter);
+    const size_t fY = align256(size_t(n_uses) * g.hidden);
+    const size_t o_tiles = align256(sizeof(Use) * n_uses);
+    const size_t list_bytes = o_tiles + align256(sizeof(MTile) * n_tiles);
+    pm_status st = ensure_workspace(s, fGU + fH + fY, list_bytes);
+    if (st) return st;
+    Partials P{};
+    P.gu = s->ws.d_buf;
+    P.h = s->ws.d_buf + fGU;
+    P.y = s->ws.d_buf + fGU + fH;
+    P.gu_smax = 1;
+    P.dn_smax = 1;
+
+    // forwards on one store run in order; on the same stream they already do
+    if (s->fwd_seq > 0 && compute != s->last_compute)
+        HIP_TRY(hipStreamWaitEvent(compute, forward_end(s, s->fwd_seq), 0));
+    // top-ups of short slots (copies that need no wait first)
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int d = 0; d < n_items; ++d) {
+            if (!late[d]) continue;
+            hipEvent_t ev = nullptr;
+            if (slot_reader_running(s, *slot[d], &ev) != (pass == 1)) continue;
+            st = topup_slot(s, *slot[d], kneed[d], s->side);
+            if (st) return st;
+        }
+    }
+    // uses and tiles through the pinned ring
+    Workspace& w = s->ws;
+    const int rs = w.next;
+    w.next = (w.next + 1) % Workspace::kSlots;
+    HIP_TRY(hipEventSynchronize(w.ring_ev[rs]));
+    char* hb = w.h_ring + size_t(rs) * w.slot_bytes;
+    char* db = w.d_ring + size_t(rs) * w.slot_bytes;
+    std::memcpy(hb, uses.data(), sizeof(Use) * n_uses);
+    size_t off[2][kBits + 1], pos = 0;
+    for (int stage = 0; stage < 2; ++stage)
+        for (int k = 1; k <= kBits; ++k) {
+            off[stage][k] = pos;
+            if (!tiles[stage][k].empty())
+                std::memcpy(hb + o_tiles + pos * sizeof(MTile), tiles[stage][k].data(),
+                            sizeof(MTile) * tiles[stage][k].size());
+            pos += tiles[stage][k].size();
+        }
+    HIP_TRY(hipMemcpyAsync(db, hb, list_bytes, hipMemcpyHostToDevice, compute));
+    HIP_TRY(hipEventRecord(w.ring_ev[rs], compute));
+    const Use* duses = reinterpret_cast<const Use*>(db);
+    const MTile* dtiles = reinterpret_cast<const MTile*>(db + o_tiles);
+    for (int d = 0; d < n_items; ++d) {
+        if (slot[d]->pending) {
+            HIP_TRY(hipStreamWaitEvent(compute, slot[d]->ready, 0));
+            slot[d]->pending = false;
+        }
+    }
+
+    MLaunch L{};
+    L.uses = duses;
+    L.x = d_x;
+    L.P = P;
+    L.pstride = g.plane_words;
+    for (int stage = 0; stage < 2; ++stage) {
+        L.rows = stage == 0 ? g.inter : g.hidden;
+        L.cols = stage == 0 ? g.hidden : g.inter;
+        L.down = stage;
+        for (int k = 1; k <= kBits; ++k) {
+            L.tiles = dtiles + off[stage][k];
+            L.n_tiles = int(tiles[stage][k].size());
+            L.k = k;
+            HIP_TRY(launch_mfma(L, compute));
+        }
+        if (stage == 0) HIP_TRY(launch_swiglu(duses, n_uses, P, g.inter, compute));
+    }
+    HIP_TRY(launch_combine(n_tokens, top_k, g.hidden, duses, P, d_y, compute));
+    return finish_forward(s, compute, slot);
+}
+
 extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, int top_k,
                                           const int32_t* h_ids, const float* h_w,
                                           const uint8_t* h_k, const float* d_x, float* d_y,
                                           void* compute_v, uint32_t flags) {
     if (!s) return failf(PM_ERR_ARG, "null store");
     if (s->host_fake) return failf(PM_ERR_STATE, "a host-backed store cannot compute");
-    if (flags & ~uint32_t(PM_AUTO_TOPUP)) return failf(PM_ERR_ARG, "unknown forward flags");
+    if (flags & ~uint32_t(PM_AUTO_TOPUP | PM_BATCH_MFMA))
+        return failf(PM_ERR_ARG, "unknown forward flags");
+    const bool mfma = flags & PM_BATCH_MFMA;
     if (layer < 0 || layer >= s->n_layers) return failf(PM_ERR_ARG, "layer %d outside store", layer);
     if (n_tokens < 0 || top_k < 1) return failf(PM_ERR_ARG, "n_tokens=%d top_k=%d", n_tokens, top_k);
     if (n_tokens == 0) return PM_OK;
@@ -988,6 +1127,9 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         return failf(PM_ERR_ARG, "top_k=%d above %d", top_k, kMaxLaunchUses);
     hipStream_t compute = (hipStream_t)compute_v;
     const Geom& g = s->geom;
+    if (mfma && (g.group != kMfmaGroup || g.hidden % kMfmaGroup || g.inter % kMfmaGroup))
+        return failf(PM_ERR_SHAPE, "the matrix-core path needs group %d and hidden, inter "
+                     "multiples of %d", kMfmaGroup, kMfmaGroup);
 
     // ---- validate and group uses by expert (order of first appearance)
     const int n_uses = n_tokens * top_k;
@@ -1029,7 +1171,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     std::vector<int> kneed(n_items, 0);
     std::vector<std::array<int, 3>> kmax(n_items, {0, 0, 0});
     for (int d = 0; d < n_items; ++d) {
-        if (int(item_uses[d].size()) > max_uses_per_item())
+        if (!mfma && int(item_uses[d].size()) > max_uses_per_item())
             return failf(PM_ERR_ARG, "expert %d is used %zu times; at most %d per call",
                         item_expert[d], item_uses[d].size(), max_uses_per_item());
         for (int u : item_uses[d])
@@ -1056,6 +1198,9 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     std::vector<int> order(n_items);
     for (int d = 0; d < n_items; ++d) order[d] = d;
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return late[a] < late[b]; });
+    if (mfma)
+        return forward_mfma(s, layer, n_tokens, top_k, uses, item_expert, item_uses, kneed, late,
+                            d_x, d_y, compute);
     int n_res = 0;
     while (n_res < n_items && !late[order[n_res]]) ++n_res;
     auto slot_of_item = [&](int d) -> Slot& {
@@ -1315,13 +1460,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         HIP_TRY(launch_combine_k(C, compute));
     }
     if (s->profiling) HIP_TRY(hipEventRecord(s->prof[3], compute));
-    const uint64_t seq = ++s->fwd_seq;
-    s->last_compute = compute;
-    if (s->has_sources) {
-        HIP_TRY(hipEventRecord(s->done[seq % pm_store::kDone], compute));
-        s->done_seq[seq % pm_store::kDone] = seq;
-        s->recorded_seq = seq;
-    }
-    for (int i = 0; i < n_items; ++i) slot_of_item(order[i]).read_seq = seq;
-    return PM_OK;
+    std::vector<Slot*> read(n_items);
+    for (int i = 0; i < n_items; ++i) read[i] = &slot_of_item(order[i]);
+    return finish_forward(s, compute, read);
 }

@@ -274,9 +274,15 @@ pm_status pm_cache_stats(const pm_cache* c, uint64_t* accesses, uint64_t* hits,
  * flags: PM_AUTO_TOPUP tops up every short slot from its host source on the
  * store's side stream and makes `compute` wait for it (kernels of resident
  * experts are issued first); without it a short slot is PM_ERR_NOT_RESIDENT.
+ * PM_BATCH_MFMA computes on the matrix cores instead (larger batches [T c65:
+ * untested on the pages]): the uses that read one matrix of one expert at one
+ * prefix form tiles of up to 16, each weight is decoded once per tile (its
+ * depth-k node) and multiplied on fp32 MFMA, so the values are the same
+ * products in another summation order.  It needs group 128 and hidden, inter
+ * multiples of 128 (else PM_ERR_SHAPE) and has no limit on uses per expert.
  * The store keeps per-call workspace; calls on one store are serialised on
  * `compute`. */
-enum { PM_AUTO_TOPUP = 1u };
+enum { PM_AUTO_TOPUP = 1u, PM_BATCH_MFMA = 2u };
 pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, int top_k,
                                const int32_t* h_ids, const float* h_w, const uint8_t* h_k,
                                const float* d_x, float* d_y, void* compute, uint32_t flags);

@@ -1,0 +1,180 @@
+"""GPU parity of the matrix-core batch path (PM_BATCH_MFMA) against the CPU
+oracle, through the C ABI: a batch crowded onto few experts (tiles split by
+prefix and by 16 uses, every k from 1 to 8, gate, up and down at different
+prefixes), a full-size 512-expert batch, agreement with the single-use path,
+top-ups, and the shape check."""
+import numpy as np
+import pytest
+import torch
+
+import bitplane_quantized_expert_amd as pm
+import oracle
+import oracle_cases as oc
+import synth
+from synth.pool import PoolFiller
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+ABS = 1e-6
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def report(name):
+    print(f"[gpu case] {name}", flush=True)
+
+
+def assert_close(got, want, scale, what=""):
+    ok = oracle.within_tolerance(got, want, scale, TOL, ABS)
+    if not ok.all():
+        i = int(np.argmin(ok))
+        raise AssertionError(f"{what}: {int((~ok).sum())} outputs out of tolerance; first at {i}: "
+                             f"got {got[i]!r} want {want[i]!r} scale {scale[i]!r}")
+
+
+def layer_batch(wl, n_tokens, top_k, n_exp, step):
+    """Routing of n_tokens fresh tokens restricted to the first n_exp experts."""
+    lg = np.stack([synth.router_logits(wl.seed, wl.cfg, 0, t, wl.n_experts, step=step)
+                   for t in range(n_tokens)])
+    lg[:, n_exp:] = -np.inf
+    ids, w = pm.pm_route_topk(lg, top_k)
+    x = np.stack([synth.activation(wl.seed, wl.cfg, 0, t, wl.hidden, step=step)
+                  for t in range(n_tokens)])
+    return ids, w, x
+
+
+@pytest.fixture(scope="module")
+def store512():
+    wl = synth.WORKLOADS[1]
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    st = pm.pm_store_create(e, 1, wl.n_experts)
+    filler = PoolFiller(wl)
+    filled = set()
+
+    def ensure(ids):
+        for i in np.unique(ids):
+            if int(i) not in filled:
+                filler.fill(st, 0, int(i))
+                filled.add(int(i))
+        torch.cuda.synchronize()
+
+    yield wl, st, ensure
+    st.close()
+
+
+def test_mfma_crowded_batch_all_k(store512):
+    """48 tokens on 8 experts, top-4: about 24 uses per expert, so tiles split
+    by prefix and by 16; every k from 1 to 8, and gate, up and down of one use
+    at different prefixes."""
+    report("PM_BATCH_MFMA: 48 tokens x top-4 on 8 experts, k 1..8 per matrix")
+    wl, st, ensure = store512
+    B, top_k = 48, 4
+    ids, w, x = layer_batch(wl, B, top_k, 8, step=7)
+    ensure(ids)
+    k = np.zeros((B, top_k, 3), np.uint8)
+    for t in range(B):
+        for j in range(top_k):
+            k[t, j] = [(t + j) % 8 + 1, (t + 2 * j + 3) % 8 + 1, (3 * t + j + 5) % 8 + 1]
+    y = torch.empty((B, wl.hidden), dtype=torch.float32, device="cuda")
+    pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y, flags=pm.PM_BATCH_MFMA)
+    got = host(y)
+    rows = oc.sample_rows(wl.hidden, 24, 5)
+    for t in (0, 19, 47):
+        want, S = oc.token_layer(1, 0, ids[t], w[t], k[t], x[t], rows)
+        assert_close(got[t][rows], want, S, f"token {t} k={k[t].tolist()}")
+    # the same call through the single-use path gives the same values, and
+    # a repeat gives the same bits
+    y1 = torch.empty_like(y)
+    pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y1, flags=0)
+    ref = host(y1)
+    assert np.all(np.abs(got - ref) <= 1e-4 * (np.abs(ref).max(axis=1, keepdims=True) + 1e-3))
+    y2 = torch.empty_like(y)
+    pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y2, flags=pm.PM_BATCH_MFMA)
+    assert np.array_equal(host(y2).view(np.uint32), got.view(np.uint32))
+
+
+def test_mfma_full_layer_batch(store512):
+    """64 tokens, top-10 of 512 experts, allocator prefixes (mean 2.5)."""
+    report("PM_BATCH_MFMA: 64 tokens x top-10 of 512 experts, mean k 2.5")
+    wl, st, ensure = store512
+    B = 64
+    ids, w, x = layer_batch(wl, B, wl.top_k, wl.n_experts, step=11)
+    ensure(ids)
+    err = synth.error_profiles(wl.seed, wl.cfg, 0, wl.n_experts)
+    kk = pm.pm_allocate_bits(ids, w, err, wl.budget)
+    k = np.repeat(kk[:, :, None], 3, axis=2).astype(np.uint8)
+    y = torch.empty((B, wl.hidden), dtype=torch.float32, device="cuda")
+    pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y, flags=pm.PM_BATCH_MFMA)
+    got = host(y)
+    rows = oc.sample_rows(wl.hidden, 16, 6)
+    want, S = oc.token_layer(1, 0, ids[0], w[0], k[0], x[0], rows)
+    assert_close(got[0][rows], want, S, "token 0")
+    # every token against the single-use path (another summation order of
+    # the same products)
+    y1 = torch.empty_like(y)
+    pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y1, flags=0)
+    ref = host(y1)
+    assert np.all(np.abs(got - ref) <= 1e-4 * (np.abs(ref).max(axis=1, keepdims=True) + 1e-3))
+
+
+def test_mfma_with_topups_and_shape_check():
+    report("PM_BATCH_MFMA: short slots topped up from pinned host; tiny shape rejected")
+    wl = synth.WORKLOADS[1]
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    pw = pm.pm_expert_plane_words(e)
+    st = pm.pm_store_create(e, 1, 4)
+    filler = PoolFiller(wl)
+    srcs = []
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    for i in range(4):
+        filler.fill(st, 0, i)
+        torch.cuda.synchronize()
+        pp, lp = pm.pm_store_slot(st, 0, i)
+        sp = torch.empty(8 * pw, dtype=torch.int32, pin_memory=True)
+        sl = torch.empty(pm.pm_expert_levels_floats(e), dtype=torch.float32, pin_memory=True)
+        assert hip.hipMemcpy(ctypes.c_void_p(sp.data_ptr()), ctypes.c_void_p(pp),
+                             ctypes.c_size_t(8 * pw * 4), 2) == 0
+        assert hip.hipMemcpy(ctypes.c_void_p(sl.data_ptr()), ctypes.c_void_p(lp),
+                             ctypes.c_size_t(sl.numel() * 4), 2) == 0
+        pm.pm_store_attach_host(st, 0, i, sp.data_ptr(), sl.data_ptr())
+        srcs.append((sp, sl))
+    B = 20
+    ids = np.array([[t % 4, (t + 1) % 4] for t in range(B)], np.int32)
+    w = np.full((B, 2), 0.5, np.float32)
+    k = np.array([[[2, 3, 2], [4, 1, 5]] for _ in range(B)], np.uint8)
+    x = np.stack([synth.activation(wl.seed, 1, 0, t, wl.hidden, step=3) for t in range(B)])
+    for i in range(4):
+        pm.pm_store_truncate(st, 0, i, 1)
+    y = torch.empty((B, wl.hidden), dtype=torch.float32, device="cuda")
+    with pytest.raises(pm.PMError) as ei:
+        pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y, flags=pm.PM_BATCH_MFMA)
+    assert ei.value.status == pm.PM_ERR_NOT_RESIDENT
+    pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y,
+                            flags=pm.PM_BATCH_MFMA | pm.PM_AUTO_TOPUP)
+    got = host(y)
+    assert all(pm.pm_store_resident(st, 0, i) == 5 for i in range(4))
+    rows = oc.sample_rows(wl.hidden, 12, 8)
+    for t in (0, 19):
+        want, S = oc.token_layer(1, 0, ids[t], w[t], k[t], x[t], rows)
+        assert_close(got[t][rows], want, S, f"token {t}")
+    st.close()
+    tiny = synth.WORKLOADS[0]
+    e0 = pm.eshape(tiny.hidden, tiny.inter, tiny.group)
+    st0 = pm.pm_store_create(e0, 1, 1)
+    PoolFiller(tiny).fill(st0, 0, 0)
+    y0 = torch.empty((1, tiny.hidden), dtype=torch.float32, device="cuda")
+    with pytest.raises(pm.PMError) as ei:
+        pm.pm_moe_token_forward(st0, 0, np.array([[0]], np.int32), np.array([[1.0]], np.float32),
+                                np.array([[[2, 2, 2]]], np.uint8),
+                                dev(synth.activation(tiny.seed, 0, 0, 0, tiny.hidden)[None]), y0,
+                                flags=pm.PM_BATCH_MFMA)
+    assert ei.value.status == pm.PM_ERR_SHAPE
+    st0.close()
