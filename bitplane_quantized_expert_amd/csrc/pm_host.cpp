@@ -775,7 +775,6 @@ static int lut_wg_target() {
 namespace {
 struct JobSpec {                       // a LUT job before it is packed into a launch
     KJob job;
-    int64_t cost;                      // rows * lut_row_cost
 };
 }  // namespace
 
@@ -856,14 +855,11 @@ static void set_starts_by_source(KLaunch& L, int n_total) {
 // (set_starts_by_source); jobs of one source should be adjacent.
 static void pack_launches(std::vector<JobSpec>& js, const KLaunch& proto,
                           std::vector<KLaunch>& out) {
-    int64_t all = 0;
-    for (auto& j : js) all += j.cost;
-    const int target = std::max(1, std::min(kMaxLaunchWgq, lut_wg_target() / proto.S));
+    // the launches of one stage run one after another: each takes the whole
+    // target (one workgroup per compute unit)
+    const int n = std::max(1, std::min(kMaxLaunchWgq, lut_wg_target() / proto.S));
     for (size_t j0 = 0; j0 < js.size(); j0 += kMaxLaunchJobs) {
         const size_t j1 = std::min(js.size(), j0 + kMaxLaunchJobs);
-        int64_t part = 0;
-        for (size_t j = j0; j < j1; ++j) part += js[j].cost;
-        const int n = std::max(1, int(std::lround(double(target) * double(part) / double(all))));
         out.push_back(proto);
         KLaunch& L = out.back();
         L.n_jobs = int(j1 - j0);
@@ -988,6 +984,56 @@ static pm_status finish_forward(pm_store* s, hipStream_t compute, const std::vec
 }
 
 // ---------------------------------------------------------------- batched forward, matrix cores
+#ifndef PM_TILE_MIN_USES
+#define PM_TILE_MIN_USES 6
+#endif
+// In the default forward the uses that read one matrix of one expert at one
+// prefix go to the matrix cores from this many on (fewer: a LUT job each, or
+// the direct kernels)
+constexpr int kTileMinUses = PM_TILE_MIN_USES;
+
+// The matrix-core tiles of one expert (slot) for matrices m0..m1-1: per
+// prefix k, the uses that read matrix m at k, 16 at a time, when at least
+// min_uses of them do.  Their (use, matrix) is marked 2 (tile, one slice).
+static void add_tiles(std::vector<Use>& uses, const std::vector<int>& item_uses,
+                      const Slot& sl, const Geom& g, int m0, int m1, int min_uses,
+                      std::vector<MTile> (&out)[kBits + 1]) {
+    const size_t nb_gu = size_t(g.inter) * (g.hidden / g.group);
+    const size_t nb_dn = size_t(g.hidden) * (g.inter / g.group);
+    for (int m = m0; m < m1; ++m) {
+        for (int k = 1; k <= kBits; ++k) {
+            int count = 0;
+            for (int u : item_uses) count += uses[u].k[m] == k;
+            if (count == 0 || count < min_uses) continue;
+            MTile t{};
+            t.planes = sl.planes + g.plane_off[m];
+            t.lvk = sl.levels + g.level_off[m] + level_offset(m < 2 ? nb_gu : nb_dn, k);
+            t.m = m;
+            for (int u : item_uses) {
+                if (uses[u].k[m] != k) continue;
+                uses[u].direct[m] = 2;
+                uses[u].slices[m] = 1;
+                t.use[t.n++] = u;
+                if (t.n == kMfmaTileUses) {
+                    out[k].push_back(t);
+                    t.n = 0;
+                }
+            }
+            if (t.n) out[k].push_back(t);
+        }
+    }
+}
+
+static pm_status launch_tiles(MLaunch L, const MTile* d_tiles, const size_t* off,
+                              const std::vector<MTile> (&tiles)[kBits + 1], hipStream_t st) {
+    for (int k = 1; k <= kBits; ++k) {
+        L.tiles = d_tiles + off[k];
+        L.n_tiles = int(tiles[k].size());
+        L.k = k;
+        HIP_TRY(launch_mfma(L, st));
+    }
+    return PM_OK;
+}
 // Uses that read one matrix of one expert at one prefix k form tiles of up to
 // 16 (mfma_kernel); one launch per stage and k, then SwiGLU and the combine
 // over all tokens.  Every use keeps its own prefix.
@@ -1007,28 +1053,10 @@ static pm_status forward_mfma(pm_store* s, int layer, int n_tokens, int top_k,
             us.slices[m] = 1;
         }
     // tiles of every stage (0 gate/up, 1 down) and prefix
-    const size_t nb_gu = size_t(g.inter) * (g.hidden / g.group);
-    const size_t nb_dn = size_t(g.hidden) * (g.inter / g.group);
     std::vector<MTile> tiles[2][kBits + 1];
     for (int d = 0; d < n_items; ++d) {
-        for (int m = 0; m < 3; ++m) {
-            const int stage = m < 2 ? 0 : 1;
-            for (int k = 1; k <= kBits; ++k) {
-                MTile t{};
-                t.planes = slot[d]->planes + g.plane_off[m];
-                t.lvk = slot[d]->levels + g.level_off[m] + level_offset(m < 2 ? nb_gu : nb_dn, k);
-                t.m = m;
-                for (int u : item_uses[d]) {
-                    if (uses[u].k[m] != k) continue;
-                    t.use[t.n++] = u;
-                    if (t.n == kMfmaTileUses) {
-                        tiles[stage][k].push_back(t);
-                        t.n = 0;
-                    }
-                }
-                if (t.n) tiles[stage][k].push_back(t);
-            }
-        }
+        add_tiles(uses, item_uses[d], *slot[d], g, 0, 2, 1, tiles[0]);
+        add_tiles(uses, item_uses[d], *slot[d], g, 2, 3, 1, tiles[1]);
     }
     size_t n_tiles = 0;
     for (auto& st2 : tiles)
@@ -1097,12 +1125,8 @@ static pm_status forward_mfma(pm_store* s, int layer, int n_tokens, int top_k,
         L.rows = stage == 0 ? g.inter : g.hidden;
         L.cols = stage == 0 ? g.hidden : g.inter;
         L.down = stage;
-        for (int k = 1; k <= kBits; ++k) {
-            L.tiles = dtiles + off[stage][k];
-            L.n_tiles = int(tiles[stage][k].size());
-            L.k = k;
-            HIP_TRY(launch_mfma(L, compute));
-        }
+        st = launch_tiles(L, dtiles, off[stage], tiles[stage], compute);
+        if (st) return st;
         if (stage == 0) HIP_TRY(launch_swiglu(duses, n_uses, P, g.inter, compute));
     }
     HIP_TRY(launch_combine(n_tokens, top_k, g.hidden, duses, P, d_y, compute));
@@ -1132,6 +1156,9 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
                      "multiples of %d", kMfmaGroup, kMfmaGroup);
 
     // ---- validate and group uses by expert (order of first appearance)
+    if (int64_t(n_tokens) * top_k > kMaxCallUses)
+        return failf(PM_ERR_ARG, "%d tokens x top-%d: more than %d uses in one call", n_tokens,
+                     top_k, kMaxCallUses);
     const int n_uses = n_tokens * top_k;
     std::vector<Use> uses(n_uses);
     std::map<int, int> item_of;
@@ -1171,9 +1198,6 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     std::vector<int> kneed(n_items, 0);
     std::vector<std::array<int, 3>> kmax(n_items, {0, 0, 0});
     for (int d = 0; d < n_items; ++d) {
-        if (!mfma && int(item_uses[d].size()) > max_uses_per_item())
-            return failf(PM_ERR_ARG, "expert %d is used %zu times; at most %d per call",
-                        item_expert[d], item_uses[d].size(), max_uses_per_item());
         for (int u : item_uses[d])
             for (int m = 0; m < 3; ++m) kmax[d][m] = std::max(kmax[d][m], uses[u].k[m]);
         kneed[d] = std::max(kmax[d][0], std::max(kmax[d][1], kmax[d][2]));
@@ -1181,7 +1205,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     // ---- residency: every short slot must be topped up (or the call fails)
     std::vector<char> late(n_items, 0);
     for (int d = 0; d < n_items; ++d) {
-        const Slot& sl = s->slots[size_t(layer) * s->n_experts + item_expert[d]];
+        Slot& sl = s->slots[size_t(layer) * s->n_experts + item_expert[d]];
         const bool ok = sl.planes && sl.levels_ready && sl.resident >= kneed[d];
         if (!ok) {
             if (!(flags & PM_AUTO_TOPUP))
@@ -1191,6 +1215,9 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
             if (!sl.h_planes || !sl.h_levels)
                 return failf(PM_ERR_STATE, "expert (%d, %d) is short and has no host source",
                             layer, item_expert[d]);
+            // the work lists take the slot's addresses before its top-up runs
+            pm_status st = ensure_slot(s, sl);
+            if (st) return st;
             late[d] = 1;
         }
     }
@@ -1207,8 +1234,27 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         return s->slots[size_t(layer) * s->n_experts + item_expert[d]];
     };
 
-    // ---- path of every (use, matrix): LUT for an unshared expert at k <= 5
-    // when the columns split into 1024-column slices (at most 15), else direct
+    // ---- the uses that read one matrix of one expert at one prefix go to
+    // the matrix-core tiles when there are at least kTileMinUses of them and
+    // the shape allows (marked 2: one slice, h by the SwiGLU kernel)
+    const bool tile_shape = g.group == kMfmaGroup && g.hidden % kMfmaGroup == 0 &&
+                            g.inter % kMfmaGroup == 0;
+    std::vector<MTile> t_gu[2][kBits + 1], t_dn[kBits + 1];
+    size_t n_tiles = 0;
+    if (tile_shape) {
+        for (int i = 0; i < n_items; ++i) {
+            const int d = order[i];
+            if (int(item_uses[d].size()) < kTileMinUses) continue;
+            add_tiles(uses, item_uses[d], slot_of_item(d), g, 0, 2, kTileMinUses,
+                      t_gu[i < n_res ? 0 : 1]);
+            add_tiles(uses, item_uses[d], slot_of_item(d), g, 2, 3, kTileMinUses, t_dn);
+        }
+        for (int k = 1; k <= kBits; ++k)
+            n_tiles += t_gu[0][k].size() + t_gu[1][k].size() + t_dn[k].size();
+    }
+
+    // ---- path of every (use, matrix) outside the tiles: LUT at k <= 5 when
+    // the columns split into 1024-column slices (at most 15), else direct
     // the LUT path takes rows in pairs (an even number of rows per matrix)
     // and blocks of kLutGroup inputs
     const bool gu_lut_shape = g.hidden % kSliceCols == 0 && g.group == kLutGroup &&
@@ -1218,13 +1264,13 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     const int S_gu = gu_lut_shape ? g.hidden / kSliceCols : 1;
     const int S_dn = dn_lut_shape ? g.inter / kSliceCols : 1;
     for (int d = 0; d < n_items; ++d) {
-        const bool alone = item_uses[d].size() == 1;
         for (int u : item_uses[d]) {
             for (int m = 0; m < 3; ++m) {
+                if (uses[u].direct[m] == 2) continue;
                 const bool shape_ok = m < 2 ? gu_lut_shape : dn_lut_shape;
                 const pm_matrix_shape ms = m < 2 ? pm_matrix_shape{g.inter, g.hidden, g.group}
                                                  : pm_matrix_shape{g.hidden, g.inter, g.group};
-                const bool lut = alone && shape_ok && uses[u].k[m] <= kLutMaxK &&
+                const bool lut = shape_ok && uses[u].k[m] <= kLutMaxK &&
                                  lut_offsets_fit(ms, uses[u].k[m], g.plane_words);
                 uses[u].direct[m] = lut ? 0 : 1;
                 uses[u].slices[m] = lut ? (m < 2 ? S_gu : S_dn) : 1;
@@ -1242,19 +1288,21 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         const int i0 = grp == 0 ? 0 : n_res, i1 = grp == 0 ? n_res : n_items;
         for (int i = i0; i < i1; ++i) {
             bool any = false;
-            for (int u : item_uses[order[i]]) any |= uses[u].direct[0] || uses[u].direct[1];
+            for (int u : item_uses[order[i]]) any |= uses[u].direct[0] == 1 || uses[u].direct[1] == 1;
             if (any) dir_gu[grp].push_back(i);
         }
     }
     for (int i = 0; i < n_items; ++i) {
         bool any = false;
-        for (int u : item_uses[order[i]]) any |= uses[u].direct[2] != 0;
+        for (int u : item_uses[order[i]]) any |= uses[u].direct[2] == 1;
         if (any) dir_dn.push_back(i);
     }
     const size_t n_dir = dir_gu[0].size() + dir_gu[1].size() + dir_dn.size();
-    const size_t list_bytes = n_dir == 0 ? 0
+    const bool upload = n_dir > 0 || n_tiles > 0;
+    const size_t list_bytes = !upload ? 0
                               : align256(sizeof(Item) * n_items) + align256(sizeof(Use) * n_uses) +
-                                    align256(sizeof(int32_t) * n_uses) + align256(sizeof(Item) * n_dir);
+                                    align256(sizeof(int32_t) * n_uses) +
+                                    align256(sizeof(Item) * n_dir) + align256(sizeof(MTile) * n_tiles);
     pm_status st = ensure_workspace(s, fGU + fH + fY, list_bytes);
     if (st) return st;
     Partials P;
@@ -1302,7 +1350,6 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
                     j.job.out = P.gu + (size_t(u) * 2 + m) * S_gu * g.inter;
                     j.job.src = int16_t(uses[u].tok);
                     j.job.k = int8_t(k);
-                    j.cost = int64_t(g.inter) * lut_row_cost(k, g.group / 32);
                     js.push_back(j);
                 }
             }
@@ -1329,7 +1376,6 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
                 j.job.src = int16_t(u);
                 j.job.k = int8_t(k);
                 j.job.gsl = uint8_t(uses[u].slices[0] | (uses[u].slices[1] << 4));
-                j.cost = int64_t(g.hidden) * lut_row_cost(k, g.group / 32);
                 js.push_back(j);
             }
         }
@@ -1359,7 +1405,9 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     const Use* duses = nullptr;
     const int32_t* dlist = nullptr;
     const Item* ddir = nullptr;
-    if (n_dir > 0) {
+    const MTile* dtiles = nullptr;
+    size_t off_gu[2][kBits + 1] = {}, off_dn[kBits + 1] = {};
+    if (upload) {
         Workspace& w = s->ws;
         const int rs = w.next;
         w.next = (w.next + 1) % Workspace::kSlots;
@@ -1376,6 +1424,20 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         const size_t o_uses = carve(sizeof(Use) * n_uses);
         const size_t o_list = carve(sizeof(int32_t) * n_uses);
         const size_t o_dir = carve(sizeof(Item) * n_dir);
+        const size_t o_tiles = carve(sizeof(MTile) * n_tiles);
+        size_t tpos = 0;
+        auto put = [&](const std::vector<MTile>& v) {
+            const size_t at = tpos;
+            if (!v.empty())
+                std::memcpy(hb + o_tiles + tpos * sizeof(MTile), v.data(), sizeof(MTile) * v.size());
+            tpos += v.size();
+            return at;
+        };
+        for (int k = 1; k <= kBits; ++k) {
+            off_gu[0][k] = put(t_gu[0][k]);
+            off_gu[1][k] = put(t_gu[1][k]);
+            off_dn[k] = put(t_dn[k]);
+        }
         Item* hitems = reinterpret_cast<Item*>(hb + o_items);
         int32_t* hlist = reinterpret_cast<int32_t*>(hb + o_list);
         int lpos = 0;
@@ -1401,7 +1463,24 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         duses = reinterpret_cast<const Use*>(db + o_uses);
         dlist = reinterpret_cast<const int32_t*>(db + o_list);
         ddir = reinterpret_cast<const Item*>(db + o_dir);
+        dtiles = reinterpret_cast<const MTile*>(db + o_tiles);
     }
+    MLaunch TL{};
+    TL.uses = duses;
+    TL.x = d_x;
+    TL.P = P;
+    TL.pstride = g.plane_words;
+    auto tiles_of = [&](const std::vector<MTile> (&v)[kBits + 1], const size_t* off, int down) {
+        TL.rows = down ? g.hidden : g.inter;
+        TL.cols = down ? g.inter : g.hidden;
+        TL.down = down;
+        return launch_tiles(TL, dtiles, off, v, compute);
+    };
+    auto any_tiles = [](const std::vector<MTile> (&v)[kBits + 1]) {
+        for (const auto& t : v)
+            if (!t.empty()) return true;
+        return false;
+    };
     const size_t d_gu0 = dir_gu[0].size(), d_gu1 = dir_gu[1].size();
 
     // ---- kernels
@@ -1414,7 +1493,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         }
     }
     // a gate/up stage of one LUT launch is timed by the launch itself
-    const bool gu_single = L_gu[0].size() == 1 && d_gu0 == 0 && n_res == n_items;
+    const bool gu_single = L_gu[0].size() == 1 && d_gu0 == 0 && n_res == n_items && n_tiles == 0;
     if (s->profiling && !gu_single) HIP_TRY(hipEventRecord(s->prof[0], compute));
     for (const KLaunch& L : L_gu[0]) {
         if (s->profiling && gu_single)
@@ -1423,6 +1502,10 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
             HIP_TRY(launch_lut(L, false, compute));
     }
     if (d_gu0) HIP_TRY(launch_direct_gateup(g, ddir, int(d_gu0), duses, dlist, d_x, P, compute));
+    if (any_tiles(t_gu[0])) {
+        st = tiles_of(t_gu[0], off_gu[0], 0);
+        if (st) return st;
+    }
     if (n_res < n_items) {
         for (int i = n_res; i < n_items; ++i) {
             Slot& sl = slot_of_item(order[i]);
@@ -1433,12 +1516,21 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         if (d_gu1)
             HIP_TRY(launch_direct_gateup(g, ddir + d_gu0, int(d_gu1), duses, dlist, d_x, P,
                                          compute));
+        if (any_tiles(t_gu[1])) {
+            st = tiles_of(t_gu[1], off_gu[1], 0);
+            if (st) return st;
+        }
     }
     if (s->profiling && !gu_single) HIP_TRY(hipEventRecord(s->prof[1], compute));
-    if (!dir_dn.empty()) {
+    if (!dir_dn.empty() || any_tiles(t_dn)) {
         HIP_TRY(launch_swiglu(duses, n_uses, P, g.inter, compute));
-        HIP_TRY(launch_direct_down(g, ddir + d_gu0 + d_gu1, int(dir_dn.size()), duses, dlist, P,
-                                   compute));
+        if (!dir_dn.empty())
+            HIP_TRY(launch_direct_down(g, ddir + d_gu0 + d_gu1, int(dir_dn.size()), duses, dlist,
+                                       P, compute));
+        if (any_tiles(t_dn)) {
+            st = tiles_of(t_dn, off_dn, 1);
+            if (st) return st;
+        }
     }
     for (const KLaunch& L : L_dn) HIP_TRY(launch_lut(L, true, compute));
     if (s->profiling) HIP_TRY(hipEventRecord(s->prof[2], compute));

@@ -39,8 +39,9 @@ struct Item {
 
 // A use: token `tok` reads the expert in routing slot `slot` with weight w.
 // Its index is tok * top_k + slot.  slices[m] is the number of partial sums
-// the stage of matrix m leaves for it (1 on the direct path, one per
-// 1024-column slice on the LUT path); direct[m] marks the direct path.
+// the stage of matrix m leaves for it (one per 1024-column slice on the LUT
+// path, else 1); direct[m] is its path: 0 LUT job, 1 direct kernels, 2 a
+// matrix-core tile.
 struct Use {
     int32_t k[3];
     float w;
@@ -87,6 +88,8 @@ constexpr int kGemvLutMaxK = 4;
 
 // LUT-path launch description, passed as kernel arguments (no upload).
 constexpr int kMaxLaunchJobs = 64;
+// Uses in one forward call: a job names its token or use in 16 bits.
+constexpr int kMaxCallUses = 32767;
 struct KJob {                      // one matrix of one use
     const uint32_t* planes;        // plane 0, row 0
     const float* lvk;              // depth-k nodes
@@ -171,8 +174,5 @@ hipError_t launch_swiglu(const Use* uses, int n_uses, Partials P, int inter, hip
 // y[t][o] = sum_j w[t][j] * sum_s Y[t*top_k + j][s][o], slots then slices in order.
 hipError_t launch_combine(int n_tokens, int top_k, int hidden, const Use* uses, Partials P,
                           float* y, hipStream_t st);
-
-// Largest number of uses of one expert in one call.
-int max_uses_per_item();
 
 }  // namespace pm

@@ -763,7 +763,7 @@ __global__ __launch_bounds__(kBlock) void direct_gateup_kernel(Geom g,
         const int m = qm & 1;
         const int u = list[it.use0 + (qm >> 1)];
         const Use* up = uses + u;
-        if (!up->direct[m]) continue;
+        if (up->direct[m] != 1) continue;      // 0: LUT job, 2: tile
         const int k = up->k[m];
         const float* xt = x + size_t(up->tok) * g.hidden;
         float acc = row_dot(it.planes + g.plane_off[m], g.plane_words,
@@ -788,7 +788,7 @@ __global__ __launch_bounds__(kBlock) void swiglu_kernel(const Use* __restrict__ 
     if (i >= size_t(n_uses) * inter) return;
     const int u = int(i / inter), c = int(i % inter);
     const Use us = uses[u];
-    if (!us.direct[2]) return;
+    if (!us.direct[2]) return;                   // h of the direct and tile paths
     P.h[i] = silu_mul(gu_sum(P, us, u, 0, inter, c), gu_sum(P, us, u, 1, inter, c));
 }
 
@@ -807,7 +807,7 @@ __global__ __launch_bounds__(kBlock) void direct_down_kernel(Geom g, const Item*
     for (int q = 0; q < it.nuse; ++q) {
         const int u = list[it.use0 + q];
         const Use us = uses[u];
-        if (!us.direct[2]) continue;
+        if (us.direct[2] != 1) continue;
         const int k = us.k[2];
         float acc = row_dot(it.planes + g.plane_off[2], g.plane_words,
                             it.levels + g.level_off[2] + level_offset(nb, k), k, o, W,
@@ -992,8 +992,6 @@ __global__ __launch_bounds__(kBlock) void gemv_fp16_kernel(int rows, int cols,
 inline unsigned grid_for(size_t n, int per) { return unsigned((n + per - 1) / per); }
 
 }  // namespace
-
-int max_uses_per_item() { return 64; }
 
 hipError_t launch_gemv(int rows, int cols, int group, int k, const uint32_t* planes,
                        size_t pstride, const float* levels, const float* x, float* y,

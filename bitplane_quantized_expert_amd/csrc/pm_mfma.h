@@ -24,8 +24,9 @@ struct MTile {
 };
 
 // One launch: tiles of one prefix k and one stage.  Gate/up: the source of
-// use u is x + uses[u].tok * cols, its output P.gu + (2u + m) * rows (one
-// slice).  Down: the source is P.h + u * cols, the output P.y + u * rows.
+// use u is x + uses[u].tok * cols, its output slice 0 of P.gu, at
+// (2u + m) * gu_smax * rows.  Down: the source is P.h + u * cols, the output
+// slice 0 of P.y, at u * dn_smax * rows.
 struct MLaunch {
     const MTile* tiles;
     int32_t n_tiles, k, rows, cols;

@@ -114,7 +114,8 @@ __global__ __launch_bounds__(256) void mfma_kernel(const MLaunch L) {
     }
     if (i < n) {
         const int u = tile.use[i];
-        float* out = L.down ? L.P.y + size_t(u) * L.rows : L.P.gu + (size_t(u) * 2 + m) * L.rows;
+        float* out = L.down ? L.P.y + size_t(u) * L.P.dn_smax * L.rows
+                            : L.P.gu + (size_t(u) * 2 + m) * L.P.gu_smax * L.rows;
 #pragma unroll
         for (int r = 0; r < 4; ++r) out[wrow + 4 * q + r] = acc[r];
     }

@@ -264,22 +264,26 @@ pm_status pm_cache_stats(const pm_cache* c, uint64_t* accesses, uint64_t* hits,
  * One MoE layer for n_tokens tokens:
  *   y[t] = sum_j w[t][j] * W_down(k2) (silu(W_gate(k0) x[t]) * W_up(k1) x[t])
  * with expert ids[t][j] read at prefixes h_k[t][j][0..2] (gate, up, down)
- * [T c4, c37; Abs].  Tokens that share an expert are grouped: its planes are
- * read once up to the largest prefix any of them needs, and each token stops
- * at its own prefix [Abs; T c25].
+ * [T c4, c37; Abs].  Tokens that share an expert are grouped: the store
+ * tops it up once, to the largest prefix any of them needs, and each token
+ * stops at its own prefix [Abs; T c25].  Each (use, matrix) runs as an
+ * activation-LUT job (k <= 5 on the 1024-column grid) or on the direct
+ * kernels; the uses that read one matrix of one expert at one prefix go to
+ * the matrix-core tiles below when there are at least 6 of them.
  *   h_ids int32 [n_tokens][top_k], h_w fp32 [n_tokens][top_k],
  *   h_k uint8 [n_tokens][top_k][3] -- host memory, read before return.
  *   d_x fp32 [n_tokens][hidden] (16-byte aligned), d_y fp32 [n_tokens][hidden]
- *   (overwritten).
+ *   (overwritten).  At most 32767 uses (n_tokens * top_k) per call, else
+ *   PM_ERR_ARG.
  * flags: PM_AUTO_TOPUP tops up every short slot from its host source on the
  * store's side stream and makes `compute` wait for it (kernels of resident
  * experts are issued first); without it a short slot is PM_ERR_NOT_RESIDENT.
- * PM_BATCH_MFMA computes on the matrix cores instead (larger batches [T c65:
+ * PM_BATCH_MFMA puts every use on the matrix cores (larger batches [T c65:
  * untested on the pages]): the uses that read one matrix of one expert at one
  * prefix form tiles of up to 16, each weight is decoded once per tile (its
  * depth-k node) and multiplied on fp32 MFMA, so the values are the same
  * products in another summation order.  It needs group 128 and hidden, inter
- * multiples of 128 (else PM_ERR_SHAPE) and has no limit on uses per expert.
+ * multiples of 128 (else PM_ERR_SHAPE).
  * The store keeps per-call workspace; calls on one store are serialised on
  * `compute`. */
 enum { PM_AUTO_TOPUP = 1u, PM_BATCH_MFMA = 2u };

@@ -95,6 +95,11 @@ def test_mfma_crowded_batch_all_k(store512):
     pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y1, flags=0)
     ref = host(y1)
     assert np.all(np.abs(got - ref) <= 1e-4 * (np.abs(ref).max(axis=1, keepdims=True) + 1e-3))
+    # the default forward (these experts carry enough uses for its tiles)
+    # against the oracle as well
+    for t in (0, 47):
+        want, S = oc.token_layer(1, 0, ids[t], w[t], k[t], x[t], rows)
+        assert_close(ref[t][rows], want, S, f"default path, token {t}")
     y2 = torch.empty_like(y)
     pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y2, flags=pm.PM_BATCH_MFMA)
     assert np.array_equal(host(y2).view(np.uint32), got.view(np.uint32))
@@ -177,4 +182,12 @@ def test_mfma_with_topups_and_shape_check():
                                 dev(synth.activation(tiny.seed, 0, 0, 0, tiny.hidden)[None]), y0,
                                 flags=pm.PM_BATCH_MFMA)
     assert ei.value.status == pm.PM_ERR_SHAPE
+    # a call with more uses than jobs can name is refused before any work
+    n_big = 32767 // 4 + 1
+    xb = torch.zeros((n_big, tiny.hidden), dtype=torch.float32, device="cuda")
+    with pytest.raises(pm.PMError) as ei:
+        pm.pm_moe_token_forward(st0, 0, np.zeros((n_big, 4), np.int32),
+                                np.full((n_big, 4), 0.25, np.float32),
+                                np.full((n_big, 4, 3), 2, np.uint8), xb, torch.empty_like(xb))
+    assert ei.value.status == pm.PM_ERR_ARG
     st0.close()

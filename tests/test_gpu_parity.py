@@ -581,3 +581,59 @@ def test_topup_waits_for_an_earlier_reader(attach_first):
         assert_close(host(ys[0])[0], first["y"], first["Sy"], f"rep {rep}: earlier forward")
         assert_close(host(ys[1])[0], second["y"], second["Sy"], f"rep {rep}: after top-up")
     st.close()
+
+
+@pytest.mark.parametrize("mfma", [False, True])
+def test_topup_into_an_unallocated_slot(mfma):
+    """Slots that hold no memory yet, with only a host source attached: the
+    forward allocates them before it takes their addresses, then tops them
+    up.  Four experts: one read by four uses (matrix-core tiles), one by two
+    (the direct kernels) and two by a single use (the LUT path)."""
+    report(f"top-up into never-allocated slots ({'PM_BATCH_MFMA' if mfma else 'default'} path)")
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    wl = synth.WORKLOADS[1]
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    pw = pm.pm_expert_plane_words(e)
+    n_exp = 4
+    donor = pm.pm_store_create(e, 1, n_exp)
+    filler = PoolFiller(wl)
+    srcs = []
+    for i in range(n_exp):
+        filler.fill(donor, 0, i)
+        torch.cuda.synchronize()
+        pp, lp = pm.pm_store_slot(donor, 0, i)
+        sp = torch.empty(8 * pw, dtype=torch.int32, pin_memory=True)
+        sl = torch.empty(pm.pm_expert_levels_floats(e), dtype=torch.float32, pin_memory=True)
+        assert hip.hipMemcpy(ctypes.c_void_p(sp.data_ptr()), ctypes.c_void_p(pp),
+                             ctypes.c_size_t(8 * pw * 4), 2) == 0
+        assert hip.hipMemcpy(ctypes.c_void_p(sl.data_ptr()), ctypes.c_void_p(lp),
+                             ctypes.c_size_t(sl.numel() * 4), 2) == 0
+        srcs.append((sp, sl))
+    st = pm.pm_store_create(e, 1, n_exp)
+    for i in range(n_exp):
+        pm.pm_store_attach_host(st, 0, i, srcs[i][0].data_ptr(), srcs[i][1].data_ptr())
+    ids = np.array([[0, 1], [0, 2], [1, 0], [0, 3]], np.int32)
+    w = np.array([[0.6, 0.4], [0.7, 0.3], [0.5, 0.5], [0.8, 0.2]], np.float32)
+    k = np.array([[[3, 2, 4], [5, 1, 2]], [[2, 2, 3], [6, 3, 2]], [[4, 1, 3], [1, 3, 2]],
+                  [[2, 5, 1], [3, 3, 3]]], np.uint8)
+    B = len(ids)
+    x = np.stack([synth.activation(wl.seed, 1, 0, t, wl.hidden, step=21) for t in range(B)])
+    xd = dev(x)
+    flags = pm.PM_AUTO_TOPUP | (pm.PM_BATCH_MFMA if mfma else 0)
+    y = torch.empty((B, wl.hidden), dtype=torch.float32, device="cuda")
+    pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y, flags=flags)
+    got = host(y)
+    want_res = [int(k[ids == i].max()) for i in range(n_exp)]
+    assert want_res == [5, 5, 6, 3]
+    assert [pm.pm_store_resident(st, 0, i) for i in range(n_exp)] == want_res
+    y_ref = torch.empty_like(y)
+    pm.pm_moe_token_forward(donor, 0, ids, w, k, xd, y_ref, flags=flags & ~pm.PM_AUTO_TOPUP)
+    ref = host(y_ref)
+    assert np.all(np.abs(got - ref) <= 1e-4 * (np.abs(ref).max(axis=1, keepdims=True) + 1e-3))
+    rows = oc.sample_rows(wl.hidden, 12, 21)
+    for t in range(B):
+        want, S = oc.token_layer(1, 0, ids[t], w[t], k[t], x[t], rows)
+        assert_close(got[t][rows], want, S, f"token {t}")
+    st.close()
+    donor.close()
