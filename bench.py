@@ -303,7 +303,9 @@ def bench_precisions(args, torch, pm, synth, PoolFiller):
 def bench_batch_topup(args, torch, pm, synth, PoolFiller):
     """B = 8 tokens per step, experts grouped; before each step 20% of the
     distinct experts (kmax >= 2) are cut back to a shorter resident prefix and
-    the step tops them up from pinned host memory on the store's side stream."""
+    the step tops them up from pinned host memory on the store's side stream.
+    Timed on the default path and with PM_READ_ONCE (an expert shared by
+    several tokens read once, by the direct kernels)."""
     wl = synth.WORKLOADS[4]
     e = pm.eshape(wl.hidden, wl.inter, wl.group)
     st = pm.pm_store_create(e, 1, wl.n_experts)
@@ -340,13 +342,13 @@ def bench_batch_topup(args, torch, pm, synth, PoolFiller):
                           for s in range(total)])
     copies = []
 
-    def step(i, topup=True, s0=args.warmup):
+    def step(i, topup=True, s0=args.warmup, extra=0):
         s = s0 + i
         if topup:
             for e_, keep in plans[s]:
                 pm.pm_store_truncate(st, 0, e_, keep)
         pm.pm_moe_token_forward(st, 0, ids[s], w[s], k3[s], x[s], y[s], stream,
-                                flags=pm.PM_AUTO_TOPUP)
+                                flags=pm.PM_AUTO_TOPUP | extra)
 
     n = args.steps
     timed(torch, lambda i: step(i, True, 0), min(args.warmup, 10))
@@ -354,9 +356,13 @@ def bench_batch_topup(args, torch, pm, synth, PoolFiller):
     el = timed(torch, step, n)
     _, _, p1, b1 = pm.pm_store_copy_stats(st)
     el_res = timed(torch, lambda i: step(i, False), n)
+    el_once = timed(torch, lambda i: step(i, True, extra=pm.PM_READ_ONCE), n)
+    el_once_res = timed(torch, lambda i: step(i, False, extra=pm.PM_READ_ONCE), n)
     st.close()
     return {"workload": wl.name, "ms_per_step": round(el / n * 1e3, 4),
             "ms_per_step_all_resident": round(el_res / n * 1e3, 4),
+            "ms_per_step_read_once": round(el_once / n * 1e3, 4),
+            "ms_per_step_all_resident_read_once": round(el_once_res / n * 1e3, 4),
             "gemv_GBs_all_resident": round(gemv_bytes * n / el_res / 1e9, 1),
             "h2d_MB_per_step": round((b1 - b0) / n / 1e6, 2),
             "h2d_GBs": round((b1 - b0) / el / 1e9, 2),

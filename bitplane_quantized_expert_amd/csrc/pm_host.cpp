@@ -1139,9 +1139,10 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
                                           void* compute_v, uint32_t flags) {
     if (!s) return failf(PM_ERR_ARG, "null store");
     if (s->host_fake) return failf(PM_ERR_STATE, "a host-backed store cannot compute");
-    if (flags & ~uint32_t(PM_AUTO_TOPUP | PM_BATCH_MFMA))
+    if (flags & ~uint32_t(PM_AUTO_TOPUP | PM_BATCH_MFMA | PM_READ_ONCE))
         return failf(PM_ERR_ARG, "unknown forward flags");
     const bool mfma = flags & PM_BATCH_MFMA;
+    const bool read_once = flags & PM_READ_ONCE;
     if (layer < 0 || layer >= s->n_layers) return failf(PM_ERR_ARG, "layer %d outside store", layer);
     if (n_tokens < 0 || top_k < 1) return failf(PM_ERR_ARG, "n_tokens=%d top_k=%d", n_tokens, top_k);
     if (n_tokens == 0) return PM_OK;
@@ -1264,13 +1265,16 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     const int S_gu = gu_lut_shape ? g.hidden / kSliceCols : 1;
     const int S_dn = dn_lut_shape ? g.inter / kSliceCols : 1;
     for (int d = 0; d < n_items; ++d) {
+        // PM_READ_ONCE: an expert of several uses is read once by the direct
+        // kernels (each use shifts the kmax prefix down to its own k)
+        const bool lut_item = !read_once || item_uses[d].size() == 1;
         for (int u : item_uses[d]) {
             for (int m = 0; m < 3; ++m) {
                 if (uses[u].direct[m] == 2) continue;
                 const bool shape_ok = m < 2 ? gu_lut_shape : dn_lut_shape;
                 const pm_matrix_shape ms = m < 2 ? pm_matrix_shape{g.inter, g.hidden, g.group}
                                                  : pm_matrix_shape{g.hidden, g.inter, g.group};
-                const bool lut = shape_ok && uses[u].k[m] <= kLutMaxK &&
+                const bool lut = lut_item && shape_ok && uses[u].k[m] <= kLutMaxK &&
                                  lut_offsets_fit(ms, uses[u].k[m], g.plane_words);
                 uses[u].direct[m] = lut ? 0 : 1;
                 uses[u].slices[m] = lut ? (m < 2 ? S_gu : S_dn) : 1;

@@ -519,6 +519,47 @@ def test_forward_batch8_grouped_with_topup():
     st.close()
 
 
+def test_read_once_matches_default():
+    """PM_READ_ONCE (an expert shared by several tokens read once, by the
+    direct kernels) against the default path (a LUT job per use) on a B = 8
+    step: both against the oracle, and bit for bit on the tokens none of whose
+    experts is shared (their jobs are the same in both)."""
+    report("configs[4] routing, all resident: PM_READ_ONCE vs default")
+    wl = synth.WORKLOADS[4]
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    st = pm.pm_store_create(e, 1, wl.n_experts)
+    filler = PoolFiller(wl)
+    B = wl.n_tokens
+    routes = [oc.route_and_bits(4, 0, step=5, token=t) for t in range(B)]
+    ids = np.stack([r[0] for r in routes])
+    w = np.stack([r[1] for r in routes])
+    k = np.stack([r[2] for r in routes])
+    for i in sorted(set(int(i) for i in ids.reshape(-1))):
+        filler.fill(st, 0, i)
+    torch.cuda.synchronize()
+    counts = {int(i): int((ids == i).sum()) for i in np.unique(ids)}
+    assert max(counts.values()) >= 2, "the step should share an expert"
+    x = np.stack([synth.activation(wl.seed, 4, 0, t, wl.hidden, step=5) for t in range(B)])
+    xd = dev(x)
+    out = {}
+    for name, flags in (("default", 0), ("read_once", pm.PM_READ_ONCE)):
+        y = torch.empty((B, wl.hidden), dtype=torch.float32, device="cuda")
+        pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y, flags=flags)
+        out[name] = host(y)
+    for t in range(B):
+        a, b = out["default"][t], out["read_once"][t]
+        if all(counts[int(i)] == 1 for i in ids[t]):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), t
+        else:
+            assert np.all(np.abs(a - b) <= 1e-4 * np.abs(a).max() + 1e-6), t
+    shared_t = next(t for t in range(B) if any(counts[int(i)] > 1 for i in ids[t]))
+    rows = oc.sample_rows(wl.hidden, 12, 30)
+    want, S = oc.token_layer(4, 0, ids[shared_t], w[shared_t], k[shared_t], x[shared_t], rows)
+    for name in out:
+        assert_close(out[name][shared_t][rows], want, S, f"{name}, token {shared_t}")
+    st.close()
+
+
 @pytest.mark.parametrize("attach_first", [True, False])
 def test_topup_waits_for_an_earlier_reader(attach_first):
     """A top-up must not overwrite planes that an earlier forward, still
