@@ -351,7 +351,13 @@ def bench_batch_topup(args, torch, pm, synth, PoolFiller):
                                 flags=pm.PM_AUTO_TOPUP | extra)
 
     n = args.steps
-    timed(torch, lambda i: step(i, True, 0), min(args.warmup, 10))
+    # warm-up: the warm-up steps, repeated for at least half a second (the
+    # first copies and launches of a process run slower)
+    t_end, i = time.perf_counter() + 0.5, 0
+    while i < min(args.warmup, 10) or time.perf_counter() < t_end:
+        step(i % max(1, min(args.warmup, 10)), True, 0)
+        i += 1
+    torch.cuda.synchronize()
     _, _, p0, b0 = pm.pm_store_copy_stats(st)
     el = timed(torch, step, n)
     _, _, p1, b1 = pm.pm_store_copy_stats(st)

@@ -491,7 +491,13 @@ struct pm_store {
     bool host_fake;
     size_t plane_bytes, level_bytes;   // per plane chunk, per slot levels
     std::vector<Slot> slots;
-    hipStream_t side = nullptr;        // the store's own top-up stream
+    // The store's own top-up streams.  Copies that need no wait take the
+    // first kSides - 1 in turn (more than one copy in flight keeps the link
+    // busier); copies that wait for an earlier forward still reading their
+    // slot take the last, so that a wait holds up no other copy.
+    static constexpr int kSides = 3;
+    hipStream_t side[kSides] = {};
+    int next_side = 0;
     // Ends of recent forwards: done[n % kDone] marks the end of forward n
     // (n >= 1).  A forward records it only when the store has host sources
     // (a top-up may need it); otherwise it is recorded later on the last
@@ -500,7 +506,7 @@ struct pm_store {
     // costs the launch-bound layer step about 3 us.  Forwards of one store
     // complete in order, so an entry that marks a later forward than the one
     // asked for is still safe to wait on.
-    static constexpr int kDone = 8;
+    static constexpr int kDone = 32;
     hipEvent_t done[kDone] = {};
     uint64_t done_seq[kDone] = {};     // the forward each entry marks the end of
     uint64_t fwd_seq = 0;              // forwards issued
@@ -570,7 +576,9 @@ extern "C" pm_status pm_store_create(pm_expert_shape e, int n_layers, int n_expe
     s->level_bytes = pm_expert_levels_floats(e) * sizeof(float);
     s->slots.resize(size_t(n_layers) * n_experts);
     if (!s->host_fake) {
-        hipError_t er = hipStreamCreateWithFlags(&s->side, hipStreamNonBlocking);
+        hipError_t er = hipSuccess;
+        for (int i = 0; i < pm_store::kSides && er == hipSuccess; ++i)
+            er = hipStreamCreateWithFlags(&s->side[i], hipStreamNonBlocking);
         for (int i = 0; i < pm_store::kDone && er == hipSuccess; ++i)
             er = hipEventCreateWithFlags(&s->done[i], hipEventDisableTiming);
         if (er != hipSuccess) {
@@ -603,7 +611,8 @@ extern "C" pm_status pm_store_destroy(pm_store* s) {
             if (ev) (void)hipEventDestroy(ev);
         for (hipEvent_t ev : s->done)
             if (ev) (void)hipEventDestroy(ev);
-        if (s->side) (void)hipStreamDestroy(s->side);
+        for (hipStream_t st : s->side)
+            if (st) (void)hipStreamDestroy(st);
     }
     delete s;
     return PM_OK;
@@ -646,12 +655,19 @@ extern "C" pm_status pm_store_attach_host(pm_store* s, int layer, int expert,
 }
 
 // The event that marks the end of forward n (1 <= n <= fwd_seq) or of a later
-// forward: its own entry, else the latest recorded end if that is not earlier,
-// else an end recorded now on the last forward's stream.
+// forward: its own entry, else the earliest recorded end after it, else an
+// end recorded now on the last forward's stream.
 static hipEvent_t forward_end(pm_store* s, uint64_t n) {
     const int e = int(n % pm_store::kDone);
     if (s->done_seq[e] == n) return s->done[e];
-    if (s->recorded_seq >= n) return s->done[s->recorded_seq % pm_store::kDone];
+    if (s->recorded_seq >= n) {
+        // the earliest recorded end after n: waiting on a later one would
+        // also wait for every forward queued since
+        int best = -1;
+        for (int i = 0; i < pm_store::kDone; ++i)
+            if (s->done_seq[i] >= n && (best < 0 || s->done_seq[i] < s->done_seq[best])) best = i;
+        return s->done[best];
+    }
     const int f = int(s->fwd_seq % pm_store::kDone);
     if (hipEventRecord(s->done[f], s->last_compute) == hipSuccess) {
         s->done_seq[f] = s->fwd_seq;
@@ -706,13 +722,32 @@ static pm_status topup_slot(pm_store* s, Slot& sl, int k, hipStream_t side) {
     return PM_OK;
 }
 
+// Top-ups of the short slots of one forward (slot i to prefix k[i]): copies
+// that need no wait first, spread over the store's first side streams, then
+// those that wait for an earlier forward's reads, on the last side stream.
+static pm_status issue_topups(pm_store* s, const std::vector<Slot*>& slots,
+                              const std::vector<int>& k) {
+    constexpr int n_free = pm_store::kSides - 1;
+    for (int pass = 0; pass < 2; ++pass) {
+        for (size_t i = 0; i < slots.size(); ++i) {
+            hipEvent_t ev = nullptr;
+            const bool waits = slot_reader_running(s, *slots[i], &ev);
+            if (waits != (pass == 1)) continue;
+            hipStream_t st = waits ? s->side[n_free] : s->side[s->next_side++ % n_free];
+            const pm_status r = topup_slot(s, *slots[i], k[i], st);
+            if (r) return r;
+        }
+    }
+    return PM_OK;
+}
+
 extern "C" pm_status pm_store_topup(pm_store* s, int layer, int expert, int k, void* side) {
     size_t i;
     pm_status st = slot_of(s, layer, expert, &i);
     if (st) return st;
     st = check_k(k);
     if (st) return st;
-    return topup_slot(s, s->slots[i], k, side ? (hipStream_t)side : s->side);
+    return topup_slot(s, s->slots[i], k, side ? (hipStream_t)side : s->side[0]);
 }
 
 extern "C" pm_status pm_store_truncate(pm_store* s, int layer, int expert, int keep) {
@@ -1078,15 +1113,17 @@ static pm_status forward_mfma(pm_store* s, int layer, int n_tokens, int top_k,
     // forwards on one store run in order; on the same stream they already do
     if (s->fwd_seq > 0 && compute != s->last_compute)
         HIP_TRY(hipStreamWaitEvent(compute, forward_end(s, s->fwd_seq), 0));
-    // top-ups of short slots (copies that need no wait first)
-    for (int pass = 0; pass < 2; ++pass) {
+    // top-ups of short slots
+    {
+        std::vector<Slot*> ls;
+        std::vector<int> lk;
         for (int d = 0; d < n_items; ++d) {
             if (!late[d]) continue;
-            hipEvent_t ev = nullptr;
-            if (slot_reader_running(s, *slot[d], &ev) != (pass == 1)) continue;
-            st = topup_slot(s, *slot[d], kneed[d], s->side);
-            if (st) return st;
+            ls.push_back(slot[d]);
+            lk.push_back(kneed[d]);
         }
+        st = issue_topups(s, ls, lk);
+        if (st) return st;
     }
     // uses and tiles through the pinned ring
     Workspace& w = s->ws;
@@ -1390,18 +1427,16 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     if (s->fwd_seq > 0 && compute != s->last_compute)
         HIP_TRY(hipStreamWaitEvent(compute, forward_end(s, s->fwd_seq), 0));
 
-    // ---- top-ups (side stream) for late items; copies that must wait for an
-    // earlier forward still reading their slot go last, so that the others
-    // start at once
-    for (int pass = 0; pass < 2; ++pass) {
+    // ---- top-ups (side streams) for late items
+    {
+        std::vector<Slot*> ls;
+        std::vector<int> lk;
         for (int i = n_res; i < n_items; ++i) {
-            const int d = order[i];
-            Slot& sl = slot_of_item(d);
-            hipEvent_t ev = nullptr;
-            if (slot_reader_running(s, sl, &ev) != (pass == 1)) continue;
-            st = topup_slot(s, sl, kneed[d], s->side);
-            if (st) return st;
+            ls.push_back(&slot_of_item(order[i]));
+            lk.push_back(kneed[order[i]]);
         }
+        st = issue_topups(s, ls, lk);
+        if (st) return st;
     }
 
 
