@@ -58,6 +58,21 @@ def step_bytes(wl, kk):
     return b + 2 * wl.hidden * 4
 
 
+def grouped_bytes(wl, ids, k3):
+    """Algorithmic bytes of one B-token layer call: every distinct expert once,
+    each matrix at its largest prefix over the tokens that share it, plus the
+    depth-k table of every distinct k it is read at; x read and y written per
+    token."""
+    b = 0
+    for e in np.unique(ids):
+        sel = k3[ids == e]                          # [uses][3]
+        for m in range(3):
+            r, c = (wl.inter, wl.hidden) if m < 2 else (wl.hidden, wl.inter)
+            ks = sorted(set(int(v) for v in sel[:, m]))
+            b += r * c * max(ks) // 8 + sum(r * (c // wl.group) * (1 << k) * 4 for k in ks)
+    return b + 2 * len(ids) * wl.hidden * 4
+
+
 def gateup_bytes(wl, kk):
     b = 0
     for k3 in kk:
@@ -338,8 +353,7 @@ def bench_batch_topup(args, torch, pm, synth, PoolFiller):
         short = [cand[int(j)] for j in pick[:int(np.ceil(0.2 * len(distinct)))]]
         r = synth.words(wl.seed, synth.KIND_TRUNC, wl.cfg, 0, s, 1, len(short))
         plans.append([(i, 1 + int(r[j] % (kmax[i] - 1))) for j, i in enumerate(short)])
-    gemv_bytes = np.mean([sum(step_bytes(wl, k3[s][t]) for t in range(wl.n_tokens))
-                          for s in range(total)])
+    gemv_bytes = float(np.mean([grouped_bytes(wl, ids[s], k3[s]) for s in range(total)]))
     copies = []
 
     def step(i, topup=True, s0=args.warmup, extra=0):
@@ -451,6 +465,10 @@ def bench_batches(args, torch, pm, synth, PoolFiller):
                 st, 0, steps[1 + i][0], steps[1 + i][1], steps[1 + i][2], steps[1 + i][3],
                 steps[1 + i][4], stream, flags=flags), n_steps)
             res[name + "_ms"] = round(el / n_steps * 1e3, 3)
+        gb = float(np.mean([grouped_bytes(wl, st_[0], st_[2]) for st_ in steps[1:]]))
+        res["algorithmic_MB"] = round(gb / 1e6, 1)
+        res["default_GBs"] = round(gb / (res["default_ms"] / 1e3) / 1e9, 1)
+        res["mfma_GBs"] = round(gb / (res["mfma_ms"] / 1e3) / 1e9, 1)
         res["tokens_per_s_mfma"] = round(B / (res["mfma_ms"] / 1e3), 1)
         res["tokens_per_s"] = round(B / (res["default_ms"] / 1e3), 1)
         res["mfma_speedup"] = round(res["default_ms"] / res["mfma_ms"], 2)
