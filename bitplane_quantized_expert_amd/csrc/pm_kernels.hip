@@ -16,10 +16,10 @@
 // the word's total.  The codebook enters as 2^k FMAs per block and row, so no
 // weight value is ever formed.  One-hot x gives exact columns.
 //
-// Direct path (any k, any shape, an expert shared by several tokens read
-// once): per weight, the prefix is assembled from the k plane words and its
-// node read from the depth-k table, which for group 128 and k >= 5 is first
-// staged in LDS (row_dot_lds).
+// Direct path (any k, any shape; an expert of several uses is read once for
+// all of them): per weight, the prefix is assembled from the k plane words
+// and its node read from the depth-k table, which for group 128 and rows of
+// whole 1024-column runs is first staged in LDS (row_dot_lds).
 //
 // All sums run in a fixed order (DPP row reductions, slices and slots in
 // index order), so every output is deterministic.
