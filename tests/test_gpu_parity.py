@@ -628,15 +628,17 @@ def test_topup_waits_for_an_earlier_reader(attach_first):
 def test_topup_into_an_unallocated_slot(mfma):
     """Slots that hold no memory yet, with only a host source attached: the
     forward allocates them before it takes their addresses, then tops them
-    up.  Four experts: one read by four uses (matrix-core tiles), one by two
-    (the direct kernels) and two by a single use (the LUT path)."""
+    up.  Expert 0 is read by all 8 tokens: gate at one prefix (a group of 8,
+    matrix-core tiles), up at eight prefixes (LUT jobs at k <= 5, the direct
+    kernels above), down at k = 2 by six tokens (tiles) and k = 7 by two
+    (direct).  Expert 1 has three uses, experts 2..6 one each."""
     report(f"top-up into never-allocated slots ({'PM_BATCH_MFMA' if mfma else 'default'} path)")
     import ctypes
     hip = ctypes.CDLL("libamdhip64.so")
     wl = synth.WORKLOADS[1]
     e = pm.eshape(wl.hidden, wl.inter, wl.group)
     pw = pm.pm_expert_plane_words(e)
-    n_exp = 4
+    n_exp = 7
     donor = pm.pm_store_create(e, 1, n_exp)
     filler = PoolFiller(wl)
     srcs = []
@@ -654,11 +656,13 @@ def test_topup_into_an_unallocated_slot(mfma):
     st = pm.pm_store_create(e, 1, n_exp)
     for i in range(n_exp):
         pm.pm_store_attach_host(st, 0, i, srcs[i][0].data_ptr(), srcs[i][1].data_ptr())
-    ids = np.array([[0, 1], [0, 2], [1, 0], [0, 3]], np.int32)
-    w = np.array([[0.6, 0.4], [0.7, 0.3], [0.5, 0.5], [0.8, 0.2]], np.float32)
-    k = np.array([[[3, 2, 4], [5, 1, 2]], [[2, 2, 3], [6, 3, 2]], [[4, 1, 3], [1, 3, 2]],
-                  [[2, 5, 1], [3, 3, 3]]], np.uint8)
-    B = len(ids)
+    B = 8
+    ids = np.array([[0, o] for o in (1, 1, 1, 2, 3, 4, 5, 6)], np.int32)
+    w = np.array([[0.5 + 0.05 * t, 0.5 - 0.05 * t] for t in range(B)], np.float32)
+    k = np.zeros((B, 2, 3), np.uint8)
+    for t in range(B):
+        k[t, 0] = [3, t + 1, 2 if t < 6 else 7]
+        k[t, 1] = [(3 * t) % 8 + 1, (5 * t + 2) % 8 + 1, (t + 4) % 8 + 1]
     x = np.stack([synth.activation(wl.seed, 1, 0, t, wl.hidden, step=21) for t in range(B)])
     xd = dev(x)
     flags = pm.PM_AUTO_TOPUP | (pm.PM_BATCH_MFMA if mfma else 0)
@@ -666,7 +670,7 @@ def test_topup_into_an_unallocated_slot(mfma):
     pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y, flags=flags)
     got = host(y)
     want_res = [int(k[ids == i].max()) for i in range(n_exp)]
-    assert want_res == [5, 5, 6, 3]
+    assert want_res[0] == 8
     assert [pm.pm_store_resident(st, 0, i) for i in range(n_exp)] == want_res
     y_ref = torch.empty_like(y)
     pm.pm_moe_token_forward(donor, 0, ids, w, k, xd, y_ref, flags=flags & ~pm.PM_AUTO_TOPUP)
