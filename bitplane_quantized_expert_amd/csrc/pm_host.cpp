@@ -704,6 +704,9 @@ static pm_status topup_slot(pm_store* s, Slot& sl, int k, hipStream_t side) {
         // for the last forward that read this slot, unless it has finished
         hipEvent_t reader = nullptr;
         if (slot_reader_running(s, sl, &reader)) HIP_TRY(hipStreamWaitEvent(side, reader, 0));
+        // an earlier copy into this slot may still run on another stream: the
+        // ready event recorded below must cover it too
+        if (sl.pending) HIP_TRY(hipStreamWaitEvent(side, sl.ready, 0));
         if (!sl.levels_ready)
             HIP_TRY(hipMemcpyAsync(sl.levels, sl.h_levels, s->level_bytes,
                                    hipMemcpyHostToDevice, side));

@@ -682,3 +682,57 @@ def test_topup_into_an_unallocated_slot(mfma):
         assert_close(got[t][rows], want, S, f"token {t}")
     st.close()
     donor.close()
+
+
+def test_forward_topup_waits_for_a_pending_explicit_topup():
+    """An explicit top-up still queued on the caller's stream, then a forward
+    that needs a deeper prefix of the same slot: the forward's own copy goes
+    to a store side stream, and the forward must still wait for both copies.
+    The planes the first copy brings are poisoned beforehand, and the first
+    copy is held back behind queued work, so a forward that waited only for
+    its own copy would read the poison."""
+    report("forward top-up after a pending explicit top-up on another stream")
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    wl = synth.WORKLOADS[0]
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    pw = pm.pm_expert_plane_words(e)
+    st = pm.pm_store_create(e, 1, 1)
+    PoolFiller(wl).fill(st, 0, 0)
+    torch.cuda.synchronize()
+    pp, lp = pm.pm_store_slot(st, 0, 0)
+    src_p = torch.empty(8 * pw, dtype=torch.int32, pin_memory=True)
+    src_l = torch.empty(pm.pm_expert_levels_floats(e), dtype=torch.float32, pin_memory=True)
+    assert hip.hipMemcpy(ctypes.c_void_p(src_p.data_ptr()), ctypes.c_void_p(pp),
+                         ctypes.c_size_t(8 * pw * 4), 2) == 0
+    assert hip.hipMemcpy(ctypes.c_void_p(src_l.data_ptr()), ctypes.c_void_p(lp),
+                         ctypes.c_size_t(src_l.numel() * 4), 2) == 0
+    pm.pm_store_attach_host(st, 0, 0, src_p.data_ptr(), src_l.data_ptr())
+    A = oracle.encode_expert(synth.expert_inputs(wl, 0, 0), wl.group)
+    x = synth.activation(wl.seed, 0, 0, 0, wl.hidden, step=4)
+    xd = dev(x[None])
+    ids = np.array([[0]], np.int32)
+    w = np.array([[1.0]], np.float32)
+    k = np.array([[[5, 5, 5]]], np.uint8)
+    want = oracle.expert_ffn(A, 5, 5, 5, x)
+    side = torch.cuda.Stream()
+    poison = torch.empty(7 * pw, dtype=torch.int32, device="cuda")
+    DeviceSynth().poison_into(poison, 9, 0)
+    busy = torch.randn(4096, 4096, device="cuda")
+    for rep in range(3):
+        pm.pm_store_truncate(st, 0, 0, 1)
+        torch.cuda.synchronize()
+        assert hip.hipMemcpy(ctypes.c_void_p(pp + 4 * pw), ctypes.c_void_p(poison.data_ptr()),
+                             ctypes.c_size_t(7 * pw * 4), 3) == 0
+        with torch.cuda.stream(side):
+            for _ in range(4):
+                busy = busy @ busy
+                busy = busy / busy.abs().max()
+        pm.pm_store_topup(st, 0, 0, 3, side)
+        y = torch.empty((1, wl.hidden), dtype=torch.float32, device="cuda")
+        pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y, torch.cuda.current_stream(),
+                                flags=pm.PM_AUTO_TOPUP)
+        torch.cuda.synchronize()
+        assert pm.pm_store_resident(st, 0, 0) == 5
+        assert_close(host(y)[0], want["y"], want["Sy"], f"rep {rep}")
+    st.close()
