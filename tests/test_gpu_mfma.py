@@ -191,3 +191,30 @@ def test_mfma_with_topups_and_shape_check():
                                 np.full((n_big, 4, 3), 2, np.uint8), xb, torch.empty_like(xb))
     assert ei.value.status == pm.PM_ERR_ARG
     st0.close()
+
+
+def test_default_path_large_batch(store512):
+    """512 tokens, top-10 of 512 experts, allocator prefixes: the default path
+    runs trains of full LUT launches (64 jobs each), cut per token, plus
+    matrix-core tiles for the crowded (expert, matrix, k) groups.  Sampled
+    tokens against the oracle; every token against PM_BATCH_MFMA."""
+    report("default path: 512 tokens x top-10 of 512 experts, mean k 2.5")
+    wl, st, ensure = store512
+    B = 512
+    ids, w, x = layer_batch(wl, B, wl.top_k, wl.n_experts, step=13)
+    ensure(ids)
+    err = synth.error_profiles(wl.seed, wl.cfg, 0, wl.n_experts)
+    kk = pm.pm_allocate_bits(ids, w, err, wl.budget)
+    k = np.repeat(kk[:, :, None], 3, axis=2).astype(np.uint8)
+    xd = dev(x)
+    y = torch.empty((B, wl.hidden), dtype=torch.float32, device="cuda")
+    pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y)
+    got = host(y)
+    rows = oc.sample_rows(wl.hidden, 8, 14)
+    for t in (0, 255, 511):
+        want, S = oc.token_layer(1, 0, ids[t], w[t], k[t], x[t], rows)
+        assert_close(got[t][rows], want, S, f"token {t}")
+    y1 = torch.empty_like(y)
+    pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y1, flags=pm.PM_BATCH_MFMA)
+    ref = host(y1)
+    assert np.all(np.abs(got - ref) <= 1e-4 * (np.abs(ref).max(axis=1, keepdims=True) + 1e-3))
