@@ -176,46 +176,70 @@ __device__ inline float quad_node(const float (&tq)[quad_share<K>()]) {
                                         true));
 }
 
-// Bucket V's term of one row: its sum S from the four chunk lookups (in chunk
-// order), taken off the running remainder, times node V.
-template <int K, int V>
-__device__ inline void lut_term(const float* r, const float (&tq)[quad_share<K>()], float& acc,
-                                float& last) {
-    if constexpr (V < (1 << K) - 1) {
-        float S = r[4 * V];
-        S += r[4 * V + 1];
-        S += r[4 * V + 2];
-        S += r[4 * V + 3];
+// One row's contribution of this lane's word at prefix K:
+// sum_v node(v) * S_v, S_v = sum of x where the prefix is v.  The buckets go
+// in chunks of PM_LUT_CHUNK: a chunk's masks, then all its lookups (one LDS
+// round trip), then its bucket sums in v order, each taken off the word's
+// total xw; the last bucket is what remains.  Chunks keep the k = 4 and 5 rows
+// within the register budget of four waves per SIMD (all 2^k - 1 lookups at
+// once spilled); the order of the sums is the same for any chunk size.
+#ifndef PM_LUT_CHUNK
+#define PM_LUT_CHUNK 8
+#endif
+// Bucket V (V0 <= V < V1) of one row: its sum S from the four chunk lookups
+// (in chunk order), taken off the running remainder, times node V.
+template <int K, int V, int V0, int V1>
+__device__ inline void lut_terms(const float* r, const float (&tq)[quad_share<K>()], float& acc,
+                                 float& last) {
+    if constexpr (V < V1) {
+        float S = r[4 * (V - V0)];
+        S += r[4 * (V - V0) + 1];
+        S += r[4 * (V - V0) + 2];
+        S += r[4 * (V - V0) + 3];
         last -= S;
         acc = fmaf(quad_node<K, V>(tq), S, acc);
-        lut_term<K, V + 1>(r, tq, acc, last);
-    } else {
-        acc = fmaf(quad_node<K, V>(tq), last, acc);
+        lut_terms<K, V + 1, V0, V1>(r, tq, acc, last);
     }
 }
+// The masks of leaves V0 .. V1 - 1 only (subtrees outside are not visited).
+template <int K, int D, int V, int V0, int V1>
+struct PrefixMasksIn {
+    static __device__ inline void go(const uint32_t (&w)[K], uint32_t m, uint32_t (&out)[V1 - V0]) {
+        if constexpr (D == K) {
+            if constexpr (V >= V0 && V < V1) out[V - V0] = m;
+        } else if constexpr (((V + 1) << (K - D)) > V0 && (V << (K - D)) < V1) {
+            PrefixMasksIn<K, D + 1, 2 * V, V0, V1>::go(w, m & ~w[D], out);
+            PrefixMasksIn<K, D + 1, 2 * V + 1, V0, V1>::go(w, m & w[D], out);
+        }
+    }
+};
 
-// One row's contribution of this lane's word at prefix K:
-// sum_v node(v) * S_v, S_v = sum of x where the prefix is v.  All lookups of
-// the row are issued before any is consumed, so one LDS round trip covers the
-// row; then the bucket sums are formed in v order and the last bucket, by
-// subtraction, from the word's total xw.
-template <int K>
-__device__ inline float lut_row(const uint32_t (&w)[K], const float (&tq)[quad_share<K>()],
-                                float xw, uint32_t b0, uint32_t b1) {
-    constexpr int N = (1 << K) - 1;
-    uint32_t m[N];
-    PrefixMasks<K, 0, 0>::go(w, 0xFFFFFFFFu, m);
-    float r[4 * N];
+template <int K, int V0, int N>
+__device__ inline void lut_chunks(const uint32_t (&w)[K], const float (&tq)[quad_share<K>()],
+                                  uint32_t b0, uint32_t b1, float& acc, float& last) {
+    constexpr int C = PM_LUT_CHUNK > 0 ? PM_LUT_CHUNK : N;
+    constexpr int V1 = V0 + C < N ? V0 + C : N;
+    uint32_t m[V1 - V0];
+    PrefixMasksIn<K, 0, 0, V0, V1>::go(w, 0xFFFFFFFFu, m);
+    float r[4 * (V1 - V0)];
 #pragma unroll
-    for (int v = 0; v < N; ++v) {
+    for (int v = 0; v < V1 - V0; ++v) {
         r[4 * v + 0] = lds_at(__builtin_amdgcn_perm(b0, m[v], 0x0C060004u));
         r[4 * v + 1] = lds_at(__builtin_amdgcn_perm(b0, m[v], 0x0C060104u) + 128);
         r[4 * v + 2] = lds_at(__builtin_amdgcn_perm(b1, m[v], 0x0C060204u));
         r[4 * v + 3] = lds_at(__builtin_amdgcn_perm(b1, m[v], 0x0C060304u) + 128);
     }
+    lut_terms<K, V0, V0, V1>(r, tq, acc, last);
+    if constexpr (V1 < N) lut_chunks<K, V1, N>(w, tq, b0, b1, acc, last);
+}
+
+template <int K>
+__device__ inline float lut_row(const uint32_t (&w)[K], const float (&tq)[quad_share<K>()],
+                                float xw, uint32_t b0, uint32_t b1) {
+    constexpr int N = (1 << K) - 1;
     float acc = 0.f, last = xw;
-    lut_term<K, 0>(r, tq, acc, last);
-    return acc;
+    lut_chunks<K, 0, N>(w, tq, b0, b1, acc, last);
+    return fmaf(quad_node<K, N>(tq), last, acc);
 }
 
 // The activation slice of this workgroup into the LUT.  Thread tid owns
