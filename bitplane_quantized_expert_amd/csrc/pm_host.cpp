@@ -497,7 +497,7 @@ struct pm_store {
     // slot take the last, so that a wait holds up no other copy.
     static constexpr int kSides = 3;
     hipStream_t side[kSides] = {};
-    int next_side = 0;
+    uint32_t next_side = 0;
     // Ends of recent forwards: done[n % kDone] marks the end of forward n
     // (n >= 1).  A forward records it only when the store has host sources
     // (a top-up may need it); otherwise it is recorded later on the last
