@@ -201,8 +201,10 @@ pm_status pm_store_set_resident(pm_store* s, int layer, int expert, int r);
 pm_status pm_store_attach_host(pm_store* s, int layer, int expert,
                                const uint32_t* h_planes, const float* h_levels);
 /* Make planes r..k-1 resident by copying exactly those plane chunks from the
- * host source (plus the levels on a slot's first fill) on `side`, then
- * record the slot's ready event there; r becomes k.  No copy if r >= k
+ * host source (plus the levels on a slot's first fill) on `side` (null: the
+ * store's first side stream), then record the slot's ready event there; r
+ * becomes k.  The copy first waits for an earlier forward still reading the
+ * slot and for an earlier copy into it still in flight.  No copy if r >= k
  * [T c13, c35: a resident deeper prefix serves a shallower request].
  * PM_ERR_STATE without a host source. */
 pm_status pm_store_topup(pm_store* s, int layer, int expert, int k, void* side);
@@ -276,8 +278,10 @@ pm_status pm_cache_stats(const pm_cache* c, uint64_t* accesses, uint64_t* hits,
  *   (overwritten).  At most 32767 uses (n_tokens * top_k) per call, else
  *   PM_ERR_ARG.
  * flags: PM_AUTO_TOPUP tops up every short slot from its host source on the
- * store's side stream and makes `compute` wait for it (kernels of resident
- * experts are issued first); without it a short slot is PM_ERR_NOT_RESIDENT.
+ * store's side streams (copies that need no wait alternate over two, copies
+ * that wait for an earlier forward's reads use a third) and makes `compute`
+ * wait for them (kernels of resident experts are issued first); without it a
+ * short slot is PM_ERR_NOT_RESIDENT.
  * PM_BATCH_MFMA puts every use on the matrix cores (larger batches [T c65:
  * untested on the pages]): the uses that read one matrix of one expert at one
  * prefix form tiles of up to 16, each weight is decoded once per tile (its
