@@ -81,6 +81,16 @@ def gateup_bytes(wl, kk):
     return b + wl.hidden * 4
 
 
+def routing_digest(ids, w, k):
+    """SHA-256 over the exact ids (int32), w (fp32) and k (uint8) of every step,
+    so that runs can be matched to their inputs (--log-inputs writes them)."""
+    import hashlib
+    h = hashlib.sha256()
+    for a, t in ((ids, np.int32), (w, np.float32), (k, np.uint8)):
+        h.update(np.ascontiguousarray(a, dtype=t).tobytes())
+    return h.hexdigest()
+
+
 def sources_digest():
     import hashlib
     h = hashlib.sha256()
@@ -624,6 +634,8 @@ def main():
     ap.add_argument("--experts", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--log-inputs", metavar="FILE",
+                    help="write the ids, w and k of every step of the layer benchmark (JSON lines)")
     ap.add_argument("--workload", default="1",
                     choices=["1", "2", "3", "4", "cache", "encode", "gemv", "batch", "all"],
                     help="1: the one-layer step (the reported line); 2: 60 layers; "
@@ -697,6 +709,13 @@ def main():
     plans = [(ids[s], w[s], k3[s]) for s in range(total)]
     stream = torch.cuda.current_stream()
     log(f"inputs ready: {total} tokens, mean k {kk.mean():.3f}")
+    inputs_digest = routing_digest(ids, w, kk)
+    if args.log_inputs:
+        with open(args.log_inputs, "w") as fh:
+            for s in range(total):
+                fh.write(json.dumps({"step": s, "timed": s >= args.warmup,
+                                     "ids": ids[s].tolist(), "w": w[s].tolist(),
+                                     "k": kk[s].tolist()}) + "\n")
 
     def run(s):
         pm.pm_moe_token_forward(st, 0, ids[s:s + 1], w[s:s + 1], k3[s:s + 1], x[s:s + 1],
@@ -763,6 +782,7 @@ def main():
                      "bytes_per_launch": int(gu_b.mean()),
                      "launch_us": round(gu_ms.mean() * 1e3, 2)},
         "stream_ceiling": ceiling,
+        "inputs_sha256": inputs_digest,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
