@@ -218,3 +218,41 @@ def test_default_path_large_batch(store512):
     pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y1, flags=pm.PM_BATCH_MFMA)
     ref = host(y1)
     assert np.all(np.abs(got - ref) <= 1e-4 * (np.abs(ref).max(axis=1, keepdims=True) + 1e-3))
+
+
+@pytest.mark.parametrize("case", range(5))
+def test_path_mixes_random(store512, case):
+    """Seeded random calls that mix every path choice: batch sizes 3 to 33,
+    top-2 to top-8 over 5 to 40 experts (so that experts are shared by up to
+    about 30 uses), and an independent prefix 1..8 per (use, matrix).  The
+    default path, PM_READ_ONCE and PM_BATCH_MFMA against the oracle on
+    sampled tokens and rows, and against each other on every token."""
+    wl, st, ensure = store512
+    rng = np.random.default_rng(1000 + case)
+    B = int(rng.integers(3, 34))
+    top_k = int(rng.integers(2, 9))
+    n_exp = int(rng.integers(max(top_k, 5), 41))
+    report(f"random path mix {case}: B={B} top-{top_k} over {n_exp} experts")
+    ids, w, x = layer_batch(wl, B, top_k, n_exp, step=40 + case)
+    ensure(ids)
+    k = rng.integers(1, 9, size=(B, top_k, 3)).astype(np.uint8)
+    # a crowded prefix on one matrix of the most used expert, so that the
+    # default path also forms a tile
+    e0 = np.bincount(ids.reshape(-1)).argmax()
+    k[..., 0][ids == e0] = 3
+    xd = dev(x)
+    outs = {}
+    for name, flags in (("default", 0), ("read_once", pm.PM_READ_ONCE),
+                        ("mfma", pm.PM_BATCH_MFMA)):
+        y = torch.empty((B, wl.hidden), dtype=torch.float32, device="cuda")
+        pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y, flags=flags)
+        outs[name] = host(y)
+    rows = oc.sample_rows(wl.hidden, 6, 50 + case)
+    for t in sorted({0, B // 2, B - 1}):
+        want, S = oc.token_layer(1, 0, ids[t], w[t], k[t], x[t], rows)
+        for name, got in outs.items():
+            assert_close(got[t][rows], want, S, f"{name}, token {t}")
+    ref = outs["default"]
+    for name in ("read_once", "mfma"):
+        got = outs[name]
+        assert np.all(np.abs(got - ref) <= 1e-4 * (np.abs(ref).max(axis=1, keepdims=True) + 1e-3)), name
