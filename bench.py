@@ -740,20 +740,26 @@ def main():
     ceiling = copy_ceiling(torch, stream)
     log(f"stream ceiling: {ceiling['GBs']} GB/s ({ceiling['kernel']})")
 
-    # roofline pass: HIP events around each stage on the library's stream
-    evs = []
-    for s in steps:
-        four = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        for ev in four:
-            ev.record(stream)
-        evs.append(four)
-    torch.cuda.synchronize()
-    for s, four in zip(steps, evs):
-        pm.pm_store_set_profile_events(st, four)
-        run(s)
-    pm.pm_store_set_profile_events(st, [])
-    torch.cuda.synchronize()
-    gu_ms = np.array([a.elapsed_time(b) for a, b, _, _ in evs])
+    # roofline pass: the gate/up launch's own start and stop events (HIP
+    # events on the library's stream), nothing else queued; then a pass with
+    # events after every stage for the stage split
+    def event_pass(n_ev):
+        evs = []
+        for s in steps:
+            group = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+            for ev in group:
+                ev.record(stream)
+            evs.append(group)
+        torch.cuda.synchronize()
+        for s, group in zip(steps, evs):
+            pm.pm_store_set_profile_events(st, group)
+            run(s)
+        pm.pm_store_set_profile_events(st, [])
+        torch.cuda.synchronize()
+        return evs
+
+    gu_ms = np.array([a.elapsed_time(b) for a, b in event_pass(2)])
+    evs = event_pass(4)
     dn_ms = np.array([b.elapsed_time(c) for _, b, c, _ in evs])
     cb_ms = np.array([c.elapsed_time(d) for _, _, c, d in evs])
     gu_b = np.array([gateup_bytes(wl, k3[s]) for s in steps])

@@ -343,7 +343,8 @@ def pm_store_copy_stats(store):
 
 
 def pm_store_set_profile_events(store, events):
-    """events: list of 4 torch.cuda.Event (or [] to switch off)."""
+    """events: list of 2 (gate/up launch only) or 4 (every stage)
+    torch.cuda.Event, or [] to switch off."""
     if not events:
         return _check(lib().pm_store_set_profile_events(store.handle, None, 0))
     arr = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])

@@ -518,6 +518,7 @@ struct pm_store {
     uint64_t total_planes = 0, total_bytes = 0;
     hipEvent_t prof[4] = {};
     bool profiling = false;
+    int n_prof = 0;                    // 2: gate/up only; 4: every stage
 };
 
 static pm_status slot_of(const pm_store* s, int layer, int expert, size_t* idx) {
@@ -787,8 +788,9 @@ extern "C" pm_status pm_store_set_profile_events(pm_store* s, void* const* event
         s->profiling = false;
         return PM_OK;
     }
-    if (n < 4 || !events) return failf(PM_ERR_ARG, "need 4 events");
-    for (int i = 0; i < 4; ++i) s->prof[i] = (hipEvent_t)events[i];
+    if ((n != 2 && n < 4) || !events) return failf(PM_ERR_ARG, "need 2 or 4 events");
+    s->n_prof = n >= 4 ? 4 : 2;
+    for (int i = 0; i < s->n_prof; ++i) s->prof[i] = (hipEvent_t)events[i];
     s->profiling = true;
     return PM_OK;
 }
@@ -1575,7 +1577,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         }
     }
     for (const KLaunch& L : L_dn) HIP_TRY(launch_lut(L, true, compute));
-    if (s->profiling) HIP_TRY(hipEventRecord(s->prof[2], compute));
+    if (s->profiling && s->n_prof >= 4) HIP_TRY(hipEventRecord(s->prof[2], compute));
     const int tok_per = std::max(1, kMaxLaunchUses / top_k);
     for (int t0 = 0; t0 < n_tokens; t0 += tok_per) {
         KCombine C{};
@@ -1593,7 +1595,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         }
         HIP_TRY(launch_combine_k(C, compute));
     }
-    if (s->profiling) HIP_TRY(hipEventRecord(s->prof[3], compute));
+    if (s->profiling && s->n_prof >= 4) HIP_TRY(hipEventRecord(s->prof[3], compute));
     std::vector<Slot*> read(n_items);
     for (int i = 0; i < n_items; ++i) read[i] = &slot_of_item(order[i]);
     return finish_forward(s, compute, read);

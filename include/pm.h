@@ -218,9 +218,10 @@ pm_status pm_store_copy_stats(const pm_store* s, int* last_first, int* last_coun
 /* Optional timing hook: when n >= 4, each pm_moe_token_forward on this store
  * records events[0] before its first kernel, events[1] after the gate/up
  * kernels, events[2] after the down kernels and events[3] after the combine
- * (hipEvent_t handles on the compute stream).  When the gate/up stage is a
- * single launch, events[0] and events[1] are that launch's own start and stop.
- * n = 0 switches it off. */
+ * (hipEvent_t handles on the compute stream); n = 2 records events[0] and
+ * events[1] only.  When the gate/up stage is a single launch, events[0] and
+ * events[1] are that launch's own start and stop.  n = 0 switches it off;
+ * other n are PM_ERR_ARG. */
 pm_status pm_store_set_profile_events(pm_store* s, void* const* events, int n);
 
 /* ---------------------------------------------------------------- expert caches

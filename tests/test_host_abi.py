@@ -184,6 +184,13 @@ def test_store_errors():
     with pytest.raises(pm.PMError) as ei:
         pm.pm_store_resident(st, 0, 2)
     assert ei.value.status == pm.PM_ERR_ARG
+    # the timing hook takes 2 or 4 events, or none
+    L = pm.lib()
+    two = (ctypes.c_void_p * 4)(1, 2, 3, 4)
+    for n, ok in ((2, True), (4, True), (0, True), (3, False), (1, False)):
+        rc = L.pm_store_set_profile_events(st.handle, two if n else None, n)
+        assert (rc == 0) == ok, n
+    assert L.pm_store_set_profile_events(st.handle, None, 0) == 0
     # a host-backed store cannot run a forward
     with pytest.raises(pm.PMError) as ei:
         pm.pm_moe_token_forward(st, 0, np.zeros((1, 1)), np.ones((1, 1)), np.ones((1, 1, 3)),
