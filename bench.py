@@ -73,6 +73,24 @@ def grouped_bytes(wl, ids, k3):
     return b + 2 * len(ids) * wl.hidden * 4
 
 
+PEAK_FP32_MFMA_TFLOPS = 157.3
+
+
+def mfma_flops(wl, ids, k3):
+    """Flops of one PM_BATCH_MFMA call: useful (2 per weight per use) and
+    issued (every tile of up to 16 uses of one (expert, matrix, k) computes
+    16 columns)."""
+    useful = issued = 0
+    for e in np.unique(ids):
+        sel = k3[ids == e]
+        for m in range(3):
+            r, c = (wl.inter, wl.hidden) if m < 2 else (wl.hidden, wl.inter)
+            n_by_k = np.bincount(sel[:, m].astype(np.int64), minlength=9)
+            useful += 2 * r * c * int(n_by_k.sum())
+            issued += 2 * r * c * 16 * int(sum((n + 15) // 16 for n in n_by_k))
+    return useful, issued
+
+
 def gateup_bytes(wl, kk):
     b = 0
     for k3 in kk:
@@ -479,6 +497,10 @@ def bench_batches(args, torch, pm, synth, PoolFiller):
         res["algorithmic_MB"] = round(gb / 1e6, 1)
         res["default_GBs"] = round(gb / (res["default_ms"] / 1e3) / 1e9, 1)
         res["mfma_GBs"] = round(gb / (res["mfma_ms"] / 1e3) / 1e9, 1)
+        fl = np.mean([mfma_flops(wl, st_[0], st_[2]) for st_ in steps[1:]], axis=0)
+        res["mfma_useful_TFLOPs"] = round(float(fl[0]) / (res["mfma_ms"] / 1e3) / 1e12, 1)
+        res["mfma_issued_TFLOPs"] = round(float(fl[1]) / (res["mfma_ms"] / 1e3) / 1e12, 1)
+        res["mfma_tile_fill"] = round(float(fl[0] / fl[1]), 3)
         res["tokens_per_s_mfma"] = round(B / (res["mfma_ms"] / 1e3), 1)
         res["tokens_per_s"] = round(B / (res["default_ms"] / 1e3), 1)
         res["mfma_speedup"] = round(res["default_ms"] / res["mfma_ms"], 2)
