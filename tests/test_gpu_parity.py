@@ -339,7 +339,8 @@ def test_forward_tiny_all_k_triples():
 
 @pytest.fixture(scope="module")
 def layer_store():
-    """configs[1]: a 512-expert layer; slots are filled on demand."""
+    """A 512-expert layer (hidden 4096, inter 1024, group 128); slots are filled on
+    demand."""
     wl = synth.WORKLOADS[1]
     e = pm.eshape(wl.hidden, wl.inter, wl.group)
     st = pm.pm_store_create(e, 1, wl.n_experts)
@@ -358,7 +359,7 @@ def layer_store():
 
 
 def test_forward_layer_full_size(layer_store):
-    report("configs[1]: 512-expert layer, one token, mean k 2.5, sampled rows")
+    report("512-expert layer, one token, top-10, mean k 2.5, sampled rows")
     wl, st, ensure = layer_store
     ids, w, k = oc.route_and_bits(1, 0, step=0)
     # the product's routing and allocation agree with the oracle's
@@ -374,7 +375,7 @@ def test_forward_layer_full_size(layer_store):
     got = host(y)[0]
     rows = oc.sample_rows(wl.hidden, 48, 1)
     want, S = oc.token_layer(1, 0, ids, w, k, x, rows)
-    assert_close(got[rows], want, S, "configs[1]")
+    assert_close(got[rows], want, S, "512-expert layer, one token")
     # determinism
     y2 = torch.empty_like(y)
     pm.pm_moe_token_forward(st, 0, ids[None], w[None], k[None], dev(x[None]), y2)
@@ -383,7 +384,7 @@ def test_forward_layer_full_size(layer_store):
 
 @pytest.mark.parametrize("kfix", [4, 8, None])
 def test_forward_uniform_precisions_and_materialize(layer_store, kfix):
-    report(f"configs[3]: k={kfix or 'mixed'} direct and materialize-fp16")
+    report(f"512-expert layer at k={kfix or 'mixed'}: direct and materialize-fp16")
     wl, st, ensure = layer_store
     ids, w, k = oc.route_and_bits(1, 0, step=0, kfix=kfix)
     ensure(ids)
@@ -408,7 +409,7 @@ def test_forward_uniform_precisions_and_materialize(layer_store, kfix):
 
 
 def test_forward_sixty_layers():
-    report("configs[2]: 60 layers x top-10, sampled rows on 2 layers")
+    report("60 layers x top-10, sampled rows on 2 layers")
     wl = synth.WORKLOADS[2]
     e = pm.eshape(wl.hidden, wl.inter, wl.group)
     st = pm.pm_store_create(e, wl.n_layers, wl.n_experts)
@@ -436,7 +437,7 @@ def test_forward_sixty_layers():
 
 
 def test_forward_batch8_grouped_with_topup():
-    report("configs[4]: B=8 grouped, 20% topped up from pinned host")
+    report("B=8 grouped, 20% of experts topped up from pinned host")
     wl = synth.WORKLOADS[4]
     e = pm.eshape(wl.hidden, wl.inter, wl.group)
     pw = pm.pm_expert_plane_words(e)
@@ -524,7 +525,7 @@ def test_read_once_matches_default():
     direct kernels) against the default path (a LUT job per use) on a B = 8
     step: both against the oracle, and bit for bit on the tokens none of whose
     experts is shared (their jobs are the same in both)."""
-    report("configs[4] routing, all resident: PM_READ_ONCE vs default")
+    report("B=8 routing, all resident: PM_READ_ONCE vs default")
     wl = synth.WORKLOADS[4]
     e = pm.eshape(wl.hidden, wl.inter, wl.group)
     st = pm.pm_store_create(e, 1, wl.n_experts)
