@@ -1,8 +1,7 @@
 // HIP kernels of libpm for gfx950 (CDNA4, 64-wide wavefronts).
 //
-// Two ways to execute a matrix directly from its k-bit prefix [Abs
-// "directly executes cached 1-8-bit prefixes without materializing
-// full-precision experts"; T c25, c37]:
+// Two ways to execute a matrix directly from its k-bit prefix, without ever
+// forming a full-precision copy [Abs; T c25, c37]:
 //
 // LUT path (k <= 5 in a layer, k <= 4 in a single GEMV; columns in slices of
 // 1024).  The result of one block of a row is sum_v node[v] * S_v, where S_v

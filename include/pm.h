@@ -89,8 +89,8 @@ pm_status pm_expert_matrix_offsets(pm_expert_shape e, int m, size_t* plane_word_
                                    size_t* level_float_off, pm_matrix_shape* shape_out);
 
 /* ---------------------------------------------------------------- encoding
- * Offline encoder [T c19, c21, c25; Abs "stores each expert once using a
- * prefix-compatible tree codebook and bitplane layout"].
+ * Offline encoder [T c19, c21, c25; Abs: one stored copy per expert, in a
+ * tree codebook whose prefixes nest, laid out as bitplanes].
  *   codes:  uint8 [rows][cols], the 8-bit leaf index of every weight.
  *   leaves: fp32 [rows][cols/group][256], ascending per block (else
  *           PM_ERR_ARG).
@@ -138,9 +138,9 @@ pm_status pm_kmeans_codebook_device(pm_matrix_shape s, const float* d_w, int max
 
 /* ---------------------------------------------------------------- prefix GEMV
  * y[o] = sum_i node(k, o, i/group, prefix_k(o, i)) * x[i]: one matrix read
- * directly at a k-bit prefix, no decoded matrix is formed [Abs "directly
- * executes cached 1-8-bit prefixes without materializing full-precision
- * experts"; T c37].  Reads planes 0..k-1 and depth k only.
+ * directly at a k-bit prefix, no decoded matrix is formed [Abs: execution
+ * straight from a cached prefix of 1 to 8 bits, never a full-precision copy;
+ * T c37].  Reads planes 0..k-1 and depth k only.
  *   d_x fp32 [cols], 16-byte aligned; d_y fp32 [rows] (overwritten; cols == 0
  *   gives zeros).
  *   Errors: PM_ERR_PREFIX (k), PM_ERR_SHAPE, PM_ERR_ARG (null pointer or
@@ -158,9 +158,9 @@ pm_status pm_expert_gemv(pm_matrix_shape s, int k, const uint32_t* d_planes,
 pm_status pm_route_topk(int n_tokens, int n_experts, int top_k, const float* logits,
                         int32_t* ids_out, float* w_out);
 
-/* Pre-I/O prefix-length allocation [T c29, c31; Abs "selects the required
- * prefix length before I/O using current routing weights and offline
- * expert-specific error profiles"].  Per token: minimise
+/* Pre-I/O prefix-length allocation [T c29, c31; Abs: the prefix length is
+ * chosen before any read, from the token's routing weights and per-expert
+ * error profiles measured offline].  Per token: minimise
  * sum_j w_j^2 * err_{ids_j}(b_j) subject to sum_j b_j = budget: start every
  * selected expert at 1 bit and grant, one at a time, the bit with the largest
  * gain (w*w) * (err(b) - err(b+1)) (fp64, w widened from fp32; ties to the
@@ -175,8 +175,8 @@ pm_status pm_allocate_bits(int n_tokens, int top_k, const int32_t* ids, const fl
 
 /* ---------------------------------------------------------------- plane store
  * HBM store of encoded experts with plane-granular residency [T c13, c35;
- * Abs "cached data ... reused or extended by fetching only missing
- * bitplanes"].  A slot (layer, expert) holds the 8 plane chunks and the levels
+ * Abs: a cached prefix is reused as is or extended by reading only the planes
+ * it lacks].  A slot (layer, expert) holds the 8 plane chunks and the levels
  * of one expert; its resident prefix r counts the leading planes that are
  * valid.  A plane is usable only when every earlier plane is resident, so r
  * is always a prefix count.  The store owns all slot memory.

@@ -30,7 +30,7 @@ NLEAF = 1 << NBITS
 
 
 # ---------------------------------------------------------------------------
-# Tree codebook  ([T] c19, c21; [Abs] "prefix-compatible tree codebook")
+# Tree codebook  ([T] c19, c21; [Abs]: a tree codebook whose prefixes nest)
 # ---------------------------------------------------------------------------
 def tree_levels(leaves, counts=None, depth=NBITS):
     """Levels of the binary-tree codebook over sorted leaves.
@@ -137,7 +137,7 @@ def prefix_codes(planes, k):
 
 
 # ---------------------------------------------------------------------------
-# Decode and GEMV  ([Abs] "directly executes cached 1-8-bit prefixes";
+# Decode and GEMV  ([Abs]: execution straight from a cached 1-8-bit prefix;
 # [T] c37: indices assembled from the requested planes, codebook lookup,
 # dot product; no full-precision matrix is needed)
 # ---------------------------------------------------------------------------
@@ -314,9 +314,9 @@ def route(logits, top_k):
 
 
 # ---------------------------------------------------------------------------
-# Pre-I/O bit allocation  ([T] c29, c31; [Abs] "selects the required prefix
-# length before I/O using current routing weights and offline
-# expert-specific error profiles")
+# Pre-I/O bit allocation  ([T] c29, c31; [Abs]: the prefix length is chosen
+# before any read, from the token's routing weights and per-expert error
+# profiles measured offline)
 # ---------------------------------------------------------------------------
 def isotonic_nonincreasing(d):
     """Least-squares fit of a non-increasing sequence to d (pool adjacent
