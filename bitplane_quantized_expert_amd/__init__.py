@@ -29,6 +29,7 @@ PM_STORE_HOST_FAKE = 1
 PM_AUTO_TOPUP = 1
 PM_BATCH_MFMA = 2
 PM_READ_ONCE = 4
+PM_DETERMINISTIC = 8
 
 _STATUS = {0: "PM_OK", -1: "PM_ERR_ARG", -2: "PM_ERR_SHAPE", -3: "PM_ERR_PREFIX",
            -4: "PM_ERR_NOT_RESIDENT", -5: "PM_ERR_OOM", -6: "PM_ERR_HIP", -7: "PM_ERR_STATE"}

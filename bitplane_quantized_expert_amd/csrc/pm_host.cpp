@@ -1181,7 +1181,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
                                           void* compute_v, uint32_t flags) {
     if (!s) return failf(PM_ERR_ARG, "null store");
     if (s->host_fake) return failf(PM_ERR_STATE, "a host-backed store cannot compute");
-    if (flags & ~uint32_t(PM_AUTO_TOPUP | PM_BATCH_MFMA | PM_READ_ONCE))
+    if (flags & ~uint32_t(PM_AUTO_TOPUP | PM_BATCH_MFMA | PM_READ_ONCE | PM_DETERMINISTIC))
         return failf(PM_ERR_ARG, "unknown forward flags");
     const bool mfma = flags & PM_BATCH_MFMA;
     const bool read_once = flags & PM_READ_ONCE;

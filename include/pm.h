@@ -294,9 +294,11 @@ pm_status pm_cache_stats(const pm_cache* c, uint64_t* accesses, uint64_t* hits,
  * prefix_kmax >> (kmax - k) [T c25, c35] (the matrix-core tiles still take
  * groups of at least 6 uses).  Same values as the default path; the default
  * (a LUT job per use) re-reads the planes but needs fewer instructions.
+ * PM_DETERMINISTIC is accepted and always holds: every sum runs in a fixed
+ * order (no atomics), so the same call on the same inputs gives the same bits.
  * The store keeps per-call workspace; calls on one store are serialised on
  * `compute`. */
-enum { PM_AUTO_TOPUP = 1u, PM_BATCH_MFMA = 2u, PM_READ_ONCE = 4u };
+enum { PM_AUTO_TOPUP = 1u, PM_BATCH_MFMA = 2u, PM_READ_ONCE = 4u, PM_DETERMINISTIC = 8u };
 pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, int top_k,
                                const int32_t* h_ids, const float* h_w, const uint8_t* h_k,
                                const float* d_x, float* d_y, void* compute, uint32_t flags);

@@ -101,8 +101,12 @@ def test_mfma_crowded_batch_all_k(store512):
         want, S = oc.token_layer(1, 0, ids[t], w[t], k[t], x[t], rows)
         assert_close(ref[t][rows], want, S, f"default path, token {t}")
     y2 = torch.empty_like(y)
-    pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y2, flags=pm.PM_BATCH_MFMA)
+    pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y2,
+                            flags=pm.PM_BATCH_MFMA | pm.PM_DETERMINISTIC)
     assert np.array_equal(host(y2).view(np.uint32), got.view(np.uint32))
+    y3 = torch.empty_like(y)
+    pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y3, flags=pm.PM_DETERMINISTIC)
+    assert np.array_equal(host(y3).view(np.uint32), ref.view(np.uint32))
 
 
 def test_mfma_full_layer_batch(store512):
