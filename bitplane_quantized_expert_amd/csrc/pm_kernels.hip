@@ -642,9 +642,11 @@ __device__ inline float row_dot_lane(const uint32_t* __restrict__ planes, size_t
     return acc;
 }
 
-// Group 128 and k >= 5: the depth-k tables dominate the bytes (8 << k per
-// 32-word run against k words of planes), and a per-weight gather straight
-// from global memory touches up to 64 cache lines per instruction.  Here a
+// Group 128, rows of whole 1024-column runs, any k (staging was first needed
+// at k >= 5, where the depth-k tables dominate the bytes: 8 << k per 32-word
+// run against k words of planes, and a per-weight gather straight from
+// global memory touches up to 64 cache lines per instruction; it also won at
+// smaller k, for experts shared by several uses).  Here a
 // wave takes a row in runs of 32 words (8 blocks, 1024 inputs); each lane
 // takes half a word.  The run's 8 tables are one contiguous range of the
 // level-major layout: they arrive as coalesced 16-byte loads (the next run's
@@ -712,8 +714,8 @@ __device__ __attribute__((always_inline)) inline float row_dot_lds(
 }
 
 // This lane's share of row o at prefix k: the LDS-staged form where it
-// applies (group 128, k >= 5, whole runs, 16-byte aligned tables), else
-// row_dot_lane.  The choice is uniform over the wave.
+// applies (group 128, k >= kLdsMinK, whole runs), else row_dot_lane.  The
+// choice is uniform over the wave.
 __device__ __attribute__((always_inline)) inline float row_dot(
     const uint32_t* __restrict__ planes, size_t pstride, const float* __restrict__ lv_k, int k,
     int o, int W, int wpg, const float* __restrict__ x, lds_f32* __restrict__ tabs, int lane) {
