@@ -1328,7 +1328,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     const size_t fGU = align256(size_t(n_uses) * 2 * S_gu * g.inter);
     const size_t fH = align256(size_t(n_uses) * g.inter);
     const size_t fY = align256(size_t(n_uses) * S_dn * g.hidden);
-    // the work list is uploaded only when direct-path items exist
+    // the work list is uploaded only when direct-path items or tiles exist
     std::vector<int> dir_gu[2], dir_dn;      // positions in `order`
     for (int grp = 0; grp < 2; ++grp) {
         const int i0 = grp == 0 ? 0 : n_res, i1 = grp == 0 ? n_res : n_items;
@@ -1445,7 +1445,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     }
 
 
-    // ---- direct-path work list into the pinned ring, then to the device
+    // ---- direct-path work list and tiles into the pinned ring, then to the device
     const Use* duses = nullptr;
     const int32_t* dlist = nullptr;
     const Item* ddir = nullptr;
