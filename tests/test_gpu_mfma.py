@@ -260,3 +260,45 @@ def test_path_mixes_random(store512, case):
     for name in ("read_once", "mfma"):
         got = outs[name]
         assert np.all(np.abs(got - ref) <= 1e-4 * (np.abs(ref).max(axis=1, keepdims=True) + 1e-3)), name
+
+
+def test_forward_degenerate_cases(store512):
+    """Edge cases of one layer call, each against the oracle through every
+    forward mode: no tokens; top-1; the same expert twice in one token; a
+    zero routing weight; uses of one (expert, matrix, k) group exactly at the
+    matrix-core threshold (6) and just below it (5)."""
+    report("degenerate layer calls: empty, top-1, repeated expert, zero weight, tile threshold")
+    wl, st, ensure = store512
+    modes = (0, pm.PM_READ_ONCE, pm.PM_BATCH_MFMA)
+    # no tokens: nothing to do, no error
+    x0 = torch.empty((0, wl.hidden), dtype=torch.float32, device="cuda")
+    for flags in modes:
+        pm.pm_moe_token_forward(st, 0, np.zeros((0, 2), np.int32), np.zeros((0, 2), np.float32),
+                                np.zeros((0, 2, 3), np.uint8), x0, torch.empty_like(x0),
+                                flags=flags)
+    rows = oc.sample_rows(wl.hidden, 6, 60)
+
+    def check(ids, w, k, what):
+        ids = np.asarray(ids, np.int32)
+        w = np.asarray(w, np.float32)
+        k = np.asarray(k, np.uint8)
+        ensure(ids)
+        B = ids.shape[0]
+        x = np.stack([synth.activation(wl.seed, wl.cfg, 0, t, wl.hidden, step=61) for t in range(B)])
+        wants = [oc.token_layer(1, 0, ids[t], w[t], k[t], x[t], rows) for t in range(B)]
+        for flags in modes:
+            y = torch.empty((B, wl.hidden), dtype=torch.float32, device="cuda")
+            pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y, flags=flags)
+            got = host(y)
+            for t in range(B):
+                assert_close(got[t][rows], wants[t][0], wants[t][1], f"{what}, flags {flags}, token {t}")
+
+    check([[3], [4], [3]], [[1.0], [1.0], [1.0]], [[[2, 3, 4]], [[5, 1, 8]], [[8, 8, 8]]], "top-1")
+    check([[5, 5]], [[0.6, 0.4]], [[[2, 2, 2], [4, 6, 1]]], "repeated expert")
+    check([[6, 7]], [[1.0, 0.0]], [[[3, 3, 3], [2, 2, 2]]], "zero weight")
+    # expert 8: gate at k = 3 for 6 uses (a tile in the default path), up at
+    # k = 2 for 5 uses (LUT jobs) plus one at k = 7, down at k = 4 for all
+    ids = [[8, 9 + t] for t in range(6)]
+    w = [[0.7, 0.3]] * 6
+    k = [[[3, 2 if t < 5 else 7, 4], [1 + t, 2, 3]] for t in range(6)]
+    check(ids, w, k, "tile threshold")
