@@ -11,8 +11,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 ARCH = os.environ.get("PM_OFFLOAD_ARCH", "gfx950")
 
-HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+COMPILE_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 VALU forms stay off; sums are written with explicit fmaf
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=off", "-Wall", "-Wno-unused-function",
@@ -27,6 +27,13 @@ TARGETS = [
      [os.path.join(ROOT, "synth", "synth_device.hip")]),
 ]
 
+# Per-source extra flags.  The LUT kernels issue many independent table
+# lookups per step; the machine scheduler's ILP strategy keeps them in flight
+# instead of interleaving each with its use.
+EXTRA = {
+    "pm_kernels.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
 
 def hipcc():
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
@@ -35,22 +42,43 @@ def hipcc():
     return "hipcc"
 
 
-def build(verbose=False):
+def _run(cmd, what, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed building {what}")
+
+
+def build(verbose=False, extra_flags=(), out_override=None):
+    """Compile every source to an object (with its own extra flags), then
+    link each library.  extra_flags / out_override serve tuning builds."""
+    import concurrent.futures as cf
+    outs = []
     for out, srcs in TARGETS:
-        tmp = out + ".tmp"
-        cmd = [hipcc()] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include")]
-        # .cpp sources hold host code only; compile them as HIP so one link works
+        if out_override and out.endswith("libpm.so"):
+            out = out_override
+        objs, jobs = [], []
         for s in srcs:
+            obj = os.path.join(os.path.dirname(out), "_build",
+                               os.path.basename(s) + "." + os.path.basename(out) + ".o")
+            os.makedirs(os.path.dirname(obj), exist_ok=True)
+            cmd = [hipcc()] + COMPILE_FLAGS + list(extra_flags) + EXTRA.get(os.path.basename(s), []) + [
+                "-I", os.path.join(ROOT, "include"), "-c"]
+            # .cpp sources hold host code only; compile them as HIP so one link works
             cmd += (["-x", "hip", s] if s.endswith(".cpp") else [s])
-        cmd += ["-o", tmp]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            sys.stderr.write(r.stdout + r.stderr)
-            raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
+            cmd += ["-o", obj]
+            objs.append(obj)
+            jobs.append((cmd, os.path.basename(s)))
+        with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+            list(ex.map(lambda j: _run(j[0], j[1], verbose), jobs))
+        tmp = out + ".tmp"
+        _run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}"] + objs + ["-o", tmp],
+             os.path.basename(out), verbose)
         os.replace(tmp, out)
-    return [t for t, _ in TARGETS]
+        outs.append(out)
+    return outs
 
 
 if __name__ == "__main__":

@@ -299,7 +299,7 @@ extern "C" pm_status pm_expert_gemv(pm_matrix_shape s, int k, const uint32_t* d_
     if (s.cols > 0 && !d_x) return failf(PM_ERR_ARG, "null x");
     if (reinterpret_cast<uintptr_t>(d_x) % 16) return failf(PM_ERR_ARG, "x not 16-byte aligned");
     if (k <= kGemvLutMaxK && s.cols > 0 && s.cols % kSliceCols == 0 && s.group == kLutGroup &&
-        s.rows % 2 == 0 && lut_offsets_fit(s, k, pstride))
+        s.rows % kLutRows == 0 && lut_offsets_fit(s, k, pstride))
         return gemv_lut(s, k, d_planes, pstride, d_levels, d_x, d_y, (hipStream_t)stream);
     HIP_TRY(launch_gemv(s.rows, s.cols, s.group, k, d_planes, pstride, d_levels, d_x, d_y,
                         (hipStream_t)stream));
@@ -819,14 +819,14 @@ struct JobSpec {                       // a LUT job before it is packed into a l
 }  // namespace
 
 // Row cuts of a launch (KLaunch::start), contiguous: the cost of all rows in
-// order is split into n_wgq equal parts, each cut at an even row of its job.
-// Cuts jobs j0 .. j1-1 of a launch into n_wg row ranges of about equal cost
-// (rows in pairs), writing L.start[w0 .. w0 + n_wg - 1].
+// order is split into equal parts, each cut at a multiple of kLutRows rows of
+// its job.  Cuts jobs j0 .. j1-1 of a launch into n_wg row ranges of about
+// equal cost, writing L.start[w0 .. w0 + n_wg - 1].
 static void cut_jobs(KLaunch& L, int j0, int j1, int n_wg, int w0) {
-    const int n = j1 - j0, rows = L.rows, pairs = (rows + 1) / 2;
+    const int n = j1 - j0, rows = L.rows, pairs = rows / kLutRows;
     std::vector<int64_t> pc(n), before(n + 1, 0);
     for (int j = 0; j < n; ++j) {
-        pc[j] = 2 * lut_row_cost(L.job[j0 + j].k, L.wpg);
+        pc[j] = kLutRows * lut_row_cost(L.job[j0 + j].k, L.wpg);
         before[j + 1] = before[j] + pc[j] * pairs;
     }
     const int64_t total = before[n];
@@ -836,20 +836,21 @@ static void cut_jobs(KLaunch& L, int j0, int j1, int n_wg, int w0) {
         const int64_t target = total * q / n_wg;
         while (j < n - 1 && before[j + 1] <= target) ++j;
         const int64_t p = (target - before[j] + pc[j] - 1) / pc[j];
-        L.start[w0 + q] = (j0 + j) * rows + int(std::min<int64_t>(rows, 2 * p));
+        L.start[w0 + q] = (j0 + j) * rows + int(std::min<int64_t>(rows, kLutRows * p));
     }
 }
 
 // Workgroup ranges of a launch whose jobs come in runs of one source (one
-// activation table): every run gets whole workgroups, in proportion to its
-// cost (largest remainder, at least one each), and no workgroup spans two
-// runs, so a workgroup builds its table once.  One run: the whole launch is
-// cut by cost.
+// activation table) and one prefix: every run gets whole workgroups, in
+// proportion to its cost (largest remainder, at least one each), and no
+// workgroup spans two runs, so a workgroup builds its table once and runs
+// one prefix's code throughout.
 static void set_starts_by_source(KLaunch& L, int n_total) {
     const int n = L.n_jobs;
     std::vector<int> r0;                       // first job of every run
     for (int j = 0; j < n; ++j)
-        if (j == 0 || L.job[j].src != L.job[j - 1].src) r0.push_back(j);
+        if (j == 0 || L.job[j].src != L.job[j - 1].src || L.job[j].k != L.job[j - 1].k)
+            r0.push_back(j);
     const int R = int(r0.size());
     r0.push_back(n);
     n_total = std::min(kMaxLaunchWgq, std::max(n_total, R));
@@ -885,6 +886,10 @@ static void set_starts_by_source(KLaunch& L, int n_total) {
     int w = 0;
     for (int r = 0; r < R; ++r) {
         cut_jobs(L, r0[r], r0[r + 1], a[r], w);
+        const KJob& jb = L.job[r0[r]];
+        const uint32_t meta = uint32_t(uint16_t(jb.src)) | (uint32_t(jb.k) << 16) |
+                              (uint32_t(jb.gsl) << 24);
+        for (int q = w; q < w + a[r]; ++q) L.meta[q] = meta;
         w += a[r];
     }
     L.start[w] = n * L.rows;
@@ -1298,12 +1303,12 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
 
     // ---- path of every (use, matrix) outside the tiles: LUT at k <= 5 when
     // the columns split into 1024-column slices (at most 15), else direct
-    // the LUT path takes rows in pairs (an even number of rows per matrix)
-    // and blocks of kLutGroup inputs
+    // the LUT path takes rows in steps of kLutRows and blocks of kLutGroup
+    // inputs
     const bool gu_lut_shape = g.hidden % kSliceCols == 0 && g.group == kLutGroup &&
-                              g.hidden / kSliceCols <= 15 && g.inter % 2 == 0;
+                              g.hidden / kSliceCols <= 15 && g.inter % kLutRows == 0;
     const bool dn_lut_shape = g.inter % kSliceCols == 0 && g.group == kLutGroup &&
-                              g.hidden % 2 == 0;
+                              g.hidden % kLutRows == 0;
     const int S_gu = gu_lut_shape ? g.hidden / kSliceCols : 1;
     const int S_dn = dn_lut_shape ? g.inter / kSliceCols : 1;
     for (int d = 0; d < n_items; ++d) {
@@ -1400,9 +1405,10 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
                 }
             }
         }
-        // jobs of one token share an activation table: keep them adjacent
+        // jobs of one token share an activation table, and a workgroup runs
+        // one prefix: keep the jobs of one (token, k) adjacent
         std::stable_sort(js.begin(), js.end(), [](const JobSpec& a, const JobSpec& b) {
-            return a.job.src < b.job.src;
+            return a.job.src != b.job.src ? a.job.src < b.job.src : a.job.k < b.job.k;
         });
         pack_launches(js, gu_proto, L_gu[grp]);
     }

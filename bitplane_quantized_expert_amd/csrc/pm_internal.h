@@ -78,8 +78,12 @@ struct Partials {
 };
 
 constexpr int kSliceCols = 1024;   // columns of x covered by one LUT
-// Block size of the LUT path: the four lanes of a block share its table.
+// Block size of the LUT path: one lane holds a block's four plane words and
+// its depth-k nodes.
 constexpr int kLutGroup = 128;
+// Rows of one wave step on the LUT path (8 rows x the 8 blocks of a slice);
+// matrices on the LUT path have a multiple of 8 rows.
+constexpr int kLutRows = 8;
 // Largest prefix read through the LUT path: in a layer forward (one launch
 // for all experts; larger prefixes add the direct launches) and in a single
 // GEMV (from k = 5 the staged-table direct path is faster).
@@ -87,7 +91,7 @@ constexpr int kLutMaxK = 5;
 constexpr int kGemvLutMaxK = 4;
 
 // LUT-path launch description, passed as kernel arguments (no upload).
-constexpr int kMaxLaunchJobs = 64;
+constexpr int kMaxLaunchJobs = 56;
 // Uses in one forward call: a job names its token or use in 16 bits.
 constexpr int kMaxCallUses = 32767;
 struct KJob {                      // one matrix of one use
@@ -99,7 +103,7 @@ struct KJob {                      // one matrix of one use
     int8_t k;
     uint8_t gsl;                   // down: gate slices (bits 0-3), up slices (bits 4-7)
 };
-// One LUT launch: n_wgq * S workgroups.  The rows of the jobs are numbered
+// One LUT launch: n_wgq x S workgroups.  The rows of the jobs are numbered
 // as one sequence (row r of job j is g = j * rows + r); workgroup q of every
 // slice runs g in [start[q], start[q + 1]), cut by the host so that the work
 // is balanced.  Scalars come first so that the fields every workgroup reads
@@ -114,16 +118,18 @@ struct KLaunch {
     int32_t W, wpg, out_stride, x_stride;
     int32_t gu_smax, inter, pad0, pad1;
     int32_t start[kMaxLaunchWgq + 2];
+    // per row range q: activation source (bits 0-15: token or use), prefix k
+    // (bits 16-19), gate/up slice counts of a down job (bits 24-31)
+    uint32_t meta[kMaxLaunchWgq + 2];
     KJob job[kMaxLaunchJobs];
 };
 static_assert(sizeof(KLaunch) <= 4096, "kernel arguments are limited to 4 KiB");
-// Cost of one row-slice when rows are split among workgroups: its execution
-// time, dominated by the 2^k - 1 mask lookups per word plus a fixed per-row
-// share (loads, reduction, store); k = 1 rows carry a larger fixed share.
-// Measured on gfx950 with the layer's rows streamed from HBM (workgroup
-// durations per prefix), in integer units.
+// Cost of one row-slice (1024 columns) when rows are split among
+// workgroups: the time of one 8-row step of a workgroup at prefix k, measured
+// on gfx950 (ns; the rows of one launch streamed from HBM), divided by 8.
 __host__ __device__ inline int64_t lut_row_cost(int k, int /*wpg*/) {
-    return k == 1 ? 400 : 220 + 75 * ((int64_t(1) << k) - 1);
+    constexpr int64_t ns8[6] = {0, 97, 143, 225, 420, 800};
+    return ns8[k < 1 ? 1 : (k > 5 ? 5 : k)];
 }
 
 // Kernel launchers (pm_kernels.hip).  All return hipError_t of the launch.
@@ -142,7 +148,8 @@ hipError_t launch_dequant(int rows, int cols, int group, int k, const uint32_t* 
 hipError_t launch_gemv_fp16(int rows, int cols, const uint16_t* w, const float* x, float* y,
                             hipStream_t st);
 
-// LUT path: n_wgq * S workgroups of 1024 threads, about 132 KiB of LDS each.
+// LUT path: n_wgq x S workgroups of 1024 threads, 128 KiB of LDS each; every
+// workgroup's rows hold jobs of one source and one k.
 // Gate/up (down == false): the activation slice comes from L.x; down: h of
 // use src, formed from the gate/up partials L.gu.
 // t0 / t1: if given, the launch's own start and stop events.

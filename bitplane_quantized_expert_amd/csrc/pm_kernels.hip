@@ -4,16 +4,18 @@
 // forming a full-precision copy [Abs; T c25, c37]:
 //
 // LUT path (k <= 5 in a layer, k <= 4 in a single GEMV; columns in slices of
-// 1024).  The result of one block of a row is sum_v node[v] * S_v, where S_v
-// is the sum of x over the block's weights whose prefix is v.  A weight word (32 inputs) has prefix v exactly
-// where the AND of the k plane words (each taken plain or inverted by the
-// bits of v) is set, and the sum of x under a 32-bit mask is four lookups in
-// a table of all 256 subset sums of each 8-input chunk of x (an activation
-// lookup table, as in T-MAC).  The table of one 1024-column slice is 128 KiB
-// of LDS; every lookup is one v_perm (the mask byte becomes the address) and
-// one ds_read.  2^k - 1 masks per word, the last bucket by subtraction from
-// the word's total.  The codebook enters as 2^k FMAs per block and row, so no
-// weight value is ever formed.  One-hot x gives exact columns.
+// 1024, rows in steps of 8).  The result of one block of a row is
+// sum_v node[v] * S_v, where S_v is the sum of x over the block's weights
+// whose prefix is v.  A weight word (32 inputs) has prefix v exactly where the
+// AND of the k plane words (each taken plain or inverted by the bits of v) is
+// set, and the sum of x under a 32-bit mask is four lookups in a table of all
+// 256 subset sums of each 8-input chunk of x (an activation lookup table, as
+// in T-MAC).  The table of one 1024-column slice is 128 KiB of LDS; every
+// lookup is one v_perm (the mask byte becomes the address) and one ds_read.
+// One lane owns one 128-input block of one row: its four plane words arrive
+// as one 16-byte load per plane and its 2^k nodes as 16-byte loads, so the
+// codebook enters as one multiply per lookup with no cross-lane traffic, and
+// no weight value is ever formed.  One-hot x gives exact columns.
 //
 // Direct path (any k, any shape; an expert of several uses is read once for
 // all of them): per weight, the prefix is assembled from the k plane words
@@ -35,13 +37,6 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kRowsPerBlock = kBlock / kWave;
-#ifndef PM_LUT_THREADS
-#define PM_LUT_THREADS 1024
-#endif
-constexpr int kLutThreads = PM_LUT_THREADS;
-constexpr int kLutWaves = kLutThreads / kWave;
-constexpr int kLutBytes = 128 * 1024;
-constexpr int kHbufBytes = (kSliceCols + kSliceCols / 32) * 4;
 
 template <int CTRL, int ROW_MASK>
 __device__ inline float dpp(float v) {
@@ -91,508 +86,475 @@ __device__ inline T* uni_ptr(T* p) {
 }
 
 // ---------------------------------------------------------------- LUT path
-typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) float lds_float;
 // Global-memory views: in out-of-line functions a plain pointer would be
 // generic and its loads flat_load, which also count against the LDS wait
 // counter and would serialise the prefetch with the table lookups.
-typedef __attribute__((address_space(1))) const uint32_t g_u32;
 typedef __attribute__((address_space(1))) const float g_f32;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(1))) const f32x2 g_f32x2;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const f32x4 g_f32x4;
 typedef __attribute__((address_space(1))) float g_f32_out;
 
-// LDS layout of the activation table of one 1024-column slice: chunk c (8
-// columns 8c..8c+7), byte value b (a subset of the chunk), t = c & 3,
-// l = c >> 2 (the word of the slice the chunk belongs to):
-//   address = (t >> 1) << 16 | b << 8 | (l + 32 * (t & 1)) << 2.
-// Lane l of a half-wave reads chunks 4l..4l+3; at every lookup the 32 lanes of
-// a half-wave touch 32 different banks.
-__device__ inline uint32_t lut_addr(int c, int b) {
-    const int t = c & 3, l = c >> 2;
-    return uint32_t(((t >> 1) << 16) | (b << 8) | ((l + 32 * (t & 1)) << 2));
+// LDS table of one 1024-column slice of the activation.  Chunk c = 16g + 4w + b
+// covers columns 8c .. 8c + 7 (block g of the slice, word w of the block, byte
+// b of the word); its entry for the subset v (bit j of v: column 8c + j) is at
+//   (w >> 1) << 16 | v << 8 | (w & 1) << 7 | g << 4 | b << 2.
+// The bank of an entry is g << 2 | b.  Lane (r, g) of a wave (row r of the
+// step's 8, block g) reads byte (b + r) & 3 of its word at lookup b, so the 32
+// lanes of a half-wave (4 rows x 8 blocks) hit 32 different banks whatever the
+// mask bytes are.
+__device__ inline uint32_t lut_addr(int c, int v) {
+    const int g = c >> 4, w = (c >> 2) & 3, b = c & 3;
+    return uint32_t(((w >> 1) << 16) | (v << 8) | ((w & 1) << 7) | (g << 4) | (b << 2));
 }
-
-// Sum of x over the set bits of mask m for lane word l: four lookups, each a
-// v_perm (mask byte -> address bits 8..15 over the lane's base b0 / b1) and a
-// ds_read.  The table sits at LDS address 0, so the perm result is the
-// address and the +128 of odd chunks is the instruction's offset.
 __device__ inline float lds_at(uint32_t a) {
     return *reinterpret_cast<const lds_float*>(size_t(a));
 }
-__device__ inline void lds_put(uint32_t a, float v) {
-    *reinterpret_cast<lds_float*>(size_t(a)) = v;
-}
-__device__ inline float lut_sum(uint32_t m, uint32_t b0, uint32_t b1) {
-    const uint32_t a0 = __builtin_amdgcn_perm(b0, m, 0x0C060004u);
-    const uint32_t a1 = __builtin_amdgcn_perm(b0, m, 0x0C060104u);
-    const uint32_t a2 = __builtin_amdgcn_perm(b1, m, 0x0C060204u);
-    const uint32_t a3 = __builtin_amdgcn_perm(b1, m, 0x0C060304u);
-    float s = lds_at(a0);
-    s += lds_at(a1 + 128);
-    s += lds_at(a2);
-    s += lds_at(a3 + 128);
-    return s;
+
+// Sum over each 8-lane group (the 8 blocks of one row); every lane of the
+// group gets it.
+__device__ inline float row8_sum(float v) {
+    v += dpp<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    v += dpp<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    v += dpp<0x141, 0xF>(v);   // row_half_mirror
+    return v;
 }
 
-// Masks of the prefix tree of one word, depth first: leaf V (D == K) gets the
-// mask of the weights whose prefix is V.  Leaf 2^K - 1 is not needed (its sum
-// comes by subtraction from the word's total).
-template <int K, int D, int V>
-struct PrefixMasks {
-    static __device__ inline void go(const uint32_t (&w)[K], uint32_t m,
-                                     uint32_t (&out)[(1 << K) - 1]) {
-        PrefixMasks<K, D + 1, 2 * V>::go(w, m & ~w[D], out);
-        PrefixMasks<K, D + 1, 2 * V + 1>::go(w, m & w[D], out);
-    }
-};
-template <int K, int V>
-struct PrefixMasks<K, K, V> {
-    static __device__ inline void go(const uint32_t (&)[K], uint32_t m,
-                                     uint32_t (&out)[(1 << K) - 1]) {
-        if constexpr (V != (1 << K) - 1) out[V] = m;
-    }
+// Per-lane constants of the lookups: the lane's table slot (block g, byte
+// position (b + r) & 3) merged with a mask byte by one v_perm, which drops
+// byte (b + r) & 3 of the mask into address bits 8..15 and keeps the slot in
+// bits 0..7 and the half (bit 16) from base.  xg: the activation summed over
+// the lane's block.
+struct LaneLut {
+    uint32_t base[2][4];
+    uint32_t sel[4];
+    float xg;
 };
 
-// Floats of a block's depth-K table held by each lane of the block's four
-// lanes (a block is 128 inputs, four 32-bit words): lane q of the quad holds
-// values q*NQ .. q*NQ + NQ - 1 (K = 1: lane q holds value q & 1).
+__device__ inline LaneLut lane_lut(int lane, const lds_float* tab) {
+    const int g = lane & 7, r = lane >> 3;
+    // the table's own address (0: it is the kernel's one LDS object) enters
+    // the lookup addresses, so the compiler keeps the stores that build it
+    const uint32_t t0 = uint32_t(reinterpret_cast<uintptr_t>(tab));
+    LaneLut L;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t bb = uint32_t((b + r) & 3);
+        L.sel[b] = 0x0C060004u | (bb << 8);
+        L.base[0][b] = t0 + (uint32_t(g << 4) | (bb << 2));
+        L.base[1][b] = L.base[0][b] | 0x10000u;
+    }
+    float xg = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) xg += tab[lut_addr(16 * g + c, 255) >> 2];
+    L.xg = xg;
+    return L;
+}
+
+// One step of a wave: 8 rows of one matrix over one column slice.  Lane
+// (r, g) holds the four plane words of block g of row r for planes 0..K-1 and
+// the block's 2^K depth-K node values.
 template <int K>
-constexpr int quad_share() {
-    return (1 << K) >= 4 ? (1 << K) / 4 : 1;
-}
-
-// Node value V of this lane's block, from the quad lane that holds it.
-template <int K, int V>
-__device__ inline float quad_node(const float (&tq)[quad_share<K>()]) {
-    constexpr int NQ = quad_share<K>();
-    constexpr int owner = K == 1 ? V : V / NQ;
-    constexpr int j = K == 1 ? 0 : V % NQ;
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, tq[j]), owner * 0x55, 0xF, 0xF,
-                                        true));
-}
-
-// One row's contribution of this lane's word at prefix K:
-// sum_v node(v) * S_v, S_v = sum of x where the prefix is v.  The buckets go
-// in chunks of PM_LUT_CHUNK: a chunk's masks, then all its lookups (one LDS
-// round trip), then its bucket sums in v order, each taken off the word's
-// total xw; the last bucket is what remains.  Chunks keep the k = 4 and 5 rows
-// within the register budget of four waves per SIMD (all 2^k - 1 lookups at
-// once spilled); the order of the sums is the same for any chunk size.
-#ifndef PM_LUT_CHUNK
-#define PM_LUT_CHUNK 8
-#endif
-// Bucket V (V0 <= V < V1) of one row: its sum S from the four chunk lookups
-// (in chunk order), taken off the running remainder, times node V.
-template <int K, int V, int V0, int V1>
-__device__ inline void lut_terms(const float* r, const float (&tq)[quad_share<K>()], float& acc,
-                                 float& last) {
-    if constexpr (V < V1) {
-        float S = r[4 * (V - V0)];
-        S += r[4 * (V - V0) + 1];
-        S += r[4 * (V - V0) + 2];
-        S += r[4 * (V - V0) + 3];
-        last -= S;
-        acc = fmaf(quad_node<K, V>(tq), S, acc);
-        lut_terms<K, V + 1, V0, V1>(r, tq, acc, last);
-    }
-}
-// The masks of leaves V0 .. V1 - 1 only (subtrees outside are not visited).
-template <int K, int D, int V, int V0, int V1>
-struct PrefixMasksIn {
-    static __device__ inline void go(const uint32_t (&w)[K], uint32_t m, uint32_t (&out)[V1 - V0]) {
-        if constexpr (D == K) {
-            if constexpr (V >= V0 && V < V1) out[V - V0] = m;
-        } else if constexpr (((V + 1) << (K - D)) > V0 && (V << (K - D)) < V1) {
-            PrefixMasksIn<K, D + 1, 2 * V, V0, V1>::go(w, m & ~w[D], out);
-            PrefixMasksIn<K, D + 1, 2 * V + 1, V0, V1>::go(w, m & w[D], out);
-        }
-    }
+struct StepIn {
+    u32x4 p[K];
+    f32x4 n[K == 1 ? 1 : (1 << K) / 4];
 };
 
-template <int K, int V0, int N>
-__device__ inline void lut_chunks(const uint32_t (&w)[K], const float (&tq)[quad_share<K>()],
-                                  uint32_t b0, uint32_t b1, float& acc, float& last) {
-    constexpr int C = PM_LUT_CHUNK > 0 ? PM_LUT_CHUNK : N;
-    constexpr int V1 = V0 + C < N ? V0 + C : N;
-    uint32_t m[V1 - V0];
-    PrefixMasksIn<K, 0, 0, V0, V1>::go(w, 0xFFFFFFFFu, m);
-    float r[4 * (V1 - V0)];
-#pragma unroll
-    for (int v = 0; v < V1 - V0; ++v) {
-        r[4 * v + 0] = lds_at(__builtin_amdgcn_perm(b0, m[v], 0x0C060004u));
-        r[4 * v + 1] = lds_at(__builtin_amdgcn_perm(b0, m[v], 0x0C060104u) + 128);
-        r[4 * v + 2] = lds_at(__builtin_amdgcn_perm(b1, m[v], 0x0C060204u));
-        r[4 * v + 3] = lds_at(__builtin_amdgcn_perm(b1, m[v], 0x0C060304u) + 128);
-    }
-    lut_terms<K, V0, V0, V1>(r, tq, acc, last);
-    if constexpr (V1 < N) lut_chunks<K, V1, N>(w, tq, b0, b1, acc, last);
+// Buffer resource over `bytes` bytes from p: loads take a wave-uniform byte
+// offset (scalar) plus the lane's byte offset, and return 0 past the end.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), 0x00020000);
 }
 
+// Where a step reads and writes.  planes: plane 0, row 0 of the step, first
+// word of the slice; nodes: depth-K nodes of the slice's first block, row 0
+// of the step; out: the slice partial of row 0 of the step.
+struct StepAt {
+    const uint32_t* planes;
+    const float* nodes;
+    float* out;
+};
+
+// Lane byte offsets that stay fixed through a launch: the plane words and
+// the node values of (row r, block g) from the step's row 0.
+struct LaneOff {
+    uint32_t pw, nd;
+};
+
+// Plane words are read once per launch: non-temporal loads (the "nt" cache
+// policy; on gfx950 a stream of them reaches about 7.3 TB/s, plain loads
+// about 4 TB/s).  Node loads keep the default policy: from k = 3 a lane's
+// nodes span 32-64 bytes, so one load instruction touches lines that the
+// lane's next node loads read again.
+constexpr int kNT = 2;
+constexpr int kNodePolicy = 0;
+
+// A step past the end (ok false) still issues its loads, against an empty
+// buffer (they return 0 and read nothing), so that every wave issues the
+// same loads in the same order and the waits on them stay exact.
 template <int K>
-__device__ inline float lut_row(const uint32_t (&w)[K], const float (&tq)[quad_share<K>()],
-                                float xw, uint32_t b0, uint32_t b1) {
-    constexpr int N = (1 << K) - 1;
-    float acc = 0.f, last = xw;
-    lut_chunks<K, 0, N>(w, tq, b0, b1, acc, last);
-    return fmaf(quad_node<K, N>(tq), last, acc);
-}
-
-// The activation slice of this workgroup into the LUT.  Thread tid owns
-// chunk c = 4l + t, l = tid % 32, t = (tid / 32) % 4, and writes its subset
-// sums b = 32q .. 32q + 31 for q = tid / 128 + j * (kLutThreads / 128),
-// j < 1024 / kLutThreads; a half-wave writes 32 different banks.  Gate/up: x
-// points at the slice.  Down: h of one use for columns tid, tid + kLutThreads,
-// .. of the slice, from the gate/up partials pg (gate, ng slices) and pu (up,
-// nu slices), `stride` floats apart.  Sums with a zero term are exact.  h is
-// staged with one pad word per 32 so that the chunk-wise reads hit 32
-// different banks.
-// A thread's eight activation values of its chunk, loaded ahead of time (a
-// vector type, so that it travels in registers into out-of-line calls).
-typedef float X8 __attribute__((ext_vector_type(8)));
-
-__device__ inline X8 load_x8(const float* x) {
-    const int tid = threadIdx.x;
-    const int c8 = 8 * (4 * (tid & 31) + ((tid >> 5) & 3));
-    const f32x4 a = *(g_f32x4*)(x + c8);
-    const f32x4 b = *(g_f32x4*)(x + c8 + 4);
-    return X8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-}
-
-__device__ inline void build_lut(lds_float* hbuf, const float* x, const float* pg,
-                                 const float* pu, int ng, int nu, int stride, const X8& xv) {
-    constexpr int kQ = kLutThreads / 128;          // q values spread over threads
-    constexpr int kPer = 8 / kQ;                   // q values per thread
-    const int tid = threadIdx.x;
-    const int l = tid & 31, t = (tid >> 5) & 3;
-    const int c8 = 8 * (4 * l + t);
-    float v[8];
-    if (pg) {
+__device__ inline void step_load(StepIn<K>& in, const StepAt& at, const LaneOff& lo,
+                                 uint32_t pstride_b, uint32_t row_b, uint32_t nrow_b, bool ok) {
+    const __amdgpu_buffer_rsrc_t rp =
+        buffer_of(at.planes, ok ? uint32_t(K - 1) * pstride_b + 8u * row_b : 0u);
+    const __amdgpu_buffer_rsrc_t rn = buffer_of(at.nodes, ok ? 8u * nrow_b : 0u);
 #pragma unroll
-        for (int half = 0; half < kSliceCols / kLutThreads; ++half) {
-            g_f32* g = (g_f32*)(pg + half * kLutThreads);
-            g_f32* u = (g_f32*)(pu + half * kLutThreads);
-            float gs, us;
-            if (ng <= 4 && nu <= 4) {      // all loads in flight at once
-                float gv[4], uv[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    gv[q] = q < ng ? g[size_t(q) * stride] : 0.f;
-                    uv[q] = q < nu ? u[size_t(q) * stride] : 0.f;
-                }
-                gs = gv[0];
-                us = uv[0];
-#pragma unroll
-                for (int q = 1; q < 4; ++q) {
-                    if (q < ng) gs += gv[q];
-                    if (q < nu) us += uv[q];
-                }
-            } else {
-                gs = g[0];
-                for (int q = 1; q < ng; ++q) gs += g[size_t(q) * stride];
-                us = u[0];
-                for (int q = 1; q < nu; ++q) us += u[size_t(q) * stride];
-            }
-            const int c = tid + half * kLutThreads;
-            hbuf[c + (c >> 5)] = silu_mul(gs, us);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = hbuf[c8 + i + ((c8 + i) >> 5)];
-    } else if (x) {
-        const f32x4 a = *(g_f32x4*)(x + c8);
-        const f32x4 b = *(g_f32x4*)(x + c8 + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    for (int p = 0; p < K; ++p)
+        in.p[p] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, int(lo.pw), int(p * pstride_b), kNT));
+    if constexpr (K == 1) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rn, int(lo.nd), 0, kNodePolicy);
+        const f32x2 f = __builtin_bit_cast(f32x2, v);
+        in.n[0] = f32x4{f.x, f.y, 0.f, 0.f};
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = xv[i];
+        for (int i = 0; i < (1 << K) / 4; ++i)
+            in.n[i] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rn, int(lo.nd + 16 * i), 0, kNodePolicy));
     }
-    const int c = 4 * l + t;
+}
+
+// The row's contribution of this lane's block at prefix K:
+//   sum_v node[v] * S_v,  S_v = sum of x over the block's inputs with prefix v.
+// S_v for v != M is the four lookups per word of the mask of prefix v (the
+// AND of the K plane words, each plain or inverted by the bits of v); S_M is
+// what remains of the block's activation sum X.  M is a middle bucket (0 at
+// K = 1): the nodes are ascending, so node[M] is the value nearest the
+// block's median and the rounding of X - sum S_v, scaled by node[M], stays
+// within a small multiple of sum |w * x| also for codebooks with large outer
+// leaves.  One-hot x gives exact columns: every S_v is 0 or 1.
+template <int K>
+__device__ inline float step_compute(const StepIn<K>& in, const LaneLut& L) {
+    constexpr int NV = 1 << K;
+    constexpr int M = K == 1 ? 0 : NV / 2;
+    // accumulators per bucket: four (one per lookup byte) at K = 1, where a
+    // single bucket would be one long dependent chain
+    constexpr int J = K == 1 ? 4 : 1;
+    // a scheduling region is RW words x CB buckets: its lookups are issued
+    // together and summed before the next region starts (larger regions would
+    // not fit the registers)
+    constexpr int RW = K <= 2 ? 4 : (K == 3 ? 2 : 1);
+    constexpr int CB = K <= 4 ? NV : 8;
+    float S[NV][J];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int j = 0; j < J; ++j) S[v][j] = 0.f;
+#pragma unroll
+    for (int w0 = 0; w0 < 4; w0 += RW) {
+#pragma unroll
+        for (int v0 = 0; v0 < NV; v0 += CB) {
+#pragma unroll
+            for (int w = w0; w < w0 + RW; ++w) {
+                uint32_t pw[K];
+#pragma unroll
+                for (int p = 0; p < K; ++p) pw[p] = in.p[p][w];
+                // masks of the 3-bit prefixes (deeper prefixes refine them)
+                uint32_t l3[8];
+                if constexpr (K > 3) {
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        l3[u] = ((u & 4) ? pw[0] : ~pw[0]) & ((u & 2) ? pw[1] : ~pw[1]) &
+                                ((u & 1) ? pw[2] : ~pw[2]);
+                }
+#pragma unroll
+                for (int v = v0; v < v0 + CB; ++v) {
+                    if (v == M) continue;
+                    uint32_t m;
+                    if constexpr (K <= 3) {
+                        m = 0xFFFFFFFFu;
+#pragma unroll
+                        for (int p = 0; p < K; ++p)
+                            m &= ((v >> (K - 1 - p)) & 1) ? pw[p] : ~pw[p];
+                    } else {
+                        m = l3[v >> (K - 3)];
+#pragma unroll
+                        for (int p = 3; p < K; ++p)
+                            m &= ((v >> (K - 1 - p)) & 1) ? pw[p] : ~pw[p];
+                    }
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const uint32_t a = __builtin_amdgcn_perm(L.base[w >> 1][b], m, L.sel[b]);
+                        S[v][b % J] += lds_at(a + 128u * (w & 1));
+                    }
+                }
+            }
+            // the region's sums complete inside it (otherwise they sink to the
+            // end of the step and every lookup result stays live)
+#pragma unroll
+            for (int v = v0; v < v0 + CB; ++v)
+#pragma unroll
+                for (int j = 0; j < J; ++j)
+                    if (v != M) __asm__ volatile("" : "+v"(S[v][j]));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    float Sv[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        if constexpr (J == 4)
+            Sv[v] = (S[v][0] + S[v][1]) + (S[v][2] + S[v][3]);
+        else
+            Sv[v] = S[v][0];
+    }
+    float rest = L.xg;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+        if (v != M) rest -= Sv[v];
+    Sv[M] = rest;
+    float acc = 0.f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) acc = fmaf(in.n[v >> 2][v & 3], Sv[v], acc);
+    return acc;
+}
+
+// Table build by the builder waves: thread t (t < 128) owns chunk
+// c = 16g + 4w + b with g << 2 | b = t % 32, w = t / 32, and writes all 256
+// subset sums of it; a half-wave writes 32 different banks.  Each entry is a
+// plain fp32 sum of its columns (a zero term adds nothing, so one-hot x gives
+// exact columns).
+#ifndef PM_LUT_THREADS
+#define PM_LUT_THREADS 512
+#endif
+constexpr int kLutThreads = PM_LUT_THREADS;
+constexpr int kLutWaves = kLutThreads / kWave;
+constexpr int kLutBytes = 128 * 1024;
+constexpr int kBuildWaves = 2;              // 128 chunks, one per builder thread
+static_assert(kLutThreads % 256 == 0 && kLutThreads <= 1024, "whole waves on every SIMD");
+
+__device__ inline int build_chunk(int t) {
+    return 16 * ((t & 31) >> 2) + 4 * ((t >> 5) & 3) + (t & 3);
+}
+
+__device__ inline void build_table(lds_float* tab, int c, const float (&v)[8]) {
     float sub[32];
     sub[0] = 0.f;
 #pragma unroll
     for (int i = 1; i < 32; ++i) sub[i] = sub[i & (i - 1)] + v[__builtin_ctz(i)];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int q = (tid >> 7) + j * kQ;
+    for (int q = 0; q < 8; ++q) {
         float base = 0.f;
         if (q & 1) base += v[5];
         if (q & 2) base += v[6];
         if (q & 4) base += v[7];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) lds_put(lut_addr(c, 32 * q + i), base + sub[i]);
+        for (int i = 0; i < 32; ++i) tab[lut_addr(c, 32 * q + i) >> 2] = base + sub[i];
     }
 }
 
-template <int K>
-struct LutRowIn {
-    uint32_t w[K];
-    float tq[quad_share<K>()];
-};
-
-// Buffer resource over `bytes` bytes from p: loads through it take a
-// wave-uniform byte offset (scalar) plus the lane's byte offset, and return 0
-// past the end.
-__device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), 0x00020000);
-}
-
-// One row pair's inputs for this lane: its word of planes 0..K-1 and its
-// share of its block's depth-K table.  prow / trow: the pair's wave-uniform
-// byte offsets into the plane and table buffers; wo / to: the lane's.
-template <int K>
-__device__ inline void lut_load(LutRowIn<K>& in, __amdgpu_buffer_rsrc_t rp, __amdgpu_buffer_rsrc_t rt,
-                                uint32_t wo, uint32_t to, uint32_t prow, uint32_t trow,
-                                uint32_t pbytes) {
-#pragma unroll
-    for (int p = 0; p < K; ++p)
-        in.w[p] = uint32_t(__builtin_amdgcn_raw_buffer_load_b32(rp, int(wo), int(prow + p * pbytes), 0));
-#pragma unroll
-    for (int j = 0; j < quad_share<K>(); ++j)
-        in.tq[j] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rt, int(to + 4 * j), int(trow), 0));
-}
-
-template <int K>
-constexpr int lut_unroll() {
-#if PM_LUT_THREADS == 1024
-    return K == 1 ? 4 : K == 2 ? 2 : 1;
-#else
-    return K == 1 ? 8 : K == 2 ? 4 : K == 3 ? 3 : K == 4 ? 2 : 1;
-#endif
-}
-
-// One job segment: the slice's first word and first block table in row 0
-// (shared by the wave), and the lane's byte offsets from them.  The LUT path
-// takes an even number of rows per matrix and cuts segments at even rows, so
-// every row pair of a segment lies inside it.
-struct Seg {
-    const uint32_t* pw;    // plane 0, row 0, first word of the slice
-    const float* tab;      // depth-k table of the slice's first block, row 0
-    float* out;            // outputs of this slice
-    uint64_t pstride;      // words between planes
-    int W;                 // words per row
-    int tab_row;           // floats between tables of consecutive rows
-    int r0, r1;            // rows [r0, r1), both even
-    uint32_t wo, to, oo;   // lane byte offsets: word, table, output
-};
-
-// A batch: U row pairs of this wave, pairs p, p + kLutWaves, ... (rows 2p + hw).
-template <int K, int U>
-struct Batch {
-    LutRowIn<K> in[U];
-    int pp[U];             // pair index (wave-uniform)
-    bool ok[U];            // the pair lies in the segment (wave-uniform)
-};
-
-template <class T>
-__device__ inline const T* at_bytes(const T* base, uint32_t off) {
-    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
-}
-
-// Loads are unconditional (a pair past the segment reloads its last pair
-// and is not stored), so that the batch is straight-line code; every
-// address is a wave-uniform base plus the lane's fixed byte offset.
-template <int K, int U>
-__device__ inline void batch_load(Batch<K, U>& B, const Seg& sg, __amdgpu_buffer_rsrc_t rp,
-                                  __amdgpu_buffer_rsrc_t rt, int p, int p1) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int q = p + u * kLutWaves;
-        const int pp = min(q, p1 - 1);
-        B.pp[u] = pp;
-        B.ok[u] = q < p1;
-        lut_load<K>(B.in[u], rp, rt, sg.wo, sg.to, uint32_t(2 * pp * sg.W) * 4u,
-                    uint32_t(2 * pp * sg.tab_row) * 4u, uint32_t(sg.pstride) * 4u);
-    }
-}
-
-// The rows of a batch are computed and reduced as one straight-line block
-// (their lookups and reductions interleave), and stored after it.
-template <int K, int U>
-__device__ inline void batch_compute(const Batch<K, U>& B, const Seg& sg, float xw, uint32_t b0,
-                                     uint32_t b1, int l) {
-    float acc[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) acc[u] = lut_row<K>(B.in[u].w, B.in[u].tq, xw, b0, b1);
-#pragma unroll
-    for (int u = 0; u < U; ++u) acc[u] = half_sum(acc[u]);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-        if (B.ok[u] && l == 31)
-            *(g_f32_out*)at_bytes(sg.out + 2 * B.pp[u], sg.oo) = acc[u];
-}
-
-// Where the LUT of a workgroup comes from (see build_lut).
-struct LutSrc {
-    const float* x;        // null with pg null: the values are in xv
-    const float* pg;
-    const float* pu;
-    int ng, nu, stride;
-    X8 xv;
-};
-
-// Rows [r0, r1) of one job for this wave, double-buffered: the next batch is
-// in flight while this one computes.  FIRST: the workgroup's first segment --
-// its first batch is issued before the LUT is built, and the lane's total of
-// x over its word is returned.  Out of line so that every prefix gets its own
-// register allocation.
-template <int K, bool FIRST>
-__device__ __noinline__ float lut_segment(lds_float* hbuf, const uint32_t* pw, const float* tab,
-                                          float* out, uint64_t pstride, int W, int tab_row,
-                                          int wpg, int r0, int r1, const float* x,
-                                          const float* pg, const float* pu, int ngnu,
-                                          int hstride, X8 xv, float xw) {
-    constexpr int U = lut_unroll<K>();
-    const int tid = threadIdx.x, wave = uni(tid / kWave), lane = tid % kWave;
-    const int hw = lane >> 5, l = lane & 31;
-    Seg sg{uni_ptr(pw), uni_ptr(tab), uni_ptr(out), uni64(pstride), uni(W), uni(tab_row),
-           uni(r0), uni(r1), 0, 0, 0};
-    // planes 0..K-1 and the tables of the rows below r1
-    const __amdgpu_buffer_rsrc_t rp =
-        buffer_of(sg.pw, uint32_t(((K - 1) * sg.pstride + uint64_t(sg.r1) * sg.W) * 4));
-    const __amdgpu_buffer_rsrc_t rt = buffer_of(sg.tab, uint32_t(uint64_t(sg.r1) * sg.tab_row * 4));
-    sg.wo = uint32_t(l + hw * sg.W) * 4u;
-    // the lane's quad share of its block's table (four lanes per block)
-    sg.to = uint32_t(hw * sg.tab_row + ((l >> 2) << K) +
-                     (K == 1 ? (l & 1) : (l & 3) * quad_share<K>())) * 4u;
-    sg.oo = uint32_t(hw) * 4u;
-    const uint32_t b0 = uint32_t(l) << 2, b1 = b0 | 0x10000u;
-    const int p1 = (sg.r1 + 1) >> 1;
-    constexpr int step = kLutWaves * U;
-    int p = (sg.r0 >> 1) + wave;
-    Batch<K, U> A, B;
-    batch_load<K, U>(A, sg, rp, rt, p, p1);
-    if constexpr (FIRST) {
-        build_lut(hbuf, x, pg, pu, ngnu & 15, ngnu >> 4, hstride, xv);
-        __syncthreads();
-        xw = 0.f;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) xw += lds_at(lut_addr(4 * l + t, 255));
-    }
-    // the scheduling barriers keep each batch's loads ahead of the other
-    // batch's arithmetic (hoisting that arithmetic would make the loads wait)
-    while (p < p1) {
-        batch_load<K, U>(B, sg, rp, rt, p + step, p1);
-        __builtin_amdgcn_sched_barrier(0);
-        batch_compute<K, U>(A, sg, xw, b0, b1, l);
-        __builtin_amdgcn_sched_barrier(0);
-        p += step;
-        if (p >= p1) break;
-        batch_load<K, U>(A, sg, rp, rt, p + step, p1);
-        __builtin_amdgcn_sched_barrier(0);
-        batch_compute<K, U>(B, sg, xw, b0, b1, l);
-        __builtin_amdgcn_sched_barrier(0);
-        p += step;
-    }
-    return xw;
-}
-
-template <bool FIRST>
-__device__ inline float lut_segment_k(int k, lds_float* hbuf, const Seg& sg, int wpg,
-                                      const LutSrc& src, float xw) {
-    const int ngnu = src.ng | (src.nu << 4);
-#define PM_SEG(KK)                                                                            \
-    lut_segment<KK, FIRST>(hbuf, sg.pw, sg.tab, sg.out, sg.pstride, sg.W, sg.tab_row, wpg,   \
-                           sg.r0, sg.r1, src.x, src.pg, src.pu, ngnu, src.stride, src.xv, xw)
-    switch (k) {
-        case 1: return PM_SEG(1);
-        case 2: return PM_SEG(2);
-        case 3: return PM_SEG(3);
-        case 4: return PM_SEG(4);
-        default: return PM_SEG(5);
-    }
-#undef PM_SEG
-}
-
-// Shape of the matrices of one launch.
-struct MatArgs {
-    uint64_t pstride;      // words between planes
-    int rows, W, wpg;      // rows, words per row, words per block
-    int out_stride;        // floats between the slice outputs of a job
-};
-
-__device__ inline MatArgs mat_of(const KLaunch& L) {
-    return MatArgs{L.pstride, L.rows, L.W, L.wpg, L.out_stride};
-}
-
-// The segment description of job jb, rows [r0, r1), for this lane.
-__device__ inline Seg make_seg(const MatArgs& M, const KJob& jb, int slice, int r0, int r1) {
-    const int w0 = (kSliceCols / 32) * slice;
-    Seg sg;
-    sg.pw = jb.planes + w0;
-    sg.tab = jb.lvk + (size_t(w0 / M.wpg) << jb.k);
-    sg.out = jb.out + size_t(slice) * M.out_stride;
-    sg.pstride = M.pstride;
-    sg.W = M.W;
-    sg.tab_row = (M.W / M.wpg) << jb.k;
-    sg.r0 = r0;
-    sg.r1 = r1;
-    sg.wo = sg.to = sg.oo = 0;
-    return sg;
-}
-
-// LUT sources: the activation slice of x, or h of a use from its gate/up
-// partials (gu: [use][2][gu_smax][inter]).
-__device__ inline LutSrc src_x(const float* x, int slice) {
-    LutSrc r{};
-    r.x = x + kSliceCols * slice;
-    return r;
-}
-__device__ inline LutSrc src_h(const float* gu, int gu_smax, int inter, const KJob& jb, int use,
-                               int slice) {
-    LutSrc r{};
-    const int c = kSliceCols * slice + int(threadIdx.x);     // and c + kLutThreads ..
-    r.pg = gu + (size_t(use) * 2) * gu_smax * inter + c;
-    r.pu = r.pg + size_t(gu_smax) * inter;
-    r.ng = jb.gsl & 15;
-    r.nu = jb.gsl >> 4;
-    r.stride = inter;
-    return r;
-}
-
-// Rows g0 .. g1-1 of the launch's row sequence (row r of job j is
-// j * rows + r), the first segment building the LUT from its job's source.
-// Every value here is the same across the workgroup; the job descriptions
-// are read straight from the argument block.
+// The 8 activation values of chunk c: x of token `src`, or h of use `src`
+// formed from its gate/up partials (slices summed in order; slices past a
+// matrix's count read slice 0 again and add 0).
 template <bool DOWN>
-__global__ __launch_bounds__(kLutThreads) void lut_kernel(const KLaunch L) {
-    // one LDS object: the table at address 0 (lut_sum relies on it), then
-    // the padded h of the down stage
-    __shared__ __attribute__((aligned(16))) char lds_buf[kLutBytes + (DOWN ? kHbufBytes : 0)];
-    lds_float* hb = (lds_float*)(lds_buf + kLutBytes);
-    const int slice = blockIdx.x % L.S, q = blockIdx.x / L.S;
-    // one activation for the whole launch (x_stride 0): its slice is loaded
-    // before the row range is known
-    X8 xpre{};
-    const bool pre = !DOWN && L.x_stride == 0;
-    if (pre) xpre = load_x8(L.x + kSliceCols * slice);
+__device__ inline void chunk_source(const KLaunch& L, int src, int gsl, int slice, int c,
+                                    float (&v)[8]) {
+    const int col = kSliceCols * slice + 8 * c;
+    if constexpr (!DOWN) {
+        const float* x = L.x + size_t(src) * L.x_stride + col;
+        const f32x4 a = *(g_f32x4*)x, b = *(g_f32x4*)(x + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        const int ngs = gsl & 15, nus = gsl >> 4;
+        const int inter = L.inter, smax = L.gu_smax;
+        const float* pg = L.gu + (size_t(src) * 2) * smax * inter + col;
+        const float* pu = pg + size_t(smax) * inter;
+        f32x4 gs[2], us[2];
+        if (smax <= 4) {
+            f32x4 gv[4][2], uv[4][2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    gv[q][h] = *(g_f32x4*)(pg + size_t(q < ngs ? q : 0) * inter + 4 * h);
+                    uv[q][h] = *(g_f32x4*)(pu + size_t(q < nus ? q : 0) * inter + 4 * h);
+                }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                gs[h] = gv[0][h];
+                us[h] = uv[0][h];
+#pragma unroll
+                for (int q = 1; q < 4; ++q) {
+                    gs[h] += q < ngs ? gv[q][h] : f32x4{0.f, 0.f, 0.f, 0.f};
+                    us[h] += q < nus ? uv[q][h] : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                gs[h] = *(g_f32x4*)(pg + 4 * h);
+                for (int q = 1; q < ngs; ++q) gs[h] += *(g_f32x4*)(pg + size_t(q) * inter + 4 * h);
+                us[h] = *(g_f32x4*)(pu + 4 * h);
+                for (int q = 1; q < nus; ++q) us[h] += *(g_f32x4*)(pu + size_t(q) * inter + 4 * h);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = silu_mul(gs[0][i], us[0][i]);
+            v[4 + i] = silu_mul(gs[1][i], us[1][i]);
+        }
+    }
+}
+
+// Steps in flight per wave (the ring): deeper where a step is short.
+template <int K>
+constexpr int lut_ring() {
+    return K == 1 ? 4 : (K == 2 ? 3 : 2);
+}
+
+// The rows [g0, g1) of a launch (row r of job j is j * rows + r; both ends
+// multiples of 8) over column slice `slice`, every job at prefix K and of
+// activation source `src`, in 8-row steps.  Each wave keeps D steps in
+// flight, also across job boundaries.  The builder waves form the table while
+// the others already stream their first steps (a wave stalls at issue once
+// its compute unit's vector-memory queue is full, so waves that issue loads
+// early must not be the ones that build).
+struct LutCtx {
+    int slice, g0, g1, src, gsl;
+    int wave, lane;
+};
+
+template <bool DOWN, int K>
+__device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L, LutCtx c,
+                                                               lds_float* tab, uint32_t* ready,
+                                                               uint32_t* next) {
+    const int lane = c.lane, r = lane >> 3, g = lane & 7;
+    const int rows = uni(L.rows), W = uni(L.W);
+    const int ng = W / 4;                                  // blocks per row
+    const uint32_t pstride_b = uni(uint32_t(L.pstride * 4u));
+    const uint32_t row_b = uint32_t(W) * 4u;               // bytes per plane row
+    const uint32_t nrow_b = uint32_t(ng << K) * 4u;        // node bytes per row
+    const LaneOff lo{uint32_t(r * W + 4 * g) * 4u, uint32_t((r * ng + g) << K) * 4u};
+    const int nsteps = (c.g1 - c.g0) / 8;
+    const int w0 = (kSliceCols / 32) * c.slice;            // first word of the slice
+    // a wave's steps only move forward: a cursor on the current job reads a
+    // job description only when a step crosses into the next job
+    int cj = c.g0 / rows;                                  // current job
+    int cend = (cj + 1) * rows;                            // its end in the row sequence
+    const uint32_t* cpl = uni_ptr(L.job[cj].planes);
+    const float* clv = uni_ptr(L.job[cj].lvk);
+    float* cout = uni_ptr(L.job[cj].out);
+    const size_t out_off = size_t(c.slice) * L.out_stride;
+    auto at = [&](int s) {
+        const int gr = c.g0 + 8 * s;
+        while (gr >= cend) {
+            ++cj;
+            cend += rows;
+            cpl = uni_ptr(L.job[cj].planes);
+            clv = uni_ptr(L.job[cj].lvk);
+            cout = uni_ptr(L.job[cj].out);
+        }
+        const int row0 = gr - (cend - rows);
+        StepAt a;
+        a.planes = cpl + size_t(row0) * W + w0;
+        a.nodes = clv + ((size_t(row0) * ng + (w0 >> 2)) << K);
+        a.out = cout + out_off + row0;
+        return a;
+    };
+    constexpr int D = lut_ring<K>();
+    StepIn<K> buf[D];
+    StepAt sat[D];
+    int sv[D];                 // the step in ring slot d (nsteps or more: none)
+    // steps are handed out in order from an LDS counter, one per slot refill,
+    // so waves that start late (the builders) or run slower take fewer
+    auto grab = [&]() {
+        uint32_t t = 0;
+        if (lane == 0) t = __hip_atomic_fetch_add(next, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+        return int(__builtin_amdgcn_readfirstlane(t));
+    };
+    auto fill = [&](int d) {
+        sv[d] = grab();
+        const bool ok = sv[d] < nsteps;
+        sat[d] = at(ok ? sv[d] : nsteps - 1);
+        step_load<K>(buf[d], sat[d], lo, pstride_b, row_b, nrow_b, ok);
+    };
+    // builders form the table and announce it on `ready`; the other waves
+    // take their first step at once and wait for the table only when they
+    // are about to compute (no workgroup barrier: a wave stalled at issue
+    // must not hold up the others)
+    const bool builder = c.wave < kBuildWaves;
+    if (builder) {
+        const int ch = build_chunk(int(threadIdx.x));
+        float v[8];
+        chunk_source<DOWN>(L, c.src, c.gsl, c.slice, ch, v);
+        build_table(tab, ch, v);
+        // LDS operations of one wave execute in order: once another wave
+        // sees this count, the table writes before it are done.  (A release
+        // here would also wait for global memory, which this does not need.)
+        __asm__ volatile("" ::: "memory");
+        __hip_atomic_fetch_add(ready, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) fill(d);
+    __builtin_amdgcn_sched_barrier(0);
+    while (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) <
+           uint32_t(kBuildWaves * kWave))
+        __builtin_amdgcn_s_sleep(1);
+    __asm__ volatile("" ::: "memory");
+    const LaneLut LL = lane_lut(lane, tab);
+
+    // Slots are filled in step order, so once the first slot of a round
+    // holds no step, none does.  Every wave issues the same vector-memory
+    // operations in the same order, with no branch around any of them (a
+    // step past the end loads from and stores to an empty buffer; lanes
+    // other than the first of a row store out of range), so the compiler's
+    // waits on them stay exact.  The scheduling barriers keep the loads ahead
+    // of the next step's arithmetic.
+    const uint32_t so = g == 0 ? uint32_t(r) * 4u : 64u;
+    for (;;) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const bool ok = sv[d] < nsteps;
+            float acc = 0.f;
+            if (ok) acc = row8_sum(step_compute<K>(buf[d], LL));
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc),
+                                                  buffer_of(sat[d].out, ok ? 32u : 0u),
+                                                  int(so), 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            fill(d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (sv[0] >= nsteps) break;
+    }
+}
+
+// Workgroup (q, slice) runs the rows [start[q], start[q + 1]) of the
+// launch's row sequence; the host cuts them so that every range holds jobs of
+// one prefix and one activation source, named in meta[q] with the range's k,
+// so that a workgroup's first reads do not depend on one another.  Job
+// descriptions are read straight from the argument block.
+// One workgroup per compute unit (its table fills the LDS).
+template <bool DOWN>
+__global__ __launch_bounds__(kLutThreads) __attribute__((amdgpu_waves_per_eu(kLutWaves / 4,
+                                                                              kLutWaves / 4))) void
+lut_kernel(const KLaunch L) {
+    // the kernel's one LDS object, at address 0: the lookups use the v_perm
+    // result as the address; then the count of builder threads done
+    __shared__ __attribute__((aligned(16))) float lds_buf[kLutBytes / 4 + 4];
+    uint32_t* ready = reinterpret_cast<uint32_t*>(lds_buf + kLutBytes / 4);
+    uint32_t* next = ready + 1;
+    if (threadIdx.x == 0) {
+        *ready = 0u;
+        *next = 0u;
+    }
+    __syncthreads();
+    const int q = blockIdx.x, slice = blockIdx.y;
+    const uint32_t meta = L.meta[q];
     const int g0 = L.start[q], g1 = L.start[q + 1];
     if (g0 >= g1) return;
-    const int rows = L.rows;
-    const int ja = g0 / rows, ra = g0 - ja * rows;
-    const int jl = (g1 - 1) / rows, rl = g1 - jl * rows;
-    const MatArgs M = mat_of(L);
-    float xw = 0.f;
-    for (int j = ja; j <= jl; ++j) {
-        const KJob job = L.job[j];
-        const int r0 = j == ja ? ra : 0, r1 = j == jl ? rl : rows;
-        const Seg sg = make_seg(M, job, slice, r0, r1);
-        if (j == ja) {
-            LutSrc src = DOWN ? src_h(L.gu, L.gu_smax, L.inter, job, job.src, slice)
-                              : src_x(L.x + size_t(job.src) * L.x_stride, slice);
-            if (pre) {
-                src.x = nullptr;
-                src.xv = xpre;
-            }
-            xw = lut_segment_k<true>(job.k, hb, sg, M.wpg, src, 0.f);
-        } else {
-            xw = lut_segment_k<false>(job.k, hb, sg, M.wpg, LutSrc{}, xw);
-        }
+    LutCtx c{slice, g0, g1, int(meta & 0xFFFFu), int(meta >> 24),
+             uni(int(threadIdx.x) / kWave), int(threadIdx.x) % kWave};
+    switch ((meta >> 16) & 15) {
+        case 1: lut_body<DOWN, 1>(L, c, (lds_float*)lds_buf, ready, next); break;
+        case 2: lut_body<DOWN, 2>(L, c, (lds_float*)lds_buf, ready, next); break;
+        case 3: lut_body<DOWN, 3>(L, c, (lds_float*)lds_buf, ready, next); break;
+        case 4: lut_body<DOWN, 4>(L, c, (lds_float*)lds_buf, ready, next); break;
+#if PM_LUT_THREADS == 512
+        default: lut_body<DOWN, 5>(L, c, (lds_float*)lds_buf, ready, next); break;
+#endif
     }
 }
 
@@ -1029,7 +991,7 @@ hipError_t launch_gemv(int rows, int cols, int group, int k, const uint32_t* pla
 hipError_t launch_lut(const KLaunch& L, bool down, hipStream_t st, hipEvent_t t0,
                       hipEvent_t t1) {
     if (L.n_jobs == 0 || L.n_wgq == 0) return hipSuccess;
-    const dim3 grid(unsigned(L.n_wgq * L.S));
+    const dim3 grid(unsigned(L.n_wgq), unsigned(L.S));
     if (t0 || t1) {
         if (down)
             hipExtLaunchKernelGGL(lut_kernel<true>, grid, dim3(kLutThreads), 0, st, t0, t1, 0, L);
