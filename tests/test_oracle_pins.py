@@ -142,6 +142,19 @@ def test_leaf_counts_histogram():
     assert c[1, 1, codes[1, 70]] >= 1
 
 
+def test_leaf_counts_hand_counted_blocks():
+    g = load("leaf_counts_row.json")
+    codes = np.zeros((1, g["cols"]), np.uint8)
+    for a, b, v in g["runs"]:
+        codes[0, a:b] = v
+    c = oracle.leaf_counts(codes, g["group"])
+    want = np.zeros_like(c)
+    for blk, d in g["counts"].items():
+        for leaf, n in d.items():
+            want[0, int(blk), int(leaf)] = n
+    assert np.array_equal(c, want)
+
+
 # ---------------------------------------------------------------- planes / prefix
 def test_prefix_is_top_bits_all_codes():
     codes = np.arange(256, dtype=np.uint8).reshape(1, 256)
@@ -244,6 +257,61 @@ def test_materialized_exact_when_fp16_representable():
         a, _ = oracle.gemv(planes, lv, k, g["group"], x)
         b, _ = oracle.gemv_materialized_fp16(planes, lv, k, g["group"], x)
         assert np.array_equal(a, b)
+
+
+def test_materialized_fp16_rounds_to_nearest_even():
+    g = load("fp16_rounding.json")
+    codes = np.full((1, g["cols"]), g["other_code"], np.uint8)
+    for c, v in g["codes_at"].items():
+        codes[0, int(c)] = v
+    leaves = np.array(g["leaves"], np.float32)
+    assert np.array_equal(leaves.astype(np.float64), np.array(g["leaves"]))   # exact in fp32
+    planes = oracle.pack_planes(codes)
+    lv = oracle.tree_levels(leaves[None, None, :])
+    k, grp = g["k"], g["group"]
+    for c, e in g["fp16_of_column"].items():
+        x = np.zeros(g["cols"])
+        x[int(c)] = 1.0
+        direct, _ = oracle.gemv(planes, lv, k, grp, x)
+        mat, _ = oracle.gemv_materialized_fp16(planes, lv, k, grp, x)
+        assert direct[0] == e["exact"], c
+        assert mat[0] == e["fp16"], c
+    x = np.zeros(g["cols"])
+    x[:5] = 1.0
+    mat, _ = oracle.gemv_materialized_fp16(planes, lv, k, grp, x)
+    sums = g["x_ones_on_columns_0_to_4"]
+    assert mat[0] == sums["fp16"]
+    # skipping the rounding, truncating or rounding to bf16 give other sums
+    assert len({sums["fp16"], sums["no_rounding"], sums["truncation"], sums["bf16"]}) == 4
+
+
+def test_relative_weight_error_hand_worked():
+    r = load("relative_error_2x32.json")
+    rows, cols, grp = r["rows"], r["cols"], r["group"]
+    codes = np.zeros((rows, cols), np.uint8)
+    codes[0, 0] = 255
+    codes[1, :] = 128
+    leaves = (np.arange(256, dtype=np.float64) - 127.5).astype(np.float32)
+    leaves = np.broadcast_to(leaves, (rows, 1, 256)).copy()
+    planes = oracle.pack_planes(codes)
+    lv = oracle.tree_levels(leaves)
+    # W by hand: the k = 8 reconstruction with two entries moved
+    W = np.full((rows, cols), -127.5)
+    W[0, 0] = 127.5
+    W[1, :] = 0.5
+    for key, v in r["W_changes"].items():
+        o, i = (int(t) for t in key.split(","))
+        W[o, i] = v
+    assert np.sum(W ** 2) == r["norm_W_sq"]
+    for k in (8, 1):
+        want = math.sqrt(r["err_sq"][str(k)] / r["norm_W_sq"])
+        got = oracle.relative_weight_error(W, planes, lv, k, grp)
+        assert math.isclose(got, want, rel_tol=1e-14), (k, got, want)
+    # the squared ratio, or the norm of the reconstruction in the
+    # denominator, would give other values
+    got8 = oracle.relative_weight_error(W, planes, lv, 8, grp)
+    assert not math.isclose(got8, r["err_sq"]["8"] / r["norm_W_sq"], rel_tol=1e-6)
+    assert not math.isclose(got8, math.sqrt(r["err_sq"]["8"] / r["norm_Wk_sq_8"]), rel_tol=1e-6)
 
 
 # ---------------------------------------------------------------- FFN brute force
