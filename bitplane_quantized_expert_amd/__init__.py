@@ -77,6 +77,7 @@ SIGNATURES = {
     "pm_store_create": (_I, [_ES, _I, _I, _Z, _U32, _P]),
     "pm_store_destroy": (_I, [_P]),
     "pm_store_slot": (_I, [_P, _I, _I, _P, _P]),
+    "pm_store_usage": (_I, [_P, _P, _P, _P]),
     "pm_store_set_resident": (_I, [_P, _I, _I, _I]),
     "pm_store_attach_host": (_I, [_P, _I, _I, _P, _P]),
     "pm_store_topup": (_I, [_P, _I, _I, _I, _P]),
@@ -307,6 +308,13 @@ def pm_store_slot(store, layer, expert):
     lv = ctypes.c_void_p()
     _check(lib().pm_store_slot(store.handle, layer, expert, ctypes.byref(p), ctypes.byref(lv)))
     return p.value, lv.value
+
+
+def pm_store_usage(store):
+    """(bytes held, plane chunks, slots holding levels)."""
+    u, c, l = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().pm_store_usage(store.handle, ctypes.byref(u), ctypes.byref(c), ctypes.byref(l)))
+    return u.value, c.value, l.value
 
 
 def pm_store_set_resident(store, layer, expert, r):

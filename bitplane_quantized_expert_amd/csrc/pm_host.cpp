@@ -458,8 +458,13 @@ extern "C" pm_status pm_allocate_bits(int n_tokens, int top_k, const int32_t* id
 // ---------------------------------------------------------------- store
 namespace {
 
+// A slot's planes live in one buffer of `cap` plane chunks (plane p at
+// planes + p * plane_words), so the kernels address any resident prefix with
+// one stride; the buffer grows and shrinks with the resident prefix, and the
+// levels are held while the slot holds any plane.
 struct Slot {
-    uint32_t* planes = nullptr;    // 8 chunks of plane_words
+    uint32_t* planes = nullptr;    // cap chunks of plane_words
+    int cap = 0;                   // plane chunks allocated
     float* levels = nullptr;
     int resident = 0;              // leading planes that are valid
     bool levels_ready = false;
@@ -487,7 +492,7 @@ struct pm_store {
     pm_expert_shape shape;
     Geom geom;
     int n_layers, n_experts;
-    size_t capacity, used = 0;
+    size_t capacity, used = 0;         // bytes: allocated plane chunks and levels
     bool host_fake;
     size_t plane_bytes, level_bytes;   // per plane chunk, per slot levels
     std::vector<Slot> slots;
@@ -530,32 +535,116 @@ static pm_status slot_of(const pm_store* s, int layer, int expert, size_t* idx) 
     return PM_OK;
 }
 
-static pm_status ensure_slot(pm_store* s, Slot& sl) {
-    if (sl.planes) return PM_OK;
-    const size_t pbytes = kBits * s->plane_bytes;
-    const size_t pad = (pbytes + 255) & ~size_t(255);
-    const size_t total = pad + s->level_bytes;
-    if (s->capacity && s->used + total > s->capacity)
-        return failf(PM_ERR_OOM, "store capacity %zu bytes exceeded (%zu used, %zu more)",
-                    s->capacity, s->used, total);
-    char* mem = nullptr;
+// ---- slot memory.  Device stores allocate and free in stream order on the
+// stream of the operation (a store side stream), after that stream has waited
+// for the slot's last reader and for any copy still in flight into the slot:
+// a buffer a queued forward may still read is released only after it.
+static pm_status dev_alloc(pm_store* s, size_t bytes, hipStream_t st, void** out) {
+    *out = nullptr;
+    if (bytes == 0) return PM_OK;
     if (s->host_fake) {
-        mem = static_cast<char*>(std::calloc(total, 1));
-        if (!mem) return failf(PM_ERR_OOM, "host allocation of %zu bytes failed", total);
-    } else {
-        hipError_t e = hipMalloc(&mem, total);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return failf(PM_ERR_OOM, "hipMalloc of %zu bytes failed: %s", total,
-                        hipGetErrorString(e));
-        }
-        HIP_TRY(hipEventCreateWithFlags(&sl.ready, hipEventDisableTiming));
+        *out = std::calloc(bytes, 1);
+        if (!*out) return failf(PM_ERR_OOM, "host allocation of %zu bytes failed", bytes);
+        return PM_OK;
     }
-    sl.planes = reinterpret_cast<uint32_t*>(mem);
-    sl.levels = reinterpret_cast<float*>(mem + pad);
-    sl.resident = 0;
+    const hipError_t e = hipMallocAsync(out, bytes, st);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        *out = nullptr;
+        return failf(PM_ERR_OOM, "device allocation of %zu bytes failed: %s", bytes,
+                     hipGetErrorString(e));
+    }
+    return PM_OK;
+}
+
+static pm_status dev_free(pm_store* s, void* p, hipStream_t st) {
+    if (!p) return PM_OK;
+    if (s->host_fake) {
+        std::free(p);
+        return PM_OK;
+    }
+    HIP_TRY(hipFreeAsync(p, st));
+    return PM_OK;
+}
+
+static bool slot_reader_running(pm_store* s, const Slot& sl, hipEvent_t* ev);
+
+// Make `st` wait for the last forward that read the slot (unless it has
+// finished) and for a copy into the slot still in flight.
+static pm_status order_after_readers(pm_store* s, Slot& sl, hipStream_t st) {
+    if (s->host_fake) return PM_OK;
+    hipEvent_t reader = nullptr;
+    if (slot_reader_running(s, sl, &reader)) HIP_TRY(hipStreamWaitEvent(st, reader, 0));
+    if (sl.pending) HIP_TRY(hipStreamWaitEvent(st, sl.ready, 0));
+    return PM_OK;
+}
+
+// The slot's planes buffer becomes `cap` chunks, keeping its first `keep`
+// valid chunks (keep <= both capacities).  Issued on `st`, which already
+// waits for the slot's readers.
+static pm_status resize_planes(pm_store* s, Slot& sl, int cap, int keep, hipStream_t st) {
+    if (cap == sl.cap) return PM_OK;
+    const size_t pb = s->plane_bytes;
+    void* nb = nullptr;
+    pm_status r = dev_alloc(s, size_t(cap) * pb, st, &nb);
+    if (r) return r;
+    if (keep > 0) {
+        if (s->host_fake)
+            std::memcpy(nb, sl.planes, size_t(keep) * pb);
+        else
+            HIP_TRY(hipMemcpyAsync(nb, sl.planes, size_t(keep) * pb, hipMemcpyDeviceToDevice, st));
+    }
+    r = dev_free(s, sl.planes, st);
+    if (r) return r;
+    s->used = s->used - size_t(sl.cap) * pb + size_t(cap) * pb;
+    sl.planes = static_cast<uint32_t*>(nb);
+    sl.cap = cap;
+    return PM_OK;
+}
+
+static pm_status ensure_levels(pm_store* s, Slot& sl, hipStream_t st) {
+    if (sl.levels) return PM_OK;
+    void* lv = nullptr;
+    pm_status r = dev_alloc(s, s->level_bytes, st, &lv);
+    if (r) return r;
+    sl.levels = static_cast<float*>(lv);
     sl.levels_ready = false;
-    s->used += total;
+    s->used += s->level_bytes;
+    return PM_OK;
+}
+
+// Bytes a slot still needs to hold k planes and its levels.
+static size_t bytes_to_hold(const pm_store* s, const Slot& sl, int k) {
+    size_t b = k > sl.cap ? size_t(k - sl.cap) * s->plane_bytes : 0;
+    if (!sl.levels) b += s->level_bytes;
+    return b;
+}
+
+static pm_status check_capacity(const pm_store* s, size_t more) {
+    if (s->capacity && s->used + more > s->capacity)
+        return failf(PM_ERR_OOM, "store capacity %zu bytes exceeded (%zu used, %zu more)",
+                     s->capacity, s->used, more);
+    return PM_OK;
+}
+
+// A slot ready for direct writes by the caller: all 8 chunks and the levels,
+// with the memory usable on return (the caller writes it from another stream
+// or the host).
+static pm_status slot_for_writes(pm_store* s, Slot& sl) {
+    if (sl.cap == kBits && sl.levels) return PM_OK;
+    pm_status r = check_capacity(s, bytes_to_hold(s, sl, kBits));
+    if (r) return r;
+    hipStream_t st = s->side[0];
+    r = order_after_readers(s, sl, st);
+    if (r) return r;
+    r = ensure_levels(s, sl, st);
+    if (r) return r;
+    r = resize_planes(s, sl, kBits, sl.resident, st);
+    if (r) return r;
+    if (!s->host_fake) {
+        HIP_TRY(hipStreamSynchronize(st));
+        sl.pending = false;
+    }
     return PM_OK;
 }
 
@@ -578,6 +667,14 @@ extern "C" pm_status pm_store_create(pm_expert_shape e, int n_layers, int n_expe
     s->slots.resize(size_t(n_layers) * n_experts);
     if (!s->host_fake) {
         hipError_t er = hipSuccess;
+        // freed slot memory stays in the device's pool for later slots
+        int dev = 0;
+        hipMemPool_t pool = nullptr;
+        if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+            uint64_t keep = UINT64_MAX;
+            (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        }
+        (void)hipGetLastError();
         for (int i = 0; i < pm_store::kSides && er == hipSuccess; ++i)
             er = hipStreamCreateWithFlags(&s->side[i], hipStreamNonBlocking);
         for (int i = 0; i < pm_store::kDone && er == hipSuccess; ++i)
@@ -595,14 +692,16 @@ extern "C" pm_status pm_store_destroy(pm_store* s) {
     if (!s) return PM_OK;
     if (!s->host_fake) (void)hipDeviceSynchronize();
     for (Slot& sl : s->slots) {
-        if (!sl.planes) continue;
         if (s->host_fake) {
             std::free(sl.planes);
+            std::free(sl.levels);
         } else {
-            (void)hipFree(sl.planes);
+            if (sl.planes) (void)hipFreeAsync(sl.planes, s->side[0]);
+            if (sl.levels) (void)hipFreeAsync(sl.levels, s->side[0]);
             if (sl.ready) (void)hipEventDestroy(sl.ready);
         }
     }
+    if (!s->host_fake && s->side[0]) (void)hipStreamSynchronize(s->side[0]);
     if (!s->host_fake) {
         Workspace& w = s->ws;
         if (w.d_buf) (void)hipFree(w.d_buf);
@@ -624,7 +723,7 @@ extern "C" pm_status pm_store_slot(pm_store* s, int layer, int expert, uint32_t*
     size_t i;
     pm_status st = slot_of(s, layer, expert, &i);
     if (st) return st;
-    st = ensure_slot(s, s->slots[i]);
+    st = slot_for_writes(s, s->slots[i]);
     if (st) return st;
     if (planes) *planes = s->slots[i].planes;
     if (levels) *levels = s->slots[i].levels;
@@ -636,7 +735,9 @@ extern "C" pm_status pm_store_set_resident(pm_store* s, int layer, int expert, i
     pm_status st = slot_of(s, layer, expert, &i);
     if (st) return st;
     if (r < 0 || r > kBits) return failf(PM_ERR_PREFIX, "resident prefix %d outside 0..8", r);
-    if (!s->slots[i].planes) return failf(PM_ERR_STATE, "slot (%d, %d) has no memory", layer, expert);
+    if (s->slots[i].cap < r || !s->slots[i].levels)
+        return failf(PM_ERR_STATE, "slot (%d, %d) holds %d plane chunks, %d declared", layer,
+                     expert, s->slots[i].cap, r);
     s->slots[i].resident = r;
     s->slots[i].levels_ready = true;
     s->slots[i].pending = false;
@@ -685,6 +786,11 @@ static bool slot_reader_running(pm_store* s, const Slot& sl, hipEvent_t* ev) {
     return hipEventQuery(*ev) != hipSuccess;
 }
 
+static pm_status slot_event(pm_store* s, Slot& sl) {
+    if (!s->host_fake && !sl.ready) HIP_TRY(hipEventCreateWithFlags(&sl.ready, hipEventDisableTiming));
+    return PM_OK;
+}
+
 static pm_status topup_slot(pm_store* s, Slot& sl, int k, hipStream_t side) {
     if (k <= sl.resident) {            // a resident deeper prefix serves it: no copy
         s->last_first = sl.resident;
@@ -692,8 +798,20 @@ static pm_status topup_slot(pm_store* s, Slot& sl, int k, hipStream_t side) {
         return PM_OK;
     }
     if (!sl.h_planes || !sl.h_levels) return failf(PM_ERR_STATE, "slot has no host source");
-    pm_status st = ensure_slot(s, sl);
+    pm_status st = check_capacity(s, bytes_to_hold(s, sl, k));
     if (st) return st;
+    st = slot_event(s, sl);
+    if (st) return st;
+    // the copy must not overwrite planes (or free a buffer) a forward may
+    // still read, nor race an earlier copy into the slot on another stream
+    st = order_after_readers(s, sl, side);
+    if (st) return st;
+    st = ensure_levels(s, sl, side);
+    if (st) return st;
+    if (k > sl.cap) {
+        st = resize_planes(s, sl, k, sl.resident, side);
+        if (st) return st;
+    }
     const int first = sl.resident;
     const size_t pw = s->plane_bytes / sizeof(uint32_t);
     if (s->host_fake) {
@@ -701,13 +819,6 @@ static pm_status topup_slot(pm_store* s, Slot& sl, int k, hipStream_t side) {
         std::memcpy(sl.planes + size_t(first) * pw, sl.h_planes + size_t(first) * pw,
                     size_t(k - first) * s->plane_bytes);
     } else {
-        // the copy must not overwrite planes a forward may still read: wait
-        // for the last forward that read this slot, unless it has finished
-        hipEvent_t reader = nullptr;
-        if (slot_reader_running(s, sl, &reader)) HIP_TRY(hipStreamWaitEvent(side, reader, 0));
-        // an earlier copy into this slot may still run on another stream: the
-        // ready event recorded below must cover it too
-        if (sl.pending) HIP_TRY(hipStreamWaitEvent(side, sl.ready, 0));
         if (!sl.levels_ready)
             HIP_TRY(hipMemcpyAsync(sl.levels, sl.h_levels, s->level_bytes,
                                    hipMemcpyHostToDevice, side));
@@ -732,16 +843,25 @@ static pm_status topup_slot(pm_store* s, Slot& sl, int k, hipStream_t side) {
 static pm_status issue_topups(pm_store* s, const std::vector<Slot*>& slots,
                               const std::vector<int>& k) {
     constexpr int n_free = pm_store::kSides - 1;
+    // whether each slot's last reader may still run, asked once: the answer
+    // can change between the two passes, and a slot must be in exactly one
+    std::vector<char> waits(slots.size());
+    for (size_t i = 0; i < slots.size(); ++i) {
+        hipEvent_t ev = nullptr;
+        waits[i] = slot_reader_running(s, *slots[i], &ev);
+    }
     for (int pass = 0; pass < 2; ++pass) {
         for (size_t i = 0; i < slots.size(); ++i) {
-            hipEvent_t ev = nullptr;
-            const bool waits = slot_reader_running(s, *slots[i], &ev);
-            if (waits != (pass == 1)) continue;
-            hipStream_t st = waits ? s->side[n_free] : s->side[s->next_side++ % n_free];
+            if (bool(waits[i]) != (pass == 1)) continue;
+            hipStream_t st = waits[i] ? s->side[n_free] : s->side[s->next_side++ % n_free];
             const pm_status r = topup_slot(s, *slots[i], k[i], st);
             if (r) return r;
         }
     }
+    for (size_t i = 0; i < slots.size(); ++i)
+        if (slots[i]->resident < k[i])
+            return failf(PM_ERR_STATE, "top-up left a slot at %d planes, %d needed",
+                         slots[i]->resident, k[i]);
     return PM_OK;
 }
 
@@ -759,7 +879,43 @@ extern "C" pm_status pm_store_truncate(pm_store* s, int layer, int expert, int k
     pm_status st = slot_of(s, layer, expert, &i);
     if (st) return st;
     if (keep < 0 || keep > kBits) return failf(PM_ERR_PREFIX, "keep %d outside 0..8", keep);
-    s->slots[i].resident = std::min(s->slots[i].resident, keep);
+    Slot& sl = s->slots[i];
+    sl.resident = std::min(sl.resident, keep);
+    // the plane chunks past `keep` (and at keep 0 the levels) are released,
+    // in stream order after the slot's last reader
+    if (keep >= sl.cap && (keep > 0 || !sl.levels)) return PM_OK;
+    hipStream_t side = s->side[0];
+    st = slot_event(s, sl);
+    if (st) return st;
+    st = order_after_readers(s, sl, side);
+    if (st) return st;
+    st = resize_planes(s, sl, std::min(sl.cap, keep), sl.resident, side);
+    if (st) return st;
+    if (keep == 0 && sl.levels) {
+        st = dev_free(s, sl.levels, side);
+        if (st) return st;
+        sl.levels = nullptr;
+        sl.levels_ready = false;
+        s->used -= s->level_bytes;
+    }
+    if (!s->host_fake) {
+        HIP_TRY(hipEventRecord(sl.ready, side));
+        sl.pending = true;
+    }
+    return PM_OK;
+}
+
+extern "C" pm_status pm_store_usage(const pm_store* s, size_t* used_bytes, size_t* plane_chunks,
+                                    size_t* level_sets) {
+    if (!s) return failf(PM_ERR_ARG, "null store");
+    size_t chunks = 0, sets = 0;
+    for (const Slot& sl : s->slots) {
+        chunks += size_t(sl.cap);
+        sets += sl.levels ? 1 : 0;
+    }
+    if (used_bytes) *used_bytes = s->used;
+    if (plane_chunks) *plane_chunks = chunks;
+    if (level_sets) *level_sets = sets;
     return PM_OK;
 }
 
@@ -1120,21 +1276,6 @@ static pm_status forward_mfma(pm_store* s, int layer, int n_tokens, int top_k,
     P.gu_smax = 1;
     P.dn_smax = 1;
 
-    // forwards on one store run in order; on the same stream they already do
-    if (s->fwd_seq > 0 && compute != s->last_compute)
-        HIP_TRY(hipStreamWaitEvent(compute, forward_end(s, s->fwd_seq), 0));
-    // top-ups of short slots
-    {
-        std::vector<Slot*> ls;
-        std::vector<int> lk;
-        for (int d = 0; d < n_items; ++d) {
-            if (!late[d]) continue;
-            ls.push_back(slot[d]);
-            lk.push_back(kneed[d]);
-        }
-        st = issue_topups(s, ls, lk);
-        if (st) return st;
-    }
     // uses and tiles through the pinned ring
     Workspace& w = s->ws;
     const int rs = w.next;
@@ -1185,7 +1326,6 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
                                           const uint8_t* h_k, const float* d_x, float* d_y,
                                           void* compute_v, uint32_t flags) {
     if (!s) return failf(PM_ERR_ARG, "null store");
-    if (s->host_fake) return failf(PM_ERR_STATE, "a host-backed store cannot compute");
     if (flags & ~uint32_t(PM_AUTO_TOPUP | PM_BATCH_MFMA | PM_READ_ONCE | PM_DETERMINISTIC))
         return failf(PM_ERR_ARG, "unknown forward flags");
     const bool mfma = flags & PM_BATCH_MFMA;
@@ -1250,29 +1390,53 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
             for (int m = 0; m < 3; ++m) kmax[d][m] = std::max(kmax[d][m], uses[u].k[m]);
         kneed[d] = std::max(kmax[d][0], std::max(kmax[d][1], kmax[d][2]));
     }
-    // ---- residency: every short slot must be topped up (or the call fails)
+    // ---- residency: every short slot must be topped up (or the call fails).
+    // Every item is checked, and the memory of all new slots counted against
+    // the capacity, before any slot is allocated: a failing call leaves the
+    // store as it was.
     std::vector<char> late(n_items, 0);
+    size_t new_bytes = 0;
     for (int d = 0; d < n_items; ++d) {
         Slot& sl = s->slots[size_t(layer) * s->n_experts + item_expert[d]];
-        const bool ok = sl.planes && sl.levels_ready && sl.resident >= kneed[d];
+        const bool ok = sl.levels_ready && sl.resident >= kneed[d];
         if (!ok) {
             if (!(flags & PM_AUTO_TOPUP))
                 return failf(PM_ERR_NOT_RESIDENT,
                             "expert (%d, %d) holds %d planes, %d requested", layer,
-                            item_expert[d], sl.planes ? sl.resident : 0, kneed[d]);
+                            item_expert[d], sl.resident, kneed[d]);
             if (!sl.h_planes || !sl.h_levels)
                 return failf(PM_ERR_STATE, "expert (%d, %d) is short and has no host source",
                             layer, item_expert[d]);
-            // the work lists take the slot's addresses before its top-up runs
-            pm_status st = ensure_slot(s, sl);
-            if (st) return st;
+            new_bytes += bytes_to_hold(s, sl, kneed[d]);
             late[d] = 1;
         }
     }
+    {
+        pm_status st = check_capacity(s, new_bytes);
+        if (st) return st;
+    }
+    if (s->host_fake) return failf(PM_ERR_STATE, "a host-backed store cannot compute");
     // resident items first so their kernels can run while top-ups copy
     std::vector<int> order(n_items);
     for (int d = 0; d < n_items; ++d) order[d] = d;
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return late[a] < late[b]; });
+
+    // forwards on one store run in order; on the same stream they already do
+    if (s->fwd_seq > 0 && compute != s->last_compute)
+        HIP_TRY(hipStreamWaitEvent(compute, forward_end(s, s->fwd_seq), 0));
+    // top-ups (side streams) of the late items, before any work list takes a
+    // slot address: a top-up may move the slot's plane buffer
+    {
+        std::vector<Slot*> ls;
+        std::vector<int> lk;
+        for (int d = 0; d < n_items; ++d) {
+            if (!late[d]) continue;
+            ls.push_back(&s->slots[size_t(layer) * s->n_experts + item_expert[d]]);
+            lk.push_back(kneed[d]);
+        }
+        pm_status st = issue_topups(s, ls, lk);
+        if (st) return st;
+    }
     if (mfma)
         return forward_mfma(s, layer, n_tokens, top_k, uses, item_expert, item_uses, kneed, late,
                             d_x, d_y, compute);
@@ -1434,21 +1598,6 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         pack_launches(js, dn_proto, L_dn);
     }
 
-    // forwards on one store run in order; on the same stream they already do
-    if (s->fwd_seq > 0 && compute != s->last_compute)
-        HIP_TRY(hipStreamWaitEvent(compute, forward_end(s, s->fwd_seq), 0));
-
-    // ---- top-ups (side streams) for late items
-    {
-        std::vector<Slot*> ls;
-        std::vector<int> lk;
-        for (int i = n_res; i < n_items; ++i) {
-            ls.push_back(&slot_of_item(order[i]));
-            lk.push_back(kneed[order[i]]);
-        }
-        st = issue_topups(s, ls, lk);
-        if (st) return st;
-    }
 
 
     // ---- direct-path work list and tiles into the pinned ring, then to the device

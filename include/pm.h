@@ -176,20 +176,30 @@ pm_status pm_allocate_bits(int n_tokens, int top_k, const int32_t* ids, const fl
 /* ---------------------------------------------------------------- plane store
  * HBM store of encoded experts with plane-granular residency [T c13, c35;
  * Abs: a cached prefix is reused as is or extended by reading only the planes
- * it lacks].  A slot (layer, expert) holds the 8 plane chunks and the levels
- * of one expert; its resident prefix r counts the leading planes that are
- * valid.  A plane is usable only when every earlier plane is resident, so r
- * is always a prefix count.  The store owns all slot memory.
+ * it lacks].  A slot (layer, expert) holds the plane chunks and the levels of
+ * one expert; its resident prefix r counts the leading planes that are valid.
+ * A plane is usable only when every earlier plane is resident, so r is always
+ * a prefix count.  The store owns all slot memory, and memory follows
+ * residency: a slot's planes sit in one buffer of as many plane chunks as a
+ * top-up needed (plane p at planes + p * pm_expert_plane_words(e)), a
+ * truncation releases the chunks past the kept prefix, and a slot holds its
+ * levels while it holds any plane.  Growing or shrinking a buffer moves it
+ * (the resident prefix is copied along) in stream order after every forward
+ * still reading the slot, so slot addresses are valid only until the next
+ * store call on that slot.
  * flags: PM_STORE_HOST_FAKE backs slots with host memory and copies with
  * memcpy (bookkeeping tests without a GPU; compute calls reject such a
- * store).  capacity_bytes > 0 caps the slot memory (PM_ERR_OOM beyond). */
+ * store).  capacity_bytes > 0 caps the slot memory, plane chunks plus levels
+ * (PM_ERR_OOM beyond). */
 typedef struct pm_store pm_store;
 enum { PM_STORE_HOST_FAKE = 1u };
 pm_status pm_store_create(pm_expert_shape e, int n_layers, int n_experts,
                           size_t capacity_bytes, uint32_t flags, pm_store** out);
 pm_status pm_store_destroy(pm_store* s);
-/* Slot memory (allocated on first use, r = 0): plane chunk p at
- * *planes + p * pm_expert_plane_words(e); levels at *levels. */
+/* Slot memory for direct writes: all 8 plane chunks and the levels are
+ * allocated (the resident prefix kept) and usable when the call returns;
+ * plane chunk p at *planes + p * pm_expert_plane_words(e); levels at
+ * *levels. */
 pm_status pm_store_slot(pm_store* s, int layer, int expert, uint32_t** planes,
                         float** levels);
 /* Declare that the caller has written planes 0..r-1 and all levels of a slot
@@ -208,8 +218,15 @@ pm_status pm_store_attach_host(pm_store* s, int layer, int expert,
  * [T c13, c35: a resident deeper prefix serves a shallower request].
  * PM_ERR_STATE without a host source. */
 pm_status pm_store_topup(pm_store* s, int layer, int expert, int k, void* side);
-/* r = min(r, keep): the deepest planes age out first [T c35]. */
+/* r = min(r, keep): the deepest planes age out first [T c35].  The plane
+ * chunks past keep are released (at keep 0 the levels too), in stream order
+ * on the store's side stream after the slot's last reader. */
 pm_status pm_store_truncate(pm_store* s, int layer, int expert, int keep);
+/* Slot memory held by the store: bytes (plane chunks and levels, what
+ * capacity_bytes caps), plane chunks, and slots holding levels.  Any output
+ * may be null. */
+pm_status pm_store_usage(const pm_store* s, size_t* used_bytes, size_t* plane_chunks,
+                         size_t* level_sets);
 pm_status pm_store_resident(const pm_store* s, int layer, int expert, int* r_out);
 /* Planes copied by the last top-up of any slot (first plane, count) and the
  * running totals of plane chunks and bytes copied by top-ups. */

@@ -462,8 +462,6 @@ def test_forward_batch8_grouped_with_topup():
     syn = DeviceSynth()
     for j, i in enumerate(short):
         pp, lp = pm.pm_store_slot(st, 0, i)
-        planes_t = torch.empty(8 * pw, dtype=torch.int32, device="cuda")
-        levels_t = torch.empty(pm.pm_expert_levels_floats(e), dtype=torch.float32, device="cuda")
         # keep a pinned host source of the full expert
         torch.cuda.synchronize()
         src_p = torch.empty(8 * pw, dtype=torch.int32, pin_memory=True)
@@ -475,12 +473,13 @@ def test_forward_batch8_grouped_with_topup():
         assert hip.hipMemcpy(ctypes.c_void_p(src_l.data_ptr()), ctypes.c_void_p(lp),
                              ctypes.c_size_t(src_l.numel() * 4), 2) == 0
         sources[i] = (src_p, src_l)
-        del planes_t, levels_t
         pm.pm_store_attach_host(st, 0, i, src_p.data_ptr(), src_l.data_ptr())
         r = 1 + int(synth.words(wl.seed, synth.KIND_TRUNC, 4, 0, 1, j, 1)[0] % (kmax[i] - 1))
         pm.pm_store_truncate(st, 0, i, r)
-        # poison the planes that are no longer resident
-        slot_planes = torch.empty(0)
+        # truncation released the chunks past r; the slot's address for
+        # direct writes holds all 8 again (r resident), and the rest is
+        # poisoned: a top-up that copied too little would read it
+        pp, _ = pm.pm_store_slot(st, 0, i)
         n_poison = (8 - r) * pw
         tmp = torch.empty(n_poison, dtype=torch.int32, device="cuda")
         syn.poison_into(tmp, 5, j)
@@ -723,6 +722,9 @@ def test_forward_topup_waits_for_a_pending_explicit_topup():
     for rep in range(3):
         pm.pm_store_truncate(st, 0, 0, 1)
         torch.cuda.synchronize()
+        # the slot again holds all 8 chunks (plane 0 resident): the explicit
+        # top-up and the forward's copy then write in place
+        pp, _ = pm.pm_store_slot(st, 0, 0)
         assert hip.hipMemcpy(ctypes.c_void_p(pp + 4 * pw), ctypes.c_void_p(poison.data_ptr()),
                              ctypes.c_size_t(7 * pw * 4), 3) == 0
         with torch.cuda.stream(side):

@@ -161,15 +161,100 @@ def test_store_residency_pages_examples():
     # a top-up copies the missing planes and leaves the resident ones alone
     pm.pm_store_truncate(st, 0, 1, 0)
     pm.pm_store_topup(st, 0, 1, 3)
-    pp, lp = pm.pm_store_slot(st, 0, 1)
-    slot = np.ctypeslib.as_array(ctypes.cast(pp, ctypes.POINTER(ctypes.c_uint32)), (8, pw))
-    lev = np.ctypeslib.as_array(ctypes.cast(lp, ctypes.POINTER(ctypes.c_float)), hl.shape)
+    def view():
+        # the slot's memory as written: plane chunks and levels (this grows
+        # the slot to 8 chunks, keeping the resident prefix)
+        pp, lp = pm.pm_store_slot(st, 0, 1)
+        slot = np.ctypeslib.as_array(ctypes.cast(pp, ctypes.POINTER(ctypes.c_uint32)), (8, pw))
+        lev = np.ctypeslib.as_array(ctypes.cast(lp, ctypes.POINTER(ctypes.c_float)), hl.shape)
+        return slot, lev
+
+    slot, lev = view()
     assert np.array_equal(slot[:3], hp[:3]) and np.array_equal(lev, hl)
     slot[3:] = 0
     slot[1] = 7                        # scribble over a resident plane
     pm.pm_store_truncate(st, 0, 1, 2)
     pm.pm_store_topup(st, 0, 1, 5)
+    slot, _ = view()
     assert np.array_equal(slot[2:5], hp[2:5]) and np.all(slot[5:] == 0) and np.all(slot[1] == 7)
+    st.close()
+
+
+def test_store_memory_follows_residency():
+    """Plane chunks are held for the resident prefix only: a top-up grows the
+    slot to k chunks, a truncation releases the chunks past the kept prefix
+    and, at 0, the levels [T c35: the deepest planes age out first]."""
+    e, st = fake_store()
+    pw = pm.pm_expert_plane_words(e)
+    lf = pm.pm_expert_levels_floats(e)
+    pb, lb = 4 * pw, 4 * lf
+    hp = np.arange(8 * pw, dtype=np.uint32).reshape(8, pw)
+    hl = np.arange(lf, dtype=np.float32)
+    for x in (0, 1):
+        pm.pm_store_attach_host(st, 0, x, hp, hl)
+    assert pm.pm_store_usage(st) == (0, 0, 0)
+    pm.pm_store_topup(st, 0, 0, 3)
+    assert pm.pm_store_usage(st) == (3 * pb + lb, 3, 1)
+    pm.pm_store_topup(st, 0, 1, 5)
+    assert pm.pm_store_usage(st) == (8 * pb + 2 * lb, 8, 2)
+    pm.pm_store_truncate(st, 0, 1, 2)
+    assert pm.pm_store_usage(st) == (5 * pb + 2 * lb, 5, 2)
+    assert pm.pm_store_resident(st, 0, 1) == 2
+    pm.pm_store_truncate(st, 0, 1, 4)          # keeping more than is held changes nothing
+    assert pm.pm_store_usage(st) == (5 * pb + 2 * lb, 5, 2)
+    pm.pm_store_topup(st, 0, 1, 4)             # copies planes 2 and 3 only
+    first, count, _, _ = pm.pm_store_copy_stats(st)
+    assert (first, count) == (2, 2)
+    assert pm.pm_store_usage(st) == (7 * pb + 2 * lb, 7, 2)
+    pm.pm_store_truncate(st, 0, 0, 0)
+    assert pm.pm_store_usage(st) == (4 * pb + lb, 4, 1)
+    pm.pm_store_truncate(st, 0, 1, 0)
+    assert pm.pm_store_usage(st) == (0, 0, 0)
+    # a slot emptied and topped up again reads its levels again
+    _, _, _, bytes0 = pm.pm_store_copy_stats(st)
+    pm.pm_store_topup(st, 0, 1, 1)
+    _, _, _, bytes1 = pm.pm_store_copy_stats(st)
+    assert bytes1 - bytes0 == pb + lb
+    # capacity counts chunks and levels: room for 3 more chunks, not 4
+    st2 = pm.pm_store_create(e, 1, 2, 3 * pb + lb, pm.PM_STORE_HOST_FAKE)
+    pm.pm_store_attach_host(st2, 0, 0, hp, hl)
+    with pytest.raises(pm.PMError) as ei:
+        pm.pm_store_topup(st2, 0, 0, 4)
+    assert ei.value.status == pm.PM_ERR_OOM
+    assert pm.pm_store_usage(st2) == (0, 0, 0)
+    pm.pm_store_topup(st2, 0, 0, 3)
+    assert pm.pm_store_usage(st2) == (3 * pb + lb, 3, 1)
+    st2.close()
+    st.close()
+
+
+def test_forward_validates_every_item_before_any_allocation():
+    """A layer call whose later item cannot be served changes nothing in the
+    store: no slot memory is taken for the earlier items."""
+    e, st = fake_store()
+    pw = pm.pm_expert_plane_words(e)
+    lf = pm.pm_expert_levels_floats(e)
+    hp = np.zeros((8, pw), np.uint32)
+    hl = np.zeros(lf, np.float32)
+    pm.pm_store_attach_host(st, 0, 0, hp, hl)          # expert 1: no host source
+    ids = np.array([[0, 1]], np.int32)
+    w = np.array([[0.5, 0.5]], np.float32)
+    k = np.full((1, 2, 3), 3, np.uint8)
+    with pytest.raises(pm.PMError) as ei:
+        pm.pm_moe_token_forward(st, 0, ids, w, k, 16, 16, flags=pm.PM_AUTO_TOPUP)
+    assert ei.value.status == pm.PM_ERR_STATE
+    assert pm.pm_store_usage(st) == (0, 0, 0)
+    assert pm.pm_store_resident(st, 0, 0) == 0
+    st.close()
+    # capacity for one expert's top-up but not for both
+    pb, lb = 4 * pw, 4 * lf
+    st = pm.pm_store_create(e, 1, 3, 3 * pb + lb + 8, pm.PM_STORE_HOST_FAKE)
+    for x in (0, 1):
+        pm.pm_store_attach_host(st, 0, x, hp, hl)
+    with pytest.raises(pm.PMError) as ei:
+        pm.pm_moe_token_forward(st, 0, ids, w, k, 16, 16, flags=pm.PM_AUTO_TOPUP)
+    assert ei.value.status == pm.PM_ERR_OOM
+    assert pm.pm_store_usage(st) == (0, 0, 0)
     st.close()
 
 
@@ -191,15 +276,17 @@ def test_store_errors():
         rc = L.pm_store_set_profile_events(st.handle, two if n else None, n)
         assert (rc == 0) == ok, n
     assert L.pm_store_set_profile_events(st.handle, None, 0) == 0
-    # a host-backed store cannot run a forward
+    # a host-backed store cannot run a forward (its inputs pass validation)
+    pm.pm_store_slot(st, 0, 0)
+    pm.pm_store_set_resident(st, 0, 0, 8)
     with pytest.raises(pm.PMError) as ei:
         pm.pm_moe_token_forward(st, 0, np.zeros((1, 1)), np.ones((1, 1)), np.ones((1, 1, 3)),
-                                1, 1)
+                                16, 16)
     assert ei.value.status == pm.PM_ERR_STATE
     st.close()
     # capacity cap
     cap_e = pm.eshape(64, 32, 32)
-    one_slot = 8 * pm.pm_expert_plane_words(cap_e) * 4 + 256 + pm.pm_expert_levels_floats(cap_e) * 4
+    one_slot = 8 * pm.pm_expert_plane_words(cap_e) * 4 + pm.pm_expert_levels_floats(cap_e) * 4
     st = pm.pm_store_create(cap_e, 1, 3, one_slot + 10, pm.PM_STORE_HOST_FAKE)
     pm.pm_store_slot(st, 0, 0)
     with pytest.raises(pm.PMError) as ei:
