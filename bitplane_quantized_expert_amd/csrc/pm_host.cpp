@@ -475,6 +475,14 @@ struct Slot {
     uint64_t read_seq = 0;         // last forward that read the slot (0: none)
 };
 
+// A released slot buffer that may still be in use: freed once the copy
+// event has completed and the forward `reader` has ended.
+struct Retired {
+    void* p;
+    hipEvent_t copied;             // after the last copy from or into the buffer
+    uint64_t reader;               // the last forward that read it (0: none)
+};
+
 struct Workspace {
     float* d_buf = nullptr;        // G, U, Y partial results
     size_t d_floats = 0;
@@ -496,13 +504,24 @@ struct pm_store {
     bool host_fake;
     size_t plane_bytes, level_bytes;   // per plane chunk, per slot levels
     std::vector<Slot> slots;
-    // The store's own top-up streams.  Copies that need no wait take the
-    // first kSides - 1 in turn (more than one copy in flight keeps the link
-    // busier); copies that wait for an earlier forward still reading their
-    // slot take the last, so that a wait holds up no other copy.
-    static constexpr int kSides = 3;
+    // The store's own streams.  side[0] is the memory stream: every
+    // allocation and release of slot memory, and the moves of truncation.
+    // Top-up copies that need no wait take side[1] and side[2] in turn (more
+    // than one copy in flight keeps the link busier); copies that wait for an
+    // earlier forward still reading their slot take side[3], so that a wait
+    // holds up no other copy.
+    static constexpr int kSides = 4;
+    static constexpr int kMem = 0, kWaits = 3;
     hipStream_t side[kSides] = {};
     uint32_t next_side = 0;
+    // Slot memory: a pool of the store's own, allocated from and released to
+    // on the memory stream only.  Buffers a queued forward or copy may still
+    // use wait in `retired` until a later store call finds them idle.
+    hipMemPool_t pool = nullptr;
+    std::vector<Retired> retired;
+    std::vector<hipEvent_t> spare_events;
+    hipEvent_t alloc_ev = nullptr;     // marks the memory stream after its last allocation
+    bool alloc_unpublished = false;    // an allocation no copy stream has waited for yet
     // Ends of recent forwards: done[n % kDone] marks the end of forward n
     // (n >= 1).  A forward records it only when the store has host sources
     // (a top-up may need it); otherwise it is recorded later on the last
@@ -535,11 +554,71 @@ static pm_status slot_of(const pm_store* s, int layer, int expert, size_t* idx) 
     return PM_OK;
 }
 
-// ---- slot memory.  Device stores allocate and free in stream order on the
-// stream of the operation (a store side stream), after that stream has waited
-// for the slot's last reader and for any copy still in flight into the slot:
-// a buffer a queued forward may still read is released only after it.
-static pm_status dev_alloc(pm_store* s, size_t bytes, hipStream_t st, void** out) {
+// ---- slot memory.  Every allocation and every release of a device store's
+// slot memory is issued on the memory stream, from and to the store's own
+// pool, so the pool reuses memory in that one stream's order.  A buffer that
+// a queued forward or copy may still use is not released at once: it is
+// retired with an event after its last copy and the forward that last read
+// it, and a later store call releases it once both have completed.  The pool
+// thus only ever takes back idle memory.
+static bool slot_reader_running(pm_store* s, const Slot& sl, hipEvent_t* ev);
+static hipEvent_t forward_end(pm_store* s, uint64_t n);
+
+static pm_status take_event(pm_store* s, hipEvent_t* ev) {
+    if (!s->spare_events.empty()) {
+        *ev = s->spare_events.back();
+        s->spare_events.pop_back();
+        return PM_OK;
+    }
+    HIP_TRY(hipEventCreateWithFlags(ev, hipEventDisableTiming));
+    return PM_OK;
+}
+
+// Release the retired buffers whose last copy and last reader have ended.
+static pm_status reclaim(pm_store* s) {
+    if (s->host_fake || s->retired.empty()) return PM_OK;
+    std::vector<Retired> keep;
+    pm_status st = PM_OK;
+    for (const Retired& r : s->retired) {
+        bool idle = st == PM_OK && (!r.copied || hipEventQuery(r.copied) == hipSuccess);
+        if (idle && r.reader) idle = hipEventQuery(forward_end(s, r.reader)) == hipSuccess;
+        if (!idle) {
+            keep.push_back(r);
+            continue;
+        }
+        const hipError_t e = hipFreeAsync(r.p, s->side[pm_store::kMem]);
+        if (e != hipSuccess) {
+            st = hip_fail(e, "hipFreeAsync");
+            keep.push_back(r);
+            continue;
+        }
+        if (r.copied) s->spare_events.push_back(r.copied);
+    }
+    s->retired.swap(keep);
+    return st;
+}
+
+// Retire buffer p: its last copy was issued on stream `last` (the event is
+// recorded there now) and forward `reader` last read it.
+static pm_status retire(pm_store* s, void* p, hipStream_t last, uint64_t reader) {
+    if (!p) return PM_OK;
+    if (s->host_fake) {
+        std::free(p);
+        return PM_OK;
+    }
+    hipEvent_t ev = nullptr;
+    pm_status st = take_event(s, &ev);
+    if (st) return st;
+    const hipError_t e = hipEventRecord(ev, last);
+    if (e != hipSuccess) {
+        s->spare_events.push_back(ev);
+        return hip_fail(e, "hipEventRecord");
+    }
+    s->retired.push_back({p, ev, reader});
+    return PM_OK;
+}
+
+static pm_status dev_alloc(pm_store* s, size_t bytes, void** out) {
     *out = nullptr;
     if (bytes == 0) return PM_OK;
     if (s->host_fake) {
@@ -547,27 +626,26 @@ static pm_status dev_alloc(pm_store* s, size_t bytes, hipStream_t st, void** out
         if (!*out) return failf(PM_ERR_OOM, "host allocation of %zu bytes failed", bytes);
         return PM_OK;
     }
-    const hipError_t e = hipMallocAsync(out, bytes, st);
+    const hipError_t e = hipMallocFromPoolAsync(out, bytes, s->pool, s->side[pm_store::kMem]);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         *out = nullptr;
         return failf(PM_ERR_OOM, "device allocation of %zu bytes failed: %s", bytes,
                      hipGetErrorString(e));
     }
+    s->alloc_unpublished = true;
     return PM_OK;
 }
 
-static pm_status dev_free(pm_store* s, void* p, hipStream_t st) {
-    if (!p) return PM_OK;
-    if (s->host_fake) {
-        std::free(p);
-        return PM_OK;
-    }
-    HIP_TRY(hipFreeAsync(p, st));
+// Make copy stream `st` wait for the allocations issued so far.
+static pm_status publish_allocs(pm_store* s, hipStream_t st) {
+    if (s->host_fake || !s->alloc_unpublished || st == s->side[pm_store::kMem]) return PM_OK;
+    if (!s->alloc_ev) HIP_TRY(hipEventCreateWithFlags(&s->alloc_ev, hipEventDisableTiming));
+    HIP_TRY(hipEventRecord(s->alloc_ev, s->side[pm_store::kMem]));
+    HIP_TRY(hipStreamWaitEvent(st, s->alloc_ev, 0));
+    s->alloc_unpublished = false;
     return PM_OK;
 }
-
-static bool slot_reader_running(pm_store* s, const Slot& sl, hipEvent_t* ev);
 
 // Make `st` wait for the last forward that read the slot (unless it has
 // finished) and for a copy into the slot still in flight.
@@ -579,22 +657,26 @@ static pm_status order_after_readers(pm_store* s, Slot& sl, hipStream_t st) {
     return PM_OK;
 }
 
-// The slot's planes buffer becomes `cap` chunks, keeping its first `keep`
-// valid chunks (keep <= both capacities).  Issued on `st`, which already
-// waits for the slot's readers.
+// The slot's planes move to a new buffer of `cap` chunks (none at 0) that
+// keeps the first `keep` valid chunks (keep <= both capacities), copied on
+// `st` after any copy still in flight into the old buffer; the old buffer is
+// retired.  Readers of the old buffer need no wait: it stays until they end.
 static pm_status resize_planes(pm_store* s, Slot& sl, int cap, int keep, hipStream_t st) {
     if (cap == sl.cap) return PM_OK;
     const size_t pb = s->plane_bytes;
     void* nb = nullptr;
-    pm_status r = dev_alloc(s, size_t(cap) * pb, st, &nb);
+    pm_status r = dev_alloc(s, size_t(cap) * pb, &nb);
     if (r) return r;
-    if (keep > 0) {
-        if (s->host_fake)
-            std::memcpy(nb, sl.planes, size_t(keep) * pb);
-        else
+    if (s->host_fake) {
+        if (keep > 0) std::memcpy(nb, sl.planes, size_t(keep) * pb);
+    } else {
+        r = publish_allocs(s, st);
+        if (r) return r;
+        if (sl.pending) HIP_TRY(hipStreamWaitEvent(st, sl.ready, 0));
+        if (keep > 0)
             HIP_TRY(hipMemcpyAsync(nb, sl.planes, size_t(keep) * pb, hipMemcpyDeviceToDevice, st));
     }
-    r = dev_free(s, sl.planes, st);
+    r = retire(s, sl.planes, st, sl.read_seq);
     if (r) return r;
     s->used = s->used - size_t(sl.cap) * pb + size_t(cap) * pb;
     sl.planes = static_cast<uint32_t*>(nb);
@@ -602,10 +684,10 @@ static pm_status resize_planes(pm_store* s, Slot& sl, int cap, int keep, hipStre
     return PM_OK;
 }
 
-static pm_status ensure_levels(pm_store* s, Slot& sl, hipStream_t st) {
+static pm_status ensure_levels(pm_store* s, Slot& sl) {
     if (sl.levels) return PM_OK;
     void* lv = nullptr;
-    pm_status r = dev_alloc(s, s->level_bytes, st, &lv);
+    pm_status r = dev_alloc(s, s->level_bytes, &lv);
     if (r) return r;
     sl.levels = static_cast<float*>(lv);
     sl.levels_ready = false;
@@ -632,12 +714,12 @@ static pm_status check_capacity(const pm_store* s, size_t more) {
 // or the host).
 static pm_status slot_for_writes(pm_store* s, Slot& sl) {
     if (sl.cap == kBits && sl.levels) return PM_OK;
-    pm_status r = check_capacity(s, bytes_to_hold(s, sl, kBits));
+    pm_status r = reclaim(s);
     if (r) return r;
-    hipStream_t st = s->side[0];
-    r = order_after_readers(s, sl, st);
+    r = check_capacity(s, bytes_to_hold(s, sl, kBits));
     if (r) return r;
-    r = ensure_levels(s, sl, st);
+    hipStream_t st = s->side[pm_store::kMem];
+    r = ensure_levels(s, sl);
     if (r) return r;
     r = resize_planes(s, sl, kBits, sl.resident, st);
     if (r) return r;
@@ -667,14 +749,29 @@ extern "C" pm_status pm_store_create(pm_expert_shape e, int n_layers, int n_expe
     s->slots.resize(size_t(n_layers) * n_experts);
     if (!s->host_fake) {
         hipError_t er = hipSuccess;
-        // freed slot memory stays in the device's pool for later slots
+        // the store's pool on the current device: released slot memory stays
+        // in it for later slots (until the store is destroyed), and it reuses
+        // memory only in the memory stream's order
         int dev = 0;
-        hipMemPool_t pool = nullptr;
-        if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
-            uint64_t keep = UINT64_MAX;
-            (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        er = hipGetDevice(&dev);
+        if (er == hipSuccess) {
+            hipMemPoolProps props{};
+            props.allocType = hipMemAllocationTypePinned;
+            props.handleTypes = hipMemHandleTypeNone;
+            props.location.type = hipMemLocationTypeDevice;
+            props.location.id = dev;
+            er = hipMemPoolCreate(&s->pool, &props);
         }
-        (void)hipGetLastError();
+        if (er == hipSuccess) {
+            uint64_t keep = UINT64_MAX;
+            int off = 0;
+            er = hipMemPoolSetAttribute(s->pool, hipMemPoolAttrReleaseThreshold, &keep);
+            if (er == hipSuccess)
+                er = hipMemPoolSetAttribute(s->pool, hipMemPoolReuseAllowOpportunistic, &off);
+            if (er == hipSuccess)
+                er = hipMemPoolSetAttribute(s->pool, hipMemPoolReuseAllowInternalDependencies,
+                                            &off);
+        }
         for (int i = 0; i < pm_store::kSides && er == hipSuccess; ++i)
             er = hipStreamCreateWithFlags(&s->side[i], hipStreamNonBlocking);
         for (int i = 0; i < pm_store::kDone && er == hipSuccess; ++i)
@@ -691,17 +788,27 @@ extern "C" pm_status pm_store_create(pm_expert_shape e, int n_layers, int n_expe
 extern "C" pm_status pm_store_destroy(pm_store* s) {
     if (!s) return PM_OK;
     if (!s->host_fake) (void)hipDeviceSynchronize();
+    hipStream_t mem = s->side[pm_store::kMem];
     for (Slot& sl : s->slots) {
         if (s->host_fake) {
             std::free(sl.planes);
             std::free(sl.levels);
-        } else {
-            if (sl.planes) (void)hipFreeAsync(sl.planes, s->side[0]);
-            if (sl.levels) (void)hipFreeAsync(sl.levels, s->side[0]);
-            if (sl.ready) (void)hipEventDestroy(sl.ready);
+        } else if (mem) {
+            if (sl.planes) (void)hipFreeAsync(sl.planes, mem);
+            if (sl.levels) (void)hipFreeAsync(sl.levels, mem);
         }
+        if (sl.ready) (void)hipEventDestroy(sl.ready);
     }
-    if (!s->host_fake && s->side[0]) (void)hipStreamSynchronize(s->side[0]);
+    if (!s->host_fake) {
+        for (const Retired& r : s->retired) {
+            if (mem) (void)hipFreeAsync(r.p, mem);
+            if (r.copied) (void)hipEventDestroy(r.copied);
+        }
+        for (hipEvent_t ev : s->spare_events) (void)hipEventDestroy(ev);
+        if (s->alloc_ev) (void)hipEventDestroy(s->alloc_ev);
+        if (mem) (void)hipStreamSynchronize(mem);
+        if (s->pool) (void)hipMemPoolDestroy(s->pool);
+    }
     if (!s->host_fake) {
         Workspace& w = s->ws;
         if (w.d_buf) (void)hipFree(w.d_buf);
@@ -798,18 +905,25 @@ static pm_status topup_slot(pm_store* s, Slot& sl, int k, hipStream_t side) {
         return PM_OK;
     }
     if (!sl.h_planes || !sl.h_levels) return failf(PM_ERR_STATE, "slot has no host source");
-    pm_status st = check_capacity(s, bytes_to_hold(s, sl, k));
+    pm_status st = reclaim(s);
+    if (st) return st;
+    st = check_capacity(s, bytes_to_hold(s, sl, k));
     if (st) return st;
     st = slot_event(s, sl);
     if (st) return st;
-    // the copy must not overwrite planes (or free a buffer) a forward may
-    // still read, nor race an earlier copy into the slot on another stream
-    st = order_after_readers(s, sl, side);
-    if (st) return st;
-    st = ensure_levels(s, sl, side);
+    st = ensure_levels(s, sl);
     if (st) return st;
     if (k > sl.cap) {
+        // into a new buffer: an earlier reader keeps the old one
         st = resize_planes(s, sl, k, sl.resident, side);
+        if (st) return st;
+    } else {
+        // in place: the copy must not overwrite planes a forward may still
+        // read (after the resident prefix was lowered), nor race an earlier
+        // copy into the slot on another stream
+        st = order_after_readers(s, sl, side);
+        if (st) return st;
+        st = publish_allocs(s, side);
         if (st) return st;
     }
     const int first = sl.resident;
@@ -842,18 +956,20 @@ static pm_status topup_slot(pm_store* s, Slot& sl, int k, hipStream_t side) {
 // those that wait for an earlier forward's reads, on the last side stream.
 static pm_status issue_topups(pm_store* s, const std::vector<Slot*>& slots,
                               const std::vector<int>& k) {
-    constexpr int n_free = pm_store::kSides - 1;
-    // whether each slot's last reader may still run, asked once: the answer
-    // can change between the two passes, and a slot must be in exactly one
+    constexpr int n_free = pm_store::kWaits - 1;
+    // whether each in-place copy must wait for the slot's last reader, asked
+    // once: the answer can change between the two passes, and a slot must be
+    // in exactly one (a copy into a new buffer never waits for a reader)
     std::vector<char> waits(slots.size());
     for (size_t i = 0; i < slots.size(); ++i) {
         hipEvent_t ev = nullptr;
-        waits[i] = slot_reader_running(s, *slots[i], &ev);
+        waits[i] = k[i] <= slots[i]->cap && slot_reader_running(s, *slots[i], &ev);
     }
     for (int pass = 0; pass < 2; ++pass) {
         for (size_t i = 0; i < slots.size(); ++i) {
             if (bool(waits[i]) != (pass == 1)) continue;
-            hipStream_t st = waits[i] ? s->side[n_free] : s->side[s->next_side++ % n_free];
+            hipStream_t st = waits[i] ? s->side[pm_store::kWaits]
+                                      : s->side[1 + s->next_side++ % n_free];
             const pm_status r = topup_slot(s, *slots[i], k[i], st);
             if (r) return r;
         }
@@ -871,7 +987,7 @@ extern "C" pm_status pm_store_topup(pm_store* s, int layer, int expert, int k, v
     if (st) return st;
     st = check_k(k);
     if (st) return st;
-    return topup_slot(s, s->slots[i], k, side ? (hipStream_t)side : s->side[0]);
+    return topup_slot(s, s->slots[i], k, side ? (hipStream_t)side : s->side[1]);
 }
 
 extern "C" pm_status pm_store_truncate(pm_store* s, int layer, int expert, int keep) {
@@ -881,25 +997,27 @@ extern "C" pm_status pm_store_truncate(pm_store* s, int layer, int expert, int k
     if (keep < 0 || keep > kBits) return failf(PM_ERR_PREFIX, "keep %d outside 0..8", keep);
     Slot& sl = s->slots[i];
     sl.resident = std::min(sl.resident, keep);
-    // the plane chunks past `keep` (and at keep 0 the levels) are released,
-    // in stream order after the slot's last reader
+    // the plane chunks past `keep` (and at keep 0 the levels) are released
+    // once the slot's last reader and copies have ended; the kept prefix
+    // moves to a buffer of its own size on the memory stream
     if (keep >= sl.cap && (keep > 0 || !sl.levels)) return PM_OK;
-    hipStream_t side = s->side[0];
+    st = reclaim(s);
+    if (st) return st;
+    hipStream_t mem = s->side[pm_store::kMem];
     st = slot_event(s, sl);
     if (st) return st;
-    st = order_after_readers(s, sl, side);
-    if (st) return st;
-    st = resize_planes(s, sl, std::min(sl.cap, keep), sl.resident, side);
+    st = resize_planes(s, sl, std::min(sl.cap, keep), sl.resident, mem);
     if (st) return st;
     if (keep == 0 && sl.levels) {
-        st = dev_free(s, sl.levels, side);
+        if (!s->host_fake && sl.pending) HIP_TRY(hipStreamWaitEvent(mem, sl.ready, 0));
+        st = retire(s, sl.levels, mem, sl.read_seq);
         if (st) return st;
         sl.levels = nullptr;
         sl.levels_ready = false;
         s->used -= s->level_bytes;
     }
     if (!s->host_fake) {
-        HIP_TRY(hipEventRecord(sl.ready, side));
+        HIP_TRY(hipEventRecord(sl.ready, mem));
         sl.pending = true;
     }
     return PM_OK;
