@@ -30,6 +30,7 @@ PM_AUTO_TOPUP = 1
 PM_BATCH_MFMA = 2
 PM_READ_ONCE = 4
 PM_DETERMINISTIC = 8
+PM_GEMV_NOALLOC_MAX_PARTIALS = 524288
 
 _STATUS = {0: "PM_OK", -1: "PM_ERR_ARG", -2: "PM_ERR_SHAPE", -3: "PM_ERR_PREFIX",
            -4: "PM_ERR_NOT_RESIDENT", -5: "PM_ERR_OOM", -6: "PM_ERR_HIP", -7: "PM_ERR_STATE"}
@@ -72,6 +73,7 @@ SIGNATURES = {
     "pm_encode_matrix_device": (_I, [_MS, _P, _P, _P, _P, _Z, _P, _P]),
     "pm_kmeans_codebook_device": (_I, [_MS, _P, _I, _P, _P, _P, _P, _P]),
     "pm_expert_gemv": (_I, [_MS, _I, _P, _Z, _P, _P, _P, _P]),
+    "pm_expert_gemv_noalloc": (_I, [_MS, _I, _P, _Z, _P, _P, _P, _P]),
     "pm_route_topk": (_I, [_I, _I, _I, _P, _P, _P]),
     "pm_allocate_bits": (_I, [_I, _I, _P, _P, _I, _P, _I, _P]),
     "pm_store_create": (_I, [_ES, _I, _I, _Z, _U32, _P]),
@@ -222,6 +224,13 @@ def pm_expert_gemv(s, k, d_planes, plane_stride_words, d_levels, d_x, d_y, strea
     return _check(lib().pm_expert_gemv(s, k, _dptr(d_planes), plane_stride_words,
                                        _dptr(d_levels), _dptr(d_x), _dptr(d_y),
                                        _stream(stream)))
+
+
+def pm_expert_gemv_noalloc(s, k, d_planes, plane_stride_words, d_levels, d_x, d_y,
+                           stream=None):
+    return _check(lib().pm_expert_gemv_noalloc(s, k, _dptr(d_planes), plane_stride_words,
+                                               _dptr(d_levels), _dptr(d_x), _dptr(d_y),
+                                               _stream(stream)))
 
 
 def pm_debug_unpack_prefix(s, k, d_planes, plane_stride_words, d_out, stream=None):

@@ -287,20 +287,99 @@ static bool lut_offsets_fit(pm_matrix_shape s, int k, size_t pstride) {
     return planes < lim && tables < lim;
 }
 
+// partials: S * rows floats for the slice partials when the columns span
+// S > 1 slices; null takes the calling stream's own (growing) buffer.
 pm_status gemv_lut(pm_matrix_shape s, int k, const uint32_t* d_planes, size_t pstride,
-                   const float* d_levels, const float* d_x, float* d_y, hipStream_t st);
+                   const float* d_levels, const float* d_x, float* d_y, hipStream_t st,
+                   float* partials);
+
+static pm_status check_gemv_call(pm_matrix_shape s, int k, const uint32_t* d_planes,
+                                 size_t pstride, const float* d_levels, const float* d_x,
+                                 float* d_y) {
+    pm_status st = check_matrix_call(s, k, d_planes, pstride, d_levels, d_y);
+    if (st) return st;
+    if (s.rows == 0 || s.cols == 0) return PM_OK;
+    if (!d_x) return failf(PM_ERR_ARG, "null x");
+    if (reinterpret_cast<uintptr_t>(d_x) % 16) return failf(PM_ERR_ARG, "x not 16-byte aligned");
+    return PM_OK;
+}
+
+static bool gemv_takes_lut(pm_matrix_shape s, int k, size_t pstride) {
+    return k <= kGemvLutMaxK && s.cols > 0 && s.cols % kSliceCols == 0 && s.group == kLutGroup &&
+           s.rows % kLutRows == 0 && lut_offsets_fit(s, k, pstride);
+}
 
 extern "C" pm_status pm_expert_gemv(pm_matrix_shape s, int k, const uint32_t* d_planes,
                                     size_t pstride, const float* d_levels, const float* d_x,
                                     float* d_y, void* stream) {
-    pm_status st = check_matrix_call(s, k, d_planes, pstride, d_levels, d_y);
+    pm_status st = check_gemv_call(s, k, d_planes, pstride, d_levels, d_x, d_y);
     if (st) return st;
     if (s.rows == 0) return PM_OK;
-    if (s.cols > 0 && !d_x) return failf(PM_ERR_ARG, "null x");
-    if (reinterpret_cast<uintptr_t>(d_x) % 16) return failf(PM_ERR_ARG, "x not 16-byte aligned");
-    if (k <= kGemvLutMaxK && s.cols > 0 && s.cols % kSliceCols == 0 && s.group == kLutGroup &&
-        s.rows % kLutRows == 0 && lut_offsets_fit(s, k, pstride))
-        return gemv_lut(s, k, d_planes, pstride, d_levels, d_x, d_y, (hipStream_t)stream);
+    if (gemv_takes_lut(s, k, pstride))
+        return gemv_lut(s, k, d_planes, pstride, d_levels, d_x, d_y, (hipStream_t)stream,
+                        nullptr);
+    HIP_TRY(launch_gemv(s.rows, s.cols, s.group, k, d_planes, pstride, d_levels, d_x, d_y,
+                        (hipStream_t)stream));
+    return PM_OK;
+}
+
+// ---- pm_expert_gemv without allocation: the slice partials live in a fixed
+// array of device memory, one per device (each device loaded the library's
+// code object holds its own copy, for the life of the process).
+namespace {
+constexpr size_t kScratchFloats = PM_GEMV_NOALLOC_MAX_PARTIALS;
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kScratchDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+// The device address of the current device's array, looked up once per
+// device with that device current.  The host-side name `scratch` is not a
+// device address and is never passed to a kernel or a copy.
+static pm_status scratch_address(float** out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kScratchDevices)
+        return failf(PM_ERR_STATE, "device %d beyond the %d with a scratch address", dev,
+                     kScratchDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return failf(PM_ERR_HIP, "scratch address on device %d: %s", dev,
+                         hipGetErrorString(e));
+        }
+        g_scratch[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch[dev];
+    return PM_OK;
+}
+
+extern "C" pm_status pm_expert_gemv_noalloc(pm_matrix_shape s, int k, const uint32_t* d_planes,
+                                            size_t pstride, const float* d_levels,
+                                            const float* d_x, float* d_y, void* stream) {
+    pm_status st = check_gemv_call(s, k, d_planes, pstride, d_levels, d_x, d_y);
+    if (st) return st;
+    const size_t slices = (size_t(s.cols) + kSliceCols - 1) / kSliceCols;
+    if (size_t(s.rows) * slices > kScratchFloats)
+        return failf(PM_ERR_SHAPE,
+                     "rows x column slices = %d x %zu exceeds the %zu partials of the fixed "
+                     "scratch (use pm_expert_gemv)",
+                     s.rows, slices, kScratchFloats);
+    if (s.rows == 0) return PM_OK;
+    if (gemv_takes_lut(s, k, pstride)) {
+        float* partials = nullptr;
+        if (s.cols / kSliceCols > 1) {
+            st = scratch_address(&partials);
+            if (st) return st;
+        }
+        return gemv_lut(s, k, d_planes, pstride, d_levels, d_x, d_y, (hipStream_t)stream,
+                        partials);
+    }
     HIP_TRY(launch_gemv(s.rows, s.cols, s.group, k, d_planes, pstride, d_levels, d_x, d_y,
                         (hipStream_t)stream));
     return PM_OK;
@@ -1219,7 +1298,8 @@ static pm_status gemv_partials(hipStream_t st, size_t n, float** out) {
 }
 
 pm_status gemv_lut(pm_matrix_shape s, int k, const uint32_t* d_planes, size_t pstride,
-                   const float* d_levels, const float* d_x, float* d_y, hipStream_t st) {
+                   const float* d_levels, const float* d_x, float* d_y, hipStream_t st,
+                   float* partials) {
     const int S = s.cols / kSliceCols;
     const size_t nb = size_t(s.rows) * (s.cols / s.group);
     KLaunch L{};
@@ -1239,6 +1319,8 @@ pm_status gemv_lut(pm_matrix_shape s, int k, const uint32_t* d_planes, size_t ps
     jb.src = 0;
     if (S == 1) {
         jb.out = d_y;
+    } else if (partials) {
+        jb.out = partials;
     } else {
         pm_status r = gemv_partials(st, size_t(S) * s.rows, &jb.out);
         if (r) return r;

@@ -149,6 +149,23 @@ pm_status pm_expert_gemv(pm_matrix_shape s, int k, const uint32_t* d_planes,
                          size_t plane_stride_words, const float* d_levels,
                          const float* d_x, float* d_y, void* stream);
 
+/* pm_expert_gemv for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and the same result, bit for bit, with the slice partials
+ * (rows x cols/1024 floats when the columns span several 1024-column slices)
+ * in a fixed array of PM_GEMV_NOALLOC_MAX_PARTIALS floats (2 MiB) that each
+ * device holds from the first call until the process ends.  No allocation
+ * and no memset: every partial is written before it is read.  Calls that
+ * overlap on one device (concurrent streams or threads) share that array and
+ * race; serialise them.  The first call on a device looks the array's
+ * address up (not allocating).  Errors: those of pm_expert_gemv, and
+ * PM_ERR_SHAPE when rows x ceil(cols/1024) > PM_GEMV_NOALLOC_MAX_PARTIALS,
+ * whichever kernel the shape takes. */
+#define PM_GEMV_NOALLOC_MAX_PARTIALS 524288
+pm_status pm_expert_gemv_noalloc(pm_matrix_shape s, int k, const uint32_t* d_planes,
+                                 size_t plane_stride_words, const float* d_levels,
+                                 const float* d_x, float* d_y, void* stream);
+
 /* ---------------------------------------------------------------- routing
  * [T c4]: a router picks a few experts per token with weights summing to 1.
  * logits fp32 [n_tokens][n_experts] -> ids int32 [n_tokens][top_k] (largest

@@ -333,3 +333,22 @@ def test_kmeans_validation_before_any_hip_call():
         pm.pm_kmeans_codebook_device(pm.mshape(2, 100, 50), 1, 5, 1, 1, 1)
     assert ei.value.status == pm.PM_ERR_SHAPE
     pm.pm_kmeans_codebook_device(pm.mshape(0, 128, 128), None, 5, None, None, None)
+
+
+def test_noalloc_gemv_validation_before_any_hip_call():
+    # the same checks as pm_expert_gemv, then the fixed scratch's limit on
+    # rows x column slices, whichever kernel the shape would take
+    lim = pm.PM_GEMV_NOALLOC_MAX_PARTIALS
+    with pytest.raises(pm.PMError) as ei:
+        pm.pm_expert_gemv_noalloc(pm.mshape(4, 64, 32), 9, 16, 8, 16, 16, 16)
+    assert ei.value.status == pm.PM_ERR_PREFIX
+    with pytest.raises(pm.PMError) as ei:
+        pm.pm_expert_gemv_noalloc(pm.mshape(4, 64, 32), 2, 16, 8, 16, 8, 16)
+    assert ei.value.status == pm.PM_ERR_ARG                 # x not 16-byte aligned
+    for rows, cols, k in ((lim // 2 + 8, 2048, 3), (lim + 8, 1024, 7), (lim // 3 + 1, 2080, 2)):
+        sh = pm.mshape(rows, cols, 32 if cols % 128 else 128)
+        with pytest.raises(pm.PMError) as ei:
+            pm.pm_expert_gemv_noalloc(sh, k, 16, rows * cols // 32, 16, 16, 16)
+        assert ei.value.status == pm.PM_ERR_SHAPE, (rows, cols)
+        assert b"scratch" in pm.lib().pm_last_error()
+    pm.pm_expert_gemv_noalloc(pm.mshape(0, 64, 32), 3, None, 0, None, None, None)
