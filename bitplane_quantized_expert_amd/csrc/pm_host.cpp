@@ -550,7 +550,12 @@ struct Slot {
     const uint32_t* h_planes = nullptr;
     const float* h_levels = nullptr;
     hipEvent_t ready = nullptr;    // recorded after the slot's last top-up copy
-    bool pending = false;          // a top-up is in flight on the side stream
+    // `ready` marks the slot's last copy (top-up or move): `copied` once it
+    // has been recorded at all; `pending` until a forward's compute stream
+    // has waited for it.  Another copy from or into the slot waits for it
+    // whatever `pending` says: a forward's wait orders only its own stream.
+    bool copied = false;
+    bool pending = false;
     uint64_t read_seq = 0;         // last forward that read the slot (0: none)
 };
 
@@ -732,7 +737,7 @@ static pm_status order_after_readers(pm_store* s, Slot& sl, hipStream_t st) {
     if (s->host_fake) return PM_OK;
     hipEvent_t reader = nullptr;
     if (slot_reader_running(s, sl, &reader)) HIP_TRY(hipStreamWaitEvent(st, reader, 0));
-    if (sl.pending) HIP_TRY(hipStreamWaitEvent(st, sl.ready, 0));
+    if (sl.copied) HIP_TRY(hipStreamWaitEvent(st, sl.ready, 0));
     return PM_OK;
 }
 
@@ -751,7 +756,7 @@ static pm_status resize_planes(pm_store* s, Slot& sl, int cap, int keep, hipStre
     } else {
         r = publish_allocs(s, st);
         if (r) return r;
-        if (sl.pending) HIP_TRY(hipStreamWaitEvent(st, sl.ready, 0));
+        if (sl.copied) HIP_TRY(hipStreamWaitEvent(st, sl.ready, 0));
         if (keep > 0)
             HIP_TRY(hipMemcpyAsync(nb, sl.planes, size_t(keep) * pb, hipMemcpyDeviceToDevice, st));
     }
@@ -1018,6 +1023,7 @@ static pm_status topup_slot(pm_store* s, Slot& sl, int k, hipStream_t side) {
         HIP_TRY(hipMemcpyAsync(sl.planes + size_t(first) * pw, sl.h_planes + size_t(first) * pw,
                                size_t(k - first) * s->plane_bytes, hipMemcpyHostToDevice, side));
         HIP_TRY(hipEventRecord(sl.ready, side));
+        sl.copied = true;
         sl.pending = true;
     }
     if (!sl.levels_ready) s->total_bytes += s->level_bytes;
@@ -1088,7 +1094,7 @@ extern "C" pm_status pm_store_truncate(pm_store* s, int layer, int expert, int k
     st = resize_planes(s, sl, std::min(sl.cap, keep), sl.resident, mem);
     if (st) return st;
     if (keep == 0 && sl.levels) {
-        if (!s->host_fake && sl.pending) HIP_TRY(hipStreamWaitEvent(mem, sl.ready, 0));
+        if (!s->host_fake && sl.copied) HIP_TRY(hipStreamWaitEvent(mem, sl.ready, 0));
         st = retire(s, sl.levels, mem, sl.read_seq);
         if (st) return st;
         sl.levels = nullptr;
@@ -1097,6 +1103,7 @@ extern "C" pm_status pm_store_truncate(pm_store* s, int layer, int expert, int k
     }
     if (!s->host_fake) {
         HIP_TRY(hipEventRecord(sl.ready, mem));
+        sl.copied = true;
         sl.pending = true;
     }
     return PM_OK;

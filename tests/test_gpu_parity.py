@@ -382,6 +382,49 @@ def test_forward_layer_full_size(layer_store):
     assert np.array_equal(host(y2).view(np.uint32), host(y).view(np.uint32))
 
 
+def test_batch_of_four_matches_single_tokens(layer_store):
+    """4 tokens x 10 uses in one call (two gate/up launches of LUT jobs)
+    against each token alone: every row is computed by one wave in one step
+    whatever the launch, and the combine sums the uses in slot order, so a
+    token whose experts no other token of the batch reads gets the same bits.
+    Then eight single-token calls back to back, with no host sync between,
+    repeat those bits."""
+    report("4-token batch vs single tokens, then 8 calls back to back")
+    wl, st, ensure = layer_store
+    routes = [oc.route_and_bits(1, 0, step=10 + t) for t in range(4)]
+    ids = np.stack([r[0] for r in routes]).astype(np.int32)
+    w = np.stack([r[1] for r in routes]).astype(np.float32)
+    k = np.stack([r[2] for r in routes]).astype(np.uint8)
+    ensure(np.unique(ids))
+    x = np.stack([synth.activation(wl.seed, 1, 0, t, wl.hidden, step=10 + t) for t in range(4)])
+    xd = dev(x)
+    yb = torch.empty((4, wl.hidden), dtype=torch.float32, device="cuda")
+    pm.pm_moe_token_forward(st, 0, ids, w, k, xd, yb)
+    batch = host(yb)
+    counts = {int(i): int((ids == i).sum()) for i in np.unique(ids)}
+    exact = 0
+    alones = []
+    for t in range(4):
+        y1 = torch.empty((1, wl.hidden), dtype=torch.float32, device="cuda")
+        pm.pm_moe_token_forward(st, 0, ids[t:t + 1], w[t:t + 1], k[t:t + 1], xd[t:t + 1], y1)
+        alone = host(y1)[0]
+        alones.append(alone)
+        if all(counts[int(i)] == 1 for i in ids[t]):
+            assert np.array_equal(alone.view(np.uint32), batch[t].view(np.uint32)), t
+            exact += 1
+        rows = oc.sample_rows(wl.hidden, 16, 30 + t)
+        want, S = oc.token_layer(1, 0, ids[t], w[t], k[t], x[t], rows)
+        assert_close(alone[rows], want, S, f"token {t} alone")
+        assert_close(batch[t][rows], want, S, f"token {t} in the batch")
+    assert exact >= 2
+    ys = [torch.full((1, wl.hidden), 7.0, dtype=torch.float32, device="cuda") for _ in range(8)]
+    for i in range(8):
+        t = i % 4
+        pm.pm_moe_token_forward(st, 0, ids[t:t + 1], w[t:t + 1], k[t:t + 1], xd[t:t + 1], ys[i])
+    for i in range(8):
+        assert np.array_equal(host(ys[i])[0].view(np.uint32), alones[i % 4].view(np.uint32)), i
+
+
 @pytest.mark.parametrize("kfix", [4, 8, None])
 def test_forward_uniform_precisions_and_materialize(layer_store, kfix):
     report(f"512-expert layer at k={kfix or 'mixed'}: direct and materialize-fp16")
