@@ -321,20 +321,27 @@ __device__ inline float step_compute(const StepIn<K>& in, const LaneLut& L) {
 constexpr int kLutThreads = PM_LUT_THREADS;
 constexpr int kLutWaves = kLutThreads / kWave;
 constexpr int kLutBytes = 128 * 1024;
-constexpr int kBuildWaves = 2;              // 128 chunks, one per builder thread
+#ifndef PM_BUILD_WAVES
+#define PM_BUILD_WAVES 2
+#endif
+// 128 chunks: one per builder thread (2 waves) or half of one (4 waves)
+constexpr int kBuildWaves = PM_BUILD_WAVES;
+constexpr int kBuildParts = kBuildWaves / 2;
+static_assert(kBuildWaves == 2 || kBuildWaves == 4, "two or four builder waves");
 static_assert(kLutThreads % 256 == 0 && kLutThreads <= 1024, "whole waves on every SIMD");
 
 __device__ inline int build_chunk(int t) {
     return 16 * ((t & 31) >> 2) + 4 * ((t >> 5) & 3) + (t & 3);
 }
 
-__device__ inline void build_table(lds_float* tab, int c, const float (&v)[8]) {
+__device__ inline void build_table(lds_float* tab, int c, const float (&v)[8], int part) {
     float sub[32];
     sub[0] = 0.f;
 #pragma unroll
     for (int i = 1; i < 32; ++i) sub[i] = sub[i & (i - 1)] + v[__builtin_ctz(i)];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q0 = 0; q0 < 8 / kBuildParts; ++q0) {
+        const int q = kBuildParts == 1 ? q0 : part * (8 / kBuildParts) + q0;
         float base = 0.f;
         if (q & 1) base += v[5];
         if (q & 2) base += v[6];
@@ -347,13 +354,28 @@ __device__ inline void build_table(lds_float* tab, int c, const float (&v)[8]) {
 // The 8 activation values of chunk c: x of token `src`, or h of use `src`
 // formed from its gate/up partials (slices summed in order; slices past a
 // matrix's count read slice 0 again and add 0).
+#ifndef PM_X_FIRST
+#define PM_X_FIRST 1
+#endif
+// Count a builder wave's source loads as issued (on `issued`, in LDS): the
+// other waves hold their first plane loads back until every builder wave's
+// are in the queue, so that the table does not wait behind them.
+__device__ inline void loads_issued(uint32_t* issued) {
+    if constexpr (PM_X_FIRST) {
+        __builtin_amdgcn_sched_barrier(0);
+        __hip_atomic_fetch_add(issued, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <bool DOWN>
 __device__ inline void chunk_source(const KLaunch& L, int src, int gsl, int slice, int c,
-                                    float (&v)[8]) {
+                                    float (&v)[8], uint32_t* issued) {
     const int col = kSliceCols * slice + 8 * c;
     if constexpr (!DOWN) {
         const float* x = L.x + size_t(src) * L.x_stride + col;
         const f32x4 a = *(g_f32x4*)x, b = *(g_f32x4*)(x + 4);
+        loads_issued(issued);
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
         v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     } else {
@@ -371,6 +393,7 @@ __device__ inline void chunk_source(const KLaunch& L, int src, int gsl, int slic
                     gv[q][h] = *(g_f32x4*)(pg + size_t(q < ngs ? q : 0) * inter + 4 * h);
                     uv[q][h] = *(g_f32x4*)(pu + size_t(q < nus ? q : 0) * inter + 4 * h);
                 }
+            loads_issued(issued);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 gs[h] = gv[0][h];
@@ -382,6 +405,7 @@ __device__ inline void chunk_source(const KLaunch& L, int src, int gsl, int slic
                 }
             }
         } else {
+            loads_issued(issued);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 gs[h] = *(g_f32x4*)(pg + 4 * h);
@@ -399,9 +423,13 @@ __device__ inline void chunk_source(const KLaunch& L, int src, int gsl, int slic
 }
 
 // Steps in flight per wave (the ring): deeper where a step is short.
+#ifndef PM_RING
+#define PM_RING 4, 3, 2, 2, 2
+#endif
+constexpr int kRing[5] = {PM_RING};
 template <int K>
 constexpr int lut_ring() {
-    return K == 1 ? 4 : (K == 2 ? 3 : 2);
+    return kRing[K - 1];
 }
 
 // The rows [g0, g1) of a launch (row r of job j is j * rows + r; both ends
@@ -477,15 +505,20 @@ __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L,
     // must not hold up the others)
     const bool builder = c.wave < kBuildWaves;
     if (builder) {
-        const int ch = build_chunk(int(threadIdx.x));
+        const int ch = build_chunk(int(threadIdx.x) & 127);
         float v[8];
-        chunk_source<DOWN>(L, c.src, c.gsl, c.slice, ch, v);
-        build_table(tab, ch, v);
+        chunk_source<DOWN>(L, c.src, c.gsl, c.slice, ch, v, ready + 2);
+        build_table(tab, ch, v, int(threadIdx.x) >> 7);
         // LDS operations of one wave execute in order: once another wave
         // sees this count, the table writes before it are done.  (A release
         // here would also wait for global memory, which this does not need.)
         __asm__ volatile("" ::: "memory");
         __hip_atomic_fetch_add(ready, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    if (PM_X_FIRST && !builder) {
+        while (__hip_atomic_load(ready + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) <
+               uint32_t(kBuildWaves * kWave))
+            __builtin_amdgcn_s_sleep(1);
     }
 #pragma unroll
     for (int d = 0; d < D; ++d) fill(d);
@@ -539,6 +572,7 @@ lut_kernel(const KLaunch L) {
     if (threadIdx.x == 0) {
         *ready = 0u;
         *next = 0u;
+        ready[2] = 0u;
     }
     __syncthreads();
     const int q = blockIdx.x, slice = blockIdx.y;
