@@ -33,8 +33,8 @@ KERNEL_SOURCES = ("bitplane_quantized_expert_amd/csrc/pm_kernels.hip",
 # passes of this benchmark, each scaled by the same counter on the 1 GiB
 # negation kernel (see --summarize-counters); reported only while the kernel
 # sources still have this digest.
-TRAFFIC = {"sources_sha256": "c265bc57880bc69cb978bbca32253ba4cf9dbd0260148bce360a7e419bb43678",
-           "bytes_per_launch": 46590559}
+TRAFFIC = {"sources_sha256": "3f98b309d5e0ef69ef7eaf11edd03ff6e39ea9eab8484c7a9ead1b4da5aed4e0",
+           "bytes_per_launch": 44831257}
 
 
 def log(msg):
@@ -186,21 +186,51 @@ def copy_ceiling(torch, stream, nbytes=1 << 30, reps=5):
             "GBs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
-def cpu_baseline(wl, plans, budget_s):
+def gemv_share(wl, rows):
+    """Expert GEMVs that one pass over an expert's three matrices cut to
+    their first `rows` rows amounts to: each matrix counts rows / its rows
+    (gate and up have `inter` rows, down has `hidden`), over three matrices."""
+    import synth
+    return sum(min(rows, synth.matrix_shape(wl, m)[0]) / synth.matrix_shape(wl, m)[0]
+               for m in range(3)) / 3.0
+
+
+def cpu_info():
+    """CPU model (from /proc/cpuinfo) and the cores this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return model, usable
+
+
+def cpu_baseline(wl, plans, budget_s, max_threads=16):
     """The oracle, untouched, on a bounded sample: the first token's 10
     experts, every matrix restricted to its first 256 rows, repeated until
-    about budget_s seconds of oracle time.  BLAS is held to one thread."""
+    about budget_s / 2 seconds of oracle time, once on one thread and once
+    with the matrices of a pass spread over the usable cores (at most
+    max_threads worker threads, BLAS held to one thread in each)."""
+    import concurrent.futures as cf
     import oracle
     import synth
     try:
         from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
     except Exception:
-        limiter = None
+        threadpool_limits = None
     ids, w, kk = plans[0]
     rows = 256
     mats = []
     nbytes = 0
+    gemv_equiv = 0.0            # expert GEMVs per pass: each matrix's share of its rows
     for j in range(len(ids)):
         for m in range(3):
             R, C = synth.matrix_shape(wl, m)
@@ -209,22 +239,47 @@ def cpu_baseline(wl, plans, budget_s):
             x = synth.activation(wl.seed, wl.cfg, 0, 0, C)
             mats.append((oracle.pack_planes(cd), oracle.tree_levels(lv), int(kk[j][m]), x))
             nbytes += matrix_bytes(rows, C, wl.group, int(kk[j][m]))
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        for pl, lvl, k, x in mats:
-            oracle.gemv(pl, lvl, k, wl.group, x)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
-    gbs = nbytes * reps / el / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        gemv_equiv += 3 * gemv_share(wl, rows)
+
+    def one(mat):
+        pl, lvl, k, x = mat
+        oracle.gemv(pl, lvl, k, wl.group, x)
+
+    def run(threads, seconds):
+        limiter = threadpool_limits(limits=1) if threadpool_limits else None
+        reps = 0
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            while True:
+                if threads == 1:
+                    for mat in mats:
+                        one(mat)
+                else:
+                    list(ex.map(one, mats))
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= seconds:
+                    break
+        if limiter is not None and hasattr(limiter, "unregister"):
+            limiter.unregister()
+        return reps, el
+
+    model, usable = cpu_info()
+    threads = max(1, min(usable, max_threads))
+    reps1, el1 = run(1, budget_s / 2)
+    repsn, eln = run(threads, budget_s / 2)
+    one_thread = {"value": round(nbytes * reps1 / el1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                  "expert_gemvs_per_s": round(gemv_equiv * reps1 / el1, 3),
+                  "passes": reps1, "seconds": round(el1, 1)}
+    return {"value": round(nbytes * repsn / eln / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
             "sample": (f"{len(mats)} matrices (10 experts x gate/up/down of step 0) x first "
-                       f"{rows} rows, {reps} passes, {el:.1f} s; numpy fp64, 1 BLAS thread"),
-            "expert_gemvs_per_s": round(len(mats) * reps / el * (rows / 1024) / 1.0, 3)}
+                       f"{rows} rows; numpy fp64, BLAS one thread per worker; {repsn} passes in "
+                       f"{eln:.1f} s on {threads} threads, then {reps1} passes in {el1:.1f} s on "
+                       f"one thread"),
+            "expert_gemvs_per_s": round(gemv_equiv * repsn / eln, 3),
+            "single_thread": one_thread,
+            "cpu_model": model, "usable_cores": usable}
 
 
 def route_steps(pm, synth, wl, layer, steps, token=0, kfix=None, n_exp=None):
@@ -654,7 +709,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--experts", type=int, default=512)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--log-inputs", metavar="FILE",
                     help="write the ids, w and k of every step of the layer benchmark (JSON lines)")
@@ -780,6 +835,52 @@ def main():
         torch.cuda.synchronize()
         return evs
 
+    # the distribution of single steps: an event at every step boundary
+    def boundary_pass(order):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i, s in enumerate(order):
+            run(s)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(len(order))]) * 1e3
+
+    def pct(us):
+        return {"mean": round(float(us.mean()), 2),
+                **{f"p{q}": round(float(np.percentile(us, q)), 2) for q in (10, 50, 90)}}
+
+    step_dist = pct(boundary_pass(list(steps)))
+    # one step alone (GPU idle before it, its own events), cold and warm:
+    # cold after 512 MiB of writes that evict the 256 MB Infinity Cache,
+    # warm right after the same step ran (its experts' planes cached)
+    n_cw = min(50, args.steps)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def alone(s, cold):
+        if cold:
+            flush.zero_()
+        else:
+            run(s)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run(s)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3
+
+    cold, warm = [], []
+    for s in list(steps)[:n_cw]:
+        cold.append(alone(s, True))
+        warm.append(alone(s, False))
+    del flush
+    cache_state = {"cold_us": pct(np.array(cold)), "warm_us": pct(np.array(warm)),
+                   "steps": n_cw,
+                   "how": "each of the first timed steps alone: cold after 512 MiB of writes, "
+                          "warm right after the same step"}
+    log(f"steps p10/p50/p90 {step_dist['p10']}/{step_dist['p50']}/{step_dist['p90']} us; "
+        f"warm p50 {cache_state['warm_us']['p50']} us, cold p50 {cache_state['cold_us']['p50']} us")
+
     gu_ms = np.array([a.elapsed_time(b) for a, b in event_pass(2)])
     evs = event_pass(4)
     dn_ms = np.array([b.elapsed_time(c) for _, b, c, _ in evs])
@@ -800,8 +901,11 @@ def main():
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "host_issue_us_per_step": round(issued / args.steps * 1e6, 2),
         "expert_gemvs_per_s": round(3 * wl.top_k * args.steps / el, 1),
+        "step_us": step_dist,
+        "cache_state": cache_state,
         "stage_us": {"gateup": round(gu_ms.mean() * 1e3, 2), "down": round(dn_ms.mean() * 1e3, 2),
                      "combine": round(cb_ms.mean() * 1e3, 2)},
+        "kernel_sum_us": round((gu_ms.mean() + dn_ms.mean() + cb_ms.mean()) * 1e3, 2),
         "roofline": {"bound": "hbm", "kernel": "gateup", "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),

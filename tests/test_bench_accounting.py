@@ -49,3 +49,11 @@ def test_mfma_flops_tiles_of_sixteen():
     assert useful == 3 * 2 * W * 20
     # gate: 20 uses -> 2 tiles; up: 17 + 3 -> 2 + 1; down: 2
     assert issued == 2 * W * 16 * (2 + 3 + 2)
+
+
+def test_cpu_sample_counts_each_matrix_by_its_own_rows():
+    # 256 rows of gate and up (1024 rows each) and of down (4096 rows): one
+    # expert's pass is (1/4 + 1/4 + 1/16) of three matrices' worth
+    wl = synth.WORKLOADS[1]
+    assert abs(3 * bench.gemv_share(wl, 256) - (0.25 + 0.25 + 0.0625)) < 1e-12
+    assert bench.gemv_share(wl, 4096) == 1.0
