@@ -8,8 +8,11 @@ not been built, loading fails loudly (there is no fallback).
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import sys
+import weakref
 
 import numpy as np
 
@@ -80,6 +83,7 @@ SIGNATURES = {
     "pm_store_destroy": (_I, [_P]),
     "pm_store_slot": (_I, [_P, _I, _I, _P, _P]),
     "pm_store_usage": (_I, [_P, _P, _P, _P]),
+    "pm_store_slot_info": (_I, [_P, _I, _I, _P, _P, _P]),
     "pm_store_set_resident": (_I, [_P, _I, _I, _I]),
     "pm_store_attach_host": (_I, [_P, _I, _I, _P, _P]),
     "pm_store_topup": (_I, [_P, _I, _I, _I, _P]),
@@ -280,27 +284,64 @@ def pm_allocate_bits(ids, w, err_profiles, budget):
     return k
 
 
+# ---------------------------------------------------------------- handles
+# Stores and caches still open when the interpreter exits are closed by an
+# exit handler, in reverse order of creation, while the HIP runtime and torch
+# are still whole.  A handle collected during interpreter shutdown is left to
+# the process exit instead: nothing calls into the library (or HIP) from a
+# finalizer then.
+_live = weakref.WeakValueDictionary()
+_live_next = [0]
+
+
+def _track(obj):
+    _live_next[0] += 1
+    _live[_live_next[0]] = obj
+
+
+@atexit.register
+def _close_live_handles():
+    for key in sorted(_live.keys(), reverse=True):
+        obj = _live.get(key)
+        if obj is not None:
+            try:
+                obj.close()
+            except Exception:
+                pass
+
+
+class _Handle:
+    _destroy = None
+
+    def close(self):
+        if self.handle:
+            getattr(lib(), self._destroy)(self.handle)
+            self.handle = None
+
+    def __del__(self, _finalizing=sys.is_finalizing):
+        # (bound at definition: module globals may already be gone here)
+        if _finalizing():
+            return
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 # ---------------------------------------------------------------- store
-class Store:
-    """Owner of a pm_store handle (pm_store_destroy on close)."""
+class Store(_Handle):
+    """Owner of a pm_store handle (pm_store_destroy on close).  Host sources
+    attached to it must stay alive until it is closed."""
+    _destroy = "pm_store_destroy"
 
     def __init__(self, e, n_layers, n_experts, capacity_bytes=0, flags=0):
+        self.handle = None
         h = ctypes.c_void_p()
         _check(lib().pm_store_create(e, n_layers, n_experts, capacity_bytes, flags,
                                      ctypes.byref(h)))
         self.handle = h.value
         self.shape = e
-
-    def close(self):
-        if self.handle:
-            lib().pm_store_destroy(self.handle)
-            self.handle = None
-
-    def __del__(self):
-        try:
-            self.close()
-        except Exception:
-            pass
+        _track(self)
 
 
 def pm_store_create(e, n_layers, n_experts, capacity_bytes=0, flags=0):
@@ -346,6 +387,14 @@ def pm_store_truncate(store, layer, expert, keep):
     return _check(lib().pm_store_truncate(store.handle, layer, expert, keep))
 
 
+def pm_store_slot_info(store, layer, expert):
+    """(planes address, levels address, plane chunks held) of a slot, as is."""
+    p, lv, n = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_int()
+    _check(lib().pm_store_slot_info(store.handle, layer, expert, ctypes.byref(p),
+                                    ctypes.byref(lv), ctypes.byref(n)))
+    return p.value or 0, lv.value or 0, n.value
+
+
 def pm_store_resident(store, layer, expert):
     r = ctypes.c_int()
     _check(lib().pm_store_resident(store.handle, layer, expert, ctypes.byref(r)))
@@ -376,24 +425,16 @@ PM_CACHE_OBJECTS = 1
 PM_CACHE_DOWNWARD = 2
 
 
-class Cache:
+class Cache(_Handle):
     """Owner of a pm_cache handle (pm_cache_destroy on close)."""
+    _destroy = "pm_cache_destroy"
 
     def __init__(self, n_experts, capacity_planes, policy=PM_CACHE_PREFIX):
+        self.handle = None
         h = ctypes.c_void_p()
         _check(lib().pm_cache_create(n_experts, capacity_planes, policy, ctypes.byref(h)))
         self.handle = h.value
-
-    def close(self):
-        if self.handle:
-            lib().pm_cache_destroy(self.handle)
-            self.handle = None
-
-    def __del__(self):
-        try:
-            self.close()
-        except Exception:
-            pass
+        _track(self)
 
 
 def pm_cache_create(n_experts, capacity_planes, policy=PM_CACHE_PREFIX):

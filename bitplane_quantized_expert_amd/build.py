@@ -81,6 +81,48 @@ def build(verbose=False, extra_flags=(), out_override=None):
     return outs
 
 
+# libpm with its host code under AddressSanitizer and UndefinedBehaviorSanitizer
+# (the device code is built as usual): for the host-only tests (the host-backed
+# store, the expert caches, routing, the allocator, argument validation), run
+# in a process that preloads the ASan runtime.  Every -fsanitize goes to the
+# host pass only.
+ASAN_LIB = os.path.join(PKG, "libpm_asan.so")
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def asan_runtime():
+    """The ASan runtime of the compiler that builds ASAN_LIB (None if absent)."""
+    import glob
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(hipcc())), "llvm", "lib",
+                                         "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    return hits[-1] if hits else None
+
+
+def build_sanitized(verbose=False):
+    import concurrent.futures as cf
+    srcs = TARGETS[0][1]
+    flags = [f for f in COMPILE_FLAGS if f != "-O3"] + ["-O1", "-g"] + SANITIZE
+    objs, jobs = [], []
+    for s in srcs:
+        obj = os.path.join(PKG, "_build", os.path.basename(s) + ".asan.o")
+        os.makedirs(os.path.dirname(obj), exist_ok=True)
+        cmd = [hipcc()] + flags + ["-I", os.path.join(ROOT, "include"), "-c"]
+        cmd += (["-x", "hip", s] if s.endswith(".cpp") else [s])
+        cmd += ["-o", obj]
+        objs.append(obj)
+        jobs.append((cmd, os.path.basename(s)))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        list(ex.map(lambda j: _run(j[0], j[1], verbose), jobs))
+    tmp = ASAN_LIB + ".tmp"
+    _run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}"] + SANITIZE[:4] +
+         ["-shared-libsan"] + objs + ["-o", tmp], os.path.basename(ASAN_LIB), verbose)
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
     for p in build(verbose=True):
         print("built", p)
+    print("built", build_sanitized(verbose=True))

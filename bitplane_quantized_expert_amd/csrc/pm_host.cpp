@@ -559,12 +559,22 @@ struct Slot {
     uint64_t read_seq = 0;         // last forward that read the slot (0: none)
 };
 
-// A released slot buffer that may still be in use: freed once the copy
-// event has completed and the forward `reader` has ended.
-struct Retired {
-    void* p;
-    hipEvent_t copied;             // after the last copy from or into the buffer
+// A range of slot memory given back while a queued forward or copy may still
+// use it: it returns to its arena once the copy event has completed and the
+// forward `reader` has ended.
+struct Released {
+    char* p;
+    size_t len;
+    hipEvent_t ev;                 // after the last copy from or into it (null: none)
     uint64_t reader;               // the last forward that read it (0: none)
+};
+
+// One block of slot memory (hipMalloc, or calloc for a host-backed store),
+// carved into ranges first fit; its free ranges by offset, coalesced.
+struct Arena {
+    char* base;
+    size_t size;
+    std::map<size_t, size_t> free;
 };
 
 struct Workspace {
@@ -588,8 +598,8 @@ struct pm_store {
     bool host_fake;
     size_t plane_bytes, level_bytes;   // per plane chunk, per slot levels
     std::vector<Slot> slots;
-    // The store's own streams.  side[0] is the memory stream: every
-    // allocation and release of slot memory, and the moves of truncation.
+    // The store's own streams.  side[0] is the memory stream: the waits that
+    // a truncation's release of memory follows.
     // Top-up copies that need no wait take side[1] and side[2] in turn (more
     // than one copy in flight keeps the link busier); copies that wait for an
     // earlier forward still reading their slot take side[3], so that a wait
@@ -598,14 +608,13 @@ struct pm_store {
     static constexpr int kMem = 0, kWaits = 3;
     hipStream_t side[kSides] = {};
     uint32_t next_side = 0;
-    // Slot memory: a pool of the store's own, allocated from and released to
-    // on the memory stream only.  Buffers a queued forward or copy may still
-    // use wait in `retired` until a later store call finds them idle.
-    hipMemPool_t pool = nullptr;
-    std::vector<Retired> retired;
+    // Slot memory: arenas of the store's own.  Ranges a queued forward or
+    // copy may still use wait in `released` until a later store call finds
+    // them idle.
+    std::vector<Arena> arenas;
+    size_t arena_bytes = 0;            // size of a new arena (a larger request gets its own)
+    std::vector<Released> released;
     std::vector<hipEvent_t> spare_events;
-    hipEvent_t alloc_ev = nullptr;     // marks the memory stream after its last allocation
-    bool alloc_unpublished = false;    // an allocation no copy stream has waited for yet
     // Ends of recent forwards: done[n % kDone] marks the end of forward n
     // (n >= 1).  A forward records it only when the store has host sources
     // (a top-up may need it); otherwise it is recorded later on the last
@@ -638,15 +647,46 @@ static pm_status slot_of(const pm_store* s, int layer, int expert, size_t* idx) 
     return PM_OK;
 }
 
-// ---- slot memory.  Every allocation and every release of a device store's
-// slot memory is issued on the memory stream, from and to the store's own
-// pool, so the pool reuses memory in that one stream's order.  A buffer that
-// a queued forward or copy may still use is not released at once: it is
-// retired with an event after its last copy and the forward that last read
-// it, and a later store call releases it once both have completed.  The pool
-// thus only ever takes back idle memory.
+// ---- slot memory.  A store carves slot memory out of arenas of its own
+// (large hipMalloc blocks, never returned before the store is destroyed), so
+// growing, shrinking and releasing a slot are host bookkeeping: no device
+// allocation or free in the path of a top-up or a truncation.  A slot's
+// planes are one range of `cap` plane chunks; a truncation gives the tail
+// back in place, and a top-up extends the range in place when the range after
+// it is free, else moves the resident prefix to a new range.  A range given
+// back while a queued forward may read it, or a copy may still write or read
+// it, waits with an event until a later store call finds it idle.
 static bool slot_reader_running(pm_store* s, const Slot& sl, hipEvent_t* ev);
 static hipEvent_t forward_end(pm_store* s, uint64_t n);
+
+constexpr size_t kRangeAlign = 256;
+static size_t range_len(size_t bytes) { return (bytes + kRangeAlign - 1) & ~(kRangeAlign - 1); }
+
+static Arena* arena_of(pm_store* s, const char* p) {
+    for (Arena& a : s->arenas)
+        if (p >= a.base && p < a.base + a.size) return &a;
+    return nullptr;
+}
+
+// Give [p, p + len) back to its arena now, merged with free neighbours.
+static void arena_put(pm_store* s, char* p, size_t len) {
+    Arena* a = arena_of(s, p);
+    if (!a || len == 0) return;
+    size_t off = size_t(p - a->base);
+    auto next = a->free.lower_bound(off);
+    if (next != a->free.end() && off + len == next->first) {
+        len += next->second;
+        next = a->free.erase(next);
+    }
+    if (next != a->free.begin()) {
+        auto prev = std::prev(next);
+        if (prev->first + prev->second == off) {
+            prev->second += len;
+            return;
+        }
+    }
+    a->free.emplace(off, len);
+}
 
 static pm_status take_event(pm_store* s, hipEvent_t* ev) {
     if (!s->spare_events.empty()) {
@@ -658,77 +698,108 @@ static pm_status take_event(pm_store* s, hipEvent_t* ev) {
     return PM_OK;
 }
 
-// Release the retired buffers whose last copy and last reader have ended.
-static pm_status reclaim(pm_store* s) {
-    if (s->host_fake || s->retired.empty()) return PM_OK;
-    std::vector<Retired> keep;
-    pm_status st = PM_OK;
-    for (const Retired& r : s->retired) {
-        bool idle = st == PM_OK && (!r.copied || hipEventQuery(r.copied) == hipSuccess);
+// Return the released ranges whose last copy and last reader have ended.
+static void reclaim(pm_store* s) {
+    if (s->released.empty()) return;
+    std::vector<Released> keep;
+    for (const Released& r : s->released) {
+        bool idle = !r.ev || hipEventQuery(r.ev) == hipSuccess;
         if (idle && r.reader) idle = hipEventQuery(forward_end(s, r.reader)) == hipSuccess;
         if (!idle) {
             keep.push_back(r);
             continue;
         }
-        const hipError_t e = hipFreeAsync(r.p, s->side[pm_store::kMem]);
-        if (e != hipSuccess) {
-            st = hip_fail(e, "hipFreeAsync");
-            keep.push_back(r);
-            continue;
-        }
-        if (r.copied) s->spare_events.push_back(r.copied);
+        arena_put(s, r.p, r.len);
+        if (r.ev) s->spare_events.push_back(r.ev);
     }
-    s->retired.swap(keep);
-    return st;
+    s->released.swap(keep);
 }
 
-// Retire buffer p: its last copy was issued on stream `last` (the event is
-// recorded there now) and forward `reader` last read it.
-static pm_status retire(pm_store* s, void* p, hipStream_t last, uint64_t reader) {
-    if (!p) return PM_OK;
+// Give back [p, p + len): at once in a host-backed store, else after the
+// copies issued on `last` so far (an event recorded there now; null: none in
+// flight) and the end of forward `reader`.
+static pm_status release_range(pm_store* s, char* p, size_t len, hipStream_t last,
+                               uint64_t reader) {
+    if (!p || len == 0) return PM_OK;
     if (s->host_fake) {
-        std::free(p);
+        arena_put(s, p, len);
         return PM_OK;
     }
     hipEvent_t ev = nullptr;
-    pm_status st = take_event(s, &ev);
-    if (st) return st;
-    const hipError_t e = hipEventRecord(ev, last);
-    if (e != hipSuccess) {
-        s->spare_events.push_back(ev);
-        return hip_fail(e, "hipEventRecord");
+    if (last) {
+        pm_status st = take_event(s, &ev);
+        if (st) return st;
+        const hipError_t e = hipEventRecord(ev, last);
+        if (e != hipSuccess) {
+            s->spare_events.push_back(ev);
+            return hip_fail(e, "hipEventRecord");
+        }
     }
-    s->retired.push_back({p, ev, reader});
+    s->released.push_back({p, len, ev, reader});
+    if (s->released.size() > 256) reclaim(s);
     return PM_OK;
 }
 
-static pm_status dev_alloc(pm_store* s, size_t bytes, void** out) {
+static bool arena_fit(pm_store* s, size_t len, char** out) {
+    for (Arena& a : s->arenas)
+        for (auto it = a.free.begin(); it != a.free.end(); ++it)
+            if (it->second >= len) {
+                const size_t off = it->first, rest = it->second - len;
+                a.free.erase(it);
+                if (rest) a.free.emplace(off + len, rest);
+                *out = a.base + off;
+                return true;
+            }
+    return false;
+}
+
+// A free range of `bytes` (rounded up to kRangeAlign): first fit, then after
+// reclaiming, then from a new arena.
+static pm_status arena_alloc(pm_store* s, size_t bytes, char** out) {
     *out = nullptr;
-    if (bytes == 0) return PM_OK;
+    const size_t len = range_len(bytes);
+    if (len == 0) return PM_OK;
+    if (arena_fit(s, len, out)) return PM_OK;
+    reclaim(s);
+    if (arena_fit(s, len, out)) return PM_OK;
+    const size_t size = std::max(s->arena_bytes, len);
+    char* base = nullptr;
     if (s->host_fake) {
-        *out = std::calloc(bytes, 1);
-        if (!*out) return failf(PM_ERR_OOM, "host allocation of %zu bytes failed", bytes);
-        return PM_OK;
+        base = static_cast<char*>(std::calloc(size, 1));
+        if (!base) return failf(PM_ERR_OOM, "host allocation of %zu bytes failed", size);
+    } else {
+        hipError_t e = hipMalloc(&base, size);
+        if (e != hipSuccess) {
+            // what queued work still holds may be enough once it ends
+            (void)hipGetLastError();
+            HIP_TRY(hipDeviceSynchronize());
+            reclaim(s);
+            if (arena_fit(s, len, out)) return PM_OK;
+            return failf(PM_ERR_OOM, "device allocation of %zu bytes failed: %s", size,
+                         hipGetErrorString(e));
+        }
     }
-    const hipError_t e = hipMallocFromPoolAsync(out, bytes, s->pool, s->side[pm_store::kMem]);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        *out = nullptr;
-        return failf(PM_ERR_OOM, "device allocation of %zu bytes failed: %s", bytes,
-                     hipGetErrorString(e));
-    }
-    s->alloc_unpublished = true;
+    Arena a{base, size, {}};
+    if (size > len) a.free.emplace(len, size - len);
+    s->arenas.push_back(std::move(a));
+    *out = base;
     return PM_OK;
 }
 
-// Make copy stream `st` wait for the allocations issued so far.
-static pm_status publish_allocs(pm_store* s, hipStream_t st) {
-    if (s->host_fake || !s->alloc_unpublished || st == s->side[pm_store::kMem]) return PM_OK;
-    if (!s->alloc_ev) HIP_TRY(hipEventCreateWithFlags(&s->alloc_ev, hipEventDisableTiming));
-    HIP_TRY(hipEventRecord(s->alloc_ev, s->side[pm_store::kMem]));
-    HIP_TRY(hipStreamWaitEvent(st, s->alloc_ev, 0));
-    s->alloc_unpublished = false;
-    return PM_OK;
+// Take the range right after [p, p + old_len) so that the range spans
+// new_len bytes, if it is free.
+static bool arena_extend(pm_store* s, char* p, size_t old_len, size_t new_len) {
+    Arena* a = arena_of(s, p);
+    if (!a) return false;
+    const size_t end = size_t(p - a->base) + range_len(old_len);
+    const size_t need = range_len(new_len) - range_len(old_len);
+    if (need == 0) return true;
+    auto it = a->free.find(end);
+    if (it == a->free.end() || it->second < need) return false;
+    const size_t rest = it->second - need;
+    a->free.erase(it);
+    if (rest) a->free.emplace(end + need, rest);
+    return true;
 }
 
 // Make `st` wait for the last forward that read the slot (unless it has
@@ -741,39 +812,48 @@ static pm_status order_after_readers(pm_store* s, Slot& sl, hipStream_t st) {
     return PM_OK;
 }
 
-// The slot's planes move to a new buffer of `cap` chunks (none at 0) that
-// keeps the first `keep` valid chunks (keep <= both capacities), copied on
-// `st` after any copy still in flight into the old buffer; the old buffer is
-// retired.  Readers of the old buffer need no wait: it stays until they end.
+// The slot's planes become `cap` chunks, keeping its first `keep` valid
+// chunks (keep <= both capacities).  Shrinking gives the tail back in place;
+// growing extends the range in place if it can, else copies the kept prefix
+// to a new range on `st`.  The caller has ordered `st` after the slot's last
+// copy; a range given back waits for that stream and for the slot's last
+// reader.
 static pm_status resize_planes(pm_store* s, Slot& sl, int cap, int keep, hipStream_t st) {
     if (cap == sl.cap) return PM_OK;
     const size_t pb = s->plane_bytes;
-    void* nb = nullptr;
-    pm_status r = dev_alloc(s, size_t(cap) * pb, &nb);
-    if (r) return r;
-    if (s->host_fake) {
-        if (keep > 0) std::memcpy(nb, sl.planes, size_t(keep) * pb);
-    } else {
-        r = publish_allocs(s, st);
+    const size_t old_len = size_t(sl.cap) * pb, new_len = size_t(cap) * pb;
+    char* p = reinterpret_cast<char*>(sl.planes);
+    pm_status r = PM_OK;
+    if (cap < sl.cap) {
+        const size_t keep_len = cap ? range_len(new_len) : 0;
+        r = release_range(s, p + keep_len, range_len(old_len) - keep_len, st, sl.read_seq);
         if (r) return r;
-        if (sl.copied) HIP_TRY(hipStreamWaitEvent(st, sl.ready, 0));
-        if (keep > 0)
-            HIP_TRY(hipMemcpyAsync(nb, sl.planes, size_t(keep) * pb, hipMemcpyDeviceToDevice, st));
+        if (cap == 0) sl.planes = nullptr;
+    } else if (!(p && arena_extend(s, p, old_len, new_len))) {
+        char* nb = nullptr;
+        r = arena_alloc(s, new_len, &nb);
+        if (r) return r;
+        if (keep > 0) {
+            if (s->host_fake)
+                std::memcpy(nb, p, size_t(keep) * pb);
+            else
+                HIP_TRY(hipMemcpyAsync(nb, p, size_t(keep) * pb, hipMemcpyDeviceToDevice, st));
+        }
+        r = release_range(s, p, range_len(old_len), st, sl.read_seq);
+        if (r) return r;
+        sl.planes = reinterpret_cast<uint32_t*>(nb);
     }
-    r = retire(s, sl.planes, st, sl.read_seq);
-    if (r) return r;
-    s->used = s->used - size_t(sl.cap) * pb + size_t(cap) * pb;
-    sl.planes = static_cast<uint32_t*>(nb);
+    s->used = s->used - old_len + new_len;
     sl.cap = cap;
     return PM_OK;
 }
 
 static pm_status ensure_levels(pm_store* s, Slot& sl) {
     if (sl.levels) return PM_OK;
-    void* lv = nullptr;
-    pm_status r = dev_alloc(s, s->level_bytes, &lv);
+    char* lv = nullptr;
+    pm_status r = arena_alloc(s, s->level_bytes, &lv);
     if (r) return r;
-    sl.levels = static_cast<float*>(lv);
+    sl.levels = reinterpret_cast<float*>(lv);
     sl.levels_ready = false;
     s->used += s->level_bytes;
     return PM_OK;
@@ -798,11 +878,10 @@ static pm_status check_capacity(const pm_store* s, size_t more) {
 // or the host).
 static pm_status slot_for_writes(pm_store* s, Slot& sl) {
     if (sl.cap == kBits && sl.levels) return PM_OK;
-    pm_status r = reclaim(s);
-    if (r) return r;
-    r = check_capacity(s, bytes_to_hold(s, sl, kBits));
+    pm_status r = check_capacity(s, bytes_to_hold(s, sl, kBits));
     if (r) return r;
     hipStream_t st = s->side[pm_store::kMem];
+    if (!s->host_fake && sl.copied) HIP_TRY(hipStreamWaitEvent(st, sl.ready, 0));
     r = ensure_levels(s, sl);
     if (r) return r;
     r = resize_planes(s, sl, kBits, sl.resident, st);
@@ -831,31 +910,16 @@ extern "C" pm_status pm_store_create(pm_expert_shape e, int n_layers, int n_expe
     s->plane_bytes = pm_expert_plane_words(e) * sizeof(uint32_t);
     s->level_bytes = pm_expert_levels_floats(e) * sizeof(float);
     s->slots.resize(size_t(n_layers) * n_experts);
+    // arenas of about eight whole experts (within 64 MiB .. 2 GiB), no larger
+    // than a capacity the store is given
+    {
+        const size_t expert_bytes = kBits * s->plane_bytes + s->level_bytes;
+        size_t ab = std::min(std::max(8 * expert_bytes, size_t(64) << 20), size_t(2) << 30);
+        if (capacity) ab = std::min(ab, std::max(capacity, expert_bytes));
+        s->arena_bytes = ab;
+    }
     if (!s->host_fake) {
         hipError_t er = hipSuccess;
-        // the store's pool on the current device: released slot memory stays
-        // in it for later slots (until the store is destroyed), and it reuses
-        // memory only in the memory stream's order
-        int dev = 0;
-        er = hipGetDevice(&dev);
-        if (er == hipSuccess) {
-            hipMemPoolProps props{};
-            props.allocType = hipMemAllocationTypePinned;
-            props.handleTypes = hipMemHandleTypeNone;
-            props.location.type = hipMemLocationTypeDevice;
-            props.location.id = dev;
-            er = hipMemPoolCreate(&s->pool, &props);
-        }
-        if (er == hipSuccess) {
-            uint64_t keep = UINT64_MAX;
-            int off = 0;
-            er = hipMemPoolSetAttribute(s->pool, hipMemPoolAttrReleaseThreshold, &keep);
-            if (er == hipSuccess)
-                er = hipMemPoolSetAttribute(s->pool, hipMemPoolReuseAllowOpportunistic, &off);
-            if (er == hipSuccess)
-                er = hipMemPoolSetAttribute(s->pool, hipMemPoolReuseAllowInternalDependencies,
-                                            &off);
-        }
         for (int i = 0; i < pm_store::kSides && er == hipSuccess; ++i)
             er = hipStreamCreateWithFlags(&s->side[i], hipStreamNonBlocking);
         for (int i = 0; i < pm_store::kDone && er == hipSuccess; ++i)
@@ -872,26 +936,16 @@ extern "C" pm_status pm_store_create(pm_expert_shape e, int n_layers, int n_expe
 extern "C" pm_status pm_store_destroy(pm_store* s) {
     if (!s) return PM_OK;
     if (!s->host_fake) (void)hipDeviceSynchronize();
-    hipStream_t mem = s->side[pm_store::kMem];
-    for (Slot& sl : s->slots) {
-        if (s->host_fake) {
-            std::free(sl.planes);
-            std::free(sl.levels);
-        } else if (mem) {
-            if (sl.planes) (void)hipFreeAsync(sl.planes, mem);
-            if (sl.levels) (void)hipFreeAsync(sl.levels, mem);
-        }
+    for (Slot& sl : s->slots)
         if (sl.ready) (void)hipEventDestroy(sl.ready);
-    }
-    if (!s->host_fake) {
-        for (const Retired& r : s->retired) {
-            if (mem) (void)hipFreeAsync(r.p, mem);
-            if (r.copied) (void)hipEventDestroy(r.copied);
-        }
-        for (hipEvent_t ev : s->spare_events) (void)hipEventDestroy(ev);
-        if (s->alloc_ev) (void)hipEventDestroy(s->alloc_ev);
-        if (mem) (void)hipStreamSynchronize(mem);
-        if (s->pool) (void)hipMemPoolDestroy(s->pool);
+    for (const Released& r : s->released)
+        if (r.ev) (void)hipEventDestroy(r.ev);
+    for (hipEvent_t ev : s->spare_events) (void)hipEventDestroy(ev);
+    for (Arena& a : s->arenas) {
+        if (s->host_fake)
+            std::free(a.base);
+        else
+            (void)hipFree(a.base);
     }
     if (!s->host_fake) {
         Workspace& w = s->ws;
@@ -989,25 +1043,23 @@ static pm_status topup_slot(pm_store* s, Slot& sl, int k, hipStream_t side) {
         return PM_OK;
     }
     if (!sl.h_planes || !sl.h_levels) return failf(PM_ERR_STATE, "slot has no host source");
-    pm_status st = reclaim(s);
-    if (st) return st;
-    st = check_capacity(s, bytes_to_hold(s, sl, k));
+    pm_status st = check_capacity(s, bytes_to_hold(s, sl, k));
     if (st) return st;
     st = slot_event(s, sl);
     if (st) return st;
     st = ensure_levels(s, sl);
     if (st) return st;
-    if (k > sl.cap) {
-        // into a new buffer: an earlier reader keeps the old one
-        st = resize_planes(s, sl, k, sl.resident, side);
-        if (st) return st;
-    } else {
-        // in place: the copy must not overwrite planes a forward may still
-        // read (after the resident prefix was lowered), nor race an earlier
-        // copy into the slot on another stream
+    // The copy must not overwrite planes a forward may still read (those
+    // past a resident prefix that was lowered below the chunks held), and it
+    // follows any earlier copy into the slot on another stream.
+    if (k <= sl.cap || sl.resident < sl.cap) {
         st = order_after_readers(s, sl, side);
         if (st) return st;
-        st = publish_allocs(s, side);
+    } else if (!s->host_fake && sl.copied) {
+        HIP_TRY(hipStreamWaitEvent(side, sl.ready, 0));
+    }
+    if (k > sl.cap) {
+        st = resize_planes(s, sl, k, sl.resident, side);
         if (st) return st;
     }
     const int first = sl.resident;
@@ -1082,30 +1134,35 @@ extern "C" pm_status pm_store_truncate(pm_store* s, int layer, int expert, int k
     if (keep < 0 || keep > kBits) return failf(PM_ERR_PREFIX, "keep %d outside 0..8", keep);
     Slot& sl = s->slots[i];
     sl.resident = std::min(sl.resident, keep);
-    // the plane chunks past `keep` (and at keep 0 the levels) are released
-    // once the slot's last reader and copies have ended; the kept prefix
-    // moves to a buffer of its own size on the memory stream
+    // the plane chunks past `keep` (and at keep 0 the levels) go back to the
+    // store's arenas in place, once the slot's last copy and last reader
+    // have ended
     if (keep >= sl.cap && (keep > 0 || !sl.levels)) return PM_OK;
-    st = reclaim(s);
-    if (st) return st;
-    hipStream_t mem = s->side[pm_store::kMem];
-    st = slot_event(s, sl);
-    if (st) return st;
+    hipStream_t mem = s->host_fake ? nullptr : s->side[pm_store::kMem];
+    if (mem && sl.copied) HIP_TRY(hipStreamWaitEvent(mem, sl.ready, 0));
     st = resize_planes(s, sl, std::min(sl.cap, keep), sl.resident, mem);
     if (st) return st;
     if (keep == 0 && sl.levels) {
-        if (!s->host_fake && sl.copied) HIP_TRY(hipStreamWaitEvent(mem, sl.ready, 0));
-        st = retire(s, sl.levels, mem, sl.read_seq);
+        st = release_range(s, reinterpret_cast<char*>(sl.levels), range_len(s->level_bytes), mem,
+                           sl.read_seq);
         if (st) return st;
         sl.levels = nullptr;
         sl.levels_ready = false;
         s->used -= s->level_bytes;
     }
-    if (!s->host_fake) {
-        HIP_TRY(hipEventRecord(sl.ready, mem));
-        sl.copied = true;
-        sl.pending = true;
-    }
+    return PM_OK;
+}
+
+extern "C" pm_status pm_store_slot_info(const pm_store* s, int layer, int expert,
+                                       const uint32_t** planes, const float** levels,
+                                       int* chunks) {
+    size_t i;
+    pm_status st = slot_of(s, layer, expert, &i);
+    if (st) return st;
+    const Slot& sl = s->slots[i];
+    if (planes) *planes = sl.planes;
+    if (levels) *levels = sl.levels;
+    if (chunks) *chunks = sl.cap;
     return PM_OK;
 }
 
@@ -1279,8 +1336,9 @@ struct StreamBuf {
     float* p = nullptr;
     size_t n = 0;
 };
+// Never destroyed: no destructor of this library runs at process exit.
 std::mutex g_gemv_mu;
-std::map<hipStream_t, StreamBuf> g_gemv_bufs;
+std::map<hipStream_t, StreamBuf>& g_gemv_bufs = *new std::map<hipStream_t, StreamBuf>();
 }  // namespace
 
 static pm_status gemv_partials(hipStream_t st, size_t n, float** out) {

@@ -202,11 +202,13 @@ pm_status pm_allocate_bits(int n_tokens, int top_k, const int32_t* ids, const fl
  * truncation releases the chunks past the kept prefix, and a slot holds its
  * levels while it holds any plane.  Growing or shrinking a buffer moves it
  * (the resident prefix is copied along), so slot addresses are valid only
- * until the next store call on that slot.  Slot memory comes from a device
- * memory pool of the store's own; a released buffer goes back to it once
- * every queued forward that read it and every copy from or into it has
- * ended (checked by later store calls), and the pool keeps it for later
- * slots until the store is destroyed.
+ * until the next store call on that slot.  Slot memory is carved out of
+ * arenas of the store's own (large device allocations kept until the store is
+ * destroyed): a truncation gives the tail back in place and a top-up extends
+ * a slot in place when it can, so neither allocates or frees device memory
+ * in the common case.  Memory given back returns to the arenas once every
+ * queued forward that read it and every copy from or into it has ended
+ * (checked by later store calls).
  * flags: PM_STORE_HOST_FAKE backs slots with host memory and copies with
  * memcpy (bookkeeping tests without a GPU; compute calls reject such a
  * store).  capacity_bytes > 0 caps the slot memory, plane chunks plus levels
@@ -233,25 +235,31 @@ pm_status pm_store_attach_host(pm_store* s, int layer, int expert,
 /* Make planes r..k-1 resident by copying exactly those plane chunks from the
  * host source (plus the levels on a slot's first fill) on `side` (null: a
  * store side stream), then record the slot's ready event there; r becomes k.
- * A slot holding fewer than k chunks moves to a new buffer first (the
- * resident prefix copied along on `side`); a copy into the slot's own buffer
- * first waits for an earlier forward still reading the slot.  Either waits
- * for an earlier copy into the slot still in flight.  No copy if r >= k
- * [T c13, c35: a resident deeper prefix serves a shallower request].
- * PM_ERR_STATE without a host source. */
+ * A slot holding fewer than k chunks grows first, in place or by moving the
+ * resident prefix to a new range (copied on `side`).  A copy that overwrites
+ * chunks the slot already held waits for an earlier forward still reading
+ * the slot; every copy waits for an earlier copy into the slot still in
+ * flight.  No copy if r >= k [T c13, c35: a resident deeper prefix serves a
+ * shallower request].  PM_ERR_STATE without a host source. */
 pm_status pm_store_topup(pm_store* s, int layer, int expert, int k, void* side);
 /* r = min(r, keep): the deepest planes age out first [T c35].  The plane
- * chunks past keep are released (at keep 0 the levels too): the kept prefix
- * moves to a buffer of its own size, and the old buffer returns to the pool
- * once the slot's last reader and copies have ended. */
+ * chunks past keep are released in place (at keep 0 the levels too); their
+ * memory returns to the store's arenas once the slot's last reader and last
+ * copy have ended. */
 pm_status pm_store_truncate(pm_store* s, int layer, int expert, int keep);
 /* Slot memory held by the store's slots: bytes (plane chunks and levels,
  * what capacity_bytes caps), plane chunks, and slots holding levels.  Memory
- * released but still in use by queued work, and memory the pool keeps, are
- * not counted.  Any output may be null. */
+ * released but still in use by queued work, and free arena space, are not
+ * counted.  Any output may be null. */
 pm_status pm_store_usage(const pm_store* s, size_t* used_bytes, size_t* plane_chunks,
                          size_t* level_sets);
 pm_status pm_store_resident(const pm_store* s, int layer, int expert, int* r_out);
+/* Where a slot's memory is now, without changing it: its planes (null when
+ * it holds no chunk), its levels (null when it holds none) and the plane
+ * chunks it holds.  Valid until the next store call on the slot.  Any output
+ * may be null. */
+pm_status pm_store_slot_info(const pm_store* s, int layer, int expert, const uint32_t** planes,
+                             const float** levels, int* chunks);
 /* Planes copied by the last top-up of any slot (first plane, count) and the
  * running totals of plane chunks and bytes copied by top-ups. */
 pm_status pm_store_copy_stats(const pm_store* s, int* last_first, int* last_count,

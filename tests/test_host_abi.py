@@ -228,6 +228,53 @@ def test_store_memory_follows_residency():
     st.close()
 
 
+def test_store_slots_grow_and_shrink_in_place():
+    """A truncation gives the tail of a slot's range back in place, and a
+    top-up extends the range in place when the range after it is free, else
+    moves the resident prefix (copied along) to a new range.  Every resident
+    plane keeps the host source's words through all of it."""
+    e, st = fake_store(3)
+    pw = pm.pm_expert_plane_words(e)
+    lf = pm.pm_expert_levels_floats(e)
+    hp = [np.arange(8 * pw, dtype=np.uint32).reshape(8, pw) + np.uint32(1000003 * x) for x in range(3)]
+    hl = np.arange(lf, dtype=np.float32)
+    for x in range(3):
+        pm.pm_store_attach_host(st, 0, x, hp[x], hl)
+
+    def planes_of(x):
+        p, _, n = pm.pm_store_slot_info(st, 0, x)
+        r = pm.pm_store_resident(st, 0, x)
+        assert n >= r
+        return p, np.ctypeslib.as_array((ctypes.c_uint32 * (r * pw)).from_address(p)).reshape(r, pw)
+
+    def check(x):
+        r = pm.pm_store_resident(st, 0, x)
+        _, got = planes_of(x)
+        assert np.array_equal(got, hp[x][:r]), x
+
+    pm.pm_store_topup(st, 0, 0, 2)
+    pm.pm_store_topup(st, 0, 1, 2)             # right after slot 0's range
+    a0 = planes_of(0)[0]
+    pm.pm_store_truncate(st, 0, 0, 1)
+    pm.pm_store_topup(st, 0, 0, 2)             # its own tail again: in place
+    assert planes_of(0)[0] == a0
+    check(0)
+    pm.pm_store_topup(st, 0, 0, 5)             # slot 1 follows: moves
+    a0b = planes_of(0)[0]
+    assert a0b != a0
+    check(0)
+    check(1)
+    pm.pm_store_truncate(st, 0, 0, 3)
+    pm.pm_store_topup(st, 0, 0, 5)             # in place at the new range
+    assert planes_of(0)[0] == a0b
+    check(0)
+    pm.pm_store_topup(st, 0, 2, 1)             # first fit: slot 0's old range
+    assert planes_of(2)[0] == a0
+    check(2)
+    assert pm.pm_store_usage(st)[1] == 5 + 2 + 1
+    st.close()
+
+
 def test_forward_validates_every_item_before_any_allocation():
     """A layer call whose later item cannot be served changes nothing in the
     store: no slot memory is taken for the earlier items."""
