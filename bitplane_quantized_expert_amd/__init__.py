@@ -102,6 +102,8 @@ SIGNATURES = {
     "pm_debug_dequant": (_I, [_MS, _I, _P, _Z, _P, _P, _P]),
     "pm_materialize_fp16": (_I, [_MS, _I, _P, _Z, _P, _P, _P]),
     "pm_gemv_fp16": (_I, [_MS, _P, _P, _P, _P]),
+    "pm_materialize_fp16_batch": (_I, [_I, _P, _P, _P, _P, _P, _P, _P]),
+    "pm_gemv_fp16_batch": (_I, [_I, _P, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -254,6 +256,31 @@ def pm_materialize_fp16(s, k, d_planes, plane_stride_words, d_levels, d_out, str
 
 def pm_gemv_fp16(s, d_w, d_x, d_y, stream=None):
     return _check(lib().pm_gemv_fp16(s, _dptr(d_w), _dptr(d_x), _dptr(d_y), _stream(stream)))
+
+
+def _ptr_array(ptrs):
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*[_dptr(p) for p in ptrs])
+    return ctypes.cast(arr, ctypes.c_void_p)
+
+
+def pm_materialize_fp16_batch(shapes, ks, d_planes, plane_stride_words, d_levels, d_w_fp16,
+                              stream=None):
+    """Lists of one length: matrix shapes, prefixes, device plane/level
+    pointers (tensors or ints), plane strides (words) and fp16 outputs."""
+    n = len(shapes)
+    sh = (pm_matrix_shape * max(1, n))(*shapes)
+    kk = np.ascontiguousarray(ks, dtype=np.int32)
+    ps = np.ascontiguousarray(plane_stride_words, dtype=np.uint64)
+    return _check(lib().pm_materialize_fp16_batch(
+        n, ctypes.cast(sh, ctypes.c_void_p), _hptr(kk), _ptr_array(d_planes), _hptr(ps),
+        _ptr_array(d_levels), _ptr_array(d_w_fp16), _stream(stream)))
+
+
+def pm_gemv_fp16_batch(shapes, d_w, d_x, d_y, stream=None):
+    n = len(shapes)
+    sh = (pm_matrix_shape * max(1, n))(*shapes)
+    return _check(lib().pm_gemv_fp16_batch(n, ctypes.cast(sh, ctypes.c_void_p), _ptr_array(d_w),
+                                           _ptr_array(d_x), _ptr_array(d_y), _stream(stream)))
 
 
 # ---------------------------------------------------------------- routing / allocation

@@ -417,12 +417,80 @@ extern "C" pm_status pm_materialize_fp16(pm_matrix_shape s, int k, const uint32_
     return PM_OK;
 }
 
+extern "C" pm_status pm_materialize_fp16_batch(int n, const pm_matrix_shape* shapes,
+                                               const int* ks, const uint32_t* const* d_planes,
+                                               const size_t* pstrides,
+                                               const float* const* d_levels,
+                                               uint16_t* const* d_w_fp16, void* stream) {
+    if (n < 0 || n > kMaxBatchMats) return failf(PM_ERR_ARG, "batch of %d matrices outside 0..%d",
+                                                 n, kMaxBatchMats);
+    if (n == 0) return PM_OK;
+    if (!shapes || !ks || !d_planes || !pstrides || !d_levels || !d_w_fp16)
+        return failf(PM_ERR_ARG, "null batch array");
+    KDequantBatch B{};
+    size_t max_elems = 0;
+    for (int m = 0; m < n; ++m) {
+        const pm_matrix_shape s = shapes[m];
+        pm_status st = check_matrix_call(s, ks[m], d_planes[m], pstrides[m], d_levels[m], d_w_fp16[m]);
+        if (st) return st;
+        if (reinterpret_cast<uintptr_t>(d_w_fp16[m]) % 16)
+            return failf(PM_ERR_ARG, "output %d not 16-byte aligned", m);
+        const size_t nb = size_t(s.rows) * (s.cols / s.group);
+        B.rows[B.n] = s.rows;
+        B.cols[B.n] = s.cols;
+        B.group[B.n] = s.group;
+        B.k[B.n] = ks[m];
+        B.pstride[B.n] = pstrides[m];
+        B.planes[B.n] = d_planes[m];
+        B.lvk[B.n] = d_levels[m] + level_offset(nb, ks[m]);
+        B.w[B.n] = d_w_fp16[m];
+        max_elems = std::max(max_elems, size_t(s.rows) * s.cols);
+        if (size_t(s.rows) * s.cols > 0) ++B.n;
+    }
+    HIP_TRY(launch_dequant_batch(B, max_elems, (hipStream_t)stream));
+    return PM_OK;
+}
+
+extern "C" pm_status pm_gemv_fp16_batch(int n, const pm_matrix_shape* shapes,
+                                        const uint16_t* const* d_w, const float* const* d_x,
+                                        float* const* d_y, void* stream) {
+    if (n < 0 || n > kMaxBatchMats) return failf(PM_ERR_ARG, "batch of %d matrices outside 0..%d",
+                                                 n, kMaxBatchMats);
+    if (n == 0) return PM_OK;
+    if (!shapes || !d_w || !d_x || !d_y) return failf(PM_ERR_ARG, "null batch array");
+    KGemv16Batch B{};
+    int max_rows = 0;
+    for (int m = 0; m < n; ++m) {
+        const pm_matrix_shape s = shapes[m];
+        pm_status st = check_shape(s);
+        if (st) return st;
+        if (s.rows == 0) continue;
+        if (s.cols == 0) return failf(PM_ERR_SHAPE, "matrix %d has no columns", m);
+        if (!d_w[m] || !d_x[m] || !d_y[m]) return failf(PM_ERR_ARG, "null device pointer");
+        if (reinterpret_cast<uintptr_t>(d_w[m]) % 16 || (size_t(s.cols) * 2) % 16)
+            return failf(PM_ERR_ARG, "weights %d: rows not 16-byte aligned", m);
+        if (reinterpret_cast<uintptr_t>(d_x[m]) % 16)
+            return failf(PM_ERR_ARG, "x %d not 16-byte aligned", m);
+        B.rows[B.n] = s.rows;
+        B.cols[B.n] = s.cols;
+        B.w[B.n] = d_w[m];
+        B.x[B.n] = d_x[m];
+        B.y[B.n] = d_y[m];
+        ++B.n;
+        max_rows = std::max(max_rows, s.rows);
+    }
+    HIP_TRY(launch_gemv_fp16_batch(B, max_rows, (hipStream_t)stream));
+    return PM_OK;
+}
+
 extern "C" pm_status pm_gemv_fp16(pm_matrix_shape s, const uint16_t* d_w, const float* d_x,
                                   float* d_y, void* stream) {
     pm_status st = check_shape(s);
     if (st) return st;
     if (s.rows == 0) return PM_OK;
     if (!d_y || (s.cols > 0 && (!d_w || !d_x))) return failf(PM_ERR_ARG, "null device pointer");
+    if (s.cols > 0 && (reinterpret_cast<uintptr_t>(d_w) % 16 || reinterpret_cast<uintptr_t>(d_x) % 16))
+        return failf(PM_ERR_ARG, "weights and x must be 16-byte aligned");
     HIP_TRY(launch_gemv_fp16(s.rows, s.cols, d_w, d_x, d_y, (hipStream_t)stream));
     return PM_OK;
 }

@@ -145,6 +145,28 @@ hipError_t launch_unpack_prefix(int rows, int cols, int k, const uint32_t* plane
 hipError_t launch_dequant(int rows, int cols, int group, int k, const uint32_t* planes,
                           size_t pstride, const float* levels, float* out_f32,
                           uint16_t* out_f16, hipStream_t st);
+// The materialize-then-multiply comparator, batched: up to kMaxBatchMats
+// matrices per launch, described in the kernel arguments.
+constexpr int kMaxBatchMats = 64;
+struct KDequantBatch {
+    int32_t n, pad;
+    int32_t rows[kMaxBatchMats], cols[kMaxBatchMats], group[kMaxBatchMats], k[kMaxBatchMats];
+    uint64_t pstride[kMaxBatchMats];
+    const uint32_t* planes[kMaxBatchMats];
+    const float* lvk[kMaxBatchMats];    // depth-k nodes
+    uint16_t* w[kMaxBatchMats];
+};
+static_assert(sizeof(KDequantBatch) <= 4096, "kernel arguments are limited to 4 KiB");
+struct KGemv16Batch {
+    int32_t n, pad;
+    int32_t rows[kMaxBatchMats], cols[kMaxBatchMats];
+    const uint16_t* w[kMaxBatchMats];
+    const float* x[kMaxBatchMats];
+    float* y[kMaxBatchMats];
+};
+static_assert(sizeof(KGemv16Batch) <= 4096, "kernel arguments are limited to 4 KiB");
+hipError_t launch_dequant_batch(const KDequantBatch& B, size_t max_elems, hipStream_t st);
+hipError_t launch_gemv_fp16_batch(const KGemv16Batch& B, int max_rows, hipStream_t st);
 hipError_t launch_gemv_fp16(int rows, int cols, const uint16_t* w, const float* x, float* y,
                             hipStream_t st);
 

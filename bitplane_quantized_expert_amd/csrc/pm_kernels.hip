@@ -24,6 +24,8 @@
 //
 // All sums run in a fixed order (DPP row reductions, slices and slots in
 // index order), so every output is deterministic.
+#include <algorithm>
+
 #include <hip/hip_fp16.h>
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -986,6 +988,28 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(int rows, int cols, int
     if (out16) out16[i] = __half_as_ushort(__float2half_rn(val));
 }
 
+// One row of an fp16 weight matrix times x, by one wave (16-byte loads; lane
+// sums in column order, then the wave sum).
+__device__ inline float row_dot_fp16(const uint16_t* __restrict__ row, int cols,
+                                     const float* __restrict__ x, int lane) {
+    float acc = 0.f;
+    for (int c = lane * 8; c < cols; c += kWave * 8) {
+        const uint4 pk = *reinterpret_cast<const uint4*>(row + c);
+        const f32x4 xa = *reinterpret_cast<const f32x4*>(x + c);
+        const f32x4 xb = *reinterpret_cast<const f32x4*>(x + c + 4);
+        const uint32_t q[4] = {pk.x, pk.y, pk.z, pk.w};
+        const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = __half2float(__ushort_as_half(uint16_t(q[i] & 0xFFFFu)));
+            const float hi = __half2float(__ushort_as_half(uint16_t(q[i] >> 16)));
+            acc = fmaf(lo, xv[2 * i], acc);
+            acc = fmaf(hi, xv[2 * i + 1], acc);
+        }
+    }
+    return wave_sum(acc);
+}
+
 __global__ __launch_bounds__(kBlock) void gemv_fp16_kernel(int rows, int cols,
                                                            const uint16_t* __restrict__ w,
                                                            const float* __restrict__ x,
@@ -993,21 +1017,84 @@ __global__ __launch_bounds__(kBlock) void gemv_fp16_kernel(int rows, int cols,
     const int lane = threadIdx.x % kWave;
     const int o = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
     if (o >= rows) return;
-    const uint16_t* row = w + size_t(o) * cols;
-    float acc = 0.f;
-    for (int c = lane * 8; c < cols; c += kWave * 8) {
-        const uint4 pk = *reinterpret_cast<const uint4*>(row + c);
-        const uint32_t q[4] = {pk.x, pk.y, pk.z, pk.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float lo = __half2float(__ushort_as_half(uint16_t(q[i] & 0xFFFFu)));
-            const float hi = __half2float(__ushort_as_half(uint16_t(q[i] >> 16)));
-            acc = fmaf(lo, x[c + 2 * i], acc);
-            acc = fmaf(hi, x[c + 2 * i + 1], acc);
-        }
-    }
-    acc = wave_sum(acc);
+    const float acc = row_dot_fp16(w + size_t(o) * cols, cols, x, lane);
     if (lane == kWave - 1) y[o] = acc;
+}
+
+// Matrix blockIdx.y of the batch: row o of its fp16 weights times its x.
+__global__ __launch_bounds__(kBlock) void gemv_fp16_batch_kernel(const KGemv16Batch B) {
+    const int m = blockIdx.y;
+    const int lane = threadIdx.x % kWave;
+    const int o = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+    if (o >= B.rows[m]) return;
+    const int cols = B.cols[m];
+    const float acc = row_dot_fp16(B.w[m] + size_t(o) * cols, cols, B.x[m], lane);
+    if (lane == kWave - 1) B.y[m][o] = acc;
+}
+
+// Matrix blockIdx.y of the batch in tiles of kDqTile consecutive weights (a
+// workgroup's share of a step, 8 per thread).  The depth-k tables of the
+// blocks a tile touches are one contiguous range of the levels: the
+// workgroup stages them in LDS with coalesced loads, then every thread takes
+// its 8 weights' k-bit prefixes from one byte of each plane word, looks their
+// nodes up in LDS (the 8 share a block), rounds them to fp16 (nearest even)
+// and stores 16 bytes.
+constexpr int kDqTile = kBlock * 8;
+constexpr int kDqStagedK = 5;
+__global__ __launch_bounds__(kBlock) void dequant_batch_kernel(const KDequantBatch B) {
+    extern __shared__ float tabs[];
+    const int m = blockIdx.y;
+    const int cols = B.cols[m], group = B.group[m], k = B.k[m];
+    const uint32_t* __restrict__ pl = B.planes[m];
+    const float* __restrict__ lvk = B.lvk[m];
+    uint16_t* __restrict__ out = B.w[m];
+    const size_t pstride = B.pstride[m];
+    const size_t n = size_t(B.rows[m]) * cols;
+    const size_t n_tiles = (n + kDqTile - 1) / kDqTile;
+    for (size_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+        const size_t i_begin = t * kDqTile, i_end = std::min(n, i_begin + kDqTile);
+        // weight i is in block i / group (blocks row-major over (row, group):
+        // a row holds a whole number of blocks)
+        const size_t b0 = i_begin / group, b1 = (i_end - 1) / group + 1;
+        const float* src = lvk + (b0 << k);
+        // deep tables are read where they lie: a tile touches a small part
+        // of each, and staging them whole would cost more than it saves
+        const bool staged = k <= kDqStagedK;
+        if (staged) {
+            const size_t n_tab = (b1 - b0) << k;
+            for (size_t q = threadIdx.x; q < n_tab; q += kBlock) tabs[q] = src[q];
+        }
+        __syncthreads();
+        const size_t i0 = i_begin + size_t(threadIdx.x) * 8;
+        if (i0 < i_end) {
+            const size_t word = i0 / 32;
+            const int sh = int(i0 % 32);
+            uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            for (int p = 0; p < k; ++p) {
+                const uint32_t bits = (pl[size_t(p) * pstride + word] >> sh) & 0xFFu;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = (v[j] << 1) | ((bits >> j) & 1u);
+            }
+            const size_t at = (i0 / group - b0) << k;
+            float node[8];
+            if (staged) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) node[j] = tabs[at + v[j]];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) node[j] = src[at + v[j]];
+            }
+            uint32_t q[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t lo = __half_as_ushort(__float2half_rn(node[2 * j]));
+                const uint32_t hi = __half_as_ushort(__float2half_rn(node[2 * j + 1]));
+                q[j] = lo | (hi << 16);
+            }
+            *reinterpret_cast<uint4*>(out + i0) = uint4{q[0], q[1], q[2], q[3]};
+        }
+        __syncthreads();
+    }
 }
 
 inline unsigned grid_for(size_t n, int per) { return unsigned((n + per - 1) / per); }
@@ -1111,6 +1198,32 @@ hipError_t launch_dequant(int rows, int cols, int group, int k, const uint32_t* 
     hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(size_t(rows) * cols, kBlock)),
                        dim3(kBlock), 0, st, rows, cols, group, k, planes, pstride, levels,
                        out32, out16);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_batch(const KDequantBatch& B, size_t max_elems, hipStream_t st) {
+    if (B.n == 0 || max_elems == 0) return hipSuccess;
+    // LDS for the tables of the most blocks a tile can touch, at the deepest
+    // staged k (up to 8.1 KiB: group 32 at k = 5)
+    size_t lds = 0;
+    for (int m = 0; m < B.n; ++m)
+        if (B.k[m] <= kDqStagedK)
+            lds = std::max(lds, (size_t(kDqTile / B.group[m] + 1) << B.k[m]) * sizeof(float));
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(dequant_batch_kernel),
+        hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
+    if (attr != hipSuccess) return attr;
+    // a workgroup per tile: the hardware starts the next as one ends, which
+    // hides the latency of a tile's loads better than a loop over tiles
+    const unsigned bx = unsigned(std::min<size_t>((max_elems + kDqTile - 1) / kDqTile, 1u << 20));
+    hipLaunchKernelGGL(dequant_batch_kernel, dim3(bx, unsigned(B.n)), dim3(kBlock), lds, st, B);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_fp16_batch(const KGemv16Batch& B, int max_rows, hipStream_t st) {
+    if (B.n == 0 || max_rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(gemv_fp16_batch_kernel, dim3(grid_for(max_rows, kRowsPerBlock), unsigned(B.n)),
+                       dim3(kBlock), 0, st, B);
     return hipGetLastError();
 }
 

@@ -359,7 +359,11 @@ pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, int top_k,
  * The materialize-then-multiply comparator [T c37; Met]:
  *   pm_materialize_fp16: d_w_fp16 uint16 [rows][cols], the depth-k node
  *                        rounded to fp16 (nearest even).
- *   pm_gemv_fp16:        y[o] = sum_i fp16 W[o][i] * x[i] (fp32 sums). */
+ *   pm_gemv_fp16:        y[o] = sum_i fp16 W[o][i] * x[i] (fp32 sums).
+ *   The _batch forms do the same for n <= 64 matrices in one launch, with
+ *   the same results bit for bit; their arrays (shapes, ks, strides and the
+ *   device pointers) are host memory.  Outputs and fp16 weight rows must be
+ *   16-byte aligned (PM_ERR_ARG otherwise). */
 pm_status pm_debug_unpack_prefix(pm_matrix_shape s, int k, const uint32_t* d_planes,
                                  size_t plane_stride_words, uint8_t* d_prefix_out,
                                  void* stream);
@@ -369,6 +373,13 @@ pm_status pm_debug_dequant(pm_matrix_shape s, int k, const uint32_t* d_planes,
 pm_status pm_materialize_fp16(pm_matrix_shape s, int k, const uint32_t* d_planes,
                               size_t plane_stride_words, const float* d_levels,
                               uint16_t* d_w_fp16, void* stream);
+pm_status pm_materialize_fp16_batch(int n, const pm_matrix_shape* shapes, const int* ks,
+                                    const uint32_t* const* d_planes,
+                                    const size_t* plane_stride_words,
+                                    const float* const* d_levels, uint16_t* const* d_w_fp16,
+                                    void* stream);
+pm_status pm_gemv_fp16_batch(int n, const pm_matrix_shape* shapes, const uint16_t* const* d_w,
+                             const float* const* d_x, float* const* d_y, void* stream);
 pm_status pm_gemv_fp16(pm_matrix_shape s, const uint16_t* d_w, const float* d_x, float* d_y,
                        void* stream);
 

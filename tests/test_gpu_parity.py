@@ -252,6 +252,35 @@ def test_lut_gemv_all_k(rows, cols):
         assert np.array_equal(M.gemv(k, xd).view(np.uint32), got.view(np.uint32))
 
 
+def test_comparator_batches_match_single_calls():
+    """One dequant launch and one fp16 GEMV launch over several matrices of
+    different shapes, groups and prefixes give the single calls' bits."""
+    report("batched materialize-fp16 and fp16 GEMV vs single calls")
+    mats = [DevMatrix(64, 4096, 128, unit=41), DevMatrix(256, 1024, 128, unit=42),
+            DevMatrix(40, 2048, 64, unit=43), DevMatrix(8, 512, 32, unit=44)]
+    ks = [1, 3, 5, 8]
+    shapes = [M.sh for M in mats]
+    outs = [torch.empty(M.sh.rows * M.sh.cols, dtype=torch.int16, device="cuda") for M in mats]
+    pm.pm_materialize_fp16_batch(shapes, ks, [M.dp for M in mats], [M.pw for M in mats],
+                                 [M.dl for M in mats], outs)
+    xs = [dev(synth.activation(14, 0, 0, i, M.sh.cols)) for i, M in enumerate(mats)]
+    ys = [torch.full((M.sh.rows,), 5.0, dtype=torch.float32, device="cuda") for M in mats]
+    pm.pm_gemv_fp16_batch(shapes, outs, xs, ys)
+    for i, (M, k) in enumerate(zip(mats, ks)):
+        one = torch.empty_like(outs[i])
+        pm.pm_materialize_fp16(M.sh, k, M.dp, M.pw, M.dl, one)
+        assert torch.equal(one, outs[i]), i
+        y1 = torch.empty_like(ys[i])
+        pm.pm_gemv_fp16(M.sh, one, xs[i], y1)
+        assert np.array_equal(host(y1).view(np.uint32), host(ys[i]).view(np.uint32)), i
+        # and the fp16 weights are the oracle's: the depth-k node rounded to nearest even
+        rows = np.arange(0, M.sh.rows, 7)
+        want = oracle.dequant(oracle.pack_planes(M.cd[rows]), oracle.tree_levels(M.lv[rows]), k,
+                              M.group).astype(np.float16)
+        got = host(outs[i]).view(np.float16).reshape(M.sh.rows, M.sh.cols)[rows]
+        assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), i
+
+
 def test_lut_gemv_onehot_and_poison():
     report("LUT-path one-hot columns and poisoned planes/levels")
     M = DevMatrix(40, 2048, 128, unit=3)

@@ -399,3 +399,25 @@ def test_noalloc_gemv_validation_before_any_hip_call():
         assert ei.value.status == pm.PM_ERR_SHAPE, (rows, cols)
         assert b"scratch" in pm.lib().pm_last_error()
     pm.pm_expert_gemv_noalloc(pm.mshape(0, 64, 32), 3, None, 0, None, None, None)
+
+
+def test_comparator_batches_validate_before_any_hip_call():
+    s = pm.mshape(64, 256, 128)
+    with pytest.raises(pm.PMError) as ei:                     # more than 64 matrices
+        pm.pm_materialize_fp16_batch([s] * 65, [2] * 65, [16] * 65, [512] * 65, [16] * 65,
+                                     [16] * 65)
+    assert ei.value.status == pm.PM_ERR_ARG
+    with pytest.raises(pm.PMError) as ei:                     # k out of range in the 2nd
+        pm.pm_materialize_fp16_batch([s, s], [2, 9], [16, 16], [512, 512], [16, 16], [16, 16])
+    assert ei.value.status == pm.PM_ERR_PREFIX
+    with pytest.raises(pm.PMError) as ei:                     # output not 16-byte aligned
+        pm.pm_materialize_fp16_batch([s], [2], [16], [512], [16], [24])
+    assert ei.value.status == pm.PM_ERR_ARG
+    with pytest.raises(pm.PMError) as ei:                     # rows of 100 columns: 200 bytes
+        pm.pm_gemv_fp16_batch([pm.mshape(4, 100, 4)], [16], [16], [16])
+    assert ei.value.status in (pm.PM_ERR_ARG, pm.PM_ERR_SHAPE)
+    with pytest.raises(pm.PMError) as ei:
+        pm.pm_gemv_fp16_batch([s], [None], [16], [16])
+    assert ei.value.status == pm.PM_ERR_ARG
+    pm.pm_materialize_fp16_batch([], [], [], [], [], [])      # an empty batch is a no-op
+    pm.pm_gemv_fp16_batch([pm.mshape(0, 256, 128)], [None], [None], [None])
