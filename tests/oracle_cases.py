@@ -14,7 +14,7 @@ def _wl(w):
     return synth.WORKLOADS[w] if isinstance(w, int) else w
 
 
-@lru_cache(maxsize=32)
+@lru_cache(maxsize=64)
 def gate_up(cfg, layer, expert):
     """Oracle-encoded gate and up matrices of one seeded expert (cfg is a
     workload index or a Workload)."""
@@ -41,6 +41,22 @@ def down_rows(cfg, layer, expert, rows):
     return oracle.pack_planes(cd), oracle.tree_levels(lv)
 
 
+@lru_cache(maxsize=48)
+def gate_up_dense(cfg, layer, expert, m, k):
+    """oracle.dequant of gate (m = 0) or up (m = 1) at prefix k: float32
+    [rows][cols], exact node values (kept for the many tokens of a batch)."""
+    p, lv = gate_up(cfg, layer, expert)[m]
+    return oracle.dequant(p, lv, k, _wl(cfg).group)
+
+
+def _gemv_gate_up(cfg, layer, expert, m, k, x):
+    # oracle.gemv written out on the cached dequantized matrix: the same fp64
+    # products and sums
+    w = gate_up_dense(cfg, layer, expert, m, k).astype(np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    return w @ x, np.abs(w) @ np.abs(x)
+
+
 def token_layer(cfg, layer, ids, w, k, x, rows, materialized=False):
     """Oracle y[rows] and its error scale for one token of one layer.
     k: int [top_k][3] prefixes of gate, up, down."""
@@ -50,9 +66,13 @@ def token_layer(cfg, layer, ids, w, k, x, rows, materialized=False):
     y = np.zeros(len(rows))
     S = np.zeros(len(rows))
     for j in range(len(ids)):
-        (pg, lg), (pu, lu) = gate_up(cfg, layer, int(ids[j]))
-        g, _ = gemv(pg, lg, int(k[j][0]), G, x)
-        u, _ = gemv(pu, lu, int(k[j][1]), G, x)
+        if materialized:
+            (pg, lg), (pu, lu) = gate_up(cfg, layer, int(ids[j]))
+            g, _ = gemv(pg, lg, int(k[j][0]), G, x)
+            u, _ = gemv(pu, lu, int(k[j][1]), G, x)
+        else:
+            g, _ = _gemv_gate_up(cfg, layer, int(ids[j]), 0, int(k[j][0]), x)
+            u, _ = _gemv_gate_up(cfg, layer, int(ids[j]), 1, int(k[j][1]), x)
         h = oracle.silu(g) * u
         pd, ld = down_rows(cfg, layer, int(ids[j]), rows)
         yd, sd = gemv(pd, ld, int(k[j][2]), G, h)

@@ -572,22 +572,20 @@ def test_forward_batch8_grouped_with_topup():
     for i in short:
         assert pm.pm_store_resident(st, 0, i) == kmax[i]
     # each token of the batch equals that token run alone: bit for bit when
-    # none of its experts is shared (same kernels, same order), else within
-    # the tolerance (a shared expert is read once on the direct path)
+    # none of its experts is shared (same kernels, same order); otherwise
+    # (a shared expert's uses grouped) both within the oracle's per-output
+    # bound
     counts = {i: int((ids == i).sum()) for i in distinct}
+    rows = oc.sample_rows(wl.hidden, 8, 10)
     for t in range(B):
         y1 = torch.empty((1, wl.hidden), dtype=torch.float32, device="cuda")
         pm.pm_moe_token_forward(st, 0, ids[t:t + 1], w[t:t + 1], k[t:t + 1], xd[t:t + 1], y1)
         alone = host(y1)[0]
         if all(counts[int(i)] == 1 for i in ids[t]):
             assert np.array_equal(alone.view(np.uint32), got[t].view(np.uint32)), t
-        else:
-            scale = np.abs(alone) + np.abs(got[t])
-            assert np.all(np.abs(alone - got[t]) <= 1e-4 * scale.max() + 1e-6), t
-    for t in (0, 3):
-        rows = oc.sample_rows(wl.hidden, 12, 10 + t)
         want, S = oc.token_layer(4, 0, ids[t], w[t], k[t], x[t], rows)
-        assert_close(got[t][rows], want, S, f"token {t}")
+        assert_close(got[t][rows], want, S, f"token {t} in the batch")
+        assert_close(alone[rows], want, S, f"token {t} alone")
     st.close()
 
 
@@ -618,17 +616,14 @@ def test_read_once_matches_default():
         y = torch.empty((B, wl.hidden), dtype=torch.float32, device="cuda")
         pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y, flags=flags)
         out[name] = host(y)
+    rows = oc.sample_rows(wl.hidden, 8, 30)
     for t in range(B):
         a, b = out["default"][t], out["read_once"][t]
         if all(counts[int(i)] == 1 for i in ids[t]):
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), t
-        else:
-            assert np.all(np.abs(a - b) <= 1e-4 * np.abs(a).max() + 1e-6), t
-    shared_t = next(t for t in range(B) if any(counts[int(i)] > 1 for i in ids[t]))
-    rows = oc.sample_rows(wl.hidden, 12, 30)
-    want, S = oc.token_layer(4, 0, ids[shared_t], w[shared_t], k[shared_t], x[shared_t], rows)
-    for name in out:
-        assert_close(out[name][shared_t][rows], want, S, f"{name}, token {shared_t}")
+        want, S = oc.token_layer(4, 0, ids[t], w[t], k[t], x[t], rows)
+        for name in out:
+            assert_close(out[name][t][rows], want, S, f"{name}, token {t}")
     st.close()
 
 
@@ -744,10 +739,11 @@ def test_topup_into_an_unallocated_slot(mfma):
     want_res = [int(k[ids == i].max()) for i in range(n_exp)]
     assert want_res[0] == 8
     assert [pm.pm_store_resident(st, 0, i) for i in range(n_exp)] == want_res
+    # the donor store holds the same planes: the same launches, the same bits
     y_ref = torch.empty_like(y)
     pm.pm_moe_token_forward(donor, 0, ids, w, k, xd, y_ref, flags=flags & ~pm.PM_AUTO_TOPUP)
     ref = host(y_ref)
-    assert np.all(np.abs(got - ref) <= 1e-4 * (np.abs(ref).max(axis=1, keepdims=True) + 1e-3))
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
     rows = oc.sample_rows(wl.hidden, 12, 21)
     for t in range(B):
         want, S = oc.token_layer(1, 0, ids[t], w[t], k[t], x[t], rows)
