@@ -1311,7 +1311,7 @@ static void cut_jobs(KLaunch& L, int j0, int j1, int n_wg, int w0) {
     const int n = j1 - j0, rows = L.rows, pairs = rows / kLutRows;
     std::vector<int64_t> pc(n), before(n + 1, 0);
     for (int j = 0; j < n; ++j) {
-        pc[j] = kLutRows * lut_row_cost(L.job[j0 + j].k, L.wpg);
+        pc[j] = lut_step_ns(L.job[j0 + j].k);
         before[j + 1] = before[j] + pc[j] * pairs;
     }
     const int64_t total = before[n];
@@ -1326,10 +1326,12 @@ static void cut_jobs(KLaunch& L, int j0, int j1, int n_wg, int w0) {
 }
 
 // Workgroup ranges of a launch whose jobs come in runs of one source (one
-// activation table) and one prefix: every run gets whole workgroups, in
-// proportion to its cost (largest remainder, at least one each), and no
-// workgroup spans two runs, so a workgroup builds its table once and runs
-// one prefix's code throughout.
+// activation table) and one prefix: every run gets whole workgroups (largest
+// remainder, at least one each), and no workgroup spans two runs, so a
+// workgroup builds its table once and runs one prefix's code throughout.
+// The shares balance the modelled workgroup time, fixed part plus steps:
+// run r with C_r ns of steps at fixed part A_r gets C_r / (T - A_r)
+// workgroups, T chosen so that the shares add up to the workgroups there are.
 static void set_starts_by_source(KLaunch& L, int n_total) {
     const int n = L.n_jobs;
     std::vector<int> r0;                       // first job of every run
@@ -1339,17 +1341,32 @@ static void set_starts_by_source(KLaunch& L, int n_total) {
     const int R = int(r0.size());
     r0.push_back(n);
     n_total = std::min(kMaxLaunchWgq, std::max(n_total, R));
-    std::vector<double> cost(R, 0.0), share(R);
-    double C = 0;
+    std::vector<double> cost(R, 0.0), fixed(R), share(R);
+    double C = 0, Amax = 0;
     for (int r = 0; r < R; ++r) {
         for (int j = r0[r]; j < r0[r + 1]; ++j)
-            cost[r] += double(L.rows) * double(lut_row_cost(L.job[j].k, L.wpg));
+            cost[r] += double(L.rows / kLutRows) * double(lut_step_ns(L.job[j].k));
+        fixed[r] = double(lut_fixed_ns(L.job[r0[r]].k));
         C += cost[r];
+        Amax = std::max(Amax, fixed[r]);
+    }
+    if (C > 0) {
+        // sum_r cost_r / (T - fixed_r) falls from +inf (T just above Amax) to
+        // below n_total (T = Amax + C): bisection
+        double lo = Amax, hi = Amax + C + 1.0;
+        for (int it = 0; it < 64; ++it) {
+            const double T = 0.5 * (lo + hi);
+            double wgs = 0;
+            for (int r = 0; r < R; ++r) wgs += cost[r] / (T - fixed[r]);
+            (wgs > n_total ? lo : hi) = T;
+        }
+        for (int r = 0; r < R; ++r) share[r] = cost[r] / (hi - fixed[r]);
+    } else {
+        for (int r = 0; r < R; ++r) share[r] = double(n_total) / R;
     }
     std::vector<int> a(R);
     int sum = 0;
     for (int r = 0; r < R; ++r) {
-        share[r] = C > 0 ? n_total * cost[r] / C : double(n_total) / R;
         a[r] = std::max(1, int(share[r]));
         sum += a[r];
     }

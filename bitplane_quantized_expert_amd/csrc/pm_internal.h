@@ -124,12 +124,23 @@ struct KLaunch {
     KJob job[kMaxLaunchJobs];
 };
 static_assert(sizeof(KLaunch) <= 4096, "kernel arguments are limited to 4 KiB");
-// Cost of one row-slice (1024 columns) when rows are split among
-// workgroups: the time of one 8-row step of a workgroup at prefix k, measured
-// on gfx950 (ns; the rows of one launch streamed from HBM), divided by 8.
-__host__ __device__ inline int64_t lut_row_cost(int k, int /*wpg*/) {
-    constexpr int64_t ns8[6] = {0, 97, 143, 225, 420, 800};
-    return ns8[k < 1 ? 1 : (k > 5 ? 5 : k)];
+// Cost model of a LUT workgroup (one 1024-column slice), fitted on gfx950 to
+// the compute phase of workgroups of the 512-expert layer step (rows
+// streamed from HBM): a fixed part per workgroup at prefix k (the latency of
+// its first and last steps) plus a part per 8-row step, both in ns.
+#ifndef PM_LUT_FIXED
+#define PM_LUT_FIXED 1600, 1200, 2000, 3200, 2900
+#endif
+#ifndef PM_LUT_STEP
+#define PM_LUT_STEP 63, 131, 223, 416, 847
+#endif
+__host__ __device__ inline int64_t lut_step_ns(int k) {
+    constexpr int64_t ns[5] = {PM_LUT_STEP};
+    return ns[k < 1 ? 0 : (k > 5 ? 4 : k - 1)];
+}
+__host__ __device__ inline int64_t lut_fixed_ns(int k) {
+    constexpr int64_t ns[5] = {PM_LUT_FIXED};
+    return ns[k < 1 ? 0 : (k > 5 ? 4 : k - 1)];
 }
 
 // Kernel launchers (pm_kernels.hip).  All return hipError_t of the launch.
