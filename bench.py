@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 METRIC = "achieved HBM GB/s (% of peak) + expert-GEMVs/s at avg 2.5-bit prefixes"
 PEAK_HBM_GBS = 8000.0
 # Device code whose HBM traffic the counters below describe.
-KERNEL_SOURCES = ("bitplane_quantized_expert_amd/csrc/pm_kernels.hip",
+KERNEL_SOURCES = ("bitplane_quantized_expert_amd/csrc/pm_lut.hip",
+                  "bitplane_quantized_expert_amd/csrc/pm_device.h",
                   "bitplane_quantized_expert_amd/csrc/pm_internal.h")
 # HBM bytes per gate/up launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
 # passes of this benchmark, each scaled by the same counter on the 1 GiB

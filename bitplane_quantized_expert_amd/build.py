@@ -21,7 +21,8 @@ COMPILE_FLAGS = [
 TARGETS = [
     (os.path.join(PKG, "libpm.so"),
      [os.path.join(PKG, "csrc", "pm_host.cpp"), os.path.join(PKG, "csrc", "pm_cache.cpp"),
-      os.path.join(PKG, "csrc", "pm_kernels.hip"), os.path.join(PKG, "csrc", "pm_encoder.hip"),
+      os.path.join(PKG, "csrc", "pm_kernels.hip"), os.path.join(PKG, "csrc", "pm_lut.hip"),
+      os.path.join(PKG, "csrc", "pm_encoder.hip"),
       os.path.join(PKG, "csrc", "pm_mfma.hip")]),
     (os.path.join(ROOT, "synth", "libpmsynth.so"),
      [os.path.join(ROOT, "synth", "synth_device.hip")]),
@@ -29,9 +30,10 @@ TARGETS = [
 
 # Per-source extra flags.  The LUT kernels issue many independent table
 # lookups per step; the machine scheduler's ILP strategy keeps them in flight
-# instead of interleaving each with its use.
+# instead of interleaving each with its use.  (The same strategy makes the
+# direct kernels about twice as slow, so they stay in another source.)
 EXTRA = {
-    "pm_kernels.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "pm_lut.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
 

@@ -136,7 +136,7 @@ def test_mfma_full_layer_batch(store512):
     y1 = torch.empty_like(y)
     pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y1, flags=0)
     ref = host(y1)
-    check_tokens({"mfma": got, "default": ref}, ids, w, k, x, range(0, B, 6),
+    check_tokens({"mfma": got, "default": ref}, ids, w, k, x, range(0, B, 12),
                  oc.sample_rows(wl.hidden, 6, 16))
 
 
@@ -228,7 +228,7 @@ def test_default_path_large_batch(store512):
     y1 = torch.empty_like(y)
     pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y1, flags=pm.PM_BATCH_MFMA)
     ref = host(y1)
-    check_tokens({"default": got, "mfma": ref}, ids, w, k, x, range(0, B, 43),
+    check_tokens({"default": got, "mfma": ref}, ids, w, k, x, range(0, B, 100),
                  oc.sample_rows(wl.hidden, 6, 17))
 
 
