@@ -856,18 +856,50 @@ static pm_status arena_alloc(pm_store* s, size_t bytes, char** out) {
 
 // Take the range right after [p, p + old_len) so that the range spans
 // new_len bytes, if it is free.
-static bool arena_extend(pm_store* s, char* p, size_t old_len, size_t new_len) {
+static bool arena_extend(pm_store* s, char* p, size_t have, size_t want) {
     Arena* a = arena_of(s, p);
     if (!a) return false;
-    const size_t end = size_t(p - a->base) + range_len(old_len);
-    const size_t need = range_len(new_len) - range_len(old_len);
-    if (need == 0) return true;
+    if (want <= have) return true;
+    const size_t end = size_t(p - a->base) + have, need = want - have;
     auto it = a->free.find(end);
     if (it == a->free.end() || it->second < need) return false;
     const size_t rest = it->second - need;
     a->free.erase(it);
     if (rest) a->free.emplace(end + need, rest);
     return true;
+}
+
+// Take back ranges given back right after [p, p + *have) while they still
+// wait in `released` (most often the slot's own tail, cut by a truncation
+// whose readers have not ended), up to `want` bytes: `st` waits for their
+// last copy and reader instead of the slot moving.  *have grows by what was
+// taken.
+static pm_status take_back_tail(pm_store* s, char* p, size_t* have, size_t want, hipStream_t st) {
+    if (s->host_fake) return PM_OK;
+    for (bool found = true; found && *have < want;) {
+        found = false;
+        for (size_t i = 0; i < s->released.size(); ++i) {
+            Released& r = s->released[i];
+            if (r.p != p + *have) continue;
+            const size_t take = std::min(r.len, want - *have);
+            if (r.ev) HIP_TRY(hipStreamWaitEvent(st, r.ev, 0));
+            if (r.reader) {
+                const hipEvent_t end = forward_end(s, r.reader);
+                if (hipEventQuery(end) != hipSuccess) HIP_TRY(hipStreamWaitEvent(st, end, 0));
+            }
+            if (take == r.len) {
+                if (r.ev) s->spare_events.push_back(r.ev);
+                s->released.erase(s->released.begin() + long(i));
+            } else {
+                r.p += take;
+                r.len -= take;
+            }
+            *have += take;
+            found = true;
+            break;
+        }
+    }
+    return PM_OK;
 }
 
 // Make `st` wait for the last forward that read the slot (unless it has
@@ -897,19 +929,29 @@ static pm_status resize_planes(pm_store* s, Slot& sl, int cap, int keep, hipStre
         r = release_range(s, p + keep_len, range_len(old_len) - keep_len, st, sl.read_seq);
         if (r) return r;
         if (cap == 0) sl.planes = nullptr;
-    } else if (!(p && arena_extend(s, p, old_len, new_len))) {
-        char* nb = nullptr;
-        r = arena_alloc(s, new_len, &nb);
-        if (r) return r;
-        if (keep > 0) {
-            if (s->host_fake)
-                std::memcpy(nb, p, size_t(keep) * pb);
-            else
-                HIP_TRY(hipMemcpyAsync(nb, p, size_t(keep) * pb, hipMemcpyDeviceToDevice, st));
+    } else {
+        // grow in place (ranges given back right after the slot, then free
+        // arena space), else move the kept prefix to a new range
+        size_t have = range_len(old_len);
+        const size_t want = range_len(new_len);
+        if (p) {
+            r = take_back_tail(s, p, &have, want, st);
+            if (r) return r;
         }
-        r = release_range(s, p, range_len(old_len), st, sl.read_seq);
-        if (r) return r;
-        sl.planes = reinterpret_cast<uint32_t*>(nb);
+        if (!(p && arena_extend(s, p, have, want))) {
+            char* nb = nullptr;
+            r = arena_alloc(s, new_len, &nb);
+            if (r) return r;
+            if (keep > 0) {
+                if (s->host_fake)
+                    std::memcpy(nb, p, size_t(keep) * pb);
+                else
+                    HIP_TRY(hipMemcpyAsync(nb, p, size_t(keep) * pb, hipMemcpyDeviceToDevice, st));
+            }
+            r = release_range(s, p, have, st, sl.read_seq);
+            if (r) return r;
+            sl.planes = reinterpret_cast<uint32_t*>(nb);
+        }
     }
     s->used = s->used - old_len + new_len;
     sl.cap = cap;
