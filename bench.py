@@ -875,6 +875,35 @@ def main():
                 **{f"p{q}": round(float(np.percentile(us, q)), 2) for q in (10, 50, 90)}}
 
     step_dist = pct(boundary_pass(list(steps)))
+    # host time of one call, with the device queue kept short (a sync every 8
+    # calls, so that no call waits for queue space): the C entry point with
+    # the argument addresses worked out beforehand (as a caller that owns its
+    # buffers makes it), and the numpy binding
+    ids_c, w_c, k_c = (np.ascontiguousarray(a) for a in (ids, w, k3))
+    tk = wl.top_k
+    a_ids, a_w, a_k = ids_c.ctypes.data, w_c.ctypes.data, k_c.ctypes.data
+    a_x, a_y, row = x.data_ptr(), y.data_ptr(), 4 * wl.hidden
+    sh = stream.cuda_stream
+
+    def raw(s):
+        pm.pm_moe_token_forward_ptr(st, 0, 1, tk, a_ids + 4 * tk * s, a_w + 4 * tk * s,
+                                    a_k + 3 * tk * s, a_x + row * s, a_y + row * s, sh)
+
+    def host_pass(fn):
+        d = []
+        for i, s in enumerate(steps):
+            if i % 8 == 0:
+                torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn(s)
+            d.append(time.perf_counter() - t0)
+        torch.cuda.synchronize()
+        return pct(np.array(d) * 1e6)
+
+    host_raw = host_pass(raw)
+    host_binding = host_pass(run)
+    log(f"host time per call: C entry {host_raw['mean']} us (p50 {host_raw['p50']}), "
+        f"numpy binding {host_binding['mean']} us")
     # one step alone (GPU idle before it, its own events), cold and warm:
     # cold after 512 MiB of writes that evict the 256 MB Infinity Cache,
     # warm right after the same step ran (its experts' planes cached)
@@ -923,7 +952,12 @@ def main():
                    "inter": wl.inter, "group": wl.group, "top_k": wl.top_k, "batch": 1,
                    "mean_k": round(float(kk[args.warmup:].mean()), 4), "pool_experts": n_exp},
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
-        "host_issue_us_per_step": round(issued / args.steps * 1e6, 2),
+        "host_issue_us_per_step": host_raw["mean"],
+        "host_issue": {"c_entry_us": host_raw, "numpy_binding_us": host_binding,
+                       "timed_loop_issue_us_per_step": round(issued / args.steps * 1e6, 2),
+                       "how": "wall time of one call on the host, the device queue kept short "
+                              "(a sync every 8 calls); the timed loop's figure includes waits "
+                              "for queue space once the device falls behind"},
         "expert_gemvs_per_s": round(3 * wl.top_k * args.steps / el, 1),
         "step_us": step_dist,
         "cache_state": cache_state,

@@ -502,6 +502,17 @@ def pm_cache_stats(cache):
                     (x.value for x in v)))
 
 
+def pm_moe_token_forward_ptr(store, layer, n_tokens, top_k, ids_addr, w_addr, k_addr, x_addr,
+                             y_addr, stream=None, flags=0):
+    """pm_moe_token_forward on buffers given by address (ints), passed through
+    unchanged: host int32 ids[n][top_k], float32 w[n][top_k],
+    uint8 k[n][top_k][3]; device float32 x, y [n][hidden].  For callers that
+    keep their own buffers (no numpy marshalling per call)."""
+    return _check(lib().pm_moe_token_forward(store.handle, layer, n_tokens, top_k, ids_addr,
+                                             w_addr, k_addr, x_addr, y_addr, _stream(stream),
+                                             flags))
+
+
 def pm_moe_token_forward(store, layer, ids, w, k, d_x, d_y, stream=None, flags=0):
     """ids int32 [n][top_k], w float32 [n][top_k], k uint8 [n][top_k][3] (host);
     d_x, d_y float32 [n][hidden] device tensors."""

@@ -49,6 +49,9 @@ __device__ inline float silu_mul(float g, float u) { return g / (1.0f + expf(-g)
 // registers: arguments of out-of-line functions and values read from LDS
 // arrive in vector registers.
 __device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline float uni_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
 __device__ inline uint64_t uni64(uint64_t v) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
     const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));

@@ -1351,19 +1351,24 @@ struct JobSpec {                       // a LUT job before it is packed into a l
 // equal cost, writing L.start[w0 .. w0 + n_wg - 1].
 static void cut_jobs(KLaunch& L, int j0, int j1, int n_wg, int w0) {
     const int n = j1 - j0, rows = L.rows, pairs = rows / kLutRows;
-    std::vector<int64_t> pc(n), before(n + 1, 0);
+    double pc[kMaxLaunchJobs], before[kMaxLaunchJobs + 1];
+    before[0] = 0;
     for (int j = 0; j < n; ++j) {
-        pc[j] = lut_step_ns(L.job[j0 + j].k);
+        pc[j] = double(lut_step_ns(L.job[j0 + j].k));
         before[j + 1] = before[j] + pc[j] * pairs;
     }
-    const int64_t total = before[n];
+    const double per_wg = before[n] / n_wg;
     L.start[w0] = j0 * rows;
     int j = 0;
+    double inv = 1.0 / pc[0];
     for (int q = 1; q < n_wg; ++q) {
-        const int64_t target = total * q / n_wg;
-        while (j < n - 1 && before[j + 1] <= target) ++j;
-        const int64_t p = (target - before[j] + pc[j] - 1) / pc[j];
-        L.start[w0 + q] = (j0 + j) * rows + int(std::min<int64_t>(rows, kLutRows * p));
+        const double target = per_wg * q;
+        while (j < n - 1 && before[j + 1] <= target) inv = 1.0 / pc[++j];
+        // the first whole step at or past the target
+        const double at = target - before[j];
+        int p = int(at * inv);
+        if (double(p) * pc[j] < at) ++p;
+        L.start[w0 + q] = (j0 + j) * rows + std::min(rows, kLutRows * p);
     }
 }
 
@@ -1376,37 +1381,47 @@ static void cut_jobs(KLaunch& L, int j0, int j1, int n_wg, int w0) {
 // workgroups, T chosen so that the shares add up to the workgroups there are.
 static void set_starts_by_source(KLaunch& L, int n_total) {
     const int n = L.n_jobs;
-    std::vector<int> r0;                       // first job of every run
+    int r0[kMaxLaunchJobs + 1];                // first job of every run
+    int R = 0;
     for (int j = 0; j < n; ++j)
         if (j == 0 || L.job[j].src != L.job[j - 1].src || L.job[j].k != L.job[j - 1].k)
-            r0.push_back(j);
-    const int R = int(r0.size());
-    r0.push_back(n);
+            r0[R++] = j;
+    r0[R] = n;
     n_total = std::min(kMaxLaunchWgq, std::max(n_total, R));
-    std::vector<double> cost(R, 0.0), fixed(R), share(R);
+    double cost[kMaxLaunchJobs], fixed[kMaxLaunchJobs], share[kMaxLaunchJobs];
     double C = 0, Amax = 0;
     for (int r = 0; r < R; ++r) {
-        for (int j = r0[r]; j < r0[r + 1]; ++j)
-            cost[r] += double(L.rows / kLutRows) * double(lut_step_ns(L.job[j].k));
-        fixed[r] = double(lut_fixed_ns(L.job[r0[r]].k));
+        const int k = L.job[r0[r]].k;         // one prefix per run
+        cost[r] = double(r0[r + 1] - r0[r]) * double(L.rows / kLutRows) * double(lut_step_ns(k));
+        fixed[r] = double(lut_fixed_ns(k));
         C += cost[r];
         Amax = std::max(Amax, fixed[r]);
     }
     if (C > 0) {
-        // sum_r cost_r / (T - fixed_r) falls from +inf (T just above Amax) to
-        // below n_total (T = Amax + C): bisection
-        double lo = Amax, hi = Amax + C + 1.0;
-        for (int it = 0; it < 64; ++it) {
-            const double T = 0.5 * (lo + hi);
-            double wgs = 0;
-            for (int r = 0; r < R; ++r) wgs += cost[r] / (T - fixed[r]);
-            (wgs > n_total ? lo : hi) = T;
+        // f(T) = sum_r cost_r / (T - fixed_r) - n_total is convex and falls
+        // from +inf just above Amax.  Newton steps from a point left of the
+        // root (where a run at Amax alone wants 2 n_total workgroups) stay
+        // left of it and converge from there.
+        double cmax = 0;
+        for (int r = 0; r < R; ++r)
+            if (fixed[r] == Amax) cmax = std::max(cmax, cost[r]);
+        double T = Amax + cmax / (2.0 * n_total);
+        for (int it = 0; it < 100; ++it) {
+            double f = -double(n_total), df = 0;
+            for (int r = 0; r < R; ++r) {
+                const double d = 1.0 / (T - fixed[r]);
+                f += cost[r] * d;
+                df -= cost[r] * d * d;
+            }
+            const double step = -f / df;
+            T += step;
+            if (!(step > 1e-9 * T)) break;
         }
-        for (int r = 0; r < R; ++r) share[r] = cost[r] / (hi - fixed[r]);
+        for (int r = 0; r < R; ++r) share[r] = cost[r] / (T - fixed[r]);
     } else {
         for (int r = 0; r < R; ++r) share[r] = double(n_total) / R;
     }
-    std::vector<int> a(R);
+    int a[kMaxLaunchJobs];
     int sum = 0;
     for (int r = 0; r < R; ++r) {
         a[r] = std::max(1, int(share[r]));
@@ -1442,7 +1457,7 @@ static void set_starts_by_source(KLaunch& L, int n_total) {
 
 // Pack jobs into launches of at most kMaxLaunchJobs, cut by source
 // (set_starts_by_source); jobs of one source should be adjacent.
-static void pack_launches(std::vector<JobSpec>& js, const KLaunch& proto,
+static void pack_launches(const std::vector<JobSpec>& js, const KLaunch& proto,
                           std::vector<KLaunch>& out) {
     // the launches of one stage run one after another: each takes the whole
     // target (one workgroup per compute unit)
@@ -1857,6 +1872,11 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
             n_tiles += t_gu[0][k].size() + t_gu[1][k].size() + t_dn[k].size();
     }
 
+    auto any_tiles = [](const std::vector<MTile> (&v)[kBits + 1]) {
+        for (const auto& t : v)
+            if (!t.empty()) return true;
+        return false;
+    };
     // ---- path of every (use, matrix) outside the tiles: LUT at k <= 5 when
     // the columns split into 1024-column slices (at most 15), else direct
     // the LUT path takes rows in steps of kLutRows and blocks of kLutGroup
@@ -1968,6 +1988,27 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         });
         pack_launches(js, gu_proto, L_gu[grp]);
     }
+    // The routing-weighted combine folds into the down launches when every
+    // down product runs on the LUT path: each row sum is added, times its
+    // use's weight, into y with a float atomic (y cleared by the first gate/up
+    // launch).  The top-k terms of an output then add up in the order they
+    // arrive; PM_DETERMINISTIC keeps the separate combine, which adds them in
+    // use order.  y may not overlap x (the clearing would race the reads).
+    const size_t xy_bytes = sizeof(float) * size_t(n_tokens) * g.hidden;
+    const bool xy_apart = reinterpret_cast<uintptr_t>(d_y) + xy_bytes <=
+                              reinterpret_cast<uintptr_t>(d_x) ||
+                          reinterpret_cast<uintptr_t>(d_x) + xy_bytes <=
+                              reinterpret_cast<uintptr_t>(d_y);
+    const bool fold = !(flags & PM_DETERMINISTIC) && dir_dn.empty() && !any_tiles(t_dn) &&
+                      (!L_gu[0].empty() || !L_gu[1].empty()) && xy_apart &&
+                      size_t(n_tokens) * g.hidden < (size_t(1) << 31);
+    if (fold) {
+        KLaunch& first = !L_gu[0].empty() ? L_gu[0].front() : L_gu[1].front();
+        first.zero = d_y;
+        first.n_zero = n_tokens * g.hidden;
+        dn_proto.fold = 1;
+        dn_proto.out_stride = 0;
+    }
     {
         std::vector<JobSpec> js;
         for (int i = 0; i < n_items; ++i) {
@@ -1980,7 +2021,9 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
                 j.job.planes = sl.planes + g.plane_off[2];
                 j.job.lvk = sl.levels + g.level_off[2] +
                             level_offset(size_t(g.hidden) * (g.inter / g.group), k);
-                j.job.out = P.y + size_t(u) * S_dn * g.hidden;
+                j.job.out = fold ? d_y + size_t(uses[u].tok) * g.hidden
+                                 : P.y + size_t(u) * S_dn * g.hidden;
+                j.job.wt = uses[u].w;
                 j.job.src = int16_t(u);
                 j.job.k = int8_t(k);
                 j.job.gsl = uint8_t(uses[u].slices[0] | (uses[u].slices[1] << 4));
@@ -2067,11 +2110,6 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         TL.down = down;
         return launch_tiles(TL, dtiles, off, v, compute);
     };
-    auto any_tiles = [](const std::vector<MTile> (&v)[kBits + 1]) {
-        for (const auto& t : v)
-            if (!t.empty()) return true;
-        return false;
-    };
     const size_t d_gu0 = dir_gu[0].size(), d_gu1 = dir_gu[1].size();
 
     // ---- kernels
@@ -2126,7 +2164,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     for (const KLaunch& L : L_dn) HIP_TRY(launch_lut(L, true, compute));
     if (s->profiling && s->n_prof >= 4) HIP_TRY(hipEventRecord(s->prof[2], compute));
     const int tok_per = std::max(1, kMaxLaunchUses / top_k);
-    for (int t0 = 0; t0 < n_tokens; t0 += tok_per) {
+    for (int t0 = 0; !fold && t0 < n_tokens; t0 += tok_per) {
         KCombine C{};
         C.Y = P.y;
         C.y = d_y;

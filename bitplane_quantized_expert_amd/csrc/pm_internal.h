@@ -98,7 +98,7 @@ struct KJob {                      // one matrix of one use
     const uint32_t* planes;        // plane 0, row 0
     const float* lvk;              // depth-k nodes
     float* out;                    // row r, slice s -> out[s * out_stride + r]
-    int32_t pad;
+    float wt;                      // down with the combine folded in: routing weight
     int16_t src;                   // gate/up: token; down: use
     int8_t k;
     uint8_t gsl;                   // down: gate slices (bits 0-3), up slices (bits 4-7)
@@ -113,10 +113,14 @@ struct KLaunch {
     const float* x;                // gate/up: activation of token t at x + t * x_stride
                                    // (x_stride 0: every job reads x itself)
     const float* gu;               // down: gate/up partials [use][2][gu_smax][inter]
+    float* zero;                   // gate/up: n_zero floats to clear (the layer output
+                                   // that a folded down launch adds into)
     uint64_t pstride;              // words between planes
     int32_t n_jobs, n_wgq, S, rows;
     int32_t W, wpg, out_stride, x_stride;
-    int32_t gu_smax, inter, pad0, pad1;
+    int32_t gu_smax, inter, n_zero;
+    int32_t fold;                  // down: add wt * row sum into out (float atomics)
+                                   // instead of storing the partial
     int32_t start[kMaxLaunchWgq + 2];
     // per row range q: activation source (bits 0-15: token or use), prefix k
     // (bits 16-19), gate/up slice counts of a down job (bits 24-31)

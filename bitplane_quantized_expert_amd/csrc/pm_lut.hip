@@ -108,6 +108,7 @@ struct StepAt {
     const uint32_t* planes;
     const float* nodes;
     float* out;
+    float wt;                  // the job's routing weight (a folded down launch)
 };
 
 // Lane byte offsets that stay fixed through a launch: the plane words and
@@ -377,7 +378,7 @@ struct LutCtx {
     int wave, lane;
 };
 
-template <bool DOWN, int K>
+template <bool DOWN, bool FOLD, int K>
 __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L, LutCtx c,
                                                                lds_float* tab, uint32_t* ready,
                                                                uint32_t* next) {
@@ -397,6 +398,7 @@ __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L,
     const uint32_t* cpl = uni_ptr(L.job[cj].planes);
     const float* clv = uni_ptr(L.job[cj].lvk);
     float* cout = uni_ptr(L.job[cj].out);
+    float cwt = FOLD ? uni_f(L.job[cj].wt) : 0.f;
     const size_t out_off = size_t(c.slice) * L.out_stride;
     auto at = [&](int s) {
         const int gr = c.g0 + 8 * s;
@@ -406,12 +408,14 @@ __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L,
             cpl = uni_ptr(L.job[cj].planes);
             clv = uni_ptr(L.job[cj].lvk);
             cout = uni_ptr(L.job[cj].out);
+            if (FOLD) cwt = uni_f(L.job[cj].wt);
         }
         const int row0 = gr - (cend - rows);
         StepAt a;
         a.planes = cpl + size_t(row0) * W + w0;
         a.nodes = clv + ((size_t(row0) * ng + (w0 >> 2)) << K);
         a.out = cout + out_off + row0;
+        a.wt = cwt;
         return a;
     };
     constexpr int D = lut_ring<K>();
@@ -476,9 +480,13 @@ __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L,
             const bool ok = sv[d] < nsteps;
             float acc = 0.f;
             if (ok) acc = row8_sum(step_compute<K>(buf[d], LL));
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc),
-                                                  buffer_of(sat[d].out, ok ? 32u : 0u),
-                                                  int(so), 0, 0);
+            if (FOLD)      // the routing-weighted combine: y[row] += w * row sum
+                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                    acc * sat[d].wt, buffer_of(sat[d].out, ok ? 32u : 0u), int(so), 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc),
+                                                      buffer_of(sat[d].out, ok ? 32u : 0u),
+                                                      int(so), 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             fill(d);
             __builtin_amdgcn_sched_barrier(0);
@@ -493,7 +501,7 @@ __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L,
 // so that a workgroup's first reads do not depend on one another.  Job
 // descriptions are read straight from the argument block.
 // One workgroup per compute unit (its table fills the LDS).
-template <bool DOWN>
+template <bool DOWN, bool FOLD>
 __global__ __launch_bounds__(kLutThreads) __attribute__((amdgpu_waves_per_eu(kLutWaves / 4,
                                                                               kLutWaves / 4))) void
 lut_kernel(const KLaunch L) {
@@ -507,6 +515,15 @@ lut_kernel(const KLaunch L) {
         *next = 0u;
         ready[2] = 0u;
     }
+    if (!DOWN) {
+        // clear the output a folded down launch will add into (it runs after
+        // this launch on the same stream)
+        const int nz = L.n_zero;
+        const int nt = int(gridDim.x * gridDim.y) * kLutThreads;
+        for (int i = int(blockIdx.y * gridDim.x + blockIdx.x) * kLutThreads + int(threadIdx.x);
+             i < nz; i += nt)
+            L.zero[i] = 0.f;
+    }
     __syncthreads();
     const int q = blockIdx.x, slice = blockIdx.y;
     const uint32_t meta = L.meta[q];
@@ -515,12 +532,12 @@ lut_kernel(const KLaunch L) {
     LutCtx c{slice, g0, g1, int(meta & 0xFFFFu), int(meta >> 24),
              uni(int(threadIdx.x) / kWave), int(threadIdx.x) % kWave};
     switch ((meta >> 16) & 15) {
-        case 1: lut_body<DOWN, 1>(L, c, (lds_float*)lds_buf, ready, next); break;
-        case 2: lut_body<DOWN, 2>(L, c, (lds_float*)lds_buf, ready, next); break;
-        case 3: lut_body<DOWN, 3>(L, c, (lds_float*)lds_buf, ready, next); break;
-        case 4: lut_body<DOWN, 4>(L, c, (lds_float*)lds_buf, ready, next); break;
+        case 1: lut_body<DOWN, FOLD, 1>(L, c, (lds_float*)lds_buf, ready, next); break;
+        case 2: lut_body<DOWN, FOLD, 2>(L, c, (lds_float*)lds_buf, ready, next); break;
+        case 3: lut_body<DOWN, FOLD, 3>(L, c, (lds_float*)lds_buf, ready, next); break;
+        case 4: lut_body<DOWN, FOLD, 4>(L, c, (lds_float*)lds_buf, ready, next); break;
 #if PM_LUT_THREADS == 512
-        default: lut_body<DOWN, 5>(L, c, (lds_float*)lds_buf, ready, next); break;
+        default: lut_body<DOWN, FOLD, 5>(L, c, (lds_float*)lds_buf, ready, next); break;
 #endif
     }
 }
@@ -541,16 +558,12 @@ hipError_t launch_lut(const KLaunch& L, bool down, hipStream_t st, hipEvent_t t0
                       hipEvent_t t1) {
     if (L.n_jobs == 0 || L.n_wgq == 0) return hipSuccess;
     const dim3 grid(unsigned(L.n_wgq), unsigned(L.S));
-    if (t0 || t1) {
-        if (down)
-            hipExtLaunchKernelGGL(lut_kernel<true>, grid, dim3(kLutThreads), 0, st, t0, t1, 0, L);
-        else
-            hipExtLaunchKernelGGL(lut_kernel<false>, grid, dim3(kLutThreads), 0, st, t0, t1, 0, L);
-    } else if (down) {
-        hipLaunchKernelGGL(lut_kernel<true>, grid, dim3(kLutThreads), 0, st, L);
-    } else {
-        hipLaunchKernelGGL(lut_kernel<false>, grid, dim3(kLutThreads), 0, st, L);
-    }
+    auto* f = !down ? lut_kernel<false, false> : L.fold ? lut_kernel<true, true>
+                                                        : lut_kernel<true, false>;
+    if (t0 || t1)
+        hipExtLaunchKernelGGL(f, grid, dim3(kLutThreads), 0, st, t0, t1, 0, L);
+    else
+        hipLaunchKernelGGL(f, grid, dim3(kLutThreads), 0, st, L);
     return hipGetLastError();
 }
 

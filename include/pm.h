@@ -267,6 +267,7 @@ pm_status pm_store_copy_stats(const pm_store* s, int* last_first, int* last_coun
 /* Optional timing hook: when n >= 4, each pm_moe_token_forward on this store
  * records events[0] before its first kernel, events[1] after the gate/up
  * kernels, events[2] after the down kernels and events[3] after the combine
+ * (right after events[2] when the combine is folded into the down launch)
  * (hipEvent_t handles on the compute stream); n = 2 records events[0] and
  * events[1] only.  When the gate/up stage is a single launch, events[0] and
  * events[1] are that launch's own start and stop.  n = 0 switches it off;
@@ -325,8 +326,15 @@ pm_status pm_cache_stats(const pm_cache* c, uint64_t* accesses, uint64_t* hits,
  *   h_ids int32 [n_tokens][top_k], h_w fp32 [n_tokens][top_k],
  *   h_k uint8 [n_tokens][top_k][3] -- host memory, read before return.
  *   d_x fp32 [n_tokens][hidden] (16-byte aligned), d_y fp32 [n_tokens][hidden]
- *   (overwritten).  At most 32767 uses (n_tokens * top_k) per call, else
- *   PM_ERR_ARG.
+ *   (overwritten; it may be d_x itself).  At most 32767 uses
+ *   (n_tokens * top_k) per call, else PM_ERR_ARG.
+ * The routing-weighted sum over j [T c37] is folded into the down launch when
+ * every down product is a LUT job and d_y does not overlap d_x: the first
+ * gate/up launch clears d_y and each down row sum is added into it, times its
+ * weight, with a float atomic, so the top_k terms of an output add up in the
+ * order they arrive (the last bits may differ from call to call).  Otherwise,
+ * and always under PM_DETERMINISTIC, a combine kernel adds them in slot
+ * order.
  * flags: PM_AUTO_TOPUP tops up every short slot from its host source on the
  * store's side streams (copies that need no wait alternate over two, copies
  * that wait for an earlier forward's reads use a third) and makes `compute`
@@ -343,7 +351,7 @@ pm_status pm_cache_stats(const pm_cache* c, uint64_t* accesses, uint64_t* hits,
  * prefix_kmax >> (kmax - k) [T c25, c35] (the matrix-core tiles still take
  * groups of at least 6 uses).  Same values as the default path; the default
  * (a LUT job per use) re-reads the planes but needs fewer instructions.
- * PM_DETERMINISTIC is accepted and always holds: every sum runs in a fixed
+ * PM_DETERMINISTIC keeps the separate combine: every sum then runs in a fixed
  * order (no atomics), so the same call on the same inputs gives the same bits.
  * The store keeps per-call workspace; calls on one store are serialised on
  * `compute`. */

@@ -337,6 +337,48 @@ def test_forward_mixed_paths_multi_slice():
     st.close()
 
 
+WIDE = synth.Workload(10, "wide-e8-h2048-i2048-g128", 2048, 2048, 128, 8, 2, 1, 3, 2.5)
+
+
+def test_forward_folded_combine_two_down_slices():
+    """Every product on the LUT path (k <= 5), so the routing-weighted combine
+    folds into the down launch: down matrices of 2048 columns, whose two
+    slice sums both add into y, three tokens top-2 with one expert shared.
+    Then the same calls in place (y is x: the separate combine runs) and with
+    the fixed-order combine, all against the oracle."""
+    report("combine folded into the down launch, 2 down slices; in place; fixed order")
+    wl = WIDE
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    st = pm.pm_store_create(e, 1, wl.n_experts)
+    filler = PoolFiller(wl)
+    for i in range(wl.n_experts):
+        filler.fill(st, 0, i)
+    torch.cuda.synchronize()
+    ks = (synth.uniform_k(wl.seed, wl.cfg, 0, 0, 18 * 4).astype(np.int32) - 1) % 5 + 1
+    rows = oc.sample_rows(wl.hidden, 20, 6)
+    for case in range(4):
+        ids = np.array([[case % 8, (case + 3) % 8], [(case + 5) % 8, (case + 6) % 8],
+                        [case % 8, (case + 1) % 8]], np.int32)
+        w = np.array([[0.625, 0.375], [0.5, 0.5], [0.875, 0.125]], np.float32)
+        k = ks[case * 18:(case + 1) * 18].reshape(3, 2, 3).astype(np.uint8)
+        x = np.stack([synth.activation(wl.seed, wl.cfg, 0, t, wl.hidden, step=case)
+                      for t in range(3)])
+        outs = {}
+        y = torch.empty((3, wl.hidden), dtype=torch.float32, device="cuda")
+        pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y)
+        outs["folded"] = host(y)
+        xy = dev(x)
+        pm.pm_moe_token_forward(st, 0, ids, w, k, xy, xy)
+        outs["in place"] = host(xy)
+        pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y, flags=pm.PM_DETERMINISTIC)
+        outs["fixed order"] = host(y)
+        for t in range(3):
+            want, S = oc.token_layer(wl, 0, ids[t], w[t], k[t], x[t], rows)
+            for name, got in outs.items():
+                assert_close(got[t][rows], want, S, f"case {case} token {t} {name} k={k[t].tolist()}")
+    st.close()
+
+
 # ---------------------------------------------------------------- MoE forward
 def single_expert_store(wl, li=None):
     e = pm.eshape(wl.hidden, wl.inter, wl.group)
@@ -404,20 +446,26 @@ def test_forward_layer_full_size(layer_store):
     got = host(y)[0]
     rows = oc.sample_rows(wl.hidden, 48, 1)
     want, S = oc.token_layer(1, 0, ids, w, k, x, rows)
-    assert_close(got[rows], want, S, "512-expert layer, one token")
-    # determinism
-    y2 = torch.empty_like(y)
-    pm.pm_moe_token_forward(st, 0, ids[None], w[None], k[None], dev(x[None]), y2)
-    assert np.array_equal(host(y2).view(np.uint32), host(y).view(np.uint32))
+    assert_close(got[rows], want, S, "512-expert layer, one token (combine folded into down)")
+    # the separate fixed-order combine: the same bound, and a repeat gives
+    # the same bits
+    y2, y3 = torch.empty_like(y), torch.empty_like(y)
+    for yy in (y2, y3):
+        pm.pm_moe_token_forward(st, 0, ids[None], w[None], k[None], dev(x[None]), yy,
+                                flags=pm.PM_DETERMINISTIC)
+    assert_close(host(y2)[0][rows], want, S, "512-expert layer, one token (fixed-order combine)")
+    assert np.array_equal(host(y3).view(np.uint32), host(y2).view(np.uint32))
 
 
 def test_batch_of_four_matches_single_tokens(layer_store):
     """4 tokens x 10 uses in one call (two gate/up launches of LUT jobs)
-    against each token alone: every row is computed by one wave in one step
+    against each token alone, with the fixed-order combine
+    (PM_DETERMINISTIC): every row is computed by one wave in one step
     whatever the launch, and the combine sums the uses in slot order, so a
     token whose experts no other token of the batch reads gets the same bits.
     Then eight single-token calls back to back, with no host sync between,
-    repeat those bits."""
+    repeat those bits.  The batch with the combine folded into the down
+    launch (the default) against the oracle."""
     report("4-token batch vs single tokens, then 8 calls back to back")
     wl, st, ensure = layer_store
     routes = [oc.route_and_bits(1, 0, step=10 + t) for t in range(4)]
@@ -428,14 +476,18 @@ def test_batch_of_four_matches_single_tokens(layer_store):
     x = np.stack([synth.activation(wl.seed, 1, 0, t, wl.hidden, step=10 + t) for t in range(4)])
     xd = dev(x)
     yb = torch.empty((4, wl.hidden), dtype=torch.float32, device="cuda")
-    pm.pm_moe_token_forward(st, 0, ids, w, k, xd, yb)
+    pm.pm_moe_token_forward(st, 0, ids, w, k, xd, yb, flags=pm.PM_DETERMINISTIC)
     batch = host(yb)
+    yf = torch.empty((4, wl.hidden), dtype=torch.float32, device="cuda")
+    pm.pm_moe_token_forward(st, 0, ids, w, k, xd, yf)
+    folded = host(yf)
     counts = {int(i): int((ids == i).sum()) for i in np.unique(ids)}
     exact = 0
     alones = []
     for t in range(4):
         y1 = torch.empty((1, wl.hidden), dtype=torch.float32, device="cuda")
-        pm.pm_moe_token_forward(st, 0, ids[t:t + 1], w[t:t + 1], k[t:t + 1], xd[t:t + 1], y1)
+        pm.pm_moe_token_forward(st, 0, ids[t:t + 1], w[t:t + 1], k[t:t + 1], xd[t:t + 1], y1,
+                                flags=pm.PM_DETERMINISTIC)
         alone = host(y1)[0]
         alones.append(alone)
         if all(counts[int(i)] == 1 for i in ids[t]):
@@ -445,11 +497,13 @@ def test_batch_of_four_matches_single_tokens(layer_store):
         want, S = oc.token_layer(1, 0, ids[t], w[t], k[t], x[t], rows)
         assert_close(alone[rows], want, S, f"token {t} alone")
         assert_close(batch[t][rows], want, S, f"token {t} in the batch")
+        assert_close(folded[t][rows], want, S, f"token {t} in the batch, combine folded")
     assert exact >= 2
     ys = [torch.full((1, wl.hidden), 7.0, dtype=torch.float32, device="cuda") for _ in range(8)]
     for i in range(8):
         t = i % 4
-        pm.pm_moe_token_forward(st, 0, ids[t:t + 1], w[t:t + 1], k[t:t + 1], xd[t:t + 1], ys[i])
+        pm.pm_moe_token_forward(st, 0, ids[t:t + 1], w[t:t + 1], k[t:t + 1], xd[t:t + 1], ys[i],
+                                flags=pm.PM_DETERMINISTIC)
     for i in range(8):
         assert np.array_equal(host(ys[i])[0].view(np.uint32), alones[i % 4].view(np.uint32)), i
 
@@ -565,21 +619,23 @@ def test_forward_batch8_grouped_with_topup():
         pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y)
     assert ei.value.status == pm.PM_ERR_NOT_RESIDENT
     _, _, planes_before, _ = pm.pm_store_copy_stats(st)
-    pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y, flags=pm.PM_AUTO_TOPUP)
+    pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y, flags=pm.PM_AUTO_TOPUP | pm.PM_DETERMINISTIC)
     got = host(y)
     _, _, planes_after, _ = pm.pm_store_copy_stats(st)
     assert planes_after - planes_before == expected_planes
     for i in short:
         assert pm.pm_store_resident(st, 0, i) == kmax[i]
-    # each token of the batch equals that token run alone: bit for bit when
-    # none of its experts is shared (same kernels, same order); otherwise
+    # each token of the batch equals that token run alone (fixed-order
+    # combine): bit for bit when none of its experts is shared (same kernels,
+    # same order); otherwise
     # (a shared expert's uses grouped) both within the oracle's per-output
     # bound
     counts = {i: int((ids == i).sum()) for i in distinct}
     rows = oc.sample_rows(wl.hidden, 8, 10)
     for t in range(B):
         y1 = torch.empty((1, wl.hidden), dtype=torch.float32, device="cuda")
-        pm.pm_moe_token_forward(st, 0, ids[t:t + 1], w[t:t + 1], k[t:t + 1], xd[t:t + 1], y1)
+        pm.pm_moe_token_forward(st, 0, ids[t:t + 1], w[t:t + 1], k[t:t + 1], xd[t:t + 1], y1,
+                                flags=pm.PM_DETERMINISTIC)
         alone = host(y1)[0]
         if all(counts[int(i)] == 1 for i in ids[t]):
             assert np.array_equal(alone.view(np.uint32), got[t].view(np.uint32)), t
@@ -592,8 +648,9 @@ def test_forward_batch8_grouped_with_topup():
 def test_read_once_matches_default():
     """PM_READ_ONCE (an expert shared by several tokens read once, by the
     direct kernels) against the default path (a LUT job per use) on a B = 8
-    step: both against the oracle, and bit for bit on the tokens none of whose
-    experts is shared (their jobs are the same in both)."""
+    step: both against the oracle, and, with the fixed-order combine, bit for
+    bit on the tokens none of whose experts is shared (their jobs are the
+    same in both)."""
     report("B=8 routing, all resident: PM_READ_ONCE vs default")
     wl = synth.WORKLOADS[4]
     e = pm.eshape(wl.hidden, wl.inter, wl.group)
@@ -612,13 +669,15 @@ def test_read_once_matches_default():
     x = np.stack([synth.activation(wl.seed, 4, 0, t, wl.hidden, step=5) for t in range(B)])
     xd = dev(x)
     out = {}
-    for name, flags in (("default", 0), ("read_once", pm.PM_READ_ONCE)):
+    for name, flags in (("default", 0), ("read_once", pm.PM_READ_ONCE),
+                        ("default_fixed", pm.PM_DETERMINISTIC),
+                        ("read_once_fixed", pm.PM_READ_ONCE | pm.PM_DETERMINISTIC)):
         y = torch.empty((B, wl.hidden), dtype=torch.float32, device="cuda")
         pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y, flags=flags)
         out[name] = host(y)
     rows = oc.sample_rows(wl.hidden, 8, 30)
     for t in range(B):
-        a, b = out["default"][t], out["read_once"][t]
+        a, b = out["default_fixed"][t], out["read_once_fixed"][t]
         if all(counts[int(i)] == 1 for i in ids[t]):
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), t
         want, S = oc.token_layer(4, 0, ids[t], w[t], k[t], x[t], rows)
@@ -732,7 +791,7 @@ def test_topup_into_an_unallocated_slot(mfma):
         k[t, 1] = [(3 * t) % 8 + 1, (5 * t + 2) % 8 + 1, (t + 4) % 8 + 1]
     x = np.stack([synth.activation(wl.seed, 1, 0, t, wl.hidden, step=21) for t in range(B)])
     xd = dev(x)
-    flags = pm.PM_AUTO_TOPUP | (pm.PM_BATCH_MFMA if mfma else 0)
+    flags = pm.PM_AUTO_TOPUP | pm.PM_DETERMINISTIC | (pm.PM_BATCH_MFMA if mfma else 0)
     y = torch.empty((B, wl.hidden), dtype=torch.float32, device="cuda")
     pm.pm_moe_token_forward(st, 0, ids, w, k, xd, y, flags=flags)
     got = host(y)
