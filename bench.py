@@ -133,8 +133,9 @@ def summarize_counters(fetch_csv, write_csv, stats_csv):
         return out
 
     def short(name):
-        for key, lab in (("lut_kernel<false>", "lut_kernel<false> (gate/up)"),
-                         ("lut_kernel<true>", "lut_kernel<true> (down)"),
+        for key, lab in (("lut_kernel<false, false>", "lut_kernel<false, false> (gate/up)"),
+                         ("lut_kernel<true, true>", "lut_kernel<true, true> (down + combine)"),
+                         ("lut_kernel<true, false>", "lut_kernel<true, false> (down)"),
                          ("combine_k_kernel", "combine_k_kernel"), ("neg_kernel", "torch.neg 1 GiB")):
             if key in name:
                 return lab

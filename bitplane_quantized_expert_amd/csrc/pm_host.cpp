@@ -666,6 +666,7 @@ struct pm_store {
     bool host_fake;
     size_t plane_bytes, level_bytes;   // per plane chunk, per slot levels
     std::vector<Slot> slots;
+    std::vector<int> item_of;          // forward scratch: expert -> item, -1 between calls
     // The store's own streams.  side[0] is the memory stream: the waits that
     // a truncation's release of memory follows.
     // Top-up copies that need no wait take side[1] and side[2] in turn (more
@@ -1020,6 +1021,7 @@ extern "C" pm_status pm_store_create(pm_expert_shape e, int n_layers, int n_expe
     s->plane_bytes = pm_expert_plane_words(e) * sizeof(uint32_t);
     s->level_bytes = pm_expert_levels_floats(e) * sizeof(float);
     s->slots.resize(size_t(n_layers) * n_experts);
+    s->item_of.assign(size_t(n_experts), -1);
     // arenas of about eight whole experts (within 64 MiB .. 2 GiB), no larger
     // than a capacity the store is given
     {
@@ -1455,6 +1457,25 @@ static void set_starts_by_source(KLaunch& L, int n_total) {
     L.n_wgq = w;
 }
 
+// Jobs of one token share an activation table, and a workgroup runs one
+// prefix: order a stage's jobs by (source, prefix), stably.  Insertion sort
+// for the short lists of a call (no allocation), std::stable_sort beyond.
+static void sort_jobs(std::vector<JobSpec>& js) {
+    auto less = [](const JobSpec& a, const JobSpec& b) {
+        return a.job.src != b.job.src ? a.job.src < b.job.src : a.job.k < b.job.k;
+    };
+    if (js.size() > 64) {
+        std::stable_sort(js.begin(), js.end(), less);
+        return;
+    }
+    for (size_t i = 1; i < js.size(); ++i) {
+        const JobSpec v = js[i];
+        size_t j = i;
+        for (; j > 0 && less(v, js[j - 1]); --j) js[j] = js[j - 1];
+        js[j] = v;
+    }
+}
+
 // Pack jobs into launches of at most kMaxLaunchJobs, cut by source
 // (set_starts_by_source); jobs of one source should be adjacent.
 static void pack_launches(const std::vector<JobSpec>& js, const KLaunch& proto,
@@ -1600,10 +1621,19 @@ static pm_status finish_forward(pm_store* s, hipStream_t compute, const std::vec
 // the direct kernels)
 constexpr int kTileMinUses = PM_TILE_MIN_USES;
 
+// The uses of one item (expert) of a forward call: a range of a flat list.
+struct UseList {
+    const int* b;
+    int n;
+    const int* begin() const { return b; }
+    const int* end() const { return b + n; }
+    size_t size() const { return size_t(n); }
+};
+
 // The matrix-core tiles of one expert (slot) for matrices m0..m1-1: per
 // prefix k, the uses that read matrix m at k, 16 at a time, when at least
 // min_uses of them do.  Their (use, matrix) is marked 2 (tile, one slice).
-static void add_tiles(std::vector<Use>& uses, const std::vector<int>& item_uses,
+static void add_tiles(std::vector<Use>& uses, const UseList& item_uses,
                       const Slot& sl, const Geom& g, int m0, int m1, int min_uses,
                       std::vector<MTile> (&out)[kBits + 1]) {
     const size_t nb_gu = size_t(g.inter) * (g.hidden / g.group);
@@ -1647,7 +1677,7 @@ static pm_status launch_tiles(MLaunch L, const MTile* d_tiles, const size_t* off
 // over all tokens.  Every use keeps its own prefix.
 static pm_status forward_mfma(pm_store* s, int layer, int n_tokens, int top_k,
                               std::vector<Use>& uses, const std::vector<int>& item_expert,
-                              const std::vector<std::vector<int>>& item_uses,
+                              const std::vector<UseList>& item_uses,
                               const std::vector<int>& kneed, const std::vector<char>& late,
                               const float* d_x, float* d_y, hipStream_t compute) {
     const Geom& g = s->geom;
@@ -1756,9 +1786,6 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
                      top_k, kMaxCallUses);
     const int n_uses = n_tokens * top_k;
     std::vector<Use> uses(n_uses);
-    std::map<int, int> item_of;
-    std::vector<int> item_expert;
-    std::vector<std::vector<int>> item_uses;
     for (int t = 0; t < n_tokens; ++t) {
         for (int j = 0; j < top_k; ++j) {
             const int u = t * top_k + j;
@@ -1776,19 +1803,34 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
             us.w = h_w[u];
             us.tok = t;
             us.slot = j;
-            auto it = item_of.find(e);
-            int d;
-            if (it == item_of.end()) {
-                d = int(item_expert.size());
-                item_of[e] = d;
-                item_expert.push_back(e);
-                item_uses.emplace_back();
-            } else {
-                d = it->second;
-            }
-            item_uses[d].push_back(u);
         }
     }
+    // items in order of first appearance, each with its uses in call order
+    // (a counting sort through the store's expert -> item map, which is all
+    // -1 between calls)
+    std::vector<int> item_expert;
+    item_expert.reserve(std::min(n_uses, s->n_experts));
+    std::vector<int> use_item(n_uses), list_off(1, 0);
+    for (int u = 0; u < n_uses; ++u) {
+        int& d = s->item_of[h_ids[u]];
+        if (d < 0) {
+            d = int(item_expert.size());
+            item_expert.push_back(h_ids[u]);
+            list_off.push_back(0);
+        }
+        use_item[u] = d;
+        ++list_off[d + 1];
+    }
+    for (int e : item_expert) s->item_of[e] = -1;
+    for (size_t d = 1; d < list_off.size(); ++d) list_off[d] += list_off[d - 1];
+    std::vector<int> use_list(n_uses);
+    {
+        std::vector<int> fill(list_off.begin(), list_off.end() - 1);
+        for (int u = 0; u < n_uses; ++u) use_list[fill[use_item[u]]++] = u;
+    }
+    std::vector<UseList> item_uses(item_expert.size());
+    for (size_t d = 0; d < item_expert.size(); ++d)
+        item_uses[d] = UseList{use_list.data() + list_off[d], list_off[d + 1] - list_off[d]};
     const int n_items = int(item_expert.size());
     std::vector<int> kneed(n_items, 0);
     std::vector<std::array<int, 3>> kmax(n_items, {0, 0, 0});
@@ -1963,6 +2005,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     for (int grp = 0; grp < 2; ++grp) {
         const int i0 = grp == 0 ? 0 : n_res, i1 = grp == 0 ? n_res : n_items;
         std::vector<JobSpec> js;
+        js.reserve(size_t(2) * n_uses);
         for (int i = i0; i < i1; ++i) {
             const int d = order[i];
             const Slot& sl = slot_of_item(d);
@@ -1981,11 +2024,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
                 }
             }
         }
-        // jobs of one token share an activation table, and a workgroup runs
-        // one prefix: keep the jobs of one (token, k) adjacent
-        std::stable_sort(js.begin(), js.end(), [](const JobSpec& a, const JobSpec& b) {
-            return a.job.src != b.job.src ? a.job.src < b.job.src : a.job.k < b.job.k;
-        });
+        sort_jobs(js);
         pack_launches(js, gu_proto, L_gu[grp]);
     }
     // The routing-weighted combine folds into the down launches when every
@@ -2011,6 +2050,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     }
     {
         std::vector<JobSpec> js;
+        js.reserve(size_t(n_uses));
         for (int i = 0; i < n_items; ++i) {
             const int d = order[i];
             const Slot& sl = slot_of_item(d);
