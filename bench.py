@@ -34,8 +34,8 @@ KERNEL_SOURCES = ("bitplane_quantized_expert_amd/csrc/pm_lut.hip",
 # passes of this benchmark, each scaled by the same counter on the 1 GiB
 # negation kernel (see --summarize-counters); reported only while the kernel
 # sources still have this digest.
-TRAFFIC = {"sources_sha256": "b86c30f0f8ab785549979e37b04e3eebbcca67fda293981b9c5b453cd866ad80",
-           "bytes_per_launch": 44974538}
+TRAFFIC = {"sources_sha256": "013b46c26fbf0e36dfedd3e5ae0c0366caa808b0ea70fc890738ed040cac3b45",
+           "bytes_per_launch": 44963488}
 
 
 def log(msg):
@@ -309,6 +309,23 @@ def timed(torch, fn, n):
     return time.perf_counter() - t0
 
 
+def graph_replay(torch, cap, body, reps):
+    """Capture body() (library calls on stream `cap`) into one HIP graph,
+    replay it once, then `reps` more times: the same kernels with the same
+    arguments, without the host's work per call.  Returns (graph, seconds per
+    replay)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        body()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    return g, (time.perf_counter() - t0) / reps
+
+
 def bench_sixty_layers(args, torch, pm, synth, PoolFiller):
     """One decode token through 60 independent layers (600 routed experts,
     all resident): a step is the 60 layer calls, fresh x and logits per layer."""
@@ -334,12 +351,33 @@ def bench_sixty_layers(args, torch, pm, synth, PoolFiller):
     timed(torch, token, max(2, args.warmup // 10))
     n = max(5, args.steps // 10)
     el = timed(torch, token, n)
+    # the token's 60 layer calls captured into one HIP graph and replayed
+    graph = {}
+    try:
+        cap = torch.cuda.Stream()
+
+        def token_on(strm):
+            for layer, ids, w, k3, x in plan:
+                pm.pm_moe_token_forward(st, layer, ids, w, k3, x, y, strm)
+
+        with torch.cuda.stream(cap):
+            token_on(cap)          # the store's last stream becomes the capture stream
+        torch.cuda.synchronize()
+        eager_y = y.clone()
+        _, g_el = graph_replay(torch, cap, lambda: token_on(cap), n)
+        diff = float((y - eager_y).abs().max())
+        graph = {"ms_per_token": round(g_el * 1e3, 4), "GBs": round(nbytes / g_el / 1e9, 1),
+                 "replays": n, "max_abs_diff_vs_eager": diff,
+                 "how": "the 60 layer calls of the token captured once on a side stream "
+                        "(HIP graph), replayed; y of the last layer checked against the eager call"}
+    except Exception as ex:
+        graph = {"error": str(ex)[:300]}
     st.close()
     ms = el / n * 1e3
     return {"workload": wl.name, "ms_per_token": round(ms, 4),
             "GBs": round(nbytes * n / el / 1e9, 1),
             "expert_gemvs_per_s": round(3 * wl.top_k * wl.n_layers * n / el, 1),
-            "bytes_per_token": nbytes}
+            "bytes_per_token": nbytes, "hip_graph": graph}
 
 
 def bench_precisions(args, torch, pm, synth, PoolFiller):
@@ -736,6 +774,9 @@ def main():
     ap.add_argument("--experts", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph-only", type=int, default=0, metavar="R",
+                    help="after the timed loop, capture its steps into a HIP graph, replay it "
+                         "R times and print only that (for kernel traces of back-to-back steps)")
     ap.add_argument("--log-inputs", metavar="FILE",
                     help="write the ids, w and k of every step of the layer benchmark (JSON lines)")
     ap.add_argument("--workload", default="1",
@@ -839,6 +880,29 @@ def main():
     log(f"timed {args.steps} steps: {ms:.4f} ms/step, {gbs:.1f} GB/s "
         f"(host issue {issued / args.steps * 1e6:.1f} us/step)")
 
+    # the timed steps as library calls on a side stream, for capture into a
+    # HIP graph (the store's last stream becomes that stream first)
+    cap = torch.cuda.Stream()
+
+    def run_cap(s):
+        pm.pm_moe_token_forward(st, 0, ids[s:s + 1], w[s:s + 1], k3[s:s + 1], x[s:s + 1],
+                                y[s:s + 1], cap)
+
+    def all_steps():
+        for s in steps:
+            run_cap(s)
+
+    if args.graph_only:
+        with torch.cuda.stream(cap):
+            run_cap(steps[0])
+        torch.cuda.synchronize()
+        _, g_el = graph_replay(torch, cap, all_steps, args.graph_only)
+        st.close()
+        print(json.dumps({"graph_only": {"replays": args.graph_only, "steps": args.steps,
+                                         "ms_per_step": round(g_el / args.steps * 1e3, 5),
+                                         "GBs": round(nbytes / g_el / 1e9, 2)}}), flush=True)
+        return 0
+
     ceiling = copy_ceiling(torch, stream)
     log(f"stream ceiling: {ceiling['GBs']} GB/s ({ceiling['kernel']})")
 
@@ -903,6 +967,22 @@ def main():
 
     host_raw = host_pass(raw)
     host_binding = host_pass(run)
+
+    # the timed steps captured into one HIP graph and replayed (no host work
+    # between launches)
+    graph = {}
+    try:
+        with torch.cuda.stream(cap):
+            run_cap(steps[0])
+        torch.cuda.synchronize()
+        _, g_el = graph_replay(torch, cap, all_steps, 3)
+        graph = {"ms_per_step": round(g_el / args.steps * 1e3, 5),
+                 "GBs": round(nbytes / g_el / 1e9, 2), "replays": 3,
+                 "how": "the timed steps captured once on a side stream and replayed"}
+        log(f"graph replay: {graph['ms_per_step'] * 1e3:.2f} us/step, {graph['GBs']} GB/s")
+    except Exception as ex:
+        graph = {"error": str(ex)[:300]}
+        log(f"graph capture failed: {graph['error']}")
     log(f"host time per call: C entry {host_raw['mean']} us (p50 {host_raw['p50']}), "
         f"numpy binding {host_binding['mean']} us")
     # one step alone (GPU idle before it, its own events), cold and warm:
@@ -953,6 +1033,7 @@ def main():
                    "inter": wl.inter, "group": wl.group, "top_k": wl.top_k, "batch": 1,
                    "mean_k": round(float(kk[args.warmup:].mean()), 4), "pool_experts": n_exp},
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "hip_graph": graph,
         "host_issue_us_per_step": host_raw["mean"],
         "host_issue": {"c_entry_us": host_raw, "numpy_binding_us": host_binding,
                        "timed_loop_issue_us_per_step": round(issued / args.steps * 1e6, 2),

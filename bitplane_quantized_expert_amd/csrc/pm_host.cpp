@@ -2161,8 +2161,14 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
             sl.pending = false;
         }
     }
-    // a gate/up stage of one LUT launch is timed by the launch itself
-    const bool gu_single = L_gu[0].size() == 1 && d_gu0 == 0 && n_res == n_items && n_tiles == 0;
+    // a gate/up stage of one LUT launch is timed by the launch itself, except
+    // under stream capture, where the events become graph nodes of their own
+    bool gu_single = L_gu[0].size() == 1 && d_gu0 == 0 && n_res == n_items && n_tiles == 0;
+    if (s->profiling && gu_single) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        HIP_TRY(hipStreamIsCapturing(compute, &cs));
+        if (cs != hipStreamCaptureStatusNone) gu_single = false;
+    }
     if (s->profiling && !gu_single) HIP_TRY(hipEventRecord(s->prof[0], compute));
     for (const KLaunch& L : L_gu[0]) {
         if (s->profiling && gu_single)
