@@ -1347,41 +1347,16 @@ struct JobSpec {                       // a LUT job before it is packed into a l
 };
 }  // namespace
 
-// Row cuts of a launch (KLaunch::start), contiguous: the cost of all rows in
-// order is split into equal parts, each cut at a multiple of kLutRows rows of
-// its job.  Cuts jobs j0 .. j1-1 of a launch into n_wg row ranges of about
-// equal cost, writing L.start[w0 .. w0 + n_wg - 1].
-static void cut_jobs(KLaunch& L, int j0, int j1, int n_wg, int w0) {
-    const int n = j1 - j0, rows = L.rows, pairs = rows / kLutRows;
-    double pc[kMaxLaunchJobs], before[kMaxLaunchJobs + 1];
-    before[0] = 0;
-    for (int j = 0; j < n; ++j) {
-        pc[j] = double(lut_step_ns(L.job[j0 + j].k));
-        before[j + 1] = before[j] + pc[j] * pairs;
-    }
-    const double per_wg = before[n] / n_wg;
-    L.start[w0] = j0 * rows;
-    int j = 0;
-    double inv = 1.0 / pc[0];
-    for (int q = 1; q < n_wg; ++q) {
-        const double target = per_wg * q;
-        while (j < n - 1 && before[j + 1] <= target) inv = 1.0 / pc[++j];
-        // the first whole step at or past the target
-        const double at = target - before[j];
-        int p = int(at * inv);
-        if (double(p) * pc[j] < at) ++p;
-        L.start[w0 + q] = (j0 + j) * rows + std::min(rows, kLutRows * p);
-    }
-}
-
-// Workgroup ranges of a launch whose jobs come in runs of one source (one
+// Workgroups of a launch whose jobs come in runs of one source (one
 // activation table) and one prefix: every run gets whole workgroups (largest
 // remainder, at least one each), and no workgroup spans two runs, so a
 // workgroup builds its table once and runs one prefix's code throughout.
+// Each workgroup takes an even share of its run's 8-row steps (the kernel
+// works it out from the run's description).
 // The shares balance the modelled workgroup time, fixed part plus steps:
 // run r with C_r ns of steps at fixed part A_r gets C_r / (T - A_r)
 // workgroups, T chosen so that the shares add up to the workgroups there are.
-static void set_starts_by_source(KLaunch& L, int n_total) {
+static void split_runs(KLaunch& L, int n_total) {
     const int n = L.n_jobs;
     int r0[kMaxLaunchJobs + 1];                // first job of every run
     int R = 0;
@@ -1446,14 +1421,16 @@ static void set_starts_by_source(KLaunch& L, int n_total) {
     }
     int w = 0;
     for (int r = 0; r < R; ++r) {
-        cut_jobs(L, r0[r], r0[r + 1], a[r], w);
         const KJob& jb = L.job[r0[r]];
-        const uint32_t meta = uint32_t(uint16_t(jb.src)) | (uint32_t(jb.k) << 16) |
-                              (uint32_t(jb.gsl) << 24);
-        for (int q = w; q < w + a[r]; ++q) L.meta[q] = meta;
+        KRun& run = L.run[r];
+        run.g0 = r0[r] * L.rows;
+        run.nsteps = (r0[r + 1] - r0[r]) * (L.rows / kLutRows);
+        run.wg0 = int16_t(w);
+        run.nwg = int16_t(a[r]);
+        run.meta = uint32_t(uint16_t(jb.src)) | (uint32_t(jb.k) << 16) | (uint32_t(jb.gsl) << 24);
+        std::memset(L.wg_run + w, r, size_t(a[r]));
         w += a[r];
     }
-    L.start[w] = n * L.rows;
     L.n_wgq = w;
 }
 
@@ -1477,7 +1454,7 @@ static void sort_jobs(std::vector<JobSpec>& js) {
 }
 
 // Pack jobs into launches of at most kMaxLaunchJobs, cut by source
-// (set_starts_by_source); jobs of one source should be adjacent.
+// (split_runs); jobs of one source should be adjacent.
 static void pack_launches(const std::vector<JobSpec>& js, const KLaunch& proto,
                           std::vector<KLaunch>& out) {
     // the launches of one stage run one after another: each takes the whole
@@ -1489,7 +1466,7 @@ static void pack_launches(const std::vector<JobSpec>& js, const KLaunch& proto,
         KLaunch& L = out.back();
         L.n_jobs = int(j1 - j0);
         for (size_t j = j0; j < j1; ++j) L.job[j - j0] = js[j].job;
-        set_starts_by_source(L, n);
+        split_runs(L, n);
     }
 }
 
@@ -1555,7 +1532,7 @@ pm_status gemv_lut(pm_matrix_shape s, int k, const uint32_t* d_planes, size_t ps
     }
     // workgroups per slice: enough to fill the device, at least 32 rows each
     const int target = std::max(1, std::min(kMaxLaunchWgq, lut_wg_target() / S));
-    set_starts_by_source(L, std::max(1, std::min(target, (s.rows + 31) / 32)));
+    split_runs(L, std::max(1, std::min(target, (s.rows + 31) / 32)));
     HIP_TRY(launch_lut(L, false, st));
     if (S > 1) HIP_TRY(launch_sum_slices(jb.out, S, s.rows, d_y, st));
     return PM_OK;

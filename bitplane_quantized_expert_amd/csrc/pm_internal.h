@@ -104,11 +104,20 @@ struct KJob {                      // one matrix of one use
     uint8_t gsl;                   // down: gate slices (bits 0-3), up slices (bits 4-7)
 };
 // One LUT launch: n_wgq x S workgroups.  The rows of the jobs are numbered
-// as one sequence (row r of job j is g = j * rows + r); workgroup q of every
-// slice runs g in [start[q], start[q + 1]), cut by the host so that the work
-// is balanced.  Scalars come first so that the fields every workgroup reads
-// at its start share one cache line.
+// as one sequence (row r of job j is g = j * rows + r).  The jobs come in
+// runs of one activation source and one prefix; run i covers the rows
+// [g0, g0 + 8 * nsteps) and has the workgroups wg0 .. wg0 + nwg - 1 of every
+// slice, which split its 8-row steps evenly (a run's steps all cost the
+// same).  Scalars come first so that the fields every workgroup reads at its
+// start share one cache line.
 constexpr int kMaxLaunchWgq = 256;
+struct KRun {
+    int32_t g0, nsteps;
+    int16_t wg0, nwg;
+    // activation source (bits 0-15: token or use), prefix k (bits 16-19),
+    // gate/up slice counts of a down job (bits 24-31)
+    uint32_t meta;
+};
 struct KLaunch {
     const float* x;                // gate/up: activation of token t at x + t * x_stride
                                    // (x_stride 0: every job reads x itself)
@@ -121,10 +130,8 @@ struct KLaunch {
     int32_t gu_smax, inter, n_zero;
     int32_t fold;                  // down: add wt * row sum into out (float atomics)
                                    // instead of storing the partial
-    int32_t start[kMaxLaunchWgq + 2];
-    // per row range q: activation source (bits 0-15: token or use), prefix k
-    // (bits 16-19), gate/up slice counts of a down job (bits 24-31)
-    uint32_t meta[kMaxLaunchWgq + 2];
+    uint8_t wg_run[kMaxLaunchWgq]; // run of workgroup q
+    KRun run[kMaxLaunchJobs];
     KJob job[kMaxLaunchJobs];
 };
 static_assert(sizeof(KLaunch) <= 4096, "kernel arguments are limited to 4 KiB");

@@ -499,10 +499,9 @@ __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L,
     }
 }
 
-// Workgroup (q, slice) runs the rows [start[q], start[q + 1]) of the
-// launch's row sequence; the host cuts them so that every range holds jobs of
-// one prefix and one activation source, named in meta[q] with the range's k,
-// so that a workgroup's first reads do not depend on one another.  Job
+// Workgroup (q, slice) runs its share of the rows of run wg_run[q]: jobs of
+// one prefix and one activation source, named in the run's meta with k, so
+// that a workgroup's first reads do not depend on one another.  Job
 // descriptions are read straight from the argument block.
 // One workgroup per compute unit (its table fills the LDS).
 template <bool DOWN, bool FOLD>
@@ -529,9 +528,13 @@ lut_kernel(const KLaunch L) {
             L.zero[i] = 0.f;
     }
     __syncthreads();
+    // the workgroup's share of its run's steps (an even split)
     const int q = blockIdx.x, slice = blockIdx.y;
-    const uint32_t meta = L.meta[q];
-    const int g0 = L.start[q], g1 = L.start[q + 1];
+    const KRun& run = L.run[L.wg_run[q]];
+    const uint32_t meta = run.meta;
+    const int i = q - run.wg0, nwg = run.nwg;
+    const int g0 = run.g0 + kLutRows * (run.nsteps * i / nwg);
+    const int g1 = run.g0 + kLutRows * (run.nsteps * (i + 1) / nwg);
     if (g0 >= g1) return;
     LutCtx c{slice, g0, g1, int(meta & 0xFFFFu), int(meta >> 24),
              uni(int(threadIdx.x) / kWave), int(threadIdx.x) % kWave};
