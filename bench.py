@@ -774,6 +774,8 @@ def main():
     ap.add_argument("--experts", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kfix", type=int, default=0, metavar="K",
+                    help="every use of the layer step at prefix K (per-prefix profiles)")
     ap.add_argument("--graph-only", type=int, default=0, metavar="R",
                     help="after the timed loop, capture its steps into a HIP graph, replay it "
                          "R times and print only that (for kernel traces of back-to-back steps)")
@@ -845,6 +847,8 @@ def main():
         logits[:, n_exp:] = -np.inf
     ids, w = pm.pm_route_topk(logits, wl.top_k)
     kk = pm.pm_allocate_bits(ids, w, err, wl.budget)
+    if args.kfix:
+        kk = np.full_like(kk, args.kfix)
     k3 = np.repeat(kk[:, :, None], 3, axis=2)
     x = torch.from_numpy(np.stack([synth.activation(wl.seed, wl.cfg, 0, 0, wl.hidden, step=s)
                                    for s in range(total)])).cuda()
