@@ -309,6 +309,46 @@ def timed(torch, fn, n):
     return time.perf_counter() - t0
 
 
+def wg_timeline(pm, torch, run, steps, btb, groups=20):
+    """Workgroup timeline of the LUT launches (the stamped build): groups of
+    `btb` steps run back to back; after each, the stamps of the group's last
+    gate/up and down launches (s_memrealtime, 10 ns) give per launch:
+    the span from the first workgroup's start to the last one's end, the
+    spread of the starts, and per workgroup the prologue (start until the
+    last wave computes) split into the builders' source load and their
+    table, the duration and the end.  Medians over the groups of the
+    per-launch figures (workgroup figures: their median, p90, max)."""
+    import ctypes
+    lib = pm.lib()
+    lib.pm_lut_stamps_fetch.restype = ctypes.c_int
+    lib.pm_lut_stamps_fetch.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    buf = np.zeros((2, 256 * 16, 8), np.uint64)
+    per = {0: [], 1: []}
+    for gi in range(groups):
+        for i in range(btb):
+            run(steps[(gi * btb + i) % len(steps)])
+        torch.cuda.synchronize()
+        assert lib.pm_lut_stamps_fetch(buf.ctypes.data, buf.nbytes) == 0
+        for down in (0, 1):
+            b = buf[down].astype(np.int64)
+            used = b[:, 4] > 0
+            t = b[used]
+            base = t[:, 0].min()
+            per[down].append({
+                "span": (t[:, 4].max() - base) / 100, "start_spread": (t[:, 0].max() - base) / 100,
+                "prologue": np.median(t[:, 3] - t[:, 0]) / 100,
+                "source": np.median(t[:, 1] - t[:, 0]) / 100,
+                "table": np.median(t[:, 2] - t[:, 1]) / 100,
+                "wg_median": np.median(t[:, 4] - t[:, 0]) / 100,
+                "wg_p90": np.percentile(t[:, 4] - t[:, 0], 90) / 100,
+                "wg_max": (t[:, 4] - t[:, 0]).max() / 100,
+                "first_end": (t[:, 4].min() - base) / 100, "workgroups": int(used.sum())})
+            b[:] = 0
+        buf[:] = 0
+    return {("down" if d else "gateup"): {k: round(float(np.median([r[k] for r in v])), 2)
+                                          for k in v[0]} for d, v in per.items()}
+
+
 def graph_replay(torch, cap, body, reps):
     """Capture body() (library calls on stream `cap`) into one HIP graph,
     replay it once, then `reps` more times: the same kernels with the same
@@ -774,6 +814,10 @@ def main():
     ap.add_argument("--experts", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--wg-timeline", type=int, default=0, metavar="N",
+                    help="with the stamped build (libpm_stamps.so): after the timed loop, run "
+                         "groups of N steps back to back and report the workgroup timeline of "
+                         "each group's last gate/up and down launches")
     ap.add_argument("--kfix", type=int, default=0, metavar="K",
                     help="every use of the layer step at prefix K (per-prefix profiles)")
     ap.add_argument("--graph-only", type=int, default=0, metavar="R",
@@ -806,6 +850,13 @@ def main():
         if args.workload == "cache":
             return 0
 
+    if args.wg_timeline:
+        stamps = os.path.join(ROOT, "bitplane_quantized_expert_amd", "libpm_stamps.so")
+        if not os.path.exists(stamps):
+            print(f"{stamps} is missing: build it (bitplane_quantized_expert_amd/build.py)",
+                  file=sys.stderr)
+            return 1
+        os.environ["PM_LIB"] = stamps
     import torch
     import bitplane_quantized_expert_amd as pm
     import synth
@@ -895,6 +946,12 @@ def main():
     def all_steps():
         for s in steps:
             run_cap(s)
+
+    if args.wg_timeline:
+        res = wg_timeline(pm, torch, run, list(steps), args.wg_timeline)
+        st.close()
+        print(json.dumps({"wg_timeline": res}), flush=True)
+        return 0
 
     if args.graph_only:
         with torch.cuda.stream(cap):

@@ -53,12 +53,13 @@ def _run(cmd, what, verbose):
         raise RuntimeError(f"hipcc failed building {what}")
 
 
-def build(verbose=False, extra_flags=(), out_override=None):
+def build(verbose=False, extra_flags=(), out_override=None, only_pm=False):
     """Compile every source to an object (with its own extra flags), then
-    link each library.  extra_flags / out_override serve tuning builds."""
+    link each library.  extra_flags / out_override / only_pm serve tuning and
+    profiling builds of libpm."""
     import concurrent.futures as cf
     outs = []
-    for out, srcs in TARGETS:
+    for out, srcs in (TARGETS[:1] if only_pm else TARGETS):
         if out_override and out.endswith("libpm.so"):
             out = out_override
         objs, jobs = [], []
@@ -124,7 +125,17 @@ def build_sanitized(verbose=False):
     return ASAN_LIB
 
 
+# libpm with per-workgroup timeline stamps in the LUT kernels (PM_LUT_STAMPS):
+# a profiling build for bench.py --wg-timeline, never the product.
+STAMPS_LIB = os.path.join(PKG, "libpm_stamps.so")
+
+
+def build_stamps(verbose=False):
+    return build(verbose, extra_flags=["-DPM_LUT_STAMPS"], out_override=STAMPS_LIB, only_pm=True)[0]
+
+
 if __name__ == "__main__":
     for p in build(verbose=True):
         print("built", p)
     print("built", build_sanitized(verbose=True))
+    print("built", build_stamps(verbose=True))

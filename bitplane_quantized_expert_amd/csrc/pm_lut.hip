@@ -382,6 +382,22 @@ struct LutCtx {
     int wave, lane;
 };
 
+// Workgroup timeline, in a build with PM_LUT_STAMPS only (a profiling build;
+// the product build has none of it): s_memrealtime (100 MHz) at the
+// workgroup's start (0), when the builders hold their source values (1),
+// when their table writes are issued (2), when the last wave starts to
+// compute (3) and at the end (4); then k (5), steps (6) and the XCD (7).
+// The last launch of each kind (gate/up, down) leaves its stamps.
+#ifdef PM_LUT_STAMPS
+constexpr int kStampWgs = kMaxLaunchWgq * 16;
+__device__ unsigned long long pm_lut_stamps[2][kStampWgs][8];
+#define PM_STAMP(i, v)                                                                      \
+    pm_lut_stamps[DOWN][(blockIdx.y * gridDim.x + blockIdx.x) % kStampWgs][i] = (v)
+#define PM_NOW() __builtin_amdgcn_s_memrealtime()
+#else
+#define PM_STAMP(i, v) ((void)0)
+#endif
+
 template <bool DOWN, bool FOLD, int K>
 __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L, LutCtx c,
                                                                lds_float* tab, uint32_t* ready,
@@ -449,7 +465,13 @@ __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L,
         const int ch = build_chunk(int(threadIdx.x) & 127);
         float v[8];
         chunk_source<DOWN>(L, c.src, c.gsl, c.slice, ch, v, ready + 2);
+#ifdef PM_LUT_STAMPS
+        if (threadIdx.x == 0) PM_STAMP(1, PM_NOW() + 0 * uint64_t(v[0] + v[7]));
+#endif
         build_table(tab, ch, v, int(threadIdx.x) >> 7);
+#ifdef PM_LUT_STAMPS
+        if (threadIdx.x == 0) PM_STAMP(2, PM_NOW());
+#endif
         // LDS operations of one wave execute in order: once another wave
         // sees this count, the table writes before it are done.  (A release
         // here would also wait for global memory, which this does not need.)
@@ -468,6 +490,9 @@ __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L,
            uint32_t(kBuildWaves * kWave))
         __builtin_amdgcn_s_sleep(1);
     __asm__ volatile("" ::: "memory");
+#ifdef PM_LUT_STAMPS
+    if (threadIdx.x == kWave * (kLutWaves - 1)) PM_STAMP(3, PM_NOW());
+#endif
     const LaneLut LL = lane_lut(lane, tab);
 
     // Slots are filled in step order, so once the first slot of a round
@@ -497,6 +522,17 @@ __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L,
         }
         if (sv[0] >= nsteps) break;
     }
+#ifdef PM_LUT_STAMPS
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t xcc;
+        __asm__ volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        PM_STAMP(4, PM_NOW());
+        PM_STAMP(5, K);
+        PM_STAMP(6, nsteps);
+        PM_STAMP(7, xcc);
+    }
+#endif
 }
 
 // Workgroup (q, slice) runs its share of the rows of run wg_run[q]: jobs of
@@ -536,6 +572,9 @@ lut_kernel(const KLaunch L) {
     const int g0 = run.g0 + kLutRows * (run.nsteps * i / nwg);
     const int g1 = run.g0 + kLutRows * (run.nsteps * (i + 1) / nwg);
     if (g0 >= g1) return;
+#ifdef PM_LUT_STAMPS
+    if (threadIdx.x == 0) PM_STAMP(0, PM_NOW());
+#endif
     LutCtx c{slice, g0, g1, int(meta & 0xFFFFu), int(meta >> 24),
              uni(int(threadIdx.x) / kWave), int(threadIdx.x) % kWave};
     switch ((meta >> 16) & 15) {
@@ -611,3 +650,17 @@ hipError_t launch_sum_slices(const float* part, int slices, int rows, float* y, 
 }
 
 }  // namespace pm
+
+#ifdef PM_LUT_STAMPS
+// Copies the stamps of the last gate/up and down launches to host memory
+// (2 x 4096 workgroups x 8 uint64) and clears them; a profiling build only.
+// Synchronous: call it with no launch in flight.
+extern "C" int pm_lut_stamps_fetch(void* host, size_t bytes) {
+    if (bytes < sizeof(pm::pm_lut_stamps)) return -1;
+    void* dev = nullptr;
+    hipError_t e = hipGetSymbolAddress(&dev, HIP_SYMBOL(pm::pm_lut_stamps));
+    if (e == hipSuccess) e = hipMemcpy(host, dev, sizeof(pm::pm_lut_stamps), hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemset(dev, 0, sizeof(pm::pm_lut_stamps));
+    return int(e);
+}
+#endif
