@@ -259,27 +259,38 @@ __device__ inline float step_compute(const StepIn<K>& in, const LaneLut& L) {
 constexpr int kLutThreads = PM_LUT_THREADS;
 constexpr int kLutWaves = kLutThreads / kWave;
 constexpr int kLutBytes = 128 * 1024;
-#ifndef PM_BUILD_WAVES
-#define PM_BUILD_WAVES 2
+// Builder waves: 2 for gate/up (one chunk per thread), 4 for down (half a
+// chunk per thread), whose builders also sum the gate/up slices and apply
+// SwiGLU before they write.
+#ifndef PM_BUILD_WAVES_GU
+#define PM_BUILD_WAVES_GU 2
 #endif
-// 128 chunks: one per builder thread (2 waves) or half of one (4 waves)
-constexpr int kBuildWaves = PM_BUILD_WAVES;
-constexpr int kBuildParts = kBuildWaves / 2;
-static_assert(kBuildWaves == 2 || kBuildWaves == 4, "two or four builder waves");
+#ifndef PM_BUILD_WAVES_DN
+#define PM_BUILD_WAVES_DN 4
+#endif
+template <bool DOWN>
+constexpr int build_waves() {
+    return DOWN ? PM_BUILD_WAVES_DN : PM_BUILD_WAVES_GU;
+}
+static_assert(build_waves<false>() == 2 || build_waves<false>() == 4, "two or four builder waves");
+static_assert(build_waves<true>() == 2 || build_waves<true>() == 4, "two or four builder waves");
 static_assert(kLutThreads % 256 == 0 && kLutThreads <= 1024, "whole waves on every SIMD");
 
 __device__ inline int build_chunk(int t) {
     return 16 * ((t & 31) >> 2) + 4 * ((t >> 5) & 3) + (t & 3);
 }
 
+// 128 chunks: with 2 builder waves a thread writes all 256 entries of one,
+// with 4 waves half of them (PARTS = 2).
+template <int PARTS>
 __device__ inline void build_table(lds_float* tab, int c, const float (&v)[8], int part) {
     float sub[32];
     sub[0] = 0.f;
 #pragma unroll
     for (int i = 1; i < 32; ++i) sub[i] = sub[i & (i - 1)] + v[__builtin_ctz(i)];
 #pragma unroll
-    for (int q0 = 0; q0 < 8 / kBuildParts; ++q0) {
-        const int q = kBuildParts == 1 ? q0 : part * (8 / kBuildParts) + q0;
+    for (int q0 = 0; q0 < 8 / PARTS; ++q0) {
+        const int q = PARTS == 1 ? q0 : part * (8 / PARTS) + q0;
         float base = 0.f;
         if (q & 1) base += v[5];
         if (q & 2) base += v[6];
@@ -460,6 +471,7 @@ __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L,
     // take their first step at once and wait for the table only when they
     // are about to compute (no workgroup barrier: a wave stalled at issue
     // must not hold up the others)
+    constexpr int kBuildWaves = build_waves<DOWN>();
     const bool builder = c.wave < kBuildWaves;
     if (builder) {
         const int ch = build_chunk(int(threadIdx.x) & 127);
@@ -468,7 +480,7 @@ __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L,
 #ifdef PM_LUT_STAMPS
         if (threadIdx.x == 0) PM_STAMP(1, PM_NOW() + 0 * uint64_t(v[0] + v[7]));
 #endif
-        build_table(tab, ch, v, int(threadIdx.x) >> 7);
+        build_table<kBuildWaves / 2>(tab, ch, v, int(threadIdx.x) >> 7);
 #ifdef PM_LUT_STAMPS
         if (threadIdx.x == 0) PM_STAMP(2, PM_NOW());
 #endif
