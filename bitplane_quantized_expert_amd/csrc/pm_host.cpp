@@ -1847,6 +1847,37 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     for (int d = 0; d < n_items; ++d) order[d] = d;
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return late[a] < late[b]; });
 
+    // Under stream capture (a HIP graph) a call may only hold LUT jobs on
+    // resident slots: a top-up, or a work list uploaded for the direct
+    // kernels or the tiles, would be recorded as a copy of host memory that
+    // later calls rewrite.  The test is conservative (an item of 6 or more
+    // uses might form tiles) and runs before any stream operation.
+    if (compute) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        HIP_TRY(hipStreamIsCapturing(compute, &cs));
+        if (cs != hipStreamCaptureStatusNone) {
+            const bool tile_shape = g.group == kMfmaGroup && g.hidden % kMfmaGroup == 0 &&
+                                    g.inter % kMfmaGroup == 0;
+            const pm_matrix_shape ms[2] = {{g.inter, g.hidden, g.group},
+                                           {g.hidden, g.inter, g.group}};
+            bool ok = !mfma && g.group == kLutGroup && g.hidden % kSliceCols == 0 &&
+                      g.hidden / kSliceCols <= 15 && g.inter % kLutRows == 0 &&
+                      g.inter % kSliceCols == 0 && g.hidden % kLutRows == 0;
+            for (int d = 0; ok && d < n_items; ++d) {
+                const size_t nu = item_uses[d].size();
+                ok = !late[d] && !(read_once && nu > 1) &&
+                     !(tile_shape && nu >= size_t(kTileMinUses));
+                for (int u : item_uses[d])
+                    for (int m = 0; ok && m < 3; ++m)
+                        ok = uses[u].k[m] <= kLutMaxK &&
+                             lut_offsets_fit(ms[m / 2], uses[u].k[m], g.plane_words);
+            }
+            if (!ok)
+                return failf(PM_ERR_STATE, "under stream capture a layer call may only run LUT "
+                             "jobs (k <= %d) on resident experts, with fewer than %d uses per "
+                             "expert and no PM_BATCH_MFMA", kLutMaxK, kTileMinUses);
+        }
+    }
     // forwards on one store run in order; on the same stream they already do
     if (s->fwd_seq > 0 && compute != s->last_compute)
         HIP_TRY(hipStreamWaitEvent(compute, forward_end(s, s->fwd_seq), 0));

@@ -83,3 +83,53 @@ def test_captured_layer_calls_replay_like_eager(flags):
         pm.pm_moe_token_forward(st, 0, ids, w, k, xd, other, flags=flags)
         torch.cuda.synchronize()
     st.close()
+
+
+def test_capture_refuses_direct_path_and_topups():
+    """Under stream capture a call that needs the direct kernels (a prefix
+    above 5) or a top-up is refused with PM_ERR_STATE before it issues
+    anything; the same call runs eagerly afterwards."""
+    report("stream capture refuses direct-path and top-up calls")
+    wl = WL
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    st = pm.pm_store_create(e, 1, wl.n_experts)
+    filler = PoolFiller(wl)
+    for i in range(wl.n_experts):
+        filler.fill(st, 0, i)
+    torch.cuda.synchronize()
+    ids = np.array([[0, 1]], np.int32)
+    w = np.array([[0.5, 0.5]], np.float32)
+    x = dev(synth.activation(wl.seed, wl.cfg, 0, 0, wl.hidden, step=70)[None])
+    y = torch.empty((1, wl.hidden), device="cuda")
+    cap = torch.cuda.Stream()
+    k_direct = np.array([[[2, 6, 3], [1, 1, 1]]], np.uint8)
+    with torch.cuda.stream(cap):
+        pm.pm_moe_token_forward(st, 0, ids, w, np.ones((1, 2, 3), np.uint8), x, y, cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(pm.PMError) as ei:
+        with torch.cuda.graph(g, stream=cap):
+            pm.pm_moe_token_forward(st, 0, ids, w, k_direct, x, y, cap)
+    assert ei.value.status == pm.PM_ERR_STATE
+    # a short slot with a host source: the top-up is refused as well
+    pw = pm.pm_expert_plane_words(e)
+    src = torch.zeros(8 * pw, dtype=torch.int32, pin_memory=True)
+    lv = torch.zeros(pm.pm_expert_levels_floats(e), dtype=torch.float32, pin_memory=True)
+    pm.pm_store_attach_host(st, 0, 2, src.data_ptr(), lv.data_ptr())
+    pm.pm_store_truncate(st, 0, 2, 1)
+    torch.cuda.synchronize()
+    g2 = torch.cuda.CUDAGraph()
+    with pytest.raises(pm.PMError) as ei:
+        with torch.cuda.graph(g2, stream=cap):
+            pm.pm_moe_token_forward(st, 0, np.array([[2, 3]], np.int32), w,
+                                    np.full((1, 2, 3), 3, np.uint8), x, y, cap,
+                                    flags=pm.PM_AUTO_TOPUP)
+    assert ei.value.status == pm.PM_ERR_STATE
+    assert pm.pm_store_resident(st, 0, 2) == 1
+    # eagerly, both run
+    pm.pm_moe_token_forward(st, 0, ids, w, k_direct, x, y, cap)
+    pm.pm_moe_token_forward(st, 0, np.array([[2, 3]], np.int32), w,
+                            np.full((1, 2, 3), 3, np.uint8), x, y, cap, flags=pm.PM_AUTO_TOPUP)
+    torch.cuda.synchronize()
+    assert pm.pm_store_resident(st, 0, 2) == 3
+    st.close()
