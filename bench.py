@@ -342,11 +342,14 @@ def wg_timeline(pm, torch, run, steps, btb, groups=20):
                 "wg_median": np.median(t[:, 4] - t[:, 0]) / 100,
                 "wg_p90": np.percentile(t[:, 4] - t[:, 0], 90) / 100,
                 "wg_max": (t[:, 4] - t[:, 0]).max() / 100,
-                "first_end": (t[:, 4].min() - base) / 100, "workgroups": int(used.sum())})
+                "first_end": (t[:, 4].min() - base) / 100, "workgroups": int(used.sum()),
+                **{f"k{k}_wg_median": float(np.median(t[t[:, 5] == k, 4] - t[t[:, 5] == k, 0]) / 100)
+                   for k in range(1, 6) if (t[:, 5] == k).sum() >= 4}})
             b[:] = 0
         buf[:] = 0
-    return {("down" if d else "gateup"): {k: round(float(np.median([r[k] for r in v])), 2)
-                                          for k in v[0]} for d, v in per.items()}
+    return {("down" if d else "gateup"): {k: round(float(np.median([r[k] for r in v if k in r])), 2)
+                                          for k in sorted({k for r in v for k in r})}
+            for d, v in per.items()}
 
 
 def graph_replay(torch, cap, body, reps):

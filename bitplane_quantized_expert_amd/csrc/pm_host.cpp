@@ -1367,10 +1367,12 @@ static void split_runs(KLaunch& L, int n_total) {
     n_total = std::min(kMaxLaunchWgq, std::max(n_total, R));
     double cost[kMaxLaunchJobs], fixed[kMaxLaunchJobs], share[kMaxLaunchJobs];
     double C = 0, Amax = 0;
+    const bool down = L.gu != nullptr;
     for (int r = 0; r < R; ++r) {
         const int k = L.job[r0[r]].k;         // one prefix per run
-        cost[r] = double(r0[r + 1] - r0[r]) * double(L.rows / kLutRows) * double(lut_step_ns(k));
-        fixed[r] = double(lut_fixed_ns(k));
+        cost[r] = double(r0[r + 1] - r0[r]) * double(L.rows / kLutRows) *
+                  double(lut_step_ns(k, down));
+        fixed[r] = double(lut_fixed_ns(k, down));
         C += cost[r];
         Amax = std::max(Amax, fixed[r]);
     }

@@ -135,23 +135,34 @@ struct KLaunch {
     KJob job[kMaxLaunchJobs];
 };
 static_assert(sizeof(KLaunch) <= 4096, "kernel arguments are limited to 4 KiB");
-// Cost model of a LUT workgroup (one 1024-column slice), fitted on gfx950 to
-// the compute phase of workgroups of the 512-expert layer step (rows
-// streamed from HBM): a fixed part per workgroup at prefix k (the latency of
-// its first and last steps) plus a part per 8-row step, both in ns.
-#ifndef PM_LUT_FIXED
-#define PM_LUT_FIXED 1600, 1200, 2000, 3200, 2900
+// Cost model of a LUT workgroup (one 1024-column slice), fitted on gfx950 by
+// least squares to the workgroup timelines of the 512-expert layer step
+// (rows streamed from HBM; greedy prefixes at a mean of 2.5 bits, and a
+// uniform draw of k = 1..5): a fixed part per workgroup at prefix k (the
+// prologue and the latency of its first and last steps) plus a part per
+// 8-row step, both in ns, for gate/up launches and for down launches (whose
+// prologue also sums the gate/up partials and applies SwiGLU).
+#ifndef PM_LUT_FIXED_GU
+#define PM_LUT_FIXED_GU 3000, 3250, 3100, 4700, 8000
 #endif
-#ifndef PM_LUT_STEP
-#define PM_LUT_STEP 63, 131, 223, 416, 847
+#ifndef PM_LUT_STEP_GU
+#define PM_LUT_STEP_GU 55, 92, 172, 316, 620
 #endif
-__host__ __device__ inline int64_t lut_step_ns(int k) {
-    constexpr int64_t ns[5] = {PM_LUT_STEP};
-    return ns[k < 1 ? 0 : (k > 5 ? 4 : k - 1)];
+#ifndef PM_LUT_FIXED_DN
+#define PM_LUT_FIXED_DN 4350, 4300, 4050, 6450, 9400
+#endif
+#ifndef PM_LUT_STEP_DN
+#define PM_LUT_STEP_DN 53, 94, 189, 265, 574
+#endif
+inline int64_t lut_step_ns(int k, bool down) {
+    constexpr int64_t gu[5] = {PM_LUT_STEP_GU}, dn[5] = {PM_LUT_STEP_DN};
+    const int i = k < 1 ? 0 : (k > 5 ? 4 : k - 1);
+    return down ? dn[i] : gu[i];
 }
-__host__ __device__ inline int64_t lut_fixed_ns(int k) {
-    constexpr int64_t ns[5] = {PM_LUT_FIXED};
-    return ns[k < 1 ? 0 : (k > 5 ? 4 : k - 1)];
+inline int64_t lut_fixed_ns(int k, bool down) {
+    constexpr int64_t gu[5] = {PM_LUT_FIXED_GU}, dn[5] = {PM_LUT_FIXED_DN};
+    const int i = k < 1 ? 0 : (k > 5 ? 4 : k - 1);
+    return down ? dn[i] : gu[i];
 }
 
 // Kernel launchers (pm_kernels.hip).  All return hipError_t of the launch.
