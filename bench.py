@@ -309,7 +309,7 @@ def timed(torch, fn, n):
     return time.perf_counter() - t0
 
 
-def wg_timeline(pm, torch, run, steps, btb, groups=20):
+def wg_timeline(pm, torch, run, steps, btb, groups=20, dump=None):
     """Workgroup timeline of the LUT launches (the stamped build): groups of
     `btb` steps run back to back; after each, the stamps of the group's last
     gate/up and down launches (s_memrealtime, 10 ns) give per launch:
@@ -322,13 +322,16 @@ def wg_timeline(pm, torch, run, steps, btb, groups=20):
     lib = pm.lib()
     lib.pm_lut_stamps_fetch.restype = ctypes.c_int
     lib.pm_lut_stamps_fetch.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
-    buf = np.zeros((2, 256 * 16, 8), np.uint64)
+    buf = np.zeros((2, 256 * 16, 12), np.uint64)
     per = {0: [], 1: []}
+    raw = []
     for gi in range(groups):
         for i in range(btb):
             run(steps[(gi * btb + i) % len(steps)])
         torch.cuda.synchronize()
         assert lib.pm_lut_stamps_fetch(buf.ctypes.data, buf.nbytes) == 0
+        if dump:
+            raw.append(buf.copy())
         for down in (0, 1):
             b = buf[down].astype(np.int64)
             used = b[:, 4] > 0
@@ -343,10 +346,14 @@ def wg_timeline(pm, torch, run, steps, btb, groups=20):
                 "wg_p90": np.percentile(t[:, 4] - t[:, 0], 90) / 100,
                 "wg_max": (t[:, 4] - t[:, 0]).max() / 100,
                 "first_end": (t[:, 4].min() - base) / 100, "workgroups": int(used.sum()),
+                "entry_spread": (t[:, 8].max() - t[:, 8].min()) / 100,
+                "entry_to_start": np.median(t[:, 0] - t[:, 8]) / 100,
                 **{f"k{k}_wg_median": float(np.median(t[t[:, 5] == k, 4] - t[t[:, 5] == k, 0]) / 100)
                    for k in range(1, 6) if (t[:, 5] == k).sum() >= 4}})
             b[:] = 0
         buf[:] = 0
+    if dump:
+        np.savez_compressed(dump, stamps=np.stack(raw))
     return {("down" if d else "gateup"): {k: round(float(np.median([r[k] for r in v if k in r])), 2)
                                           for k in sorted({k for r in v for k in r})}
             for d, v in per.items()}
@@ -822,6 +829,8 @@ def main():
                     help="with the stamped build (libpm_stamps.so): after the timed loop, run "
                          "groups of N steps back to back and report the workgroup timeline of "
                          "each group's last gate/up and down launches")
+    ap.add_argument("--wg-dump", metavar="FILE",
+                    help="with --wg-timeline: also save the raw stamps of every group (.npz)")
     ap.add_argument("--kfix", type=int, default=0, metavar="K",
                     help="every use of the layer step at prefix K (per-prefix profiles)")
     ap.add_argument("--graph-only", type=int, default=0, metavar="R",
@@ -956,7 +965,7 @@ def main():
             run_cap(s)
 
     if args.wg_timeline:
-        res = wg_timeline(pm, torch, run, list(steps), args.wg_timeline)
+        res = wg_timeline(pm, torch, run, list(steps), args.wg_timeline, dump=args.wg_dump)
         st.close()
         print(json.dumps({"wg_timeline": res}), flush=True)
         return 0

@@ -1430,7 +1430,9 @@ static void split_runs(KLaunch& L, int n_total) {
         run.wg0 = int16_t(w);
         run.nwg = int16_t(a[r]);
         run.meta = uint32_t(uint16_t(jb.src)) | (uint32_t(jb.k) << 16) | (uint32_t(jb.gsl) << 24);
-        std::memset(L.wg_run + w, r, size_t(a[r]));
+        const uint32_t info = uint32_t(r) | (uint32_t(uint16_t(jb.src)) << 8) |
+                              (uint32_t(jb.gsl) << 24);
+        for (int q = w; q < w + a[r]; ++q) L.wg_info[q] = info;
         w += a[r];
     }
     L.n_wgq = w;

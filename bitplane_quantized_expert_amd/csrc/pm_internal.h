@@ -130,7 +130,10 @@ struct KLaunch {
     int32_t gu_smax, inter, n_zero;
     int32_t fold;                  // down: add wt * row sum into out (float atomics)
                                    // instead of storing the partial
-    uint8_t wg_run[kMaxLaunchWgq]; // run of workgroup q
+    // workgroup q: its run (bits 0-7) and that run's activation source
+    // (bits 8-23) and gate/up slice counts (bits 24-31), so that its first
+    // reads of the source need no second lookup
+    uint32_t wg_info[kMaxLaunchWgq];
     KRun run[kMaxLaunchJobs];
     KJob job[kMaxLaunchJobs];
 };

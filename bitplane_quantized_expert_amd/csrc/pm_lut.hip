@@ -300,9 +300,6 @@ __device__ inline void build_table(lds_float* tab, int c, const float (&v)[8], i
     }
 }
 
-// The 8 activation values of chunk c: x of token `src`, or h of use `src`
-// formed from its gate/up partials (slices summed in order; slices past a
-// matrix's count read slice 0 again and add 0).
 #ifndef PM_X_FIRST
 #define PM_X_FIRST 1
 #endif
@@ -317,58 +314,53 @@ __device__ inline void loads_issued(uint32_t* issued) {
     }
 }
 
-template <bool DOWN>
-__device__ inline void chunk_source(const KLaunch& L, int src, int gsl, int slice, int c,
-                                    float (&v)[8], uint32_t* issued) {
-    const int col = kSliceCols * slice + 8 * c;
-    if constexpr (!DOWN) {
-        const float* x = L.x + size_t(src) * L.x_stride + col;
-        const f32x4 a = *(g_f32x4*)x, b = *(g_f32x4*)(x + 4);
+// The 8 values of x of token `src` in chunk c of the slice.
+__device__ inline void chunk_x(const KLaunch& L, int src, int slice, int c, float (&v)[8],
+                               uint32_t* issued) {
+    const float* x = L.x + size_t(src) * L.x_stride + kSliceCols * slice + 8 * c;
+    const f32x4 a = *(g_f32x4*)x, b = *(g_f32x4*)(x + 4);
+    loads_issued(issued);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// Down's h = SiLU(g) * u for the slice's columns 4t .. 4t + 3 of use `src`
+// (t < 256, one builder thread each): the gate/up partials of those columns
+// summed over the slices of each matrix in slice order (slices past a
+// matrix's count read slice 0 again and add 0).  The loads are counted on
+// `issued` once they are in the memory queue.
+__device__ inline f32x4 h_cols(const KLaunch& L, int src, int gsl, int slice, int t,
+                               uint32_t* issued) {
+    const int ngs = gsl & 15, nus = gsl >> 4;
+    const int inter = L.inter, smax = L.gu_smax;
+    const int col = kSliceCols * slice + 4 * t;
+    const float* pg = L.gu + (size_t(src) * 2) * smax * inter + col;
+    const float* pu = pg + size_t(smax) * inter;
+    f32x4 gs, us;
+    if (smax <= 4) {
+        f32x4 gv[4], uv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            gv[q] = *(g_f32x4*)(pg + size_t(q < ngs ? q : 0) * inter);
+            uv[q] = *(g_f32x4*)(pu + size_t(q < nus ? q : 0) * inter);
+        }
         loads_issued(issued);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        gs = gv[0];
+        us = uv[0];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) {
+            gs += q < ngs ? gv[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+            us += q < nus ? uv[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     } else {
-        const int ngs = gsl & 15, nus = gsl >> 4;
-        const int inter = L.inter, smax = L.gu_smax;
-        const float* pg = L.gu + (size_t(src) * 2) * smax * inter + col;
-        const float* pu = pg + size_t(smax) * inter;
-        f32x4 gs[2], us[2];
-        if (smax <= 4) {
-            f32x4 gv[4][2], uv[4][2];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    gv[q][h] = *(g_f32x4*)(pg + size_t(q < ngs ? q : 0) * inter + 4 * h);
-                    uv[q][h] = *(g_f32x4*)(pu + size_t(q < nus ? q : 0) * inter + 4 * h);
-                }
-            loads_issued(issued);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                gs[h] = gv[0][h];
-                us[h] = uv[0][h];
-#pragma unroll
-                for (int q = 1; q < 4; ++q) {
-                    gs[h] += q < ngs ? gv[q][h] : f32x4{0.f, 0.f, 0.f, 0.f};
-                    us[h] += q < nus ? uv[q][h] : f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-            }
-        } else {
-            loads_issued(issued);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                gs[h] = *(g_f32x4*)(pg + 4 * h);
-                for (int q = 1; q < ngs; ++q) gs[h] += *(g_f32x4*)(pg + size_t(q) * inter + 4 * h);
-                us[h] = *(g_f32x4*)(pu + 4 * h);
-                for (int q = 1; q < nus; ++q) us[h] += *(g_f32x4*)(pu + size_t(q) * inter + 4 * h);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[i] = silu_mul(gs[0][i], us[0][i]);
-            v[4 + i] = silu_mul(gs[1][i], us[1][i]);
-        }
+        loads_issued(issued);
+        gs = *(g_f32x4*)pg;
+        for (int q = 1; q < ngs; ++q) gs += *(g_f32x4*)(pg + size_t(q) * inter);
+        us = *(g_f32x4*)pu;
+        for (int q = 1; q < nus; ++q) us += *(g_f32x4*)(pu + size_t(q) * inter);
     }
+    return f32x4{silu_mul(gs.x, us.x), silu_mul(gs.y, us.y), silu_mul(gs.z, us.z),
+                 silu_mul(gs.w, us.w)};
 }
 
 // Steps in flight per wave (the ring): deeper where a step is short.
@@ -389,25 +381,78 @@ constexpr int lut_ring() {
 // its compute unit's vector-memory queue is full, so waves that issue loads
 // early must not be the ones that build).
 struct LutCtx {
-    int slice, g0, g1, src, gsl;
+    int slice, g0, g1;
     int wave, lane;
 };
 
 // Workgroup timeline, in a build with PM_LUT_STAMPS only (a profiling build;
 // the product build has none of it): s_memrealtime (100 MHz) at the
-// workgroup's start (0), when the builders hold their source values (1),
-// when their table writes are issued (2), when the last wave starts to
-// compute (3) and at the end (4); then k (5), steps (6) and the XCD (7).
+// workgroup's start (0, once it holds its info word), when the builders hold
+// their source values (1), when their table writes are issued (2), when the
+// last wave starts to compute (3) and at the end (4); then k (5), steps (6)
+// and the XCD (7); then the workgroup's first instruction (8).
 // The last launch of each kind (gate/up, down) leaves its stamps.
 #ifdef PM_LUT_STAMPS
 constexpr int kStampWgs = kMaxLaunchWgq * 16;
-__device__ unsigned long long pm_lut_stamps[2][kStampWgs][8];
+constexpr int kStampFields = 12;
+__device__ unsigned long long pm_lut_stamps[2][kStampWgs][kStampFields];
 #define PM_STAMP(i, v)                                                                      \
     pm_lut_stamps[DOWN][(blockIdx.y * gridDim.x + blockIdx.x) % kStampWgs][i] = (v)
 #define PM_NOW() __builtin_amdgcn_s_memrealtime()
 #else
 #define PM_STAMP(i, v) ((void)0)
 #endif
+
+// The builder waves form the table: the slice's activation (x of token
+// `src`, or h of use `src`, formed once per column by the builders together
+// in LDS behind the table and its counters), then its subset sums, and
+// announce it on `ready`.  This needs no more than the workgroup's info word,
+// so it starts before the workgroup reads its run.
+template <bool DOWN>
+__device__ inline void build_lut(const KLaunch& L, int src, int gsl, int slice, lds_float* tab,
+                                 uint32_t* ready) {
+    constexpr int kBuildWaves = build_waves<DOWN>();
+    const int ch = build_chunk(int(threadIdx.x) & 127);
+    float v[8];
+    if constexpr (!DOWN) {
+        chunk_x(L, src, slice, ch, v, ready + 2);
+    } else {
+        static_assert(build_waves<true>() * kWave * 4 == kSliceCols, "4 columns per builder");
+        typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+        lds_float* hb = tab + kLutBytes / 4 + 4;
+        const int t = int(threadIdx.x);
+        *reinterpret_cast<lds_f32x4*>(hb + 4 * t) = h_cols(L, src, gsl, slice, t, ready + 2);
+        __asm__ volatile("" ::: "memory");
+        __hip_atomic_fetch_add(ready + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        while (__hip_atomic_load(ready + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) <
+               uint32_t(kBuildWaves * kWave))
+            __builtin_amdgcn_s_sleep(1);
+        __asm__ volatile("" ::: "memory");
+        const f32x4 a = *reinterpret_cast<const lds_f32x4*>(hb + 8 * ch);
+        const f32x4 b = *reinterpret_cast<const lds_f32x4*>(hb + 8 * ch + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+#ifdef PM_LUT_STAMPS
+    if (threadIdx.x == 0) {
+        // the stamp follows the arrival of the builder's source values
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sum += v[i];
+        __asm__ volatile("" ::"v"(sum));
+        PM_STAMP(1, PM_NOW());
+    }
+#endif
+    build_table<kBuildWaves / 2>(tab, ch, v, int(threadIdx.x) >> 7);
+#ifdef PM_LUT_STAMPS
+    if (threadIdx.x == 0) PM_STAMP(2, PM_NOW());
+#endif
+    // LDS operations of one wave execute in order: once another wave sees
+    // this count, the table writes before it are done.  (A release here
+    // would also wait for global memory, which this does not need.)
+    __asm__ volatile("" ::: "memory");
+    __hip_atomic_fetch_add(ready, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
 template <bool DOWN, bool FOLD, int K>
 __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L, LutCtx c,
@@ -473,23 +518,6 @@ __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L,
     // must not hold up the others)
     constexpr int kBuildWaves = build_waves<DOWN>();
     const bool builder = c.wave < kBuildWaves;
-    if (builder) {
-        const int ch = build_chunk(int(threadIdx.x) & 127);
-        float v[8];
-        chunk_source<DOWN>(L, c.src, c.gsl, c.slice, ch, v, ready + 2);
-#ifdef PM_LUT_STAMPS
-        if (threadIdx.x == 0) PM_STAMP(1, PM_NOW() + 0 * uint64_t(v[0] + v[7]));
-#endif
-        build_table<kBuildWaves / 2>(tab, ch, v, int(threadIdx.x) >> 7);
-#ifdef PM_LUT_STAMPS
-        if (threadIdx.x == 0) PM_STAMP(2, PM_NOW());
-#endif
-        // LDS operations of one wave execute in order: once another wave
-        // sees this count, the table writes before it are done.  (A release
-        // here would also wait for global memory, which this does not need.)
-        __asm__ volatile("" ::: "memory");
-        __hip_atomic_fetch_add(ready, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
     if (PM_X_FIRST && !builder) {
         while (__hip_atomic_load(ready + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) <
                uint32_t(kBuildWaves * kWave))
@@ -547,56 +575,70 @@ __device__ __attribute__((always_inline)) inline void lut_body(const KLaunch& L,
 #endif
 }
 
-// Workgroup (q, slice) runs its share of the rows of run wg_run[q]: jobs of
-// one prefix and one activation source, named in the run's meta with k, so
-// that a workgroup's first reads do not depend on one another.  Job
-// descriptions are read straight from the argument block.
-// One workgroup per compute unit (its table fills the LDS).
+// Workgroup (q, slice) runs its share of the rows of its run (named in its
+// info word, with the run's source): jobs of one prefix and one activation
+// source, named in the run's meta with k.  Its builder waves start on the
+// table as soon as the info word is read; job descriptions are read straight
+// from the argument block.  One workgroup per compute unit (its table fills
+// the LDS).
 template <bool DOWN, bool FOLD>
 __global__ __launch_bounds__(kLutThreads) __attribute__((amdgpu_waves_per_eu(kLutWaves / 4,
                                                                               kLutWaves / 4))) void
 lut_kernel(const KLaunch L) {
     // the kernel's one LDS object, at address 0: the lookups use the v_perm
     // result as the address; then the count of builder threads done
-    __shared__ __attribute__((aligned(16))) float lds_buf[kLutBytes / 4 + 4];
+#ifdef PM_LUT_STAMPS
+    const unsigned long long t_entry = PM_NOW();
+#endif
+    __shared__ __attribute__((aligned(16))) float lds_buf[kLutBytes / 4 + 4 + (DOWN ? kSliceCols : 0)];
     uint32_t* ready = reinterpret_cast<uint32_t*>(lds_buf + kLutBytes / 4);
     uint32_t* next = ready + 1;
     if (threadIdx.x == 0) {
         *ready = 0u;
         *next = 0u;
         ready[2] = 0u;
-    }
-    if (!DOWN) {
-        // clear the output a folded down launch will add into (it runs after
-        // this launch on the same stream)
-        const int nz = L.n_zero;
-        const int nt = int(gridDim.x * gridDim.y) * kLutThreads;
-        for (int i = int(blockIdx.y * gridDim.x + blockIdx.x) * kLutThreads + int(threadIdx.x);
-             i < nz; i += nt)
-            L.zero[i] = 0.f;
+        ready[3] = 0u;
     }
     __syncthreads();
-    // the workgroup's share of its run's steps (an even split)
     const int q = blockIdx.x, slice = blockIdx.y;
-    const KRun& run = L.run[L.wg_run[q]];
+    const uint32_t info = L.wg_info[q];
+#ifdef PM_LUT_STAMPS
+    if (threadIdx.x == 0) {
+        PM_STAMP(0, PM_NOW());
+        PM_STAMP(8, t_entry);
+    }
+#endif
+    const int wave = uni(int(threadIdx.x) / kWave);
+    if (wave < build_waves<DOWN>())
+        build_lut<DOWN>(L, int((info >> 8) & 0xFFFFu), int(info >> 24), slice,
+                        (lds_float*)lds_buf, ready);
+    // the workgroup's share of its run's steps (an even split)
+    const KRun& run = L.run[info & 255u];
     const uint32_t meta = run.meta;
     const int i = q - run.wg0, nwg = run.nwg;
     const int g0 = run.g0 + kLutRows * (run.nsteps * i / nwg);
     const int g1 = run.g0 + kLutRows * (run.nsteps * (i + 1) / nwg);
-    if (g0 >= g1) return;
-#ifdef PM_LUT_STAMPS
-    if (threadIdx.x == 0) PM_STAMP(0, PM_NOW());
-#endif
-    LutCtx c{slice, g0, g1, int(meta & 0xFFFFu), int(meta >> 24),
-             uni(int(threadIdx.x) / kWave), int(threadIdx.x) % kWave};
-    switch ((meta >> 16) & 15) {
-        case 1: lut_body<DOWN, FOLD, 1>(L, c, (lds_float*)lds_buf, ready, next); break;
-        case 2: lut_body<DOWN, FOLD, 2>(L, c, (lds_float*)lds_buf, ready, next); break;
-        case 3: lut_body<DOWN, FOLD, 3>(L, c, (lds_float*)lds_buf, ready, next); break;
-        case 4: lut_body<DOWN, FOLD, 4>(L, c, (lds_float*)lds_buf, ready, next); break;
+    if (g0 < g1) {
+        LutCtx c{slice, g0, g1, wave, int(threadIdx.x) % kWave};
+        switch ((meta >> 16) & 15) {
+            case 1: lut_body<DOWN, FOLD, 1>(L, c, (lds_float*)lds_buf, ready, next); break;
+            case 2: lut_body<DOWN, FOLD, 2>(L, c, (lds_float*)lds_buf, ready, next); break;
+            case 3: lut_body<DOWN, FOLD, 3>(L, c, (lds_float*)lds_buf, ready, next); break;
+            case 4: lut_body<DOWN, FOLD, 4>(L, c, (lds_float*)lds_buf, ready, next); break;
 #if PM_LUT_THREADS == 512
-        default: lut_body<DOWN, FOLD, 5>(L, c, (lds_float*)lds_buf, ready, next); break;
+            default: lut_body<DOWN, FOLD, 5>(L, c, (lds_float*)lds_buf, ready, next); break;
 #endif
+        }
+    }
+    if (!DOWN) {
+        // clear the output a folded down launch will add into (it runs after
+        // this launch on the same stream), last, so that no wait of this
+        // launch covers these stores
+        const int nz = L.n_zero;
+        const int nt = int(gridDim.x * gridDim.y) * kLutThreads;
+        for (int j = int(blockIdx.y * gridDim.x + blockIdx.x) * kLutThreads + int(threadIdx.x);
+             j < nz; j += nt)
+            L.zero[j] = 0.f;
     }
 }
 
@@ -665,7 +707,7 @@ hipError_t launch_sum_slices(const float* part, int slices, int rows, float* y, 
 
 #ifdef PM_LUT_STAMPS
 // Copies the stamps of the last gate/up and down launches to host memory
-// (2 x 4096 workgroups x 8 uint64) and clears them; a profiling build only.
+// (2 x 4096 workgroups x 12 uint64) and clears them; a profiling build only.
 // Synchronous: call it with no launch in flight.
 extern "C" int pm_lut_stamps_fetch(void* host, size_t bytes) {
     if (bytes < sizeof(pm::pm_lut_stamps)) return -1;
