@@ -138,24 +138,27 @@ struct KLaunch {
     KJob job[kMaxLaunchJobs];
 };
 static_assert(sizeof(KLaunch) <= 4096, "kernel arguments are limited to 4 KiB");
-// Cost model of a LUT workgroup (one 1024-column slice), fitted on gfx950 by
-// least squares to the workgroup timelines of the 512-expert layer step
-// (rows streamed from HBM; greedy prefixes at a mean of 2.5 bits, and a
-// uniform draw of k = 1..5): a fixed part per workgroup at prefix k (the
-// prologue and the latency of its first and last steps) plus a part per
-// 8-row step, both in ns, for gate/up launches and for down launches (whose
-// prologue also sums the gate/up partials and applies SwiGLU).
+// Cost model of a LUT workgroup (one 1024-column slice), fitted on gfx950 to
+// the workgroup timelines of the 512-expert layer step (rows streamed from
+// HBM; greedy prefixes at a mean of 2.5 bits): a part per 8-row step, the
+// workgroup's steady rate from its first computing step to its end, plus a
+// fixed part per workgroup at prefix k, the median remainder of its end
+// after the launch's first workgroup started (prologue, latency of the first
+// and last steps), both in ns, for gate/up launches and for down launches
+// (whose prologue also forms h from the gate/up partials).  Down workgroups
+// at k = 4, 5 hold fewer steps than waves, so their per-step part is gate/up's
+// at the same k (the same work per step) and the rest goes to the fixed part.
 #ifndef PM_LUT_FIXED_GU
-#define PM_LUT_FIXED_GU 3000, 3250, 3100, 4700, 8000
+#define PM_LUT_FIXED_GU 2460, 2410, 2540, 3760, 4880
 #endif
 #ifndef PM_LUT_STEP_GU
-#define PM_LUT_STEP_GU 55, 92, 172, 316, 620
+#define PM_LUT_STEP_GU 67, 112, 204, 429, 1090
 #endif
 #ifndef PM_LUT_FIXED_DN
-#define PM_LUT_FIXED_DN 4350, 4300, 4050, 6450, 9400
+#define PM_LUT_FIXED_DN 3010, 2930, 2910, 4700, 5100
 #endif
 #ifndef PM_LUT_STEP_DN
-#define PM_LUT_STEP_DN 53, 94, 189, 265, 574
+#define PM_LUT_STEP_DN 71, 117, 226, 430, 1000
 #endif
 inline int64_t lut_step_ns(int k, bool down) {
     constexpr int64_t gu[5] = {PM_LUT_STEP_GU}, dn[5] = {PM_LUT_STEP_DN};
