@@ -34,8 +34,8 @@ KERNEL_SOURCES = ("bitplane_quantized_expert_amd/csrc/pm_lut.hip",
 # passes of this benchmark, each scaled by the same counter on the 1 GiB
 # negation kernel (see --summarize-counters); reported only while the kernel
 # sources still have this digest.
-TRAFFIC = {"sources_sha256": "8e44278d134a1536272d0ed709378882f2e288aa06b83f177257e21faa6c96d7",
-           "bytes_per_launch": 44910937}
+TRAFFIC = {"sources_sha256": "97a079b090cce033984ac75aed401ee56ab948585114f7da4cd8c4b7921c915c",
+           "bytes_per_launch": 44718390}
 
 
 def log(msg):

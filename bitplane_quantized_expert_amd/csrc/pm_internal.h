@@ -138,27 +138,27 @@ struct KLaunch {
     KJob job[kMaxLaunchJobs];
 };
 static_assert(sizeof(KLaunch) <= 4096, "kernel arguments are limited to 4 KiB");
-// Cost model of a LUT workgroup (one 1024-column slice), fitted on gfx950 to
-// the workgroup timelines of the 512-expert layer step (rows streamed from
-// HBM; greedy prefixes at a mean of 2.5 bits): a part per 8-row step, the
-// workgroup's steady rate from its first computing step to its end, plus a
-// fixed part per workgroup at prefix k, the median remainder of its end
-// after the launch's first workgroup started (prologue, latency of the first
-// and last steps), both in ns, for gate/up launches and for down launches
-// (whose prologue also forms h from the gate/up partials).  Down workgroups
-// at k = 4, 5 hold fewer steps than waves, so their per-step part is gate/up's
-// at the same k (the same work per step) and the rest goes to the fixed part.
+// Cost model of a LUT workgroup (16 waves, one 1024-column slice), fitted on
+// gfx950 to the workgroup timelines of the 512-expert layer step (rows
+// streamed from HBM; greedy prefixes at a mean of 2.5 bits): a part per
+// 8-row step, the workgroup's steady rate from its first computing step to
+// its end, plus a fixed part per workgroup at prefix k, the median remainder
+// of its end after the launch's first workgroup started (prologue, latency of
+// the first and last steps), both in ns, for gate/up launches and for down
+// launches (whose prologue also forms h from the gate/up partials).  At
+// k = 4, 5 a workgroup holds fewer steps than waves, so there the "step" part
+// is mostly the latency of one step.
 #ifndef PM_LUT_FIXED_GU
-#define PM_LUT_FIXED_GU 2460, 2410, 2540, 3760, 4880
+#define PM_LUT_FIXED_GU 2760, 3630, 2840, 4280, 5800
 #endif
 #ifndef PM_LUT_STEP_GU
-#define PM_LUT_STEP_GU 67, 112, 204, 429, 1090
+#define PM_LUT_STEP_GU 57, 81, 173, 303, 1250
 #endif
 #ifndef PM_LUT_FIXED_DN
-#define PM_LUT_FIXED_DN 3010, 2930, 2910, 4700, 5100
+#define PM_LUT_FIXED_DN 2890, 3080, 2920, 3250, 4710
 #endif
 #ifndef PM_LUT_STEP_DN
-#define PM_LUT_STEP_DN 71, 117, 226, 430, 1000
+#define PM_LUT_STEP_DN 49, 91, 178, 460, 2120
 #endif
 inline int64_t lut_step_ns(int k, bool down) {
     constexpr int64_t gu[5] = {PM_LUT_STEP_GU}, dn[5] = {PM_LUT_STEP_DN};

@@ -253,8 +253,10 @@ __device__ inline float step_compute(const StepIn<K>& in, const LaneLut& L) {
 // subset sums of it; a half-wave writes 32 different banks.  Each entry is a
 // plain fp32 sum of its columns (a zero term adds nothing, so one-hot x gives
 // exact columns).
+// A workgroup is 16 waves (4 per SIMD): at 126 VGPRs each, enough waves to
+// hide the lookups' LDS latency and the loads' HBM latency between them.
 #ifndef PM_LUT_THREADS
-#define PM_LUT_THREADS 512
+#define PM_LUT_THREADS 1024
 #endif
 constexpr int kLutThreads = PM_LUT_THREADS;
 constexpr int kLutWaves = kLutThreads / kWave;
@@ -363,9 +365,11 @@ __device__ inline f32x4 h_cols(const KLaunch& L, int src, int gsl, int slice, in
                  silu_mul(gs.w, us.w)};
 }
 
-// Steps in flight per wave (the ring): deeper where a step is short.
+// Steps in flight per wave (the ring): two where a step is short (k <= 2),
+// one from k = 3 (with 16 waves, deeper rings cost registers the lookups
+// need; two at k = 4 made the launch a third slower).
 #ifndef PM_RING
-#define PM_RING 4, 3, 2, 2, 2
+#define PM_RING 2, 2, 1, 1, 1
 #endif
 constexpr int kRing[5] = {PM_RING};
 template <int K>
@@ -625,9 +629,7 @@ lut_kernel(const KLaunch L) {
             case 2: lut_body<DOWN, FOLD, 2>(L, c, (lds_float*)lds_buf, ready, next); break;
             case 3: lut_body<DOWN, FOLD, 3>(L, c, (lds_float*)lds_buf, ready, next); break;
             case 4: lut_body<DOWN, FOLD, 4>(L, c, (lds_float*)lds_buf, ready, next); break;
-#if PM_LUT_THREADS == 512
             default: lut_body<DOWN, FOLD, 5>(L, c, (lds_float*)lds_buf, ready, next); break;
-#endif
         }
     }
     if (!DOWN) {
