@@ -36,6 +36,13 @@ KERNEL_SOURCES = ("bitplane_quantized_expert_amd/csrc/pm_lut.hip",
 # sources still have this digest.
 TRAFFIC = {"sources_sha256": "97a079b090cce033984ac75aed401ee56ab948585114f7da4cd8c4b7921c915c",
            "bytes_per_launch": 44718390}
+# Mean kernel durations of the same step in a rocprofv3 kernel trace of
+# graph-replayed steps (back to back, as in the timed loop): the gate/up
+# launch, the down launch with the combine folded in, and the step from one
+# gate/up start to the next; reported only while the kernel sources still
+# have this digest.
+TRACE = {"sources_sha256": TRAFFIC["sources_sha256"], "gateup_us": 12.95, "down_us": 8.75,
+         "step_us": 21.98, "profile": "profiles/lut_kernel_moe_layer_e512_h4096_i1024_g128_k2.5.md"}
 
 
 def log(msg):
@@ -1100,6 +1107,9 @@ def main():
     evs = event_pass(4)
     dn_ms = np.array([b.elapsed_time(c) for _, b, c, _ in evs])
     cb_ms = np.array([c.elapsed_time(d) for _, _, c, d in evs])
+    # a step whose down launch folds the combine in runs no combine kernel:
+    # its third stage holds only the events themselves
+    folded = np.array([int(k3[s].max()) <= 5 for s in steps])
     gu_b = np.array([gateup_bytes(wl, k3[s]) for s in steps])
     achieved = float(gu_b.mean() / (gu_ms.mean() * 1e-3) / 1e9)
     log(f"gate/up {gu_ms.mean() * 1e3:.1f} us, down {dn_ms.mean() * 1e3:.1f} us, "
@@ -1125,13 +1135,28 @@ def main():
         "step_us": step_dist,
         "cache_state": cache_state,
         "stage_us": {"gateup": round(gu_ms.mean() * 1e3, 2), "down": round(dn_ms.mean() * 1e3, 2),
-                     "combine": round(cb_ms.mean() * 1e3, 2)},
-        "kernel_sum_us": round((gu_ms.mean() + dn_ms.mean() + cb_ms.mean()) * 1e3, 2),
+                     "combine": (round(cb_ms[~folded].mean() * 1e3, 2) if (~folded).any()
+                                 else None),
+                     "steps_with_combine_kernel": int((~folded).sum()),
+                     "how": "HIP events on the library's stream: gate/up between its own start "
+                            "and stop events (one pass), down between events after each stage "
+                            "(another pass); each launch that carries events runs longer than "
+                            "in the timed loop. The combine is its own kernel only in steps "
+                            "with a prefix above 5; otherwise the down launch adds into y"},
+        "kernel_sum_us": (round(TRACE["gateup_us"] + TRACE["down_us"], 2)
+                          if TRACE["sources_sha256"] == sources_digest() else None),
+        "kernel_trace": ({k: TRACE[k] for k in ("gateup_us", "down_us", "step_us", "profile")}
+                         if TRACE["sources_sha256"] == sources_digest() else None),
         "roofline": {"bound": "hbm", "kernel": "gateup", "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": (TRAFFIC["bytes_per_launch"]
                                  if TRAFFIC["sources_sha256"] == sources_digest() else None),
+                     "trace_launch_us": (TRACE["gateup_us"]
+                                         if TRACE["sources_sha256"] == sources_digest() else None),
+                     "trace_frac": (round(float(gu_b.mean()) / (TRACE["gateup_us"] * 1e-6) / 1e9
+                                          / PEAK_HBM_GBS, 4)
+                                    if TRACE["sources_sha256"] == sources_digest() else None),
                      "bytes_per_launch": int(gu_b.mean()),
                      "launch_us": round(gu_ms.mean() * 1e3, 2)},
         "stream_ceiling": ceiling,
