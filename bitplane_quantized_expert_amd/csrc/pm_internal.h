@@ -149,16 +149,16 @@ static_assert(sizeof(KLaunch) <= 4096, "kernel arguments are limited to 4 KiB");
 // k = 4, 5 a workgroup holds fewer steps than waves, so there the "step" part
 // is mostly the latency of one step.
 #ifndef PM_LUT_FIXED_GU
-#define PM_LUT_FIXED_GU 2760, 3630, 2840, 4280, 5800
+#define PM_LUT_FIXED_GU 2720, 2530, 2760, 4180, 5280
 #endif
 #ifndef PM_LUT_STEP_GU
-#define PM_LUT_STEP_GU 57, 81, 173, 303, 1250
+#define PM_LUT_STEP_GU 55, 96, 167, 293, 1390
 #endif
 #ifndef PM_LUT_FIXED_DN
-#define PM_LUT_FIXED_DN 2890, 3080, 2920, 3250, 4710
+#define PM_LUT_FIXED_DN 2880, 2880, 2910, 3250, 3550
 #endif
 #ifndef PM_LUT_STEP_DN
-#define PM_LUT_STEP_DN 49, 91, 178, 460, 2120
+#define PM_LUT_STEP_DN 48, 95, 179, 434, 2910
 #endif
 inline int64_t lut_step_ns(int k, bool down) {
     constexpr int64_t gu[5] = {PM_LUT_STEP_GU}, dn[5] = {PM_LUT_STEP_DN};

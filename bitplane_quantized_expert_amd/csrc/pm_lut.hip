@@ -365,11 +365,11 @@ __device__ inline f32x4 h_cols(const KLaunch& L, int src, int gsl, int slice, in
                  silu_mul(gs.w, us.w)};
 }
 
-// Steps in flight per wave (the ring): two where a step is short (k <= 2),
-// one from k = 3 (with 16 waves, deeper rings cost registers the lookups
-// need; two at k = 4 made the launch a third slower).
+// Steps in flight per wave (the ring): two at k = 1, one from k = 2.  With
+// 16 waves the first rings alone take about 3 us of HBM; a second step at
+// k = 2 made the k = 2 launch 9% slower, at k = 4 a third slower.
 #ifndef PM_RING
-#define PM_RING 2, 2, 1, 1, 1
+#define PM_RING 2, 1, 1, 1, 1
 #endif
 constexpr int kRing[5] = {PM_RING};
 template <int K>
