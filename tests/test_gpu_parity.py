@@ -379,6 +379,45 @@ def test_forward_folded_combine_two_down_slices():
     st.close()
 
 
+WIDE_H = synth.Workload(11, "wideh-e6-h5120-i1024-g128", 5120, 1024, 128, 6, 2, 1, 3, 2.5)
+
+
+def test_forward_five_gate_up_slices():
+    """Gate/up matrices of 5120 columns: five 1024-column slice partials per
+    output, more than the four the down builders load at once, so h is summed
+    over the slices in a loop.  Three tokens top-2, one expert shared; prefixes
+    1..5 (every product a LUT job, the combine folded into the down launch),
+    then the fixed-order combine, then prefixes 1..8 (LUT and direct kernels
+    mixed), all against the oracle."""
+    report("five gate/up slices: h summed over the slices in a loop")
+    wl = WIDE_H
+    e = pm.eshape(wl.hidden, wl.inter, wl.group)
+    st = pm.pm_store_create(e, 1, wl.n_experts)
+    filler = PoolFiller(wl)
+    for i in range(wl.n_experts):
+        filler.fill(st, 0, i)
+    torch.cuda.synchronize()
+    ks8 = synth.uniform_k(wl.seed, wl.cfg, 0, 0, 18 * 3).astype(np.int32)
+    ks5 = (ks8 - 1) % 5 + 1
+    rows = oc.sample_rows(wl.hidden, 20, 7)
+    for case in range(3):
+        ids = np.array([[case % 6, (case + 2) % 6], [(case + 3) % 6, (case + 4) % 6],
+                        [case % 6, (case + 1) % 6]], np.int32)
+        w = np.array([[0.625, 0.375], [0.5, 0.5], [0.875, 0.125]], np.float32)
+        x = np.stack([synth.activation(wl.seed, wl.cfg, 0, t, wl.hidden, step=case)
+                      for t in range(3)])
+        for name, ks, flags in (("lut", ks5, 0), ("lut fixed order", ks5, pm.PM_DETERMINISTIC),
+                                ("mixed", ks8, 0)):
+            k = ks[case * 18:(case + 1) * 18].reshape(3, 2, 3).astype(np.uint8)
+            y = torch.empty((3, wl.hidden), dtype=torch.float32, device="cuda")
+            pm.pm_moe_token_forward(st, 0, ids, w, k, dev(x), y, flags=flags)
+            got = host(y)
+            for t in range(3):
+                want, S = oc.token_layer(wl, 0, ids[t], w[t], k[t], x[t], rows)
+                assert_close(got[t][rows], want, S, f"case {case} token {t} {name} k={k[t].tolist()}")
+    st.close()
+
+
 # ---------------------------------------------------------------- MoE forward
 def single_expert_store(wl, li=None):
     e = pm.eshape(wl.hidden, wl.inter, wl.group)
