@@ -474,21 +474,30 @@ __global__ __launch_bounds__(kBlock) void dequant_batch_kernel(const KDequantBat
         // a row holds a whole number of blocks)
         const size_t b0 = i_begin / group, b1 = (i_end - 1) / group + 1;
         const float* src = lvk + (b0 << k);
+        // the plane words first: they do not depend on the staged tables, so
+        // their loads and the tables' are in flight together
+        const size_t i0 = i_begin + size_t(threadIdx.x) * 8;
+        const bool mine = i0 < i_end;
+        const size_t word = i0 / 32;
+        const int sh = int(i0 % 32);
+        uint32_t pw[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) pw[p] = (mine && p < k) ? pl[size_t(p) * pstride + word] : 0u;
         // deep tables are read where they lie: a tile touches a small part
         // of each, and staging them whole would cost more than it saves
         const bool staged = k <= kDqStagedK;
         if (staged) {
             const size_t n_tab = (b1 - b0) << k;
+#pragma unroll 4
             for (size_t q = threadIdx.x; q < n_tab; q += kBlock) tabs[q] = src[q];
         }
         __syncthreads();
-        const size_t i0 = i_begin + size_t(threadIdx.x) * 8;
-        if (i0 < i_end) {
-            const size_t word = i0 / 32;
-            const int sh = int(i0 % 32);
+        if (mine) {
             uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            for (int p = 0; p < k; ++p) {
-                const uint32_t bits = (pl[size_t(p) * pstride + word] >> sh) & 0xFFu;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                if (p >= k) break;
+                const uint32_t bits = (pw[p] >> sh) & 0xFFu;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) v[j] = (v[j] << 1) | ((bits >> j) & 1u);
             }
