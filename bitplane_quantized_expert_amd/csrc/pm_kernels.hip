@@ -449,34 +449,41 @@ __global__ __launch_bounds__(kBlock) void gemv_fp16_batch_kernel(const KGemv16Ba
     if (lane == kWave - 1) B.y[m][o] = acc;
 }
 
-// Matrix blockIdx.y of the batch in tiles of kDqTile consecutive weights (a
-// workgroup's share of a step, 8 per thread).  The depth-k tables of the
-// blocks a tile touches are one contiguous range of the levels: the
+// Matrix blockIdx.y of the batch in tiles of consecutive weights (a
+// workgroup's share of a step, 8 or 16 per thread).  The depth-k tables of
+// the blocks a tile touches are one contiguous range of the levels: the
 // workgroup stages them in LDS with coalesced loads, then every thread takes
-// its 8 weights' k-bit prefixes from one byte of each plane word, looks their
-// nodes up in LDS (the 8 share a block), rounds them to fp16 (nearest even)
-// and stores 16 bytes.
-constexpr int kDqTile = kBlock * 8;
+// its weights' k-bit prefixes from one byte (8 weights) or half (16) of each
+// plane word, looks their nodes up in LDS (they share a block), rounds them
+// to fp16 (nearest even) and stores 16 bytes per 8 weights.
 constexpr int kDqStagedK = 5;
-__global__ __launch_bounds__(kBlock) void dequant_batch_kernel(const KDequantBatch B) {
-    extern __shared__ float tabs[];
-    const int m = blockIdx.y;
+// Weights per thread: 16 (half of each plane word) where the tables are
+// staged in LDS, 8 (a byte) where they are read from global memory (k > 5):
+// the gathers of 16 weights per thread left too few threads in flight.
+template <int PER>
+constexpr int dq_tile() {
+    return kBlock * PER;
+}
+template <int PER>
+__device__ inline void dequant_tiles(const KDequantBatch& B, int m, float* tabs) {
+    constexpr int kTile = dq_tile<PER>();
     const int cols = B.cols[m], group = B.group[m], k = B.k[m];
     const uint32_t* __restrict__ pl = B.planes[m];
     const float* __restrict__ lvk = B.lvk[m];
     uint16_t* __restrict__ out = B.w[m];
     const size_t pstride = B.pstride[m];
     const size_t n = size_t(B.rows[m]) * cols;
-    const size_t n_tiles = (n + kDqTile - 1) / kDqTile;
+    const size_t n_tiles = (n + kTile - 1) / kTile;
+    const bool staged = k <= kDqStagedK;
     for (size_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-        const size_t i_begin = t * kDqTile, i_end = std::min(n, i_begin + kDqTile);
+        const size_t i_begin = t * kTile, i_end = std::min(n, i_begin + kTile);
         // weight i is in block i / group (blocks row-major over (row, group):
         // a row holds a whole number of blocks)
         const size_t b0 = i_begin / group, b1 = (i_end - 1) / group + 1;
         const float* src = lvk + (b0 << k);
         // the plane words first: they do not depend on the staged tables, so
         // their loads and the tables' are in flight together
-        const size_t i0 = i_begin + size_t(threadIdx.x) * 8;
+        const size_t i0 = i_begin + size_t(threadIdx.x) * PER;
         const bool mine = i0 < i_end;
         const size_t word = i0 / 32;
         const int sh = int(i0 % 32);
@@ -485,7 +492,6 @@ __global__ __launch_bounds__(kBlock) void dequant_batch_kernel(const KDequantBat
         for (int p = 0; p < 8; ++p) pw[p] = (mine && p < k) ? pl[size_t(p) * pstride + word] : 0u;
         // deep tables are read where they lie: a tile touches a small part
         // of each, and staging them whole would cost more than it saves
-        const bool staged = k <= kDqStagedK;
         if (staged) {
             const size_t n_tab = (b1 - b0) << k;
 #pragma unroll 4
@@ -493,34 +499,48 @@ __global__ __launch_bounds__(kBlock) void dequant_batch_kernel(const KDequantBat
         }
         __syncthreads();
         if (mine) {
-            uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            uint32_t v[PER];
+#pragma unroll
+            for (int j = 0; j < PER; ++j) v[j] = 0u;
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
                 if (p >= k) break;
-                const uint32_t bits = (pw[p] >> sh) & 0xFFu;
+                const uint32_t bits = (pw[p] >> sh) & ((1u << PER) - 1u);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) v[j] = (v[j] << 1) | ((bits >> j) & 1u);
+                for (int j = 0; j < PER; ++j) v[j] = (v[j] << 1) | ((bits >> j) & 1u);
             }
+            // the thread's weights lie in one block (groups are multiples of 32)
             const size_t at = (i0 / group - b0) << k;
-            float node[8];
+            float node[PER];
             if (staged) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) node[j] = tabs[at + v[j]];
+                for (int j = 0; j < PER; ++j) node[j] = tabs[at + v[j]];
             } else {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) node[j] = src[at + v[j]];
+                for (int j = 0; j < PER; ++j) node[j] = src[at + v[j]];
             }
-            uint32_t q[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t lo = __half_as_ushort(__float2half_rn(node[2 * j]));
-                const uint32_t hi = __half_as_ushort(__float2half_rn(node[2 * j + 1]));
-                q[j] = lo | (hi << 16);
+            for (int h = 0; h < PER / 8; ++h) {
+                uint32_t q[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t lo = __half_as_ushort(__float2half_rn(node[8 * h + 2 * j]));
+                    const uint32_t hi = __half_as_ushort(__float2half_rn(node[8 * h + 2 * j + 1]));
+                    q[j] = lo | (hi << 16);
+                }
+                *reinterpret_cast<uint4*>(out + i0 + 8 * h) = uint4{q[0], q[1], q[2], q[3]};
             }
-            *reinterpret_cast<uint4*>(out + i0) = uint4{q[0], q[1], q[2], q[3]};
         }
         __syncthreads();
     }
+}
+__global__ __launch_bounds__(kBlock) void dequant_batch_kernel(const KDequantBatch B) {
+    extern __shared__ float tabs[];
+    const int m = blockIdx.y;
+    if (B.k[m] <= kDqStagedK)
+        dequant_tiles<16>(B, m, tabs);
+    else
+        dequant_tiles<8>(B, m, tabs);
 }
 
 }  // namespace
@@ -605,18 +625,19 @@ hipError_t launch_dequant(int rows, int cols, int group, int k, const uint32_t* 
 hipError_t launch_dequant_batch(const KDequantBatch& B, size_t max_elems, hipStream_t st) {
     if (B.n == 0 || max_elems == 0) return hipSuccess;
     // LDS for the tables of the most blocks a tile can touch, at the deepest
-    // staged k (up to 8.1 KiB: group 32 at k = 5)
+    // staged k (up to 16.5 KiB: group 32 at k = 5, 16 weights per thread)
     size_t lds = 0;
     for (int m = 0; m < B.n; ++m)
         if (B.k[m] <= kDqStagedK)
-            lds = std::max(lds, (size_t(kDqTile / B.group[m] + 1) << B.k[m]) * sizeof(float));
+            lds = std::max(lds, (size_t(dq_tile<16>() / B.group[m] + 1) << B.k[m]) * sizeof(float));
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(dequant_batch_kernel),
         hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
     if (attr != hipSuccess) return attr;
     // a workgroup per tile: the hardware starts the next as one ends, which
     // hides the latency of a tile's loads better than a loop over tiles
-    const unsigned bx = unsigned(std::min<size_t>((max_elems + kDqTile - 1) / kDqTile, 1u << 20));
+    const unsigned bx =
+        unsigned(std::min<size_t>((max_elems + dq_tile<8>() - 1) / dq_tile<8>(), 1u << 20));
     hipLaunchKernelGGL(dequant_batch_kernel, dim3(bx, unsigned(B.n)), dim3(kBlock), lds, st, B);
     return hipGetLastError();
 }
