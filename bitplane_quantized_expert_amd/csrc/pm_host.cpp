@@ -1326,7 +1326,7 @@ extern "C" pm_status pm_store_set_profile_events(pm_store* s, void* const* event
 
 // ---- LUT path: launch descriptions travel as kernel arguments.
 // Target number of LUT workgroups per launch: one per compute unit (each
-// holds 132 KiB of LDS).
+// holds its 128 KiB activation table in LDS).
 static int lut_wg_target() {
     static int n = 0;
     if (n == 0) {
