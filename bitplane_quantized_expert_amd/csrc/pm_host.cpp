@@ -2210,7 +2210,12 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
     }
     if (s->profiling && !gu_single) HIP_TRY(hipEventRecord(s->prof[1], compute));
     if (!dir_dn.empty() || any_tiles(t_dn)) {
-        HIP_TRY(launch_swiglu(duses, n_uses, P, g.inter, compute));
+        // h of the direct and tiled down products, where the direct gate/up
+        // kernel has not formed it
+        bool swiglu = false;
+        for (int u = 0; u < n_uses && !swiglu; ++u)
+            swiglu = uses[u].direct[2] != 0 && !h_by_gateup(uses[u]);
+        if (swiglu) HIP_TRY(launch_swiglu(duses, n_uses, P, g.inter, compute));
         if (!dir_dn.empty())
             HIP_TRY(launch_direct_down(g, ddir + d_gu0 + d_gu1, int(dir_dn.size()), duses, dlist,
                                        P, compute));

@@ -50,6 +50,12 @@ struct Use {
     int32_t direct[3];
 };
 
+// Whether the direct gate/up kernel forms h = SiLU(g) * u of a use: its gate
+// and up rows both run there, and a direct or tiled down product reads h.
+__host__ __device__ inline bool h_by_gateup(const Use& u) {
+    return u.direct[0] == 1 && u.direct[1] == 1 && u.direct[2] != 0;
+}
+
 // LUT path: one matrix of one use.  Row r's partial sum over column slice s
 // goes to out[s * out_stride + r].
 struct LutJob {

@@ -198,7 +198,10 @@ __global__ __launch_bounds__(kBlock) void direct_gateup_kernel(Geom g,
     const int W = g.hidden / 32;
     const size_t nb = size_t(g.inter) * (g.hidden / g.group);
     // one (use, matrix) per step; fields read from memory by index, so no
-    // copy of the use record is indexed in registers
+    // copy of the use record is indexed in registers.  A use whose gate and
+    // up rows both run here (gate first) also gets h = SiLU(g) * u of row o
+    // (a direct matrix has one slice, so this is the SwiGLU kernel's value).
+    float acc_gate = 0.f;
     for (int qm = 0; qm < 2 * it.nuse; ++qm) {
         const int m = qm & 1;
         const int u = list[it.use0 + (qm >> 1)];
@@ -210,7 +213,13 @@ __global__ __launch_bounds__(kBlock) void direct_gateup_kernel(Geom g,
                             it.levels + g.level_off[m] + level_offset(nb, k), k, o, W,
                             g.group / 32, xt, (lds_f32*)tabs[threadIdx.x / kWave], lane);
         acc = wave_sum(acc);
-        if (lane == kWave - 1) P.gu[(size_t(u) * 2 + m) * P.gu_smax * g.inter + o] = acc;
+        if (lane == kWave - 1) {
+            P.gu[(size_t(u) * 2 + m) * P.gu_smax * g.inter + o] = acc;
+            if (m == 0)
+                acc_gate = acc;
+            else if (h_by_gateup(*up))
+                P.h[size_t(u) * g.inter + o] = silu_mul(acc_gate, acc);
+        }
     }
 }
 
@@ -228,7 +237,8 @@ __global__ __launch_bounds__(kBlock) void swiglu_kernel(const Use* __restrict__ 
     if (i >= size_t(n_uses) * inter) return;
     const int u = int(i / inter), c = int(i % inter);
     const Use us = uses[u];
-    if (!us.direct[2]) return;                   // h of the direct and tile paths
+    // h of the direct and tile paths, unless the direct gate/up kernel formed it
+    if (!us.direct[2] || h_by_gateup(us)) return;
     P.h[i] = silu_mul(gu_sum(P, us, u, 0, inter, c), gu_sum(P, us, u, 1, inter, c));
 }
 
