@@ -2039,10 +2039,10 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         sort_jobs(js);
         pack_launches(js, gu_proto, L_gu[grp]);
     }
-    // The routing-weighted combine folds into the down launches when every
-    // down product runs on the LUT path: each row sum is added, times its
-    // use's weight, into y with a float atomic (y cleared by the first gate/up
-    // launch).  The top-k terms of an output then add up in the order they
+    // The routing-weighted combine folds into the down launches (LUT and
+    // direct) when no down product runs in a matrix-core tile: each row sum
+    // is added, times its use's weight, into y with a float atomic (y cleared
+    // by the first gate/up launch).  The top-k terms of an output then add up in the order they
     // arrive; PM_DETERMINISTIC keeps the separate combine, which adds them in
     // use order.  y may not overlap x (the clearing would race the reads).
     const size_t xy_bytes = sizeof(float) * size_t(n_tokens) * g.hidden;
@@ -2050,13 +2050,23 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
                               reinterpret_cast<uintptr_t>(d_x) ||
                           reinterpret_cast<uintptr_t>(d_x) + xy_bytes <=
                               reinterpret_cast<uintptr_t>(d_y);
-    const bool fold = !(flags & PM_DETERMINISTIC) && dir_dn.empty() && !any_tiles(t_dn) &&
-                      (!L_gu[0].empty() || !L_gu[1].empty()) && xy_apart &&
-                      size_t(n_tokens) * g.hidden < (size_t(1) << 31);
+    const bool lut_gu = !L_gu[0].empty() || !L_gu[1].empty();
+    const bool dir_gu_any = !dir_gu[0].empty() || !dir_gu[1].empty();
+    const bool fold = !(flags & PM_DETERMINISTIC) && !any_tiles(t_dn) && (lut_gu || dir_gu_any) &&
+                      xy_apart && size_t(n_tokens) * g.hidden < (size_t(1) << 31);
+    // the first gate/up launch clears y: a LUT launch if there is one, else
+    // the first direct gate/up launch
+    float* dir_zero = nullptr;
+    int dir_n_zero = 0;
     if (fold) {
-        KLaunch& first = !L_gu[0].empty() ? L_gu[0].front() : L_gu[1].front();
-        first.zero = d_y;
-        first.n_zero = n_tokens * g.hidden;
+        if (lut_gu) {
+            KLaunch& first = !L_gu[0].empty() ? L_gu[0].front() : L_gu[1].front();
+            first.zero = d_y;
+            first.n_zero = n_tokens * g.hidden;
+        } else {
+            dir_zero = d_y;
+            dir_n_zero = n_tokens * g.hidden;
+        }
         dn_proto.fold = 1;
         dn_proto.out_stride = 0;
     }
@@ -2188,7 +2198,9 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         else
             HIP_TRY(launch_lut(L, false, compute));
     }
-    if (d_gu0) HIP_TRY(launch_direct_gateup(g, ddir, int(d_gu0), duses, dlist, d_x, P, compute));
+    if (d_gu0)
+        HIP_TRY(launch_direct_gateup(g, ddir, int(d_gu0), duses, dlist, d_x, P, compute, dir_zero,
+                                     dir_n_zero));
     if (any_tiles(t_gu[0])) {
         st = tiles_of(t_gu[0], off_gu[0], 0);
         if (st) return st;
@@ -2202,7 +2214,8 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         for (const KLaunch& L : L_gu[1]) HIP_TRY(launch_lut(L, false, compute));
         if (d_gu1)
             HIP_TRY(launch_direct_gateup(g, ddir + d_gu0, int(d_gu1), duses, dlist, d_x, P,
-                                         compute));
+                                         compute, d_gu0 ? nullptr : dir_zero,
+                                         d_gu0 ? 0 : dir_n_zero));
         if (any_tiles(t_gu[1])) {
             st = tiles_of(t_gu[1], off_gu[1], 0);
             if (st) return st;
@@ -2218,7 +2231,7 @@ extern "C" pm_status pm_moe_token_forward(pm_store* s, int layer, int n_tokens, 
         if (swiglu) HIP_TRY(launch_swiglu(duses, n_uses, P, g.inter, compute));
         if (!dir_dn.empty())
             HIP_TRY(launch_direct_down(g, ddir + d_gu0 + d_gu1, int(dir_dn.size()), duses, dlist,
-                                       P, compute));
+                                       P, compute, fold ? d_y : nullptr));
         if (any_tiles(t_dn)) {
             st = tiles_of(t_dn, off_dn, 1);
             if (st) return st;

@@ -237,12 +237,17 @@ hipError_t launch_sum_slices(const float* part, int slices, int rows, float* y, 
 
 // Direct path (any prefix, any shape, shared experts read once per call):
 // over `n_items` items, rows_per_block rows per block.  Writes slice 0 of the
-// partials of every (use, matrix) marked direct.
+// partials of every (use, matrix) marked direct.  The gate/up launch also
+// clears n_zero floats at `zero` (the output a folded down stage adds into);
+// with y_fold the down launch adds w * row sum into y_fold[tok] (device-scope
+// float atomics) instead of writing its partials.
 hipError_t launch_direct_gateup(const Geom& g, const Item* items, int n_items,
                                 const Use* uses, const int32_t* list, const float* x,
-                                Partials P, hipStream_t st);
+                                Partials P, hipStream_t st, float* zero = nullptr,
+                                int n_zero = 0);
 hipError_t launch_direct_down(const Geom& g, const Item* items, int n_items, const Use* uses,
-                              const int32_t* list, Partials P, hipStream_t st);
+                              const int32_t* list, Partials P, hipStream_t st,
+                              float* y_fold = nullptr);
 // h of every use marked direct for down, from the gate/up partials.
 hipError_t launch_swiglu(const Use* uses, int n_uses, Partials P, int inter, hipStream_t st);
 // y[t][o] = sum_j w[t][j] * sum_s Y[t*top_k + j][s][o], slots then slices in order.

@@ -189,8 +189,15 @@ __global__ __launch_bounds__(kBlock) void direct_gateup_kernel(Geom g,
                                                                const Use* __restrict__ uses,
                                                                const int32_t* __restrict__ list,
                                                                const float* __restrict__ x,
-                                                               Partials P) {
+                                                               Partials P,
+                                                               float* __restrict__ zero,
+                                                               int n_zero) {
     __shared__ float tabs[kRowsPerBlock][kRunTabFloatsMax];
+    // clear the layer output a folded down stage adds into (it runs after
+    // this launch on the same stream)
+    for (int i = int(blockIdx.x) * kBlock + int(threadIdx.x); i < n_zero;
+         i += int(gridDim.x) * kBlock)
+        zero[i] = 0.f;
     const Item it = items[blockIdx.x / bpi];
     const int lane = threadIdx.x % kWave;
     const int o = (blockIdx.x % bpi) * kRowsPerBlock + threadIdx.x / kWave;
@@ -246,7 +253,7 @@ __global__ __launch_bounds__(kBlock) void direct_down_kernel(Geom g, const Item*
                                                              int bpi,
                                                              const Use* __restrict__ uses,
                                                              const int32_t* __restrict__ list,
-                                                             Partials P) {
+                                                             Partials P, float* __restrict__ yf) {
     __shared__ float tabs[kRowsPerBlock][kRunTabFloatsMax];
     const Item it = items[blockIdx.x / bpi];
     const int lane = threadIdx.x % kWave;
@@ -264,7 +271,13 @@ __global__ __launch_bounds__(kBlock) void direct_down_kernel(Geom g, const Item*
                             g.group / 32, P.h + size_t(u) * g.inter, (lds_f32*)tabs[threadIdx.x / kWave],
                             lane);
         acc = wave_sum(acc);
-        if (lane == kWave - 1) P.y[size_t(u) * P.dn_smax * g.hidden + o] = acc;
+        if (lane == kWave - 1) {
+            if (yf)    // the routing-weighted combine folded in: y[tok][o] += w * row sum
+                __hip_atomic_fetch_add(yf + size_t(us.tok) * g.hidden + o, us.w * acc,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                P.y[size_t(u) * P.dn_smax * g.hidden + o] = acc;
+        }
     }
 }
 
@@ -565,20 +578,20 @@ hipError_t launch_gemv(int rows, int cols, int group, int k, const uint32_t* pla
 
 hipError_t launch_direct_gateup(const Geom& g, const Item* items, int n_items, const Use* uses,
                                 const int32_t* list, const float* x, Partials P,
-                                hipStream_t st) {
+                                hipStream_t st, float* zero, int n_zero) {
     if (n_items == 0) return hipSuccess;
     const int bpi = (g.inter + kRowsPerBlock - 1) / kRowsPerBlock;
     hipLaunchKernelGGL(direct_gateup_kernel, dim3(n_items * bpi), dim3(kBlock), 0, st, g, items,
-                       bpi, uses, list, x, P);
+                       bpi, uses, list, x, P, zero, n_zero);
     return hipGetLastError();
 }
 
 hipError_t launch_direct_down(const Geom& g, const Item* items, int n_items, const Use* uses,
-                              const int32_t* list, Partials P, hipStream_t st) {
+                              const int32_t* list, Partials P, hipStream_t st, float* y_fold) {
     if (n_items == 0) return hipSuccess;
     const int bpi = (g.hidden + kRowsPerBlock - 1) / kRowsPerBlock;
     hipLaunchKernelGGL(direct_down_kernel, dim3(n_items * bpi), dim3(kBlock), 0, st, g, items,
-                       bpi, uses, list, P);
+                       bpi, uses, list, P, y_fold);
     return hipGetLastError();
 }
 
